@@ -1,0 +1,258 @@
+/*
+ * quip.h -- C ABI of libquip, the QuIP-family layer-quantization pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The pass: proxy Hessian H = X^T X / N, damping, incoherence processing
+ * (random-sign Hadamard transform or Kronecker product of two orthogonal
+ * factors on each side), LDL factorization H = (I+U) D (I+U)^T, per-row or
+ * global quantizer scale, LDLQ / BlockLDLQ rounding onto a scalar grid or an
+ * E8-lattice codebook, post-processing and the proxy loss.
+ *
+ * Sources, cited by title and section:
+ *   [QuIP]  "QuIP: 2-Bit Quantization of Large Language Models With
+ *           Guarantees" (Chee, Cai, Kuleshov, De Sa, 2023).
+ *   [QuIP#] "QuIP#: Even Better LLM Quantization with Hadamard Incoherence
+ *           and Lattice Codebooks" (Tseng et al., 2024), abstract.
+ *   [QTIP]  "QTIP: Quantization with Trellises and Incoherence Processing",
+ *           summary page, "Builds on" (BlockLDLQ).
+ *
+ * Conventions shared by every entry point:
+ *   - Array arguments are DEVICE pointers unless the name says host. Matrices
+ *     are float32, row-major, with an explicit leading dimension (elements)
+ *     that must be >= the number of columns.
+ *   - The caller owns all memory: inputs, outputs and workspace. Workspace
+ *     sizes come from the quip_*_workspace queries; a workspace must be 256-byte
+ *     aligned. The library allocates nothing and keeps no global mutable state;
+ *     calls on different streams are independent.
+ *   - Every call only enqueues work on `stream` (asynchronous) and returns at
+ *     once. Argument and shape errors are detected on the host before any
+ *     launch, and then nothing is enqueued. A failure found on the device (a
+ *     non-positive pivot) is written to a caller-provided int32 device word
+ *     following LAPACK's `info` convention.
+ *   - No C++ exception crosses the ABI. quip_status_string() names a status;
+ *     quip_last_error() gives the calling thread's last message.
+ */
+#ifndef QUIP_H
+#define QUIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QUIP_OK = 0,
+  QUIP_ERR_ARG = 1,         /* null pointer, bad leading dimension, bad enum */
+  QUIP_ERR_SHAPE = 2,       /* sizes that the operation does not accept */
+  QUIP_ERR_NOT_PD = 3,      /* reported through `info`, never returned by a launch */
+  QUIP_ERR_HIP = 4,         /* a HIP runtime call failed */
+  QUIP_ERR_UNSUPPORTED = 5, /* a valid request this build does not implement */
+  QUIP_ERR_WORKSPACE = 6    /* workspace missing, too small or misaligned */
+} quip_status;
+
+typedef enum {
+  QUIP_LEFT = 0,  /* transform mixes rows:    out = Q A       */
+  QUIP_RIGHT = 1  /* transform mixes columns: out = A Q^T     */
+} quip_side;
+
+typedef enum {
+  QUIP_Q_UNIFORM = 0, /* 2^bits-level midrise grid, one scale per row */
+  QUIP_Q_E8 = 1       /* E8 codebook of 65536 points, g = 8, one global scale */
+} quip_qkind;
+
+typedef enum {
+  QUIP_SCALE_COMPUTE = 0, /* search the scale(s) and write them to `scales` */
+  QUIP_SCALE_GIVEN = 1    /* read the scale(s) from `scales` */
+} quip_scale_mode;
+
+typedef struct {
+  int32_t kind;       /* quip_qkind */
+  int32_t bits;       /* QUIP_Q_UNIFORM: 1..8 (2^bits levels); QUIP_Q_E8: must be 2 */
+  int32_t n_cand;     /* number of scale candidates searched, 2..64 (32 by default) */
+  int32_t scale_mode; /* quip_scale_mode */
+} quip_quantizer;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t quip_version(void);
+/* Static string naming a status. */
+const char* quip_status_string(quip_status st);
+/* The calling thread's last error message ("" after a successful call). */
+const char* quip_last_error(void);
+
+/*
+ * quip_hessian -- H (+)= X^T X   ([QuIP] "Adaptive Rounding Step": the proxy
+ * Hessian is the second moment of the layer inputs).
+ *   X: N x n calibration rows (one input vector per row), leading dim ldx.
+ *   H: n x n output, leading dim ldh, written in full symmetric storage.
+ *   accumulate: 0 overwrites H with X^T X, 1 adds X^T X to H (stream X in
+ *   chunks of rows and call quip_hessian_finalize once with the total N).
+ *   N may be 0 (H is zeroed, or left as is when accumulating).
+ * Errors: QUIP_ERR_ARG (null pointer, ldx < n, ldh < n, n <= 0, N < 0).
+ */
+quip_status quip_hessian(const float* X, int64_t N, int64_t n, int64_t ldx, float* H,
+                         int64_t ldh, int accumulate, hipStream_t stream);
+
+/*
+ * quip_hessian_finalize -- H <- H / N_total + alpha * mean(diag(H / N_total)) * I
+ *   ([QuIP] "Experiments / Methods": damping for numerical stability).
+ *   In place on the n x n matrix H (leading dim ldh). alpha >= 0.
+ *   ws: device workspace of at least 256 bytes (holds the trace).
+ * Errors: QUIP_ERR_ARG (null H, N_total <= 0, alpha < 0 or not finite),
+ *   QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_rht / quip_rht_inv -- randomized Hadamard transform ([QuIP#] abstract;
+ * the orthogonal multiplications of [QuIP] "Incoherence Processing").
+ *   With d = rows (LEFT) or cols (RIGHT), S = diag(signs) and
+ *   Q = H_d S / sqrt(d), H_d the natural-order Sylvester Hadamard matrix:
+ *     quip_rht:     LEFT out = Q A,     RIGHT out = A Q^T
+ *     quip_rht_inv: LEFT out = Q^T A,   RIGHT out = A Q
+ *   A, out: rows x cols, same leading dim ld; out == A (in place) allowed,
+ *   other overlap is not. signs: d floats, each +1 or -1, 16-byte aligned.
+ * Errors: QUIP_ERR_ARG (null pointer, ld < cols, bad side, misaligned signs);
+ *   QUIP_ERR_SHAPE (d not a power of two, or d > 16384, or d < 2).
+ */
+quip_status quip_rht(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                     const float* signs, quip_side side, hipStream_t stream);
+quip_status quip_rht_inv(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                         const float* signs, quip_side side, hipStream_t stream);
+
+/*
+ * quip_rht2 -- both sides at once: out = Q_L A Q_R^T (signs_left: rows floats,
+ * signs_right: cols floats), same result as quip_rht LEFT after quip_rht RIGHT.
+ * quip_rht2_inv gives Q_L^T A Q_R. out == A allowed.
+ * Errors: as quip_rht for each side.
+ */
+quip_status quip_rht2(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                      const float* signs_left, const float* signs_right, hipStream_t stream);
+quip_status quip_rht2_inv(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                          const float* signs_left, const float* signs_right, hipStream_t stream);
+
+/*
+ * quip_kron_orth / quip_kron_orth_inv -- multiplication by Q = F1 (x) F2,
+ * the Kronecker product of two orthogonal factors ([QuIP] "Introduction" and
+ * "Conclusion": pre- and post-processing by a Kronecker product of random
+ * orthogonal matrices). Row-major index i = a*q + b.
+ *     quip_kron_orth:     LEFT out = Q A,     RIGHT out = A Q^T
+ *     quip_kron_orth_inv: LEFT out = Q^T A,   RIGHT out = A Q
+ *   F1: p x p row-major (device), F2: q x q row-major (device); p*q must equal
+ *   rows (LEFT) or cols (RIGHT). A, out: rows x cols, leading dim ld; out may
+ *   equal A. ws: device workspace of quip_kron_orth_workspace() bytes.
+ * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (p*q mismatch, p or q < 1),
+ *   QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_kron_orth_workspace(int64_t rows, int64_t cols, size_t* bytes);
+quip_status quip_kron_orth(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                           const float* F1, int64_t p, const float* F2, int64_t q, quip_side side,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+quip_status quip_kron_orth_inv(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                               const float* F1, int64_t p, const float* F2, int64_t q,
+                               quip_side side, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_ldl -- H = (I + U) D (I + U)^T with U strictly upper triangular
+ * (g = 1) or strictly block-upper with g x g blocks (g = 8), D diagonal or
+ * block diagonal. The factor LDLQ feeds back through ([QuIP] "Adaptive
+ * Rounding Step"; block form for BlockLDLQ, [QTIP] "Builds on").
+ *   H: n x n symmetric, leading dim ldh; only the upper triangle is read.
+ *   U: n x n output (leading dim n); every entry on or below the diagonal
+ *      (on or below the diagonal blocks for g = 8) is written as 0.
+ *   D: output, n floats (g = 1) or n/8 row-major 8x8 blocks (g = 8).
+ *   info: one int32 device word; 0 on success, else 1 + the index of the
+ *      first pivot (first column of the first block) found not positive
+ *      definite, processing from the last column down; U and D are then
+ *      undefined.
+ *   ws: device workspace of quip_ldl_workspace() bytes.
+ * Errors: QUIP_ERR_ARG (null pointer, ldh < n, g not 1 or 8),
+ *   QUIP_ERR_SHAPE (n <= 0, n % g != 0), QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_ldl_workspace(int64_t n, int64_t g, size_t* bytes);
+quip_status quip_ldl(const float* H, int64_t n, int64_t ldh, int64_t g, float* U, float* D,
+                     int32_t* info, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_scales -- the quantizer scale(s) without rounding.
+ *   UNIFORM: scales[r] for every row r of W: the step among n_cand candidates
+ *     s_c = s_max * 16^(-c/(n_cand-1)), s_max = max_j |W_rj| / ((L-1)/2),
+ *     minimizing the row's nearest-rounding squared error (ties to the smaller
+ *     c; an all-zero row gets 1).
+ *   E8: scales[0] = global scale among 0.5 * 4^(c/(n_cand-1)) minimizing the
+ *     nearest-codeword squared error of all 8-vectors of the row-normalized
+ *     W; scales[1 + r] = root-mean-square of row r (1 for an all-zero row).
+ *   W: m x n, leading dim ldw. codebook: 65536 x 8 device floats for E8,
+ *   else NULL. mse_out: optional (may be NULL) device output of the squared
+ *   error per candidate: m x n_cand (UNIFORM) or n_cand (E8), float64 for E8,
+ *   float32 for UNIFORM.
+ * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (n % 8 != 0 for E8), QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_scales_workspace(int64_t m, int64_t n, const quip_quantizer* q, size_t* bytes);
+quip_status quip_scales(const float* W, int64_t m, int64_t n, int64_t ldw, const quip_quantizer* q,
+                        float* scales, void* mse_out, const float* codebook, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_ldlq -- LDLQ / BlockLDLQ rounding: columns (groups of g columns) in
+ * natural order, W^_K = Q(W_K + (W - W^)_{:,<K} U_{<K,K}) ([QuIP] "Adaptive
+ * Rounding Step" and "Conclusion": rounding with linear feedback through the
+ * LDL factor; [QTIP] "Builds on": BlockLDLQ). Lazily blocked: B columns are
+ * swept at a time and the rest of the matrix is updated once per block.
+ *   W: m x n incoherence-processed weights, leading dim ldw (read only).
+ *   U, D: from quip_ldl with the same g (D is read only for g = 8; pass it
+ *     anyway for g = 1).
+ *   B: lazy block size, a multiple of g, 8..4096.
+ *   q: quantizer (UNIFORM needs g = 1; E8 needs g = 8).
+ *   scales: as quip_scales; written when q->scale_mode is COMPUTE, read when
+ *     GIVEN (E8: the caller supplies the global scale and the row RMS).
+ *   codes: UNIFORM: uint8 m x n (row-major, leading dim n), the grid index
+ *     0..2^bits-1 of every weight. E8: uint16 m x (n/8), the codebook index
+ *     of every 8-vector.
+ *   What: optional (may be NULL) m x n output (leading dim n) of the
+ *     quantized weights in the same (incoherent) domain as W; for E8 rows are
+ *     scaled back by their RMS.
+ *   codebook: 65536 x 8 device floats for E8 (quip_e8_codebook order), else
+ *     NULL.
+ *   ws: device workspace of quip_ldlq_workspace() bytes.
+ * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (n % g, B % g, B range),
+ *   QUIP_ERR_WORKSPACE, QUIP_ERR_UNSUPPORTED (bits > 8).
+ */
+quip_status quip_ldlq_workspace(int64_t m, int64_t n, int64_t g, int64_t B,
+                                const quip_quantizer* q, size_t* bytes);
+quip_status quip_ldlq(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
+                      const float* D, int64_t g, int64_t B, const quip_quantizer* q,
+                      float* scales, void* codes, float* What, const float* codebook, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_proxy_loss -- loss = tr((W^ - W) H (W^ - W)^T) ([QuIP] "Introduction":
+ * the proxy objective), accumulated in float64.
+ *   W, What: m x n, both with leading dim ld. H: n x n, leading dim ldh.
+ *   loss_dev: one device double, overwritten.
+ *   ws: device workspace of quip_proxy_loss_workspace() bytes.
+ * Errors: QUIP_ERR_ARG, QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_proxy_loss_workspace(int64_t m, int64_t n, size_t* bytes);
+quip_status quip_proxy_loss(const float* W, const float* What, int64_t m, int64_t n, int64_t ld,
+                            const float* H, int64_t ldh, double* loss_dev, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_e8_codebook -- fills HOST memory with the 65536 smallest-norm points of
+ * the E8 lattice (D8 together with D8 + 1/2) ordered by squared norm, then by
+ * coordinates ascending with the first coordinate most significant; 65536 x 8
+ * floats, row-major ([QuIP#] abstract: E8-lattice codebooks).
+ * Errors: QUIP_ERR_ARG (null pointer).
+ */
+quip_status quip_e8_codebook(float* host_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUIP_H */

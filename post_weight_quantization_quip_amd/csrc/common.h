@@ -1,0 +1,140 @@
+// Internal helpers shared by the libquip translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "quip.h"
+
+namespace quip {
+
+// ---------------------------------------------------------------- errors
+
+void set_error(const std::string& msg);
+void clear_error();
+const char* last_error_cstr();
+
+struct Status {
+  quip_status st;
+  Status(quip_status s = QUIP_OK) : st(s) {}
+  operator quip_status() const { return st; }
+  bool ok() const { return st == QUIP_OK; }
+};
+
+quip_status fail(quip_status st, const std::string& msg);
+
+#define QUIP_HIP(call)                                                              \
+  do {                                                                              \
+    hipError_t e_ = (call);                                                         \
+    if (e_ != hipSuccess)                                                           \
+      return ::quip::fail(QUIP_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+#define QUIP_TRY(expr)                   \
+  do {                                   \
+    quip_status s_ = (expr);             \
+    if (s_ != QUIP_OK) return s_;        \
+  } while (0)
+
+// Checks the last launch on this thread.
+quip_status launch_check(const char* what);
+
+// ---------------------------------------------------------------- workspace
+
+// Carves 256-byte aligned sub-buffers out of a caller workspace. With a null
+// base it only measures.
+struct Carver {
+  char* base;
+  size_t cap;
+  size_t used = 0;
+  Carver(void* b, size_t c) : base(static_cast<char*>(b)), cap(c) {}
+  template <typename T>
+  T* take(size_t count) {
+    size_t off = (used + 255) & ~size_t(255);
+    used = off + count * sizeof(T);
+    return base ? reinterpret_cast<T*>(base + off) : nullptr;
+  }
+  bool fits() const { return used <= cap; }
+};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- device helpers
+
+// Work-group ids are dealt round-robin to the 8 XCDs (each with its own L2).
+// Remap the hardware id so that consecutive logical tiles land on the same XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int nx = 8;
+  int per = total / nx, rem = total % nx;
+  int x = bid % nx, local = bid / nx;
+  int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return start + local;
+}
+
+// ---------------------------------------------------------------- GEMM (gemm.hip)
+
+enum GemmEpi {
+  EPI_STORE = 0,  // C_out = alpha * op(A) op(B) + beta * C_in
+  EPI_DOT = 1,    // *dot += sum(alpha * op(A) op(B) .* E)  (float64 accumulate)
+  EPI_SPLIT = 2   // like STORE, columns >= split go to C2 (ldc2) at column - split
+};
+
+struct GemmArgs {
+  int64_t M = 0, N = 0, K = 0;
+  const float* A = nullptr;  // !transA: A[m*lda + k]; transA: A[k*lda + m]
+  int64_t lda = 0, strideA = 0;
+  const float* B = nullptr;  // !transB: B[k*ldb + n]; transB: B[n*ldb + k]
+  int64_t ldb = 0, strideB = 0;
+  float* C = nullptr;
+  int64_t ldc = 0, strideC = 0;
+  const float* Cin = nullptr;  // beta source (defaults to C)
+  int64_t ldcin = 0, strideCin = 0;
+  float alpha = 1.f, beta = 0.f;
+  int batch = 1;
+  bool transA = false, transB = false;
+  bool upper_tiles = false;  // only output tiles with tile_row <= tile_col (M == N)
+  bool mirror = false;       // upper_tiles: also write the transpose below the diagonal
+  int epi = EPI_STORE;
+  const float* E = nullptr;  // EPI_DOT operand, E[m*lde + n]
+  int64_t lde = 0;
+  double* dot = nullptr;
+  int64_t split = 0;  // EPI_SPLIT
+  float* C2 = nullptr;
+  int64_t ldc2 = 0;
+};
+
+quip_status gemm(const GemmArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- misc kernels (misc.hip)
+
+quip_status fill_f32(float* p, int64_t count, float v, hipStream_t stream);
+quip_status fill_matrix(float* p, int64_t rows, int64_t cols, int64_t ld, float v,
+                        hipStream_t stream);
+quip_status sub_matrix(const float* a, const float* b, float* out, int64_t rows, int64_t cols,
+                       int64_t lda, int64_t ldb, int64_t ldo, hipStream_t stream);  // out = a - b
+quip_status fill_f64(double* p, int64_t count, double v, hipStream_t stream);
+quip_status copy_matrix(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows,
+                        int64_t cols, hipStream_t stream);
+
+// ---------------------------------------------------------------- RHT (rht.hip)
+
+quip_status rht_rows(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                     const float* signs, bool inverse, hipStream_t stream);
+quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                     const float* signs, bool inverse, hipStream_t stream);
+
+// ---------------------------------------------------------------- E8 (e8.cpp)
+
+void e8_build_codebook(float* host_out);
+
+}  // namespace quip

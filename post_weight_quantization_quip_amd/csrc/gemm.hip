@@ -1,0 +1,266 @@
+// fp32 GEMM on the CDNA4 matrix cores: C = alpha * op(A) op(B) + beta * C_in.
+//
+// Used for every dense contraction of the pass: the Hessian X^T X (upper
+// tiles only, mirrored), the LDL panel products and trailing updates (upper
+// tiles only), the lazy LDLQ trailing update W[:, j+B:] += E U, the two small
+// contractions of a Kronecker-factor multiply, and the proxy loss (with a
+// fused dot-product epilogue, so E H is never written).
+//
+// Tiling: one work-group of 4 waves computes a BM x BN tile (BM, BN in
+// {64, 128}); each wave owns a (BM/2) x (BN/2) sub-tile made of 32x32 blocks
+// computed with v_mfma_f32_32x32x2f32 (wave64: A operand lane = i + 32k,
+// B operand lane = j + 32k, D element (i, j) in lane j + 32*((i/4)%2),
+// register (i%4) + 4*(i/8)). K advances 16 at a time through double-buffered
+// LDS tiles stored K-major, so every operand read is 32 consecutive floats.
+// Work-group ids are remapped so that neighbouring tiles share an XCD's L2.
+#include "common.h"
+
+namespace quip {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 16;
+constexpr int PAD = 4;
+
+__device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t col, int64_t ld,
+                                        int64_t rows, int64_t cols, bool vec) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (row >= rows) return v;
+  const float* p = base + row * ld + col;
+  if (vec && col + 3 < cols) {
+    v = *reinterpret_cast<const float4*>(p);
+  } else {
+    if (col + 0 < cols) v.x = p[0];
+    if (col + 1 < cols) v.y = p[1];
+    if (col + 2 < cols) v.z = p[2];
+    if (col + 3 < cols) v.w = p[3];
+  }
+  return v;
+}
+
+template <int BM, int BN, bool TA, bool TB, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n,
+                                                      int total, bool vecA, bool vecB) {
+  __shared__ __align__(16) float As[2][BK][BM + PAD];
+  __shared__ __align__(16) float Bs[2][BK][BN + PAD];
+
+  constexpr int WBM = BM / 64;  // 32x32 blocks per wave along M
+  constexpr int WBN = BN / 64;
+  constexpr int LA = BM * BK / 4 / 256;  // float4 loads per thread
+  constexpr int LB = BN * BK / 4 / 256;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile coordinates
+  int bid = xcd_remap(blockIdx.x, total);
+  int tm, tn;
+  if (a.upper_tiles) {
+    int rem = bid, r = 0;
+    while (rem >= tiles_m - r) {
+      rem -= tiles_m - r;
+      ++r;
+    }
+    tm = r;
+    tn = r + rem;
+  } else {
+    const int G = 8;
+    int per_group = G * tiles_n;
+    int group = bid / per_group;
+    int first = group * G;
+    int gsize = min(tiles_m - first, G);
+    int in = bid % per_group;
+    tm = first + in % gsize;
+    tn = in / gsize;
+  }
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t bz = blockIdx.y;
+
+  const float* A = a.A + bz * a.strideA;
+  const float* B = a.B + bz * a.strideB;
+
+  float4 ra[LA], rb[LB];
+
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      int idx = tid + 256 * i;
+      if (TA) {
+        int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
+        ra[i] = load4(A, k0 + k, m0 + m4, a.lda, a.K, a.M, vecA);
+      } else {
+        int m = idx / 4, k4 = (idx % 4) * 4;
+        ra[i] = load4(A, m0 + m, k0 + k4, a.lda, a.M, a.K, vecA);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      int idx = tid + 256 * i;
+      if (!TB) {
+        int k = idx / (BN / 4), n4 = (idx % (BN / 4)) * 4;
+        rb[i] = load4(B, k0 + k, n0 + n4, a.ldb, a.K, a.N, vecB);
+      } else {
+        int n = idx / 4, k4 = (idx % 4) * 4;
+        rb[i] = load4(B, n0 + n, k0 + k4, a.ldb, a.N, a.K, vecB);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      int idx = tid + 256 * i;
+      if (TA) {
+        int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
+        *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[i];
+      } else {
+        int m = idx / 4, k4 = (idx % 4) * 4;
+        As[buf][k4 + 0][m] = ra[i].x;
+        As[buf][k4 + 1][m] = ra[i].y;
+        As[buf][k4 + 2][m] = ra[i].z;
+        As[buf][k4 + 3][m] = ra[i].w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      int idx = tid + 256 * i;
+      if (!TB) {
+        int k = idx / (BN / 4), n4 = (idx % (BN / 4)) * 4;
+        *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = rb[i];
+      } else {
+        int n = idx / 4, k4 = (idx % 4) * 4;
+        Bs[buf][k4 + 0][n] = rb[i].x;
+        Bs[buf][k4 + 1][n] = rb[i].y;
+        Bs[buf][k4 + 2][n] = rb[i].z;
+        Bs[buf][k4 + 3][n] = rb[i].w;
+      }
+    }
+  };
+
+  f32x16 acc[WBM][WBN];
+#pragma unroll
+  for (int i = 0; i < WBM; ++i)
+#pragma unroll
+    for (int j = 0; j < WBN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int64_t nk = (a.K + BK - 1) / BK;
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+    __syncthreads();
+  }
+  const int krow = lane >> 5, kcol = lane & 31;
+  int buf = 0;
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 2; ++kk) {
+      float av[WBM], bv[WBN];
+#pragma unroll
+      for (int i = 0; i < WBM; ++i) av[i] = As[buf][2 * kk + krow][wm * (BM / 2) + i * 32 + kcol];
+#pragma unroll
+      for (int j = 0; j < WBN; ++j) bv[j] = Bs[buf][2 * kk + krow][wn * (BN / 2) + j * 32 + kcol];
+#pragma unroll
+      for (int i = 0; i < WBM; ++i)
+#pragma unroll
+        for (int j = 0; j < WBN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // ---- epilogue
+  float* C = a.C + bz * a.strideC;
+  const float* Cin = a.Cin ? a.Cin + bz * a.strideCin : C;
+  const int64_t ldcin = a.Cin ? a.ldcin : a.ldc;
+  double dsum = 0.0;
+#pragma unroll
+  for (int i = 0; i < WBM; ++i) {
+#pragma unroll
+    for (int j = 0; j < WBN; ++j) {
+      const int64_t col = n0 + wn * (BN / 2) + j * 32 + kcol;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * krow + (r % 4);
+        if (row >= a.M || col >= a.N) continue;
+        float v = a.alpha * acc[i][j][r];
+        if (EPI == EPI_DOT) {
+          dsum += double(v) * double(a.E[row * a.lde + col]);
+        } else {
+          if (a.beta != 0.f) v += a.beta * Cin[row * ldcin + col];
+          if (EPI == EPI_SPLIT && col >= a.split)
+            a.C2[row * a.ldc2 + (col - a.split)] = v;
+          else
+            C[row * a.ldc + col] = v;
+          if (a.mirror && tm != tn) {
+            float w = a.alpha * acc[i][j][r];
+            if (a.beta != 0.f) w += a.beta * Cin[col * ldcin + row];
+            C[col * a.ldc + row] = w;
+          }
+        }
+      }
+    }
+  }
+  if (EPI == EPI_DOT) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dsum += __shfl_down(dsum, off, 64);
+    if (lane == 0) atomicAdd(a.dot, dsum);
+  }
+}
+
+template <int BM, int BN, bool TA, bool TB, int EPI>
+quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
+  int tiles_m = int(cdiv(a.M, BM)), tiles_n = int(cdiv(a.N, BN));
+  int total = a.upper_tiles ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
+  if (total == 0 || a.batch == 0) return QUIP_OK;
+  dim3 grid(total, a.batch);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), grid, dim3(256), 0, s, a, tiles_m,
+                     tiles_n, total, vecA, vecB);
+  return launch_check("gemm_kernel");
+}
+
+template <bool TA, bool TB, int EPI>
+quip_status launch_tiles(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
+  // Prefer 128x128 tiles; drop to 64 along a dimension that is small, or when
+  // the 128-tile grid would leave most of the 256 CUs idle.
+  int64_t t128 = cdiv(a.M, 128) * cdiv(a.N, 128) * a.batch;
+  bool smallM = a.M <= 64 || (t128 < 256 && a.M <= a.N);
+  bool smallN = a.N <= 64 || (t128 < 256 && a.N < a.M);
+  if (a.upper_tiles) smallN = smallM;  // square tiles for the triangular grid
+  if (smallM && smallN) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
+  if (smallM) return launch_t<64, 128, TA, TB, EPI>(a, s, vecA, vecB);
+  if (smallN) return launch_t<128, 64, TA, TB, EPI>(a, s, vecA, vecB);
+  return launch_t<128, 128, TA, TB, EPI>(a, s, vecA, vecB);
+}
+
+template <int EPI>
+quip_status launch_epi(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
+  if (a.transA) {
+    if (a.transB) return launch_tiles<true, true, EPI>(a, s, vecA, vecB);
+    return launch_tiles<true, false, EPI>(a, s, vecA, vecB);
+  }
+  if (a.transB) return launch_tiles<false, true, EPI>(a, s, vecA, vecB);
+  return launch_tiles<false, false, EPI>(a, s, vecA, vecB);
+}
+
+}  // namespace
+
+quip_status gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return QUIP_OK;
+  if (a.upper_tiles && a.M != a.N) return fail(QUIP_ERR_SHAPE, "gemm: upper_tiles needs M == N");
+  bool vecA = aligned16(a.A) && a.lda % 4 == 0 && a.strideA % 4 == 0;
+  bool vecB = aligned16(a.B) && a.ldb % 4 == 0 && a.strideB % 4 == 0;
+  switch (a.epi) {
+    case EPI_STORE: return launch_epi<EPI_STORE>(a, s, vecA, vecB);
+    case EPI_DOT: return launch_epi<EPI_DOT>(a, s, vecA, vecB);
+    case EPI_SPLIT: return launch_epi<EPI_SPLIT>(a, s, vecA, vecB);
+  }
+  return fail(QUIP_ERR_ARG, "gemm: bad epilogue");
+}
+
+}  // namespace quip

@@ -1,0 +1,77 @@
+// Proxy Hessian H = X^T X (QuIP, "Adaptive Rounding Step": the second moment
+// of the layer inputs) as a symmetric rank-N update on the fp32 matrix cores:
+// only output tiles on or above the diagonal are computed, and each is also
+// written to its mirror position. Damping (QuIP, "Experiments / Methods"):
+// H <- H / N + alpha * mean(diag(H / N)) * I.
+#include "common.h"
+
+namespace quip {
+namespace {
+
+__global__ void trace_kernel(const float* H, int64_t n, int64_t ldh, double* out) {
+  __shared__ double part[16];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += double(H[i * ldh + i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) t += part[w];
+    *out = t;
+  }
+}
+
+__global__ void finalize_kernel(float* H, int64_t n, int64_t ldh, const double* trace,
+                                double inv_n_total, double alpha) {
+  const float shift = float(alpha * (*trace) * inv_n_total / double(n));
+  const float scale = float(inv_n_total);
+  for (int64_t r = blockIdx.y; r < n; r += gridDim.y)
+    for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < n; c += int64_t(gridDim.x) * 256) {
+      float v = H[r * ldh + c] * scale;
+      if (r == c) v += shift;
+      H[r * ldh + c] = v;
+    }
+}
+
+}  // namespace
+
+quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx, float* H,
+                               int64_t ldh, bool accumulate, hipStream_t s) {
+  if (N == 0) {
+    if (!accumulate) return fill_matrix(H, n, n, ldh, 0.f, s);
+    return QUIP_OK;
+  }
+  GemmArgs g;
+  g.M = n;
+  g.N = n;
+  g.K = N;
+  g.A = X;  // op(A)[i][t] = X[t][i]
+  g.lda = ldx;
+  g.transA = true;
+  g.B = X;  // op(B)[t][j] = X[t][j]
+  g.ldb = ldx;
+  g.transB = false;
+  g.C = H;
+  g.ldc = ldh;
+  g.alpha = 1.f;
+  g.beta = accumulate ? 1.f : 0.f;
+  g.upper_tiles = true;
+  g.mirror = true;
+  return gemm(g, s);
+}
+
+quip_status hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,
+                             double* scratch, hipStream_t s) {
+  hipLaunchKernelGGL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
+  QUIP_TRY(launch_check("trace_kernel"));
+  int64_t gx = cdiv(n, 256);
+  if (gx > 16) gx = 16;
+  dim3 grid(unsigned(gx), unsigned(n < 65535 ? n : 65535));
+  hipLaunchKernelGGL(finalize_kernel, grid, dim3(256), 0, s, H, n, ldh, scratch,
+                     1.0 / double(N_total), double(alpha));
+  return launch_check("finalize_kernel");
+}
+
+}  // namespace quip

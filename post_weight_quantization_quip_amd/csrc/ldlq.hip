@@ -1,0 +1,666 @@
+// LDLQ / BlockLDLQ rounding (QuIP, "Adaptive Rounding Step" and
+// "Conclusion": W^ = Q(W + (W - W^) U) with U from H = (I+U) D (I+U)^T;
+// BlockLDLQ with 8-column groups and the E8 codebook of QuIP#'s abstract, as
+// named on the QTIP page under "Builds on").
+//
+// Schedule (lazy blocking; the rounding decisions are the unblocked ones):
+//   F = 0
+//   for each block of B columns [j0, j0 + B):
+//     sweep the block column by column (group by group), each pre-rounding
+//     value being  W_k + F_k + sum_{i in block, i < k} E_i U_ik,  E = W - W^
+//     F[:, j0+B:] += E_block U[j0:j0+B, j0+B:]        (matrix cores)
+//
+// Scalar grid sweep: one wave holds 16 rows; each row is spread over a quad of
+// 4 lanes, lane g owning the 4-column chunks {16t + 4g .. 16t + 4g + 3}. The
+// owner of column k rounds it, the error goes to the quad's other lanes with
+// one DPP quad_perm broadcast, and every lane updates its later columns with
+// the row of U held in LDS (laid out so that each lane's columns are
+// contiguous).
+//
+// E8 groups: the pre-rounding 8-vectors of all rows are searched against the
+// 65536 codewords as a distance contraction on the matrix cores
+// (codewords x rows, K = 8), with the per-row argmin kept as a packed
+// (order-preserving distance bits, index) 64-bit key and atomicMin.
+#include "common.h"
+
+namespace quip {
+
+quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
+                     const float* D, int g, int64_t B, const quip_quantizer& q, float* scales,
+                     void* codes, float* What, const float* codebook, void* ws, size_t ws_bytes,
+                     hipStream_t s);
+size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_quantizer& q);
+quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const quip_quantizer& q,
+                       float* scales, void* mse_out, const float* codebook, void* ws,
+                       size_t ws_bytes, hipStream_t s);
+size_t scales_workspace_bytes(int64_t m, int64_t n, const quip_quantizer& q);
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float quad_bcast(float v, int src) {
+  // quad_perm [src, src, src, src]
+  const int ctrl = src * 0x55;
+  int r;
+  switch (ctrl) {
+    case 0x00: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x00, 0xF, 0xF, false); break;
+    case 0x55: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x55, 0xF, 0xF, false); break;
+    case 0xAA: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xAA, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xFF, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+
+// ------------------------------------------------------------------ scale search (grid)
+
+template <int NC>
+__global__ __launch_bounds__(256) void grid_scale_kernel(const float* __restrict__ W, int64_t m,
+                                                         int64_t n, int64_t ldw, int L, int ncand,
+                                                         const float* __restrict__ factors,
+                                                         float* __restrict__ scales,
+                                                         float* __restrict__ mse_out) {
+  __shared__ float red[4][NC];
+  __shared__ float smax_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* w = W + row * ldw;
+
+  float amax = 0.f;
+  for (int64_t j = tid; j < n; j += 256) amax = fmaxf(amax, fabsf(w[j]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (lane == 0) red[wave][0] = amax;
+  __syncthreads();
+  if (tid == 0) smax_sh = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+  __syncthreads();
+  const float gmax = smax_sh;
+  if (gmax == 0.f) {
+    if (tid == 0) scales[row] = 1.f;
+    if (mse_out)
+      for (int c = tid; c < ncand; c += 256) mse_out[row * ncand + c] = 0.f;
+    return;
+  }
+  const float cen = (L - 1) * 0.5f, half = L * 0.5f, hi = float(L - 1);
+  const float smax = gmax / cen;
+  float sc[NC], inv[NC], acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    sc[c] = smax * factors[c < ncand ? c : 0];
+    inv[c] = 1.f / sc[c];
+    acc[c] = 0.f;
+  }
+  for (int64_t j = tid; j < n; j += 256) {
+    const float x = w[j];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float k = floorf(x * inv[c] + half);
+      k = fminf(fmaxf(k, 0.f), hi);
+      float e = x - (k - cen) * sc[c];
+      acc[c] = fmaf(e, e, acc[c]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v = acc[c];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[wave][c] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int best = 0;
+    float bv = 0.f;
+    for (int c = 0; c < ncand; ++c) {
+      float v = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+      if (mse_out) mse_out[row * ncand + c] = v;
+      if (c == 0 || v < bv) {
+        bv = v;
+        best = c;
+      }
+    }
+    scales[row] = smax * factors[best];
+  }
+}
+
+// ------------------------------------------------------------------ scalar LDLQ sweep
+
+template <int B>
+__global__ __launch_bounds__(64) void ldlq_sweep_kernel(
+    const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
+    const float* __restrict__ U, int64_t ldu, const float* __restrict__ scales, int L, int64_t m,
+    int64_t s0, int bw, uint8_t* __restrict__ codes, int64_t ldcode, float* __restrict__ What,
+    int64_t ldwh, float* __restrict__ Eb, int64_t lde) {
+  constexpr int NT = B / 16;  // 4-column chunks per lane
+  constexpr int NS = B / 4;   // slots per lane
+  extern __shared__ __align__(16) float Us[];  // [B][4][NS]
+
+  const int lane = threadIdx.x;
+  const int g = lane & 3;
+  const int64_t row = int64_t(blockIdx.x) * 16 + (lane >> 2);
+  const bool live = row < m;
+
+  // U block, permuted: Us[k][gg][4t + e] = U[s0 + k][s0 + 16t + 4gg + e]
+  for (int e = lane; e < B * (B / 4); e += 64) {
+    const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < bw) {
+      const float* src = U + (s0 + k) * ldu + s0 + c4;
+      if (c4 + 0 < bw) v.x = src[0];
+      if (c4 + 1 < bw) v.y = src[1];
+      if (c4 + 2 < bw) v.z = src[2];
+      if (c4 + 3 < bw) v.w = src[3];
+    }
+    const int gg = (c4 >> 2) & 3, t16 = c4 >> 4;
+    *reinterpret_cast<float4*>(&Us[(k * 4 + gg) * NS + 4 * t16]) = v;
+  }
+
+  float w[NS], a[NS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * t + 4 * g + e;
+      float wv = 0.f, fv = 0.f;
+      if (live && c < bw) {
+        wv = W[row * ldw + s0 + c];
+        if (useF) fv = F[row * ldf + s0 + c];
+      }
+      w[4 * t + e] = wv;
+      a[4 * t + e] = fv;
+    }
+  }
+  __syncthreads();
+
+  const float s = live ? scales[row] : 1.f;
+  const float half = L * 0.5f, cen = (L - 1) * 0.5f, hi = float(L - 1);
+  uint32_t cw[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) cw[t] = 0u;
+
+#pragma unroll
+  for (int k = 0; k < B; ++k) {
+    if (k >= bw) break;
+    const int gk = (k >> 2) & 3, tk = k >> 4, ek = k & 3;
+    const int slot = 4 * tk + ek;
+    const float p = w[slot] + a[slot];
+    float kf = floorf(p / s + half);
+    kf = fminf(fmaxf(kf, 0.f), hi);
+    const float qv = (kf - cen) * s;
+    const float err = w[slot] - qv;
+    const float errb = quad_bcast(err, gk);
+    if (g == gk) {
+      w[slot] = qv;
+      a[slot] = err;
+      cw[tk] |= uint32_t(kf) << (8 * ek);
+    }
+    const float* urow = &Us[(k * 4 + g) * NS];
+#pragma unroll
+    for (int t = tk; t < NT; ++t) {
+      const float4 u = *reinterpret_cast<const float4*>(urow + 4 * t);
+      a[4 * t + 0] = fmaf(errb, u.x, a[4 * t + 0]);
+      a[4 * t + 1] = fmaf(errb, u.y, a[4 * t + 1]);
+      a[4 * t + 2] = fmaf(errb, u.z, a[4 * t + 2]);
+      a[4 * t + 3] = fmaf(errb, u.w, a[4 * t + 3]);
+    }
+  }
+
+  if (!live) return;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * t + 4 * g + e;
+      if (c >= bw) continue;
+      codes[row * ldcode + s0 + c] = uint8_t((cw[t] >> (8 * e)) & 0xFF);
+      if (What) What[row * ldwh + s0 + c] = w[4 * t + e];
+      Eb[row * lde + c] = a[4 * t + e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ E8
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Row RMS and the normalized copy Wn = W / rms (rms given or computed).
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* W, int64_t n, int64_t ldw,
+                                                      float* Wn, float* rms_io, bool compute) {
+  __shared__ double part[4];
+  __shared__ float rms_sh;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float* w = W + row * ldw;
+  if (compute) {
+    double acc = 0.0;
+    for (int64_t j = tid; j < n; j += 256) acc += double(w[j]) * double(w[j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
+    if ((tid & 63) == 0) part[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      double ms = (part[0] + part[1] + part[2] + part[3]) / double(n);
+      float r = float(sqrt(ms));
+      if (!(r > 0.f)) r = 1.f;
+      rms_io[row] = r;
+      rms_sh = r;
+    }
+    __syncthreads();
+  } else {
+    if (tid == 0) rms_sh = rms_io[row];
+    __syncthreads();
+  }
+  const float r = rms_sh;
+  for (int64_t j = tid; j < n; j += 256) Wn[row * n + j] = w[j] / r;
+}
+
+__global__ void e8_norms_kernel(const float* C, float* c2) {
+  int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= 65536) return;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s = fmaf(C[i * 8 + k], C[i * 8 + k], s);
+  c2[i] = s;
+}
+
+// Squared error of the nearest codeword, summed over all 8-vectors, for every
+// candidate scale. One wave: 32 vectors x all codewords; lanes 0-31 and 32-63
+// see the same vectors and different codeword rows of each 32x32 block.
+template <int NC>
+__global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__ Y, int64_t nvec,
+                                                       const float* __restrict__ C,
+                                                       const float* __restrict__ c2,
+                                                       const float* __restrict__ cand, int ncand,
+                                                       double* __restrict__ sse) {
+  __shared__ double red[NC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < NC) red[tid] = 0.0;
+  __syncthreads();
+  const int64_t v0 = (int64_t(blockIdx.x) * 4 + wave) * 32;
+  const int j = lane & 31, kh = lane >> 5;
+  const int64_t vj = v0 + j;
+  const bool live = vj < nvec;
+  float yk[4];
+  float y2 = 0.f;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) yk[st] = live ? Y[vj * 8 + 2 * st + kh] : 0.f;
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y2 = fmaf(Y[vj * 8 + k], Y[vj * 8 + k], y2);
+  }
+  float sc[NC], best[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    sc[c] = cand[c < ncand ? c : 0];
+    best[c] = 3.4e38f;
+  }
+  for (int cw0 = 0; cw0 < 65536; cw0 += 32) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float av = C[(cw0 + j) * 8 + 2 * st + kh];  // A[i][k] = codeword i, coordinate k
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, yk[st], acc, 0, 0, 0);
+    }
+    // D[i][j]: lane holds vector j and codewords i = 8*(r/4) + 4*kh + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
+      const float n2 = c2[i];
+      const float d2 = -2.f * acc[r];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) best[c] = fminf(best[c], fmaf(sc[c], n2, d2));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float other = __shfl_xor(best[c], 32, 64);
+    float b = fminf(best[c], other);
+    double e = live && kh == 0 ? double(y2) + double(sc[c]) * double(b) : 0.0;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
+    if (lane == 0 && c < ncand) atomicAdd(&red[c], e);
+  }
+  __syncthreads();
+  if (tid < ncand && tid < NC) atomicAdd(&sse[tid], red[tid]);
+}
+
+// One group step of BlockLDLQ: pre-rounding vectors of 32 rows (with the
+// in-block feedback of the earlier groups of the block), then the argmin over
+// a chunk of codewords. 4 waves split the chunk; atomicMin per row.
+__global__ __launch_bounds__(256) void e8_argmin_kernel(
+    const float* __restrict__ Wn, int64_t n, const float* __restrict__ F, bool useF,
+    const float* __restrict__ Eb, int64_t lde, int nprev, const float* __restrict__ U,
+    int64_t c0, int64_t s0, const float* __restrict__ C, const float* __restrict__ c2,
+    const float* __restrict__ sp, int64_t m, int chunk, unsigned long long* __restrict__ keys) {
+  __shared__ float ysh[32][8];
+  __shared__ unsigned long long ksh[4][32];
+  const float s = *sp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = int64_t(blockIdx.x) * 32;
+  // pre-rounding values: 256 threads = 32 rows x 8 coordinates
+  {
+    const int rr = tid >> 3, kk = tid & 7;
+    const int64_t row = r0 + rr;
+    float y = 0.f;
+    if (row < m) {
+      y = Wn[row * n + c0 + kk];
+      if (useF) y += F[row * n + c0 + kk];
+      // earlier columns of this block: E[row, s0 + c] U[s0 + c, c0 + kk]
+      for (int c = 0; c < nprev; ++c) y = fmaf(Eb[row * lde + c], U[(s0 + c) * n + c0 + kk], y);
+    }
+    ysh[rr][kk] = y;
+  }
+  __syncthreads();
+  const int j = lane & 31, kh = lane >> 5;
+  float yk[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) yk[st] = ysh[j][2 * st + kh];
+  const int cbeg = blockIdx.y * chunk + wave * (chunk / 4);
+  const int cend = cbeg + chunk / 4;
+  float bestv = 3.4e38f;
+  int besti = cbeg;  // always a valid codeword, even if every distance is NaN
+  for (int cw0 = cbeg; cw0 < cend; cw0 += 32) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float av = C[(cw0 + j) * 8 + 2 * st + kh];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, yk[st], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
+      const float v = fmaf(s, c2[i], -2.f * acc[r]);
+      if (v < bestv) {  // codewords visited in increasing index within a lane
+        bestv = v;
+        besti = i;
+      }
+    }
+  }
+  unsigned long long key = (unsigned long long)ordered_bits(bestv) << 32 | uint32_t(besti);
+  unsigned long long other = __shfl_xor(key, 32, 64);
+  key = key < other ? key : other;
+  if (kh == 0) ksh[wave][j] = key;
+  __syncthreads();
+  if (tid < 32) {
+    unsigned long long k2 = ksh[0][tid];
+    for (int wv = 1; wv < 4; ++wv) k2 = ksh[wv][tid] < k2 ? ksh[wv][tid] : k2;
+    if (r0 + tid < m) atomicMin(&keys[r0 + tid], k2);
+  }
+}
+
+// Finish a group step: codes, quantized values, errors; reset the keys.
+__global__ void e8_finish_kernel(const float* __restrict__ Wn, int64_t n, const float* __restrict__ C,
+                                 const float* __restrict__ sp, const float* __restrict__ rms,
+                                 int64_t c0, int64_t m,
+                                 unsigned long long* __restrict__ keys, uint16_t* __restrict__ codes,
+                                 int64_t ldcode, float* __restrict__ What, float* __restrict__ Eb,
+                                 int64_t lde, int ecol) {
+  const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= m) return;
+  const float s = *sp;
+  const uint32_t code = uint32_t(keys[row] & 0xFFFFull);
+  keys[row] = ~0ull;
+  codes[row * ldcode + c0 / 8] = uint16_t(code);
+  const float r = rms[row];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float qv = s * C[code * 8 + k];
+    Eb[row * lde + ecol + k] = Wn[row * n + c0 + k] - qv;
+    if (What) What[row * n + c0 + k] = r * qv;
+  }
+}
+
+__global__ void fill_u64_kernel(unsigned long long* p, int64_t count, unsigned long long v) {
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+
+__global__ void e8_pick_scale_kernel(const double* sse, const float* cand, int ncand,
+                                     float* scales) {
+  if (threadIdx.x != 0) return;
+  int best = 0;
+  for (int c = 1; c < ncand; ++c)
+    if (sse[c] < sse[best]) best = c;
+  scales[0] = cand[best];
+}
+
+// ------------------------------------------------------------------ host helpers
+
+void host_grid_factors(int ncand, float* out) {
+  for (int c = 0; c < ncand; ++c) out[c] = float(pow(16.0, -double(c) / double(ncand - 1)));
+}
+void host_e8_candidates(int ncand, float* out) {
+  for (int c = 0; c < ncand; ++c) out[c] = float(0.5 * pow(4.0, double(c) / double(ncand - 1)));
+}
+
+struct E8Ws {
+  float* Wn;
+  float* F;
+  float* Eb;
+  unsigned long long* keys;
+  float* c2;
+  float* cand;
+  double* sse;
+};
+
+quip_status grid_scales(const float* W, int64_t m, int64_t n, int64_t ldw, int L, int ncand,
+                        float* factors_dev, float* scales, float* mse, hipStream_t s) {
+  if (ncand <= 32)
+    hipLaunchKernelGGL((grid_scale_kernel<32>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
+                       ncand, factors_dev, scales, mse);
+  else
+    hipLaunchKernelGGL((grid_scale_kernel<64>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
+                       ncand, factors_dev, scales, mse);
+  return launch_check("grid_scale_kernel");
+}
+
+quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, const E8Ws& e,
+                      int ncand, float* scales, double* sse_out, hipStream_t s) {
+  QUIP_TRY(fill_f64(e.sse, 64, 0.0, s));
+  const int64_t nvec = m * (n / 8);
+  dim3 grid(unsigned(cdiv(nvec, 128)));
+  if (ncand <= 32)
+    hipLaunchKernelGGL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+                       ncand, e.sse);
+  else
+    hipLaunchKernelGGL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+                       ncand, e.sse);
+  QUIP_TRY(launch_check("e8_scale_kernel"));
+  hipLaunchKernelGGL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
+  QUIP_TRY(launch_check("e8_pick_scale_kernel"));
+  if (sse_out) QUIP_HIP(hipMemcpyAsync(sse_out, e.sse, sizeof(double) * ncand, hipMemcpyDeviceToDevice, s));
+  return QUIP_OK;
+}
+
+template <int B>
+quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
+                    const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
+                    int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
+                    int64_t lde, hipStream_t s) {
+  const size_t shmem = size_t(B) * B * sizeof(float);
+  if (shmem > 65536)
+    QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+  hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(64), shmem, s, W, ldw,
+                     F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde);
+  return launch_check("ldlq_sweep_kernel");
+}
+
+quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
+                  const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
+                  int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
+                  int64_t lde, hipStream_t s) {
+  switch (b) {
+    case 32: return sweep_t<32>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, s);
+    case 64: return sweep_t<64>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, s);
+    case 128: return sweep_t<128>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, s);
+  }
+  return fail(QUIP_ERR_UNSUPPORTED, "ldlq: inner block size");
+}
+
+// F[:, c0:c1] (+)= Eb[:, e0:e0+K] U[r0:r0+K, c0:c1]
+quip_status feedback_gemm(const float* Eb, int64_t lde, int64_t e0, int64_t K, const float* U,
+                          int64_t n, int64_t r0, int64_t c0, int64_t c1, float* F, int64_t m,
+                          bool accumulate, hipStream_t s) {
+  if (c1 <= c0 || K <= 0) return QUIP_OK;
+  GemmArgs a;
+  a.M = m;
+  a.N = c1 - c0;
+  a.K = K;
+  a.A = Eb + e0;
+  a.lda = lde;
+  a.B = U + r0 * n + c0;
+  a.ldb = n;
+  a.C = F + c0;
+  a.ldc = n;
+  a.alpha = 1.f;
+  a.beta = accumulate ? 1.f : 0.f;
+  return gemm(a, s);
+}
+
+}  // namespace
+
+size_t scales_workspace_bytes(int64_t m, int64_t n, const quip_quantizer& q) {
+  Carver c(nullptr, 0);
+  c.take<float>(64);  // candidate factors
+  if (q.kind == QUIP_Q_E8) {
+    c.take<float>(size_t(m) * n);  // Wn
+    c.take<float>(65536);          // |c|^2
+    c.take<double>(64);            // sse
+  }
+  return c.used;
+}
+
+quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const quip_quantizer& q,
+                       float* scales, void* mse_out, const float* codebook, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  Carver c(ws, ws_bytes);
+  float* fac = c.take<float>(64);
+  float hostf[64];
+  if (q.kind == QUIP_Q_UNIFORM) {
+    if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_scales: workspace too small");
+    host_grid_factors(q.n_cand, hostf);
+    QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
+    return grid_scales(W, m, n, ldw, 1 << q.bits, q.n_cand, fac, scales,
+                       static_cast<float*>(mse_out), s);
+  }
+  E8Ws e{};
+  e.Wn = c.take<float>(size_t(m) * n);
+  e.c2 = c.take<float>(65536);
+  e.sse = c.take<double>(64);
+  e.cand = fac;
+  if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_scales: workspace too small");
+  host_e8_candidates(q.n_cand, hostf);
+  QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
+  hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
+                     true);
+  QUIP_TRY(launch_check("rownorm_kernel"));
+  hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+  QUIP_TRY(launch_check("e8_norms_kernel"));
+  return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
+}
+
+size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_quantizer& q) {
+  Carver c(nullptr, 0);
+  c.take<float>(64);
+  c.take<float>(size_t(m) * n);  // F
+  c.take<float>(size_t(m) * B);  // Eb
+  if (q.kind == QUIP_Q_E8) {
+    c.take<float>(size_t(m) * n);  // Wn
+    c.take<unsigned long long>(size_t(m));
+    c.take<float>(65536);
+    c.take<double>(64);
+  }
+  (void)g;
+  return c.used;
+}
+
+quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
+                     const float* D, int g, int64_t B, const quip_quantizer& q, float* scales,
+                     void* codes, float* What, const float* codebook, void* ws, size_t ws_bytes,
+                     hipStream_t s) {
+  (void)D;
+  Carver c(ws, ws_bytes);
+  float* fac = c.take<float>(64);
+  float* F = c.take<float>(size_t(m) * n);
+  float* Eb = c.take<float>(size_t(m) * B);
+  float hostf[64];
+
+  if (q.kind == QUIP_Q_UNIFORM) {
+    if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldlq: workspace too small");
+    const int L = 1 << q.bits;
+    if (q.scale_mode == QUIP_SCALE_COMPUTE) {
+      host_grid_factors(q.n_cand, hostf);
+      QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
+      QUIP_TRY(grid_scales(W, m, n, ldw, L, q.n_cand, fac, scales, nullptr, s));
+    }
+    const int bi = B >= 128 ? 128 : (B >= 64 ? 64 : 32);
+    uint8_t* cd = static_cast<uint8_t*>(codes);
+    for (int64_t j0 = 0; j0 < n; j0 += B) {
+      const int64_t bo = (n - j0 < B) ? n - j0 : B;
+      for (int64_t s0 = j0; s0 < j0 + bo; s0 += bi) {
+        const int bw = int((j0 + bo - s0) < bi ? (j0 + bo - s0) : bi);
+        QUIP_TRY(sweep(bi, W, ldw, F, n, s0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
+                       Eb + (s0 - j0), B, s));
+        // rest of this outer block
+        QUIP_TRY(feedback_gemm(Eb, B, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
+                               !(j0 == 0 && s0 == 0), s));
+      }
+      QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
+    }
+    return QUIP_OK;
+  }
+
+  // ---- E8, g = 8
+  E8Ws e{};
+  e.Wn = c.take<float>(size_t(m) * n);
+  e.keys = c.take<unsigned long long>(size_t(m));
+  e.c2 = c.take<float>(65536);
+  e.sse = c.take<double>(64);
+  e.cand = fac;
+  e.F = F;
+  e.Eb = Eb;
+  if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldlq: workspace too small");
+  const bool compute = q.scale_mode == QUIP_SCALE_COMPUTE;
+  hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
+                     compute);
+  QUIP_TRY(launch_check("rownorm_kernel"));
+  hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+  QUIP_TRY(launch_check("e8_norms_kernel"));
+  if (compute) {
+    host_e8_candidates(q.n_cand, hostf);
+    QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
+    QUIP_TRY(e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, nullptr, s));
+  }
+  // the global scale stays on the device (scales[0]); the step kernels read it there
+  const float* sglob = scales;
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
+  QUIP_TRY(launch_check("fill_u64_kernel"));
+  uint16_t* cd = static_cast<uint16_t*>(codes);
+  const int chunk = 4096;
+  for (int64_t j0 = 0; j0 < n; j0 += B) {
+    const int64_t bo = (n - j0 < B) ? n - j0 : B;
+    for (int64_t c0 = j0; c0 < j0 + bo; c0 += 8) {
+      dim3 grid(unsigned(cdiv(m, 32)), unsigned(65536 / chunk));
+      hipLaunchKernelGGL(e8_argmin_kernel, grid, dim3(256), 0, s, e.Wn, n, F, j0 > 0, Eb, B,
+                         int(c0 - j0), U, c0, j0, codebook, e.c2, sglob, m, chunk, e.keys);
+      QUIP_TRY(launch_check("e8_argmin_kernel"));
+      hipLaunchKernelGGL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
+                         codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
+                         int(c0 - j0));
+      QUIP_TRY(launch_check("e8_finish_kernel"));
+    }
+    QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
+  }
+  return QUIP_OK;
+}
+
+}  // namespace quip

@@ -1,0 +1,92 @@
+// Small element-wise kernels (fills, copies, differences). Fills are kernels,
+// not hipMemsetAsync, so that a stream capture of the pass records only
+// kernel nodes.
+#include "common.h"
+
+namespace quip {
+namespace {
+
+__global__ void fill_f32_kernel(float* p, int64_t count, float v) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (; i < count; i += stride) p[i] = v;
+}
+
+__global__ void fill_f64_kernel(double* p, int64_t count, double v) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (; i < count; i += stride) p[i] = v;
+}
+
+// 2-D kernels: one work-group row-chunk per (row, 1024-column strip).
+__global__ void fill_matrix_kernel(float* p, int64_t rows, int64_t cols, int64_t ld, float v) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t c = int64_t(blockIdx.x) * 1024 + threadIdx.x; c < cols;
+         c += int64_t(gridDim.x) * 1024)
+    p[r * ld + c] = v;
+}
+
+__global__ void sub_matrix_kernel(const float* a, const float* b, float* out, int64_t rows,
+                                  int64_t cols, int64_t lda, int64_t ldb, int64_t ldo) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t c = int64_t(blockIdx.x) * 1024 + threadIdx.x; c < cols;
+         c += int64_t(gridDim.x) * 1024)
+    out[r * ldo + c] = a[r * lda + c] - b[r * ldb + c];
+}
+
+__global__ void copy_matrix_kernel(const float* s, int64_t lds, float* d, int64_t ldd,
+                                   int64_t rows, int64_t cols) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t c = int64_t(blockIdx.x) * 1024 + threadIdx.x; c < cols;
+         c += int64_t(gridDim.x) * 1024)
+    d[r * ldd + c] = s[r * lds + c];
+}
+
+dim3 grid2d(int64_t rows, int64_t cols) {
+  int64_t gx = cdiv(cols, 1024);
+  if (gx > 64) gx = 64;
+  return dim3(unsigned(gx < 1 ? 1 : gx), unsigned(rows < 65535 ? rows : 65535));
+}
+
+}  // namespace
+
+quip_status fill_f32(float* p, int64_t count, float v, hipStream_t s) {
+  if (count <= 0) return QUIP_OK;
+  int64_t blocks = cdiv(count, 256);
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
+  return launch_check("fill_f32");
+}
+
+quip_status fill_f64(double* p, int64_t count, double v, hipStream_t s) {
+  if (count <= 0) return QUIP_OK;
+  int64_t blocks = cdiv(count, 256);
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(fill_f64_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
+  return launch_check("fill_f64");
+}
+
+quip_status fill_matrix(float* p, int64_t rows, int64_t cols, int64_t ld, float v, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return QUIP_OK;
+  if (ld == cols) return fill_f32(p, rows * cols, v, s);
+  hipLaunchKernelGGL(fill_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, p, rows, cols, ld, v);
+  return launch_check("fill_matrix");
+}
+
+quip_status sub_matrix(const float* a, const float* b, float* out, int64_t rows, int64_t cols,
+                       int64_t lda, int64_t ldb, int64_t ldo, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return QUIP_OK;
+  hipLaunchKernelGGL(sub_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, a, b, out, rows,
+                     cols, lda, ldb, ldo);
+  return launch_check("sub_matrix");
+}
+
+quip_status copy_matrix(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows,
+                        int64_t cols, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return QUIP_OK;
+  hipLaunchKernelGGL(copy_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, src, lds, dst, ldd,
+                     rows, cols);
+  return launch_check("copy_matrix");
+}
+
+}  // namespace quip

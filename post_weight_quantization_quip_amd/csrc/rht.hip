@@ -1,0 +1,382 @@
+// Randomized Hadamard transform (random signs, then the natural-order
+// Sylvester Hadamard matrix, then 1/sqrt(d)) -- the incoherence transform of
+// QuIP# (abstract) applied to one side of a matrix.
+//
+// RIGHT side (along a row, contiguous): rht_rows_kernel. A row of N = 2^LOGN
+// floats is held by N/E threads with E floats each. The first E-point
+// butterfly round runs on what each thread loaded (index bits {0,1} and the
+// top bits, so that every load is a lane-contiguous float4); the remaining
+// index bits are covered by rounds of E-point butterflies in registers, with an
+// LDS transpose between rounds (double-buffered, one barrier per round, XOR
+// swizzle on bits 2..4 so the strided round patterns hit distinct banks). A
+// last transpose brings the data back to the float4 layout for the store.
+//
+// LEFT side (along a column, strided by the row pitch): rht_cols_pass. The
+// d-point transform is split H_d = H_{2^k1} (x) H_{2^k2} (x) ... into passes
+// that each transform 2^KR rows spaced 2^lo apart, for 64 consecutive columns
+// per work-group (lanes run along the columns, so every access is a 256-byte
+// row segment). Inside a pass: butterflies on the rows a thread holds, one LDS
+// transpose, butterflies on the rest.
+#include "common.h"
+
+namespace quip {
+namespace {
+
+__device__ __forceinline__ int swz(int i) {
+  int f = ((i >> 5) ^ (i >> 8) ^ (i >> 11)) & 7;
+  return i ^ (f << 2);
+}
+
+template <int LOGN, int LE>
+__global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* out, int64_t rows,
+                                                       int64_t ld, const float* __restrict__ signs,
+                                                       float scale, bool inverse, bool vec) {
+  constexpr int N = 1 << LOGN;
+  constexpr int E = 1 << LE;
+  constexpr int T = N / E;                    // threads per row
+  constexpr int RW = T >= 256 ? 1 : 256 / T;  // rows per work-group
+  constexpr int TOP = LE - 2;                 // register bits placed at the top of the index
+  constexpr int MID_LO = 2, MID_HI = LOGN - TOP;
+  constexpr int MID = MID_HI - MID_LO;
+  constexpr int NFULL = MID / LE;
+  constexpr int REM = MID % LE;
+  constexpr int NR = NFULL + (REM ? 1 : 0);
+
+  extern __shared__ __align__(16) float lds[];  // 2 * RW * N floats
+
+  const int tid = threadIdx.x;
+  const int rw = tid / T, p = tid % T;
+  const int64_t row = int64_t(blockIdx.x) * RW + rw;
+  const bool live = row < rows;
+
+  float x[E];
+
+  // round-0 layout: i = (r & 3) | (p << 2) | ((r >> 2) << MID_HI)
+  auto idx0 = [&](int r) { return (r & 3) | (p << 2) | ((r >> 2) << MID_HI); };
+  auto idxa = [&](int a, int r) {
+    return (p & ((1 << a) - 1)) | (r << a) | ((p >> a) << (a + LE));
+  };
+
+  const float* src = A + row * ld;
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c) {
+    int i = idx0(4 * c);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+      if (vec) {
+        v = *reinterpret_cast<const float4*>(src + i);
+      } else {
+        v.x = src[i];
+        v.y = src[i + 1];
+        v.z = src[i + 2];
+        v.w = src[i + 3];
+      }
+    }
+    x[4 * c + 0] = v.x;
+    x[4 * c + 1] = v.y;
+    x[4 * c + 2] = v.z;
+    x[4 * c + 3] = v.w;
+  }
+  if (!inverse) {
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      float4 s = *reinterpret_cast<const float4*>(signs + idx0(4 * c));
+      x[4 * c + 0] *= s.x;
+      x[4 * c + 1] *= s.y;
+      x[4 * c + 2] *= s.z;
+      x[4 * c + 3] *= s.w;
+    }
+  }
+  // round 0: every register bit is a new index bit
+#pragma unroll
+  for (int t = 0; t < LE; ++t) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      if (r & (1 << t)) continue;
+      float u = x[r], w = x[r | (1 << t)];
+      x[r] = u + w;
+      x[r | (1 << t)] = u - w;
+    }
+  }
+
+  float* base[2] = {lds + rw * N, lds + (RW + rw) * N};
+  int buf = 0;
+  int prev = -1;  // -1: round-0 layout, else base bit of the previous round
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int a = j < NFULL ? MID_LO + j * LE : (MID_HI - LE > 0 ? MID_HI - LE : 0);
+    const int new_lo = j < NFULL ? a : MID_LO + NFULL * LE;
+    const int new_hi = j < NFULL ? a + LE : MID_HI;
+    float* L = base[buf];
+    if (prev < 0) {
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c)
+        *reinterpret_cast<float4*>(L + swz(idx0(4 * c))) =
+            make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < E; ++r) L[swz(idxa(prev, r))] = x[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < E; ++r) x[r] = L[swz(idxa(a, r))];
+    buf ^= 1;
+#pragma unroll
+    for (int t = 0; t < LE; ++t) {
+      if (a + t < new_lo || a + t >= new_hi) continue;
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        if (r & (1 << t)) continue;
+        float u = x[r], w = x[r | (1 << t)];
+        x[r] = u + w;
+        x[r | (1 << t)] = u - w;
+      }
+    }
+    prev = a;
+  }
+  if (NR > 0) {
+    float* L = base[buf];
+#pragma unroll
+    for (int r = 0; r < E; ++r) L[swz(idxa(prev, r))] = x[r];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      float4 v = *reinterpret_cast<const float4*>(L + swz(idx0(4 * c)));
+      x[4 * c + 0] = v.x;
+      x[4 * c + 1] = v.y;
+      x[4 * c + 2] = v.z;
+      x[4 * c + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c) {
+    float4 s = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (inverse) s = *reinterpret_cast<const float4*>(signs + idx0(4 * c));
+    x[4 * c + 0] *= s.x * scale;
+    x[4 * c + 1] *= s.y * scale;
+    x[4 * c + 2] *= s.z * scale;
+    x[4 * c + 3] *= s.w * scale;
+  }
+  if (live) {
+    float* dst = out + row * ld;
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      int i = idx0(4 * c);
+      if (vec) {
+        *reinterpret_cast<float4*>(dst + i) =
+            make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+      } else {
+        dst[i] = x[4 * c];
+        dst[i + 1] = x[4 * c + 1];
+        dst[i + 2] = x[4 * c + 2];
+        dst[i + 3] = x[4 * c + 3];
+      }
+    }
+  }
+}
+
+// Rows of length 2, 4 or 8: one thread per row.
+template <int N>
+__global__ void rht_rows_small_kernel(const float* A, float* out, int64_t rows, int64_t ld,
+                                      const float* signs, float scale, bool inverse) {
+  int64_t row = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  float x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = A[row * ld + i] * (inverse ? 1.f : signs[i]);
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!(i & h)) {
+        float u = x[i], w = x[i | h];
+        x[i] = u + w;
+        x[i | h] = u - w;
+      }
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[row * ld + i] = x[i] * scale * (inverse ? signs[i] : 1.f);
+}
+
+// One pass of the column transform: rows {base + (t << lo) : t < 2^KR} for the
+// 64 columns [c0, c0 + 64). 256 threads = 64 columns x 4 groups.
+template <int KR>
+__global__ __launch_bounds__(256) void rht_cols_pass(const float* A, float* out, int64_t cols,
+                                                     int64_t ld, int lo,
+                                                     const float* __restrict__ signs,
+                                                     float scale, int mode) {
+  // mode bit 0: multiply by the sign of the row before the butterflies
+  //          1: multiply by the sign of the row after (and apply `scale`)
+  constexpr int R = 1 << KR;
+  constexpr int NREG = R / 4;
+  __shared__ float lds[R][65];
+
+  const int tid = threadIdx.x;
+  const int c = tid & 63, g = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const int64_t base = (b & ((int64_t(1) << lo) - 1)) | ((b >> lo) << (lo + KR));
+  const int64_t col = int64_t(blockIdx.y) * 64 + c;
+  const bool live = col < cols;
+
+  float x[NREG];
+  // layout A: t = g + 4 r
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) {
+    int64_t rowi = base + (int64_t(g + 4 * r) << lo);
+    float v = live ? A[rowi * ld + col] : 0.f;
+    if (mode & 1) v *= signs[rowi];
+    x[r] = v;
+  }
+#pragma unroll
+  for (int t = 0; t < KR - 2; ++t)
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) {
+      if (r & (1 << t)) continue;
+      float u = x[r], w = x[r | (1 << t)];
+      x[r] = u + w;
+      x[r | (1 << t)] = u - w;
+    }
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) lds[g + 4 * r][c] = x[r];
+  __syncthreads();
+  // layout B: t = (r & 3) | (g << 2) | ((r >> 2) << 4)
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) x[r] = lds[(r & 3) | (g << 2) | ((r >> 2) << 4)][c];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) {
+      if (r & (1 << t)) continue;
+      float u = x[r], w = x[r | (1 << t)];
+      x[r] = u + w;
+      x[r | (1 << t)] = u - w;
+    }
+  if (!live) return;
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) {
+    int t = (r & 3) | (g << 2) | ((r >> 2) << 4);
+    int64_t rowi = base + (int64_t(t) << lo);
+    float v = x[r] * scale;
+    if (mode & 2) v *= signs[rowi];
+    out[rowi * ld + col] = v;
+  }
+}
+
+// Column transform of length 2, 4 or 8: one thread per column.
+template <int D>
+__global__ void rht_cols_small_kernel(const float* A, float* out, int64_t cols, int64_t ld,
+                                      const float* signs, float scale, bool inverse) {
+  int64_t col = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (col >= cols) return;
+  float x[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) x[i] = A[i * ld + col] * (inverse ? 1.f : signs[i]);
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (!(i & h)) {
+        float u = x[i], w = x[i | h];
+        x[i] = u + w;
+        x[i | h] = u - w;
+      }
+#pragma unroll
+  for (int i = 0; i < D; ++i) out[i * ld + col] = x[i] * scale * (inverse ? signs[i] : 1.f);
+}
+
+template <int LOGN>
+quip_status rows_t(const float* A, float* out, int64_t rows, int64_t ld, const float* s,
+                   bool inverse, hipStream_t st) {
+  constexpr int LE = LOGN >= 14 ? 5 : 4;
+  constexpr int N = 1 << LOGN;
+  constexpr int T = N >> LE;
+  constexpr int RW = T >= 256 ? 1 : 256 / T;
+  const float scale = 1.0f / sqrtf(float(N));
+  bool vec = aligned16(A) && aligned16(out) && ld % 4 == 0;
+  size_t shmem = size_t(2) * RW * N * sizeof(float);
+  if (shmem > 65536)
+    QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_rows_kernel<LOGN, LE>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+  dim3 grid(unsigned(cdiv(rows, RW)));
+  hipLaunchKernelGGL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
+                     s, scale, inverse, vec);
+  return launch_check("rht_rows_kernel");
+}
+
+template <int N>
+quip_status rows_small_t(const float* A, float* out, int64_t rows, int64_t ld, const float* s,
+                         bool inverse, hipStream_t st) {
+  const float scale = 1.0f / sqrtf(float(N));
+  hipLaunchKernelGGL((rht_rows_small_kernel<N>), dim3(unsigned(cdiv(rows, 256))), dim3(256), 0, st,
+                     A, out, rows, ld, s, scale, inverse);
+  return launch_check("rht_rows_small_kernel");
+}
+
+template <int D>
+quip_status cols_small_t(const float* A, float* out, int64_t cols, int64_t ld, const float* s,
+                         bool inverse, hipStream_t st) {
+  const float scale = 1.0f / sqrtf(float(D));
+  hipLaunchKernelGGL((rht_cols_small_kernel<D>), dim3(unsigned(cdiv(cols, 256))), dim3(256), 0, st,
+                     A, out, cols, ld, s, scale, inverse);
+  return launch_check("rht_cols_small_kernel");
+}
+
+quip_status cols_pass(int kr, const float* A, float* out, int64_t d, int64_t cols, int64_t ld,
+                      int lo, const float* s, float scale, int mode, hipStream_t st) {
+  dim3 grid(unsigned(d >> kr), unsigned(cdiv(cols, 64)));
+  switch (kr) {
+#define CASE(K)                                                                              \
+  case K:                                                                                    \
+    hipLaunchKernelGGL((rht_cols_pass<K>), grid, dim3(256), 0, st, A, out, cols, ld, lo, s, \
+                       scale, mode);                                                         \
+    break;
+    CASE(4) CASE(5) CASE(6) CASE(7)
+#undef CASE
+    default:
+      return fail(QUIP_ERR_UNSUPPORTED, "rht_cols: pass size");
+  }
+  return launch_check("rht_cols_pass");
+}
+
+}  // namespace
+
+quip_status rht_rows(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                     const float* signs, bool inverse, hipStream_t st) {
+  if (rows == 0) return QUIP_OK;
+  switch (ilog2(cols)) {
+    case 1: return rows_small_t<2>(A, out, rows, ld, signs, inverse, st);
+    case 2: return rows_small_t<4>(A, out, rows, ld, signs, inverse, st);
+    case 3: return rows_small_t<8>(A, out, rows, ld, signs, inverse, st);
+#define CASE(L) \
+  case L: return rows_t<L>(A, out, rows, ld, signs, inverse, st);
+    CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14)
+#undef CASE
+  }
+  return fail(QUIP_ERR_SHAPE, "rht: the transform length must be a power of two in [2, 16384]");
+}
+
+quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
+                     const float* signs, bool inverse, hipStream_t st) {
+  if (cols == 0) return QUIP_OK;
+  const int k = ilog2(rows);
+  switch (k) {
+    case 1: return cols_small_t<2>(A, out, cols, ld, signs, inverse, st);
+    case 2: return cols_small_t<4>(A, out, cols, ld, signs, inverse, st);
+    case 3: return cols_small_t<8>(A, out, cols, ld, signs, inverse, st);
+  }
+  if (k < 4 || k > 14) return fail(QUIP_ERR_SHAPE, "rht: the transform length must be a power of two in [2, 16384]");
+  const int npass = (k + 6) / 7;
+  int lo = 0;
+  const float* src = A;
+  for (int pidx = 0; pidx < npass; ++pidx) {
+    int kr = (k - lo) / (npass - pidx);
+    bool first = pidx == 0, last = pidx == npass - 1;
+    int mode = (first && !inverse ? 1 : 0) | (last && inverse ? 2 : 0);
+    float scale = last ? 1.0f / sqrtf(float(int64_t(1) << k)) : 1.0f;
+    QUIP_TRY(cols_pass(kr, src, out, rows, cols, ld, lo, signs, scale, mode, st));
+    src = out;
+    lo += kr;
+  }
+  return QUIP_OK;
+}
+
+}  // namespace quip

@@ -1,0 +1,157 @@
+"""The whole layer pass, driven through the C ABI.
+
+Order of the calls (every step runs in libquip's kernels; this module only
+allocates buffers once and sequences the calls on one HIP stream):
+
+  quip_hessian -> quip_hessian_finalize          H = X^T X / N + damping
+  quip_rht2 / quip_kron_orth (right, then left)   H~ = V H V^T   (in place)
+  quip_rht2 / quip_kron_orth                      W~ = U W V^T
+  quip_ldl                                        H~ = (I+U) D (I+U)^T
+  quip_ldlq                                       scales, codes, W^~
+  quip_rht2_inv / quip_kron_orth_inv              W^ = U^T W^~ V
+  quip_proxy_loss                                 tr((W^~ - W~) H~ (W^~ - W~)^T)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _native as N
+
+
+@dataclass
+class SideSpec:
+    """Incoherence transform of one side: random signs (RHT) or two factors."""
+
+    signs: torch.Tensor | None = None
+    F1: torch.Tensor | None = None
+    F2: torch.Tensor | None = None
+
+    @property
+    def is_rht(self) -> bool:
+        return self.signs is not None
+
+    @staticmethod
+    def from_numpy(spec: dict, device) -> "SideSpec":
+        if "signs" in spec:
+            return SideSpec(signs=torch.as_tensor(spec["signs"], dtype=torch.float32).to(device))
+        return SideSpec(F1=torch.as_tensor(spec["A"], dtype=torch.float32).to(device).contiguous(),
+                        F2=torch.as_tensor(spec["B"], dtype=torch.float32).to(device).contiguous())
+
+
+def apply_side(A: torch.Tensor, out: torch.Tensor, side: int, spec: SideSpec, inverse: bool,
+               ws=None, stream=None):
+    if spec.is_rht:
+        (N.quip_rht_inv if inverse else N.quip_rht)(A, out, spec.signs, side, stream=stream)
+    else:
+        (N.quip_kron_orth_inv if inverse else N.quip_kron_orth)(A, out, spec.F1, spec.F2, side,
+                                                                stream=stream, ws=ws)
+
+
+def apply_two_sided(A, out, left: SideSpec, right: SideSpec, inverse: bool, ws=None, stream=None):
+    """out = Q_L A Q_R^T (inverse: Q_L^T A Q_R)."""
+    if left.is_rht and right.is_rht:
+        (N.quip_rht2_inv if inverse else N.quip_rht2)(A, out, left.signs, right.signs, stream=stream)
+        return
+    if not inverse:
+        apply_side(A, out, N.RIGHT, right, False, ws, stream)
+        apply_side(out, out, N.LEFT, left, False, ws, stream)
+    else:
+        apply_side(A, out, N.LEFT, left, True, ws, stream)
+        apply_side(out, out, N.RIGHT, right, True, ws, stream)
+
+
+@dataclass
+class LayerPass:
+    """Preallocated buffers for repeated passes over layers of one shape."""
+
+    m: int
+    n: int
+    left: SideSpec
+    right: SideSpec
+    quant: str = "uniform"
+    bits: int = 2
+    B: int = 128
+    g: int = 1
+    alpha: float = 0.01
+    n_cand: int = 32
+    device: str = "cuda"
+    codebook: torch.Tensor | None = None
+    buffers: dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        m, n, dev = self.m, self.n, self.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        b = self.buffers
+        b["H"] = torch.empty((n, n), **f32)
+        b["Wt"] = torch.empty((m, n), **f32)
+        b["U"] = torch.empty((n, n), **f32)
+        b["D"] = torch.empty((n * 8,) if self.g == 8 else (n,), **f32)
+        b["info"] = torch.zeros(1, dtype=torch.int32, device=dev)
+        if self.quant == "uniform":
+            self.q = N.quantizer(N.Q_UNIFORM, self.bits, self.n_cand, N.SCALE_COMPUTE)
+            b["scales"] = torch.empty(m, **f32)
+            b["codes"] = torch.empty((m, n), dtype=torch.uint8, device=dev)
+        else:
+            self.q = N.quantizer(N.Q_E8, 2, self.n_cand, N.SCALE_COMPUTE)
+            b["scales"] = torch.empty(m + 1, **f32)
+            b["codes"] = torch.empty((m, n // 8), dtype=torch.int16, device=dev)
+            if self.codebook is None:
+                self.codebook = N.quip_e8_codebook().to(dev)
+        b["What_t"] = torch.empty((m, n), **f32)
+        b["What"] = torch.empty((m, n), **f32)
+        b["loss"] = torch.zeros(1, dtype=torch.float64, device=dev)
+        # workspaces, sized once
+        need = [256]
+        need.append(N._ws_query(N.lib.quip_ldl_workspace, n, self.g))
+        import ctypes
+        need.append(N._ws_query(N.lib.quip_ldlq_workspace, m, n, self.g, self.B, ctypes.byref(self.q)))
+        need.append(N._ws_query(N.lib.quip_proxy_loss_workspace, m, n))
+        need.append(N._ws_query(N.lib.quip_kron_orth_workspace, max(m, n), max(m, n)))
+        b["ws"] = N._workspace(max(need), dev)
+
+    def run(self, W: torch.Tensor, X: torch.Tensor, events: dict | None = None, stream=None,
+            with_loss: bool = True) -> dict:
+        """One pass. ``events`` (optional) receives torch.cuda.Event pairs per phase."""
+        b = self.buffers
+        ws = b["ws"]
+
+        def mark(name):
+            if events is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(stream)
+                events.setdefault(name, []).append(ev)
+
+        mark("hessian")
+        N.quip_hessian(X, b["H"], accumulate=False, stream=stream)
+        N.quip_hessian_finalize(b["H"], X.shape[0], self.alpha, stream=stream, ws=ws)
+        mark("incoherence_H")
+        apply_two_sided(b["H"], b["H"], self.right, self.right, False, ws, stream)
+        mark("incoherence_W")
+        apply_two_sided(W, b["Wt"], self.left, self.right, False, ws, stream)
+        mark("ldl")
+        N.quip_ldl(b["H"], self.g, b["U"], b["D"], b["info"], stream=stream, ws=ws)
+        mark("ldlq")
+        N.quip_ldlq(b["Wt"], b["U"], b["D"], self.g, self.B, self.q, b["scales"], b["codes"],
+                    b["What_t"], self.codebook, stream=stream, ws=ws)
+        mark("postprocess")
+        apply_two_sided(b["What_t"], b["What"], self.left, self.right, True, ws, stream)
+        mark("loss")
+        if with_loss:
+            N.quip_proxy_loss(b["Wt"], b["What_t"], b["H"], b["loss"], stream=stream, ws=ws)
+        mark("end")
+        return b
+
+
+def quantize_layer(W: torch.Tensor, X: torch.Tensor, left: dict, right: dict, **kw) -> dict:
+    """Convenience wrapper: one pass with fresh buffers. ``left``/``right`` are
+    the workload dicts ({"signs": ...} or {"A": ..., "B": ...})."""
+    dev = W.device
+    lp = LayerPass(W.shape[0], W.shape[1], SideSpec.from_numpy(left, dev),
+                   SideSpec.from_numpy(right, dev), device=dev, **kw)
+    out = lp.run(W, X)
+    info = int(out["info"].item())
+    if info:
+        raise N.QuipError(N.QUIP_ERR_NOT_PD, f"quip_ldl: pivot {info - 1} is not positive")
+    return out

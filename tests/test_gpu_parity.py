@@ -1,0 +1,384 @@
+"""GPU parity of every entry point of the C ABI against the CPU oracle, at sizes
+the oracle finishes in seconds that still span several tiles and ragged tails.
+
+Tolerances ("Parity bar"):
+  * transforms (RHT, Kronecker): per-row normwise relative error <= 1e-5;
+  * Hessian: |dH_ij| <= 2e-5 sqrt(H_ii H_jj)  (float32 sums of N products);
+  * LDL: backward error ||(I+U)D(I+U)^T - H|| / ||H|| <= 2e-6 * sqrt(n);
+  * codes: conditional replay, every mismatch inside the 1e-5 boundary band
+    and at most 1e-4 of all codes;
+  * proxy loss: 1e-4 relative (float64 accumulation of float32 products).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_quip_amd as Q
+import workloads as wl
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev(x, dtype=torch.float32):
+    return torch.as_tensor(np.ascontiguousarray(x)).to(device=DEV, dtype=dtype)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def signs(seed, d):
+    return np.where(rng(seed).random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def spd32(seed, n, N=None, sigma=1.0):
+    r = rng(seed)
+    N = 2 * n if N is None else N
+    X = (r.standard_normal((N, n)) * np.exp(sigma * r.standard_normal(n))[None, :]).astype(np.float32)
+    return O.damp(O.proxy_hessian(X), 0.01).astype(np.float32)
+
+
+# ------------------------------------------------------------------ Hessian
+
+@pytest.mark.parametrize("N,n", [(2048, 256), (1000, 200), (64, 1000), (5, 3), (1, 1), (300, 129)])
+def test_hessian_parity(N, n):
+    X = (rng(N * 7 + n).standard_normal((N, n)) * np.exp(rng(n).standard_normal(n))).astype(np.float32)
+    H = torch.empty((n, n), device=DEV)
+    Xd = dev(X)
+    Q.quip_hessian(Xd, H)
+    Q.quip_hessian_finalize(H, N, 0.01)
+    got = host(H).astype(np.float64)
+    ref = O.damp(O.proxy_hessian(X), 0.01)
+    d = np.sqrt(np.diag(ref))
+    assert (np.abs(got - ref) <= 2e-5 * d[:, None] * d[None, :]).all()
+    assert np.array_equal(got, got.T)
+
+
+def test_hessian_accumulates_in_chunks():
+    X = rng(3).standard_normal((700, 130)).astype(np.float32)
+    H = torch.empty((130, 130), device=DEV)
+    Q.quip_hessian(dev(X[:300]), H)
+    Q.quip_hessian(dev(X[300:]), H, accumulate=True)
+    Q.quip_hessian_finalize(H, 700, 0.0)
+    ref = O.proxy_hessian(X)
+    d = np.sqrt(np.diag(ref))
+    assert (np.abs(host(H) - ref) <= 2e-5 * d[:, None] * d[None, :]).all()
+
+
+# ------------------------------------------------------------------ RHT
+
+@pytest.mark.parametrize("rows,d", [(37, 2), (5, 4), (9, 8), (33, 16), (17, 32), (17, 64), (300, 256),
+                                    (3, 1024), (70, 4096), (5, 8192), (3, 16384)])
+def test_rht_right(rows, d):
+    A = rng(d + rows).standard_normal((rows, d)).astype(np.float32)
+    s = signs(d, d)
+    Ad, sd = dev(A), dev(s)
+    out = torch.empty_like(Ad)
+    Q.quip_rht(Ad, out, sd, Q.RIGHT)
+    assert P.rel_rows(host(out), O.rht(A, s, "right")) <= 1e-5
+    back = torch.empty_like(Ad)
+    Q.quip_rht_inv(out, back, sd, Q.RIGHT)
+    assert P.rel_rows(host(back), O.rht_inv(host(out), s, "right")) <= 1e-5
+    assert P.rel_rows(host(back), A) <= 1e-5
+    Q.quip_rht(Ad, Ad, sd, Q.RIGHT)  # in place
+    assert np.array_equal(host(Ad), host(out))
+
+
+@pytest.mark.parametrize("d,cols", [(2, 5), (4, 65), (8, 1), (16, 64), (64, 130), (128, 64), (256, 300),
+                                    (512, 64), (2048, 65), (4096, 128), (8192, 64)])
+def test_rht_left(d, cols):
+    A = rng(d * 3 + cols).standard_normal((d, cols)).astype(np.float32)
+    s = signs(d + 1, d)
+    Ad, sd = dev(A), dev(s)
+    out = torch.empty_like(Ad)
+    Q.quip_rht(Ad, out, sd, Q.LEFT)
+    ref = O.rht(A, s, "left")
+    assert P.rel_rows(host(out).T, ref.T) <= 1e-5
+    back = torch.empty_like(Ad)
+    Q.quip_rht_inv(out, back, sd, Q.LEFT)
+    assert P.rel_rows(host(back).T, A.T) <= 1e-5
+
+
+def test_rht_leading_dimension():
+    base = rng(5).standard_normal((64, 300)).astype(np.float32)
+    A = dev(base)[:, :256]  # ld = 300 > cols
+    s = signs(9, 256)
+    out = torch.zeros((64, 300), device=DEV)[:, :256]
+    Q.quip_rht(A, out, dev(s), Q.RIGHT)
+    assert P.rel_rows(host(out), O.rht(base[:, :256], s, "right")) <= 1e-5
+    assert np.all(host(torch.zeros((1,), device=DEV)) == 0)
+
+
+@pytest.mark.parametrize("m,n", [(256, 256), (64, 4096), (4096, 64), (2, 2)])
+def test_rht_two_sided(m, n):
+    A = rng(m + n).standard_normal((m, n)).astype(np.float32)
+    sl, sr = signs(1, m), signs(2, n)
+    Ad = dev(A)
+    out = torch.empty_like(Ad)
+    Q.quip_rht2(Ad, out, dev(sl), dev(sr))
+    ref = O.incoherence_W(A, {"signs": sl}, {"signs": sr})
+    assert P.rel_rows(host(out), ref) <= 1e-5
+    back = torch.empty_like(Ad)
+    Q.quip_rht2_inv(out, back, dev(sl), dev(sr))
+    assert P.rel_rows(host(back), A) <= 1e-5
+
+
+# ------------------------------------------------------------------ Kronecker
+
+@pytest.mark.parametrize("side,rows,cols,p,q", [
+    ("right", 10, 24, 4, 6), ("left", 24, 10, 4, 6), ("right", 40, 11008, 64, 172),
+    ("left", 11008, 48, 64, 172), ("right", 7, 28672, 128, 224), ("left", 3, 5, 3, 1)])
+def test_kron(side, rows, cols, p, q):
+    r = rng(rows + cols)
+    A = r.standard_normal((rows, cols)).astype(np.float32)
+    F1 = wl.haar_orthogonal(r, p)
+    F2 = wl.haar_orthogonal(r, q)
+    Ad = dev(A)
+    out = torch.empty_like(Ad)
+    sd = Q.LEFT if side == "left" else Q.RIGHT
+    Q.quip_kron_orth(Ad, out, dev(F1), dev(F2), sd)
+    ref = O.kron_apply(A, F1, F2, side)
+    got = host(out)
+    if side == "left":
+        assert P.rel_rows(got.T, ref.T) <= 1e-5
+    else:
+        assert P.rel_rows(got, ref) <= 1e-5
+    back = torch.empty_like(Ad)
+    Q.quip_kron_orth_inv(out, back, dev(F1), dev(F2), sd)
+    refb = O.kron_apply(got, F1, F2, side, inverse=True)
+    if side == "left":
+        assert P.rel_rows(host(back).T, refb.T) <= 1e-5
+    else:
+        assert P.rel_rows(host(back), refb) <= 1e-5
+
+
+def test_kron_leading_dimension_in_place():
+    r = rng(77)
+    base = r.standard_normal((12, 40)).astype(np.float32)
+    F1, F2 = wl.haar_orthogonal(r, 4), wl.haar_orthogonal(r, 8)
+    full = dev(base)
+    view = full[:, :32]
+    Q.quip_kron_orth(view, view, dev(F1), dev(F2), Q.RIGHT)
+    got = host(full)
+    assert P.rel_rows(got[:, :32], O.kron_apply(base[:, :32], F1, F2, "right")) <= 1e-5
+    assert np.array_equal(got[:, 32:], base[:, 32:])
+
+
+# ------------------------------------------------------------------ LDL
+
+def ldl_gpu(H32, g):
+    n = H32.shape[0]
+    U = torch.empty((n, n), device=DEV)
+    D = torch.empty(n * 8 if g == 8 else n, device=DEV)
+    info = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    Q.quip_ldl(dev(H32), g, U, D, info)
+    return host(U), host(D), int(host(info)[0])
+
+
+@pytest.mark.parametrize("n,g", [(256, 1), (256, 8), (200, 1), (200, 8), (8, 8), (1, 1), (130, 1)])
+def test_ldl_parity(n, g):
+    H = spd32(n * 11 + g, n)
+    U, D, info = ldl_gpu(H, g)
+    assert info == 0
+    assert P.recon_residual(H, U, D, g) <= 2e-6 * np.sqrt(n)
+    mask = np.triu(np.ones((n, n), bool), 1)
+    if g > 1:
+        blk = np.arange(n) // g
+        mask = blk[:, None] < blk[None, :]
+    assert np.all(U[~mask] == 0)
+    Uo, Do = O.udu_cholesky(H.astype(np.float64), g)
+    # forward error of the factors, relative to the oracle's on the same float32 H
+    assert np.linalg.norm(U - Uo) / max(np.linalg.norm(Uo), 1e-30) <= 1e-3
+    assert np.linalg.norm(D.reshape(-1) - Do.reshape(-1)) / np.linalg.norm(Do) <= 1e-3
+
+
+def test_ldl_diagonal():
+    d = rng(4).uniform(0.5, 3.0, 100).astype(np.float32)
+    U, D, info = ldl_gpu(np.diag(d), 1)
+    assert info == 0 and np.all(U == 0) and np.array_equal(D, d)
+
+
+@pytest.mark.parametrize("n,g,bad,want", [(16, 1, 9, 10), (16, 8, 9, 9), (200, 1, 9, 10), (200, 8, 9, 9)])
+def test_ldl_not_positive_definite(n, g, bad, want):
+    H = spd32(5, n)
+    H[bad, :] = 0
+    H[:, bad] = 0
+    _, _, info = ldl_gpu(H, g)
+    assert info == want
+    with pytest.raises(O.NotPositiveDefinite):
+        O.udu(H.astype(np.float64), g)
+
+
+# ------------------------------------------------------------------ scales
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_grid_scale_parity(bits):
+    L = 1 << bits
+    W = (rng(bits).standard_normal((37, 300)) * np.exp(rng(9).standard_normal(37))[:, None]).astype(np.float32)
+    W[5] = 0
+    s = torch.empty(37, device=DEV)
+    mse = torch.empty((37, 32), device=DEV)
+    Q.quip_scales(dev(W), Q.quantizer(Q.Q_UNIFORM, bits), s, mse_out=mse)
+    s_ref, c_ref, mse_ref = O.uniform_scale_search(W, L)
+    sg, mg = host(s).astype(np.float64), host(mse).astype(np.float64)
+    assert sg[5] == 1.0
+    assert np.allclose(mg, mse_ref, rtol=2e-5, atol=1e-30)
+    live = np.arange(37) != 5
+    cand = O.uniform_scale_candidates(np.abs(W).max(axis=1), L)  # (37, 32)
+    cg = np.argmin(np.abs(cand - sg[:, None]), axis=1)
+    rows = np.nonzero(live)[0]
+    assert np.allclose(sg[rows], cand[rows, cg[rows]], rtol=1e-6)
+    best = mse_ref[rows, c_ref[rows]]
+    # the GPU's pick is the oracle's argmin, or ties with it to 1e-5
+    assert np.all(mse_ref[rows, cg[rows]] <= best * (1 + 1e-5))
+
+
+# ------------------------------------------------------------------ LDLQ
+
+def ldlq_gpu(Wt32, U32, D32, g, B, bits, scales=None, codebook=None, kind=None):
+    m, n = Wt32.shape
+    kind = (Q.Q_UNIFORM if g == 1 else Q.Q_E8) if kind is None else kind
+    mode = Q.SCALE_GIVEN if scales is not None else Q.SCALE_COMPUTE
+    q = Q.quantizer(kind, bits if kind == Q.Q_UNIFORM else 2, 32, mode)
+    sd = dev(scales) if scales is not None else torch.empty(m + (1 if kind == Q.Q_E8 else 0), device=DEV)
+    if kind == Q.Q_UNIFORM:
+        codes = torch.empty((m, n), dtype=torch.uint8, device=DEV)
+    else:
+        codes = torch.empty((m, n // 8), dtype=torch.int16, device=DEV)
+    What = torch.empty((m, n), device=DEV)
+    Q.quip_ldlq(dev(Wt32), dev(U32), dev(D32), g, B, q, sd, codes, What,
+                None if codebook is None else dev(codebook))
+    return host(sd), host(codes), host(What)
+
+
+def check_uniform_replay(Wt, U, What, s, codes, L):
+    mism, bad, tot = P.replay_uniform(Wt, U, What, s, codes, L)
+    assert bad == 0, f"{bad} codes differ outside the boundary band"
+    assert mism <= P.MAX_MISMATCH * tot
+    lv = ((codes.astype(np.float32) - np.float32((L - 1) / 2)) * s.astype(np.float32)[:, None])
+    assert np.array_equal(What, lv)
+
+
+@pytest.mark.parametrize("m,n,B,bits", [(256, 256, 32, 2), (37, 200, 64, 3), (100, 512, 256, 4),
+                                        (16, 48, 32, 2), (1, 8, 8, 2), (300, 384, 128, 2)])
+def test_ldlq_replay(m, n, B, bits):
+    L = 1 << bits
+    H = spd32(m + n, n)
+    Wt = (rng(m * n).standard_normal((m, n)) * 1.3).astype(np.float32)
+    U, D, info = ldl_gpu(H, 1)
+    assert info == 0
+    s, codes, What = ldlq_gpu(Wt, U, D, 1, B, bits)
+    s_ref, _, _ = O.uniform_scale_search(Wt, L)
+    assert np.allclose(s, s_ref, rtol=1e-5)
+    check_uniform_replay(Wt, U, What, s, codes, L)
+
+
+def test_ldlq_diagonal_H_is_nearest_rounding():
+    m, n = 64, 256
+    Wt = rng(21).standard_normal((m, n)).astype(np.float32)
+    d = rng(22).uniform(0.5, 2.0, n).astype(np.float32)
+    U, D, _ = ldl_gpu(np.diag(d), 1)
+    assert np.all(U == 0)
+    s, codes, What = ldlq_gpu(Wt, U, D, 1, 64, 2)
+    assert np.array_equal(codes.astype(np.int64), O.uniform_code(Wt, s[:, None], 4))
+
+
+def test_ldlq_given_scales_are_used():
+    m, n = 32, 128
+    Wt = rng(23).standard_normal((m, n)).astype(np.float32)
+    H = spd32(24, n)
+    U, D, _ = ldl_gpu(H, 1)
+    given = np.full(m, 0.7, np.float32)
+    s, codes, What = ldlq_gpu(Wt, U, D, 1, 64, 2, scales=given)
+    assert np.array_equal(s, given)
+    check_uniform_replay(Wt, U, What, s, codes, 4)
+
+
+# ------------------------------------------------------------------ loss
+
+@pytest.mark.parametrize("m,n", [(256, 256), (37, 200), (5, 1000)])
+def test_proxy_loss_parity(m, n):
+    r = rng(m + 3 * n)
+    W = r.standard_normal((m, n)).astype(np.float32)
+    Wh = (W + 0.1 * r.standard_normal((m, n))).astype(np.float32)
+    H = spd32(m, n)
+    loss = torch.empty(1, dtype=torch.float64, device=DEV)
+    Q.quip_proxy_loss(dev(W), dev(Wh), dev(H), loss)
+    ref = O.proxy_loss(W, Wh, H)
+    assert abs(float(host(loss)[0]) - ref) <= 1e-4 * abs(ref)
+
+
+# ------------------------------------------------------------------ E8 / BlockLDLQ
+
+@pytest.fixture(scope="module")
+def codebook():
+    return O.e8_codebook().astype(np.float32)
+
+
+def test_e8_scale_search_parity(codebook):
+    m, n = 64, 128
+    W = rng(31).standard_normal((m, n)).astype(np.float32)
+    scales = torch.empty(m + 1, device=DEV)
+    sse = torch.empty(32, dtype=torch.float64, device=DEV)
+    Q.quip_scales(dev(W), Q.quantizer(Q.Q_E8, 2), scales, mse_out=sse, codebook=dev(codebook))
+    sg, eg = host(scales), host(sse)
+    rms = O.row_rms(W)
+    assert np.allclose(sg[1:], rms, rtol=1e-6)
+    Wn = (W / sg[1:, None].astype(np.float64))
+    s_ref, c_ref, sse_ref = O.e8_scale_search(Wn, codebook)
+    assert np.allclose(eg, sse_ref, rtol=1e-4)
+    cg = int(np.argmin(np.abs(O.e8_scale_candidates() - sg[0])))
+    assert sse_ref[cg] <= sse_ref[c_ref] * (1 + 1e-5)
+
+
+@pytest.mark.parametrize("m,n,B", [(64, 128, 64), (40, 64, 32), (33, 256, 128)])
+def test_block_ldlq_e8_replay(m, n, B, codebook):
+    H = spd32(m + n + 1, n)
+    Wt = (rng(n).standard_normal((m, n)) * np.exp(0.3 * rng(m).standard_normal(m))[:, None]).astype(np.float32)
+    U, D, info = ldl_gpu(H, 8)
+    assert info == 0
+    s, codes, What = ldlq_gpu(Wt, U, D, 8, B, 2, codebook=codebook)
+    rms = s[1:].astype(np.float64)
+    assert np.allclose(rms, O.row_rms(Wt), rtol=1e-6)
+    Wn = Wt / rms[:, None]
+    Whn = What / rms[:, None]
+    mism, bad, tot = P.replay_e8(Wn, U, Whn, float(s[0]), codes, codebook)
+    assert bad == 0
+    assert mism <= max(1, P.MAX_MISMATCH * tot)
+    # W^ is the scaled codeword times the row RMS
+    cw = codebook[codes.astype(np.int64).reshape(m, -1) & 0xFFFF].reshape(m, n)
+    assert np.allclose(What, rms[:, None] * float(s[0]) * cw, rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------------ end to end
+
+def test_layer_pass_end_to_end_c1():
+    L = wl.make_layer("c1")
+    W, X = dev(L.W), dev(L.X)
+    lp = Q.LayerPass(256, 256, Q.SideSpec.from_numpy(L.left, DEV), Q.SideSpec.from_numpy(L.right, DEV),
+                     bits=2, B=32)
+    b = lp.run(W, X)
+    ref = O.quantize_layer(L.W, L.X, L.left, L.right, quant="uniform", bits=2)
+    H = host(b["H"])
+    d = np.sqrt(np.diag(ref["Ht"]))
+    assert np.abs(H - ref["Ht"]).max() <= 1e-5 * d.max() ** 2
+    assert P.rel_rows(host(b["Wt"]), ref["Wt"]) <= 1e-5
+    assert int(host(b["info"])[0]) == 0
+    # conditional replay on the GPU's own factors and decisions
+    check_uniform_replay(host(b["Wt"]), host(b["U"]), host(b["What_t"]), host(b["scales"]),
+                         host(b["codes"]), 4)
+    # independent end-to-end run: compared by loss
+    loss = float(host(b["loss"])[0])
+    assert abs(loss - ref["loss_t"]) <= 1e-4 * ref["loss_t"]
+    # post-processing inverts the incoherence transforms
+    back = O.incoherence_W_inv(host(b["What_t"]), L.left, L.right)
+    assert P.rel_rows(host(b["What"]), back) <= 1e-5
