@@ -19,170 +19,260 @@
 
 namespace quip {
 
+constexpr int LDL_NB = 64;   // columns per diagonal block (one register column per thread)
+constexpr int LDL_NO = 256;  // columns per outer block (K of the trailing update)
+
 quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, float* D,
                        int32_t* info, void* ws, size_t ws_bytes, hipStream_t s);
 size_t ldl_workspace_bytes(int64_t n);
 
 namespace {
 
-constexpr int NB = 64;
-
 // Factor the w x w diagonal block at (k0, k0) of `src` (upper triangle read).
-// Writes U[k0.., k0..] (whole w x w block, zeros on/below the diagonal or the
-// diagonal blocks), D, R (w x 2w, row-major) and, on the first failure, info.
-template <int G>
-__global__ __launch_bounds__(256) void ldl_diag_kernel(const float* src, int64_t lds_, int64_t k0,
-                                                       int w, float* U, int64_t n, float* D,
-                                                       float* R, int32_t* info) {
-  __shared__ float S[NB][NB + 1];
-  __shared__ float V[NB][NB + 1];
-  __shared__ float Us[NB][NB + 1];
-  __shared__ float dinv[NB][G];  // G = 1: 1/d_k; G = 8: rows of the inverse diagonal block
-  __shared__ float dval[NB][G];
-  __shared__ int bad;
+//
+// Thread (j, q) holds rows [16q, 16q + 16) of column j of the block in
+// registers. A column that has not been pivoted yet holds the partially
+// reduced block S (full symmetric storage); once column j has been pivoted it
+// holds column j of V = (I + U_KK)^{-1}, built as a product of elementary
+// factors V <- (I - u_k e_k^T) V. Both updates of pivot k take the same form
+//     R[i] -= c_i * h_j   (i < k),   c_i = S[i][k],   h_j = R_j[k] / d,
+// except for the pivot column itself, which uses h = 1 + 1/d to turn its S
+// column into the V column (-u). Row k of every column is broadcast through
+// LDS by the row group that holds it (one barrier per pivot, double-buffered).
+// For 8x8 pivots (G = 8) c and h are 8-vectors and 1/d is D_K^{-1}, which one
+// thread computes (Cholesky) into LDS.
+// Outputs: U[k0.., k0..] (the whole w x w block), D, R = [V^T | V^T D^{-1}]
+// (w x 2w, row-major) and, on the first failing pivot, info.
+template <int NB, int G>
+__global__ __launch_bounds__(NB * NB / 16) void ldl_diag_kernel(const float* src, int64_t lds_,
+                                                                int64_t k0, int w, float* U,
+                                                                int64_t n, float* D, float* R,
+                                                                int32_t* info) {
+  constexpr int RG = 16;
+  constexpr int NT = NB * NB / RG;
+  __shared__ float tile[NB][NB + 1];  // input block, then the U block
+  __shared__ __align__(16) float colk[2][G][NB];
+  __shared__ float dsh[NB][G];
+  __shared__ float dinv[NB][G];
+  __shared__ float Dis[8][8];
+  __shared__ float Lsh[8][8], Lish[8][8];
+  __shared__ int bad_sh;
 
-  const int tid = threadIdx.x;
-  for (int e = tid; e < NB * NB; e += 256) {
-    int i = e / NB, j = e % NB;
-    float v = 0.f;
-    if (i < w && j < w) {
-      int a = i < j ? i : j, b = i < j ? j : i;
-      v = src[(k0 + a) * lds_ + (k0 + b)];
+  const int t = threadIdx.x;
+  const int j = t % NB, q = t / NB;
+  const int r0 = RG * q;
+  {
+    constexpr int NL = NB * NB / NT;  // loads per thread, all issued before the stores
+    float v[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = t + NT * i;
+      const int r = e / NB, c = e % NB;
+      v[i] = (r < w && c < w && r <= c) ? src[(k0 + r) * lds_ + (k0 + c)] : 0.f;
     }
-    S[i][j] = v;
-    V[i][j] = i == j ? 1.f : 0.f;
-    Us[i][j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = t + NT * i;
+      tile[e / NB][e % NB] = v[i];
+    }
   }
-  if (tid == 0) bad = -1;
+  if (t == 0) bad_sh = -1;
+  __syncthreads();
+  float Rr[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int i = r0 + r;
+    Rr[r] = (i <= j) ? tile[i][j] : tile[j][i];
+  }
+  __syncthreads();
+  for (int e = t; e < NB * NB; e += NT) tile[e / NB][e % NB] = 0.f;  // becomes the U block
   __syncthreads();
 
-  if (G == 1) {
-    for (int k = w - 1; k >= 0; --k) {
-      const float d = S[k][k];
-      if (tid == 0) {
-        if (!(d > 0.f) && bad < 0) bad = k;
-        dval[k][0] = d;
-        dinv[k][0] = 1.f / d;
+  if constexpr (G == 1) {
+    // pivots k = 16 qk + r, last to first; r is a compile-time register index
+    for (int qk = (w - 1) / RG; qk >= 0; --qk) {
+#pragma unroll
+      for (int r = RG - 1; r >= 0; --r) {
+        const int k = RG * qk + r;
+        if (k < w) {
+          float* ck = colk[k & 1][0];
+          if (q == qk) ck[j] = Rr[r];
+          __syncthreads();
+          // every LDS read of this pivot up front, one wait
+          const float d = ck[k];
+          const float rkj = ck[j];
+          float cc[RG];
+          {
+            const float4* c4 = reinterpret_cast<const float4*>(ck + r0);
+#pragma unroll
+            for (int v = 0; v < RG / 4; ++v) {
+              const float4 c = c4[v];
+              cc[4 * v + 0] = c.x;
+              cc[4 * v + 1] = c.y;
+              cc[4 * v + 2] = c.z;
+              cc[4 * v + 3] = c.w;
+            }
+          }
+          const float rd = __builtin_amdgcn_rcpf(d);  // pivot reciprocal (1 ulp)
+          const float h = (j == k) ? 1.f + rd : rd * rkj;
+          if (t == 0) {
+            if (!(d > 0.f) && bad_sh < 0) bad_sh = k;
+            dsh[k][0] = d;
+            dinv[k][0] = rd;
+          }
+          if (q == 0 && j < k) tile[j][k] = rkj * rd;
+          if (r0 + RG <= k) {  // whole row group above the pivot
+#pragma unroll
+            for (int rr = 0; rr < RG; ++rr) Rr[rr] = fmaf(-cc[rr], h, Rr[rr]);
+          } else if (r0 < k) {  // the row group of the pivot: rows below k are kept
+#pragma unroll
+            for (int rr = 0; rr < RG; ++rr) Rr[rr] = (rr < r) ? fmaf(-cc[rr], h, Rr[rr]) : Rr[rr];
+          }
+          if (j == k && q == qk) Rr[r] = 1.f;
+        }
       }
-      const float rd = 1.f / d;
-      if (tid < k) Us[tid][k] = S[tid][k] * rd;
-      __syncthreads();
-      // S[i][j] -= S[i][k] * u_j  for i <= j < k ;  V[i][j] -= u_i V[k][j] for i < k <= j
-      for (int e = tid; e < k * k; e += 256) {
-        int i = e / k, j = e % k;
-        if (i <= j) S[i][j] -= S[i][k] * Us[j][k];
-      }
-      for (int e = tid; e < k * (w - k); e += 256) {
-        int i = e / (w - k), j = k + e % (w - k);
-        V[i][j] -= Us[i][k] * V[k][j];
-      }
-      __syncthreads();
     }
   } else {
-    __shared__ float Dk[8][8];
-    __shared__ float Di[8][8];
-    for (int kb = w / 8 - 1; kb >= 0; --kb) {
+    for (int qk = (w - 1) / RG; qk >= 0; --qk) {
+#pragma unroll
+    for (int hb = 1; hb >= 0; --hb) {  // the two 8-row halves of row group qk
+      const int kb = 2 * qk + hb;
       const int c0 = kb * 8;
-      if (tid == 0) {
-        // Cholesky of the 8x8 pivot block, then its inverse.
-        float L[8][8];
+      if (c0 >= w) continue;
+      float(*ck)[NB] = colk[kb & 1];
+      if (q == qk) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a) ck[a][j] = Rr[8 * hb + a];
+      }
+      __syncthreads();
+      if (t == 0) {
+        float(*Lc)[8] = Lsh;  // thread 0 works in LDS to keep registers free
         bool ok = true;
-        for (int a = 0; a < 8; ++a)
-          for (int b = 0; b < 8; ++b) {
-            int lo = a < b ? a : b, hi = a < b ? b : a;
-            Dk[a][b] = S[c0 + lo][c0 + hi];
-            L[a][b] = 0.f;
-          }
-        for (int j = 0; j < 8; ++j) {
-          float sdiag = Dk[j][j];
-          for (int t = 0; t < j; ++t) sdiag -= L[j][t] * L[j][t];
-          if (!(sdiag > 0.f)) ok = false;
-          float ljj = sqrtf(sdiag);
-          L[j][j] = ljj;
-          for (int i = j + 1; i < 8; ++i) {
-            float v = Dk[i][j];
-            for (int t = 0; t < j; ++t) v -= L[i][t] * L[j][t];
-            L[i][j] = v / ljj;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+          float sd = ck[a][c0 + a];
+#pragma unroll
+          for (int x = 0; x < a; ++x) sd -= Lc[a][x] * Lc[a][x];
+          ok = ok && (sd > 0.f);
+          const float la = sqrtf(sd);
+          Lc[a][a] = la;
+#pragma unroll
+          for (int b = a + 1; b < 8; ++b) {
+            float v = ck[a][c0 + b];
+#pragma unroll
+            for (int x = 0; x < a; ++x) v -= Lc[b][x] * Lc[a][x];
+            Lc[b][a] = v / la;
           }
         }
-        if (!ok && bad < 0) bad = c0;
-        // inverse of L (lower), then Di = L^-T L^-1
-        float Li[8][8];
+        if (!ok && bad_sh < 0) bad_sh = c0;
+        float(*Li)[8] = Lish;
+#pragma unroll
         for (int c = 0; c < 8; ++c)
+#pragma unroll
           for (int i = 0; i < 8; ++i) {
-            float v = i == c ? 1.f : 0.f;
-            for (int t = c; t < i; ++t) v -= L[i][t] * Li[t][c];
-            Li[i][c] = i < c ? 0.f : v / L[i][i];
+            if (i < c) {
+              Li[i][c] = 0.f;
+            } else {
+              float v = (i == c) ? 1.f : 0.f;
+#pragma unroll
+              for (int x = c; x < i; ++x) v -= Lc[i][x] * Li[x][c];
+              Li[i][c] = v / Lc[i][i];
+            }
           }
+#pragma unroll
         for (int a = 0; a < 8; ++a)
+#pragma unroll
           for (int b = 0; b < 8; ++b) {
             float v = 0.f;
-            for (int t = 0; t < 8; ++t) v += Li[t][a] * Li[t][b];
-            Di[a][b] = v;
-          }
-        for (int a = 0; a < 8; ++a)
-          for (int b = 0; b < 8; ++b) {
-            dinv[c0 + a][b] = Di[a][b];
-            dval[c0 + a][b] = Dk[a][b];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v += Li[x][a] * Li[x][b];
+            Dis[a][b] = v;
+            dinv[c0 + a][b] = v;
+            dsh[c0 + a][b] = ck[b][c0 + a];
           }
       }
       __syncthreads();
-      // U_{i, c0+b} = sum_a S[i][c0+a] Di[a][b], rows i < c0
-      for (int e = tid; e < c0 * 8; e += 256) {
-        int i = e / 8, b = e % 8;
+      const bool piv = (j >= c0) && (j < c0 + 8);
+      const int jp = piv ? j - c0 : 0;
+      float h[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
         float v = 0.f;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) v += S[i][c0 + a] * Di[a][b];
-        Us[i][c0 + b] = v;
+        for (int a = 0; a < 8; ++a) v = fmaf(Dis[b][a], ck[a][j], v);
+        h[b] = piv ? ((b == jp ? 1.f : 0.f) + Dis[b][jp]) : v;
       }
-      __syncthreads();
-      for (int e = tid; e < c0 * c0; e += 256) {
-        int i = e / c0, j = e % c0;
-        if (i <= j) {
+      if (q == 0 && j < c0) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
           float v = 0.f;
 #pragma unroll
-          for (int a = 0; a < 8; ++a) v += Us[i][c0 + a] * S[j][c0 + a];
-          S[i][j] -= v;
+          for (int a = 0; a < 8; ++a) v = fmaf(ck[a][j], Dis[a][b], v);
+          tile[j][c0 + b] = v;
         }
       }
-      for (int e = tid; e < c0 * (w - c0); e += 256) {
-        int i = e / (w - c0), j = c0 + e % (w - c0);
-        float v = 0.f;
+      if (r0 < c0) {
 #pragma unroll
-        for (int a = 0; a < 8; ++a) v += Us[i][c0 + a] * V[c0 + a][j];
-        V[i][j] -= v;
+        for (int b = 0; b < 8; ++b) {
+          const float4* c4 = reinterpret_cast<const float4*>(&ck[b][r0]);
+#pragma unroll
+          for (int v = 0; v < RG / 4; ++v) {
+            const float4 c = c4[v];
+            const float cc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * v + e;
+              const float ci = (r0 + r < c0) ? cc[e] : 0.f;
+              Rr[r] = fmaf(-ci, h[b], Rr[r]);
+            }
+          }
+        }
       }
-      __syncthreads();
-    }
-  }
-
-  // outputs
-  for (int e = tid; e < w * w; e += 256) {
-    int i = e / w, j = e % w;
-    U[(k0 + i) * n + (k0 + j)] = Us[i][j];
-    // R[r][c] = V[c][r] ; R[r][w + c] = sum_b V[b][r] Dinv[b][c]
-    float rv = V[j][i];
-    float rd;
-    if (G == 1) {
-      rd = V[j][i] * dinv[j][0];
-    } else {
-      int cb = (j / 8) * 8;
-      rd = 0.f;
+      if (piv && q == qk) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) rd += V[cb + b][i] * dinv[cb + b][j - cb];
+        for (int a = 0; a < 8; ++a) Rr[8 * hb + a] = (a == jp) ? 1.f : 0.f;
+      }
     }
-    R[i * (2 * w) + j] = rv;
-    R[i * (2 * w) + w + j] = rd;
-  }
-  if (G == 1) {
-    for (int i = tid; i < w; i += 256) D[k0 + i] = dval[i][0];
-  } else {
-    for (int e = tid; e < w * 8; e += 256) {
-      int i = e / 8, b = e % 8;
-      D[(k0 + i) * 8 + b] = dval[i][b];  // block (k0+i)/8, row (k0+i)%8, column b
     }
   }
-  if (tid == 0 && bad >= 0) atomicCAS(info, 0, int32_t(k0 + bad + 1));
+  __syncthreads();
+
+  // U block
+  for (int e = t; e < w * w; e += NT) {
+    const int r = e / w, c = e % w;
+    U[(k0 + r) * n + (k0 + c)] = tile[r][c];
+  }
+  if (q == 0 && j < w) {
+#pragma unroll
+    for (int b = 0; b < G; ++b) D[(k0 + j) * G + b] = dsh[j][b];
+  }
+  // R[j][c] = V[c][j] for c < j (1 at c = j, 0 above); R[j][w + c] = sum_b V[b][j] Dinv[b][c]
+  if (j < w) {
+    float* Rrow = R + j * (2 * w);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int c = r0 + r;
+      if (c < w) {
+        const float v = c < j ? Rr[r] : (c == j ? 1.f : 0.f);
+        Rrow[c] = v;
+        float vd;
+        if constexpr (G == 1) {
+          vd = v * dinv[c][0];
+        } else {
+          const int rb = r & ~7;  // first row of c's 8-block inside this thread
+          vd = 0.f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const int cbb = r0 + rb + b;
+            const float vb = cbb < j ? Rr[rb + b] : (cbb == j ? 1.f : 0.f);
+            vd = fmaf(vb, dinv[cbb][c - (r0 + rb)], vd);
+          }
+        }
+        Rrow[w + c] = vd;
+      }
+    }
+  }
+  if (t == 0 && bad_sh >= 0) atomicCAS(info, 0, int32_t(k0 + bad_sh + 1));
 }
 
 }  // namespace
@@ -190,8 +280,8 @@ __global__ __launch_bounds__(256) void ldl_diag_kernel(const float* src, int64_t
 size_t ldl_workspace_bytes(int64_t n) {
   Carver c(nullptr, 0);
   c.take<float>(size_t(n) * n);       // working copy of the upper triangle
-  c.take<float>(size_t(n) * NB);      // X panel
-  c.take<float>(size_t(NB) * 2 * NB);  // R
+  c.take<float>(size_t(n) * LDL_NO);          // X panel of an outer block
+  c.take<float>(size_t(LDL_NB) * 2 * LDL_NB);  // R
   return c.used;
 }
 
@@ -199,54 +289,90 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
                        int32_t* info, void* ws, size_t ws_bytes, hipStream_t s) {
   Carver c(ws, ws_bytes);
   float* Aw = c.take<float>(size_t(n) * n);
-  float* Xp = c.take<float>(size_t(n) * NB);
+  constexpr int NB = LDL_NB;
+  constexpr int NO = LDL_NO;
+  float* Xp = c.take<float>(size_t(n) * NO);
   float* R = c.take<float>(size_t(NB) * 2 * NB);
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldl: workspace too small");
 
   QUIP_TRY(fill_matrix(U, n, n, n, 0.f, s));
-  {
-    // info <- 0 (one int32): reuse the float fill on its bit pattern
-    QUIP_TRY(fill_f32(reinterpret_cast<float*>(info), 1, 0.f, s));
-  }
-  const int64_t nblk = cdiv(n, NB);
-  bool first = true;
-  for (int64_t K = nblk - 1; K >= 0; --K) {
-    const int64_t k0 = K * NB;
-    const int w = int(n - k0 < NB ? n - k0 : NB);
-    const float* src = first ? H : Aw;
-    const int64_t lsrc = first ? ldh : n;
-    if (g == 1)
-      hipLaunchKernelGGL((ldl_diag_kernel<1>), dim3(1), dim3(256), 0, s, src, lsrc, k0, w, U, n, D,
-                         R, info);
-    else
-      hipLaunchKernelGGL((ldl_diag_kernel<8>), dim3(1), dim3(256), 0, s, src, lsrc, k0, w, U, n, D,
-                         R, info);
-    QUIP_TRY(launch_check("ldl_diag_kernel"));
-    if (k0 == 0) break;
-    // [X | U_IK] = A_IK R
-    GemmArgs p;
-    p.M = k0;
-    p.N = 2 * w;
-    p.K = w;
-    p.A = src + k0;
-    p.lda = lsrc;
-    p.B = R;
-    p.ldb = 2 * w;
-    p.C = Xp;
-    p.ldc = w;
-    p.epi = EPI_SPLIT;
-    p.split = w;
-    p.C2 = U + k0;
-    p.ldc2 = n;
-    QUIP_TRY(gemm(p, s));
-    // A_IJ -= X_I U_J^T  (upper tiles of the leading k0 x k0 block)
+  QUIP_TRY(fill_f32(reinterpret_cast<float*>(info), 1, 0.f, s));  // info <- 0 (bit pattern)
+
+  // Outer blocks of NO columns from the last to the first; inside each, inner
+  // blocks of NB columns (diagonal factor, panel product for every row above,
+  // update of the outer block's remaining columns); then one trailing update
+  // of the leading block with K = NO.
+  const int64_t nouter = cdiv(n, NO);
+  // Which copy holds the current values: the leading block [0, o1)^2 is in Aw
+  // once an outer trailing update has run (aw_lead); inside an outer block its
+  // columns are in Aw once aw_lead held or an inner update has run (aw_outer).
+  bool aw_lead = false;
+  for (int64_t O = nouter - 1; O >= 0; --O) {
+    const int64_t o0 = O * NO;
+    const int64_t o1 = (o0 + NO < n) ? o0 + NO : n;
+    const int64_t nin = cdiv(o1 - o0, NB);
+    bool aw_outer = aw_lead;
+    for (int64_t b = nin - 1; b >= 0; --b) {
+      const int64_t k0 = o0 + b * NB;
+      const int w = int((o1 - k0) < NB ? (o1 - k0) : NB);
+      const float* src = aw_outer ? Aw : H;
+      const int64_t lsrc = aw_outer ? n : ldh;
+      if (g == 1)
+        hipLaunchKernelGGL((ldl_diag_kernel<NB, 1>), dim3(1), dim3(NB * NB / 16), 0, s, src, lsrc,
+                           k0, w, U, n, D, R, info);
+      else
+        hipLaunchKernelGGL((ldl_diag_kernel<NB, 8>), dim3(1), dim3(NB * NB / 16), 0, s, src, lsrc,
+                           k0, w, U, n, D, R, info);
+      QUIP_TRY(launch_check("ldl_diag_kernel"));
+      if (k0 == 0) break;
+      // [X | U_IK] = A_IK R for all rows above the block
+      GemmArgs p;
+      p.M = k0;
+      p.N = 2 * w;
+      p.K = w;
+      p.A = src + k0;
+      p.lda = lsrc;
+      p.B = R;
+      p.ldb = 2 * w;
+      p.C = Xp + (k0 - o0);
+      p.ldc = NO;
+      p.epi = EPI_SPLIT;
+      p.split = w;
+      p.C2 = U + k0;
+      p.ldc2 = n;
+      QUIP_TRY(gemm(p, s));
+      if (b > 0) {
+        // the outer block's columns left of this one: A[:k0, o0:k0] -= X U[o0:k0, blk]^T
+        GemmArgs t;
+        t.M = k0;
+        t.N = k0 - o0;
+        t.K = w;
+        t.A = Xp + (k0 - o0);
+        t.lda = NO;
+        t.B = U + o0 * n + k0;  // op(B)[k][jj] = U[o0 + jj][k0 + k]
+        t.ldb = n;
+        t.transB = true;
+        t.C = Aw + o0;
+        t.ldc = n;
+        t.Cin = src + o0;
+        t.ldcin = lsrc;
+        t.alpha = -1.f;
+        t.beta = 1.f;
+        QUIP_TRY(gemm(t, s));
+        aw_outer = true;
+      }
+    }
+    if (o0 == 0) break;
+    // trailing update of the leading o0 x o0 block (upper tiles), K = outer width
+    const float* src = aw_lead ? Aw : H;
+    const int64_t lsrc = aw_lead ? n : ldh;
     GemmArgs t;
-    t.M = k0;
-    t.N = k0;
-    t.K = w;
+    t.M = o0;
+    t.N = o0;
+    t.K = o1 - o0;
     t.A = Xp;
-    t.lda = w;
-    t.B = U + k0;  // op(B)[k][j] = U[j][k0 + k]
+    t.lda = NO;
+    t.B = U + o0;  // op(B)[k][jj] = U[jj][o0 + k]
     t.ldb = n;
     t.transB = true;
     t.C = Aw;
@@ -257,7 +383,7 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
     t.beta = 1.f;
     t.upper_tiles = true;
     QUIP_TRY(gemm(t, s));
-    first = false;
+    aw_lead = true;
   }
   return QUIP_OK;
 }

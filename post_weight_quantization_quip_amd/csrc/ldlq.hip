@@ -21,6 +21,8 @@
 // 65536 codewords as a distance contraction on the matrix cores
 // (codewords x rows, K = 8), with the per-row argmin kept as a packed
 // (order-preserving distance bits, index) 64-bit key and atomicMin.
+#include <type_traits>
+
 #include "common.h"
 
 namespace quip {
@@ -126,96 +128,206 @@ __global__ __launch_bounds__(256) void grid_scale_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ scalar LDLQ sweep
 
+// Scalar LDLQ sweep of one block of B columns for 16 rows per wave.
+//
+// Lanes: row r = lane / 4 of the wave, quad position g = lane % 4. The block is
+// walked in chunks of 16 columns; inside the current chunk lane g owns the 4
+// columns 16 tk + 4 g + e. A column is rounded by its owner, the error is sent
+// to the other lanes of the quad with one DPP quad_perm, and the 4 current-chunk
+// accumulators of every lane are updated at once (rank-1, registers). The later
+// chunks of the block get one rank-16 update per chunk from the 16 broadcast
+// errors; their accumulators live in per-lane LDS (so the code stays a short
+// loop and every register index is static). U's block is staged in LDS,
+// permuted so that each lane's 4 columns are one float4 and padded so that the
+// 4 lanes of a quad hit different banks.
 template <int B>
 __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
     const float* __restrict__ U, int64_t ldu, const float* __restrict__ scales, int L, int64_t m,
     int64_t s0, int bw, uint8_t* __restrict__ codes, int64_t ldcode, float* __restrict__ What,
-    int64_t ldwh, float* __restrict__ Eb, int64_t lde) {
-  constexpr int NT = B / 16;  // 4-column chunks per lane
-  constexpr int NS = B / 4;   // slots per lane
-  extern __shared__ __align__(16) float Us[];  // [B][4][NS]
+    int64_t ldwh, float* __restrict__ Eb, int64_t lde, bool vec) {
+  constexpr int NT = B / 16;  // 16-column chunks
+  constexpr int NS = B / 4;   // columns per lane over the whole block
+  constexpr int PS = NS + 4;  // padded row of the permuted U block
+  extern __shared__ __align__(16) float sm[];
+  float* Us = sm;                  // [B][4][PS]: Us[(k*4 + g)*PS + 4t + e] = U[s0+k][s0+16t+4g+e]
+  float* Ar = sm + B * 4 * PS;     // [64][NS]: per-lane accumulators of the later chunks
 
   const int lane = threadIdx.x;
   const int g = lane & 3;
   const int64_t row = int64_t(blockIdx.x) * 16 + (lane >> 2);
   const bool live = row < m;
 
-  // U block, permuted: Us[k][gg][4t + e] = U[s0 + k][s0 + 16t + 4gg + e]
-  for (int e = lane; e < B * (B / 4); e += 64) {
-    const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < bw) {
-      const float* src = U + (s0 + k) * ldu + s0 + c4;
-      if (c4 + 0 < bw) v.x = src[0];
-      if (c4 + 1 < bw) v.y = src[1];
-      if (c4 + 2 < bw) v.z = src[2];
-      if (c4 + 3 < bw) v.w = src[3];
-    }
-    const int gg = (c4 >> 2) & 3, t16 = c4 >> 4;
-    *reinterpret_cast<float4*>(&Us[(k * 4 + gg) * NS + 4 * t16]) = v;
-  }
-
-  float w[NS], a[NS];
+  // U block -> LDS in batches: all loads of a batch are issued before any store
+  {
+    constexpr int NL = B * (B / 4) / 64;  // float4 per lane
+    constexpr int BATCH = NL < 16 ? NL : 16;
+    const bool fast = vec && bw == B;
+    for (int b0 = 0; b0 < NL; b0 += BATCH) {
+      float4 v[BATCH];
+      if (fast) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+        for (int i = 0; i < BATCH; ++i) {
+          const int e = lane + 64 * (b0 + i);
+          const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
+          v[i] = *reinterpret_cast<const float4*>(U + (s0 + k) * ldu + s0 + c4);
+        }
+      } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = 16 * t + 4 * g + e;
-      float wv = 0.f, fv = 0.f;
-      if (live && c < bw) {
-        wv = W[row * ldw + s0 + c];
-        if (useF) fv = F[row * ldf + s0 + c];
+        for (int i = 0; i < BATCH; ++i) {
+          const int e = lane + 64 * (b0 + i);
+          const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
+          v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (k < bw) {
+            const float* src = U + (s0 + k) * ldu + s0 + c4;
+            if (c4 + 0 < bw) v[i].x = src[0];
+            if (c4 + 1 < bw) v[i].y = src[1];
+            if (c4 + 2 < bw) v[i].z = src[2];
+            if (c4 + 3 < bw) v[i].w = src[3];
+          }
+        }
       }
-      w[4 * t + e] = wv;
-      a[4 * t + e] = fv;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int e = lane + 64 * (b0 + i);
+        const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
+        const int gg = (c4 >> 2) & 3, t16 = c4 >> 4;
+        *reinterpret_cast<float4*>(&Us[(k * 4 + gg) * PS + 4 * t16]) = v[i];
+      }
     }
+  }
+  auto load4 = [&](const float* base, int64_t ld, int c) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!live) return v;
+    const float* p = base + row * ld + s0 + c;
+    if (vec && c + 3 < bw) return *reinterpret_cast<const float4*>(p);
+    if (c + 0 < bw) v.x = p[0];
+    if (c + 1 < bw) v.y = p[1];
+    if (c + 2 < bw) v.z = p[2];
+    if (c + 3 < bw) v.w = p[3];
+    return v;
+  };
+  {
+    float4 fv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      fv[t] = useF ? load4(F, ldf, 16 * t + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<float4*>(&Ar[lane * NS + 4 * t]) = fv[t];
   }
   __syncthreads();
 
   const float s = live ? scales[row] : 1.f;
+  const float inv = 1.f / s;
   const float half = L * 0.5f, cen = (L - 1) * 0.5f, hi = float(L - 1);
-  uint32_t cw[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) cw[t] = 0u;
 
+  float4 wn = load4(W, ldw, 4 * g);
+  for (int tk = 0; tk < NT; ++tk) {
+    if (16 * tk >= bw) break;
+    float wc[4] = {wn.x, wn.y, wn.z, wn.w};
+    const float4 a4 = *reinterpret_cast<const float4*>(&Ar[lane * NS + 4 * tk]);
+    float ac[4] = {a4.x, a4.y, a4.z, a4.w};
+    if (tk + 1 < NT) wn = load4(W, ldw, 16 * (tk + 1) + 4 * g);
+    const float w0[4] = {wc[0], wc[1], wc[2], wc[3]};
+    const float a0[4] = {ac[0], ac[1], ac[2], ac[3]};
+    // row k = 16 tk + kk of the permuted U block, this lane's 4 columns of chunk tk
+    const float* ub = Us + (64 * tk + g) * PS + 4 * tk;
+    const int nk = (bw - 16 * tk) < 16 ? (bw - 16 * tk) : 16;
+    float e16[16];
+    uint32_t cw = 0u;
+    // One pass over the 16 columns of the chunk. EXACT = false rounds with
+    // p * (1/s); it reports whether an owner lane came within 1e-4 of a
+    // decision boundary, where p * (1/s) and the IEEE quotient p / s might
+    // differ, and then the chunk is redone with EXACT = true.
+    auto pass = [&](auto exact_tag, auto full_tag) -> bool {
+      constexpr bool EXACT = decltype(exact_tag)::value;
+      constexpr bool FULL = decltype(full_tag)::value;
+      bool near = false;
+      float4 u16[16];  // the chunk's 16 rows of U, read up front (off the rounding chain)
 #pragma unroll
-  for (int k = 0; k < B; ++k) {
-    if (k >= bw) break;
-    const int gk = (k >> 2) & 3, tk = k >> 4, ek = k & 3;
-    const int slot = 4 * tk + ek;
-    const float p = w[slot] + a[slot];
-    float kf = floorf(p / s + half);
-    kf = fminf(fmaxf(kf, 0.f), hi);
-    const float qv = (kf - cen) * s;
-    const float err = w[slot] - qv;
-    const float errb = quad_bcast(err, gk);
-    if (g == gk) {
-      w[slot] = qv;
-      a[slot] = err;
-      cw[tk] |= uint32_t(kf) << (8 * ek);
+      for (int kk = 0; kk < 16; ++kk) u16[kk] = *reinterpret_cast<const float4*>(ub + kk * 4 * PS);
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const int gk = kk >> 2, ek = kk & 3;
+        e16[kk] = 0.f;
+        if (!FULL && kk >= nk) continue;
+        const float4 u = u16[kk];
+        const float p = wc[ek] + ac[ek];
+        float y;
+        if constexpr (EXACT) {
+          y = p / s + half;
+        } else {
+          y = fmaf(p, inv, half);
+        }
+        const float kfl = floorf(y);
+        if constexpr (!EXACT) {
+          const float fr = y - kfl;
+          near = near | (live & (g == gk) & ((fr < 1e-4f) | (fr > 0.9999f)));
+        }
+        const float kf = __builtin_amdgcn_fmed3f(kfl, 0.f, hi);
+        const float qv = (kf - cen) * s;
+        const float err = wc[ek] - qv;
+        const float errb = quad_bcast(err, gk);
+        if (g == gk) {
+          wc[ek] = qv;
+          ac[ek] = err;
+          cw |= uint32_t(kf) << (8 * ek);
+        }
+        // columns of this chunk after k (U is zero on and below the diagonal)
+        ac[0] = fmaf(errb, u.x, ac[0]);
+        ac[1] = fmaf(errb, u.y, ac[1]);
+        ac[2] = fmaf(errb, u.z, ac[2]);
+        ac[3] = fmaf(errb, u.w, ac[3]);
+        e16[kk] = errb;
+      }
+      return near;
+    };
+    using T = std::true_type;
+    using Fz = std::false_type;
+    const bool fullchunk = nk == 16;
+    const bool near = fullchunk ? pass(Fz{}, T{}) : pass(Fz{}, Fz{});
+    if (__builtin_amdgcn_ballot_w64(near)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wc[e] = w0[e];
+        ac[e] = a0[e];
+      }
+      cw = 0u;
+      if (fullchunk)
+        pass(T{}, T{});
+      else
+        pass(T{}, Fz{});
     }
-    const float* urow = &Us[(k * 4 + g) * NS];
+    // outputs of this chunk: lane g's columns 16 tk + 4 g + e
+    if (live) {
+      const int c = 16 * tk + 4 * g;
+      if (vec && c + 3 < bw) {
+        *reinterpret_cast<uint32_t*>(codes + row * ldcode + s0 + c) = cw;
+        if (What)
+          *reinterpret_cast<float4*>(What + row * ldwh + s0 + c) = make_float4(wc[0], wc[1], wc[2], wc[3]);
+        *reinterpret_cast<float4*>(Eb + row * lde + c) = make_float4(ac[0], ac[1], ac[2], ac[3]);
+      } else {
 #pragma unroll
-    for (int t = tk; t < NT; ++t) {
-      const float4 u = *reinterpret_cast<const float4*>(urow + 4 * t);
-      a[4 * t + 0] = fmaf(errb, u.x, a[4 * t + 0]);
-      a[4 * t + 1] = fmaf(errb, u.y, a[4 * t + 1]);
-      a[4 * t + 2] = fmaf(errb, u.z, a[4 * t + 2]);
-      a[4 * t + 3] = fmaf(errb, u.w, a[4 * t + 3]);
+        for (int e = 0; e < 4; ++e) {
+          if (c + e >= bw) continue;
+          codes[row * ldcode + s0 + c + e] = uint8_t((cw >> (8 * e)) & 0xFF);
+          if (What) What[row * ldwh + s0 + c + e] = wc[e];
+          Eb[row * lde + c + e] = ac[e];
+        }
+      }
     }
-  }
-
-  if (!live) return;
+    // rank-16 update of the later chunks
+    for (int t = tk + 1; t < NT; ++t) {
+      float4 acc = *reinterpret_cast<const float4*>(&Ar[lane * NS + 4 * t]);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = 16 * t + 4 * g + e;
-      if (c >= bw) continue;
-      codes[row * ldcode + s0 + c] = uint8_t((cw[t] >> (8 * e)) & 0xFF);
-      if (What) What[row * ldwh + s0 + c] = w[4 * t + e];
-      Eb[row * lde + c] = a[4 * t + e];
+      for (int kk = 0; kk < 16; ++kk) {
+        const float4 u = *reinterpret_cast<const float4*>(ub + kk * 4 * PS + 4 * (t - tk));
+        acc.x = fmaf(e16[kk], u.x, acc.x);
+        acc.y = fmaf(e16[kk], u.y, acc.y);
+        acc.z = fmaf(e16[kk], u.z, acc.z);
+        acc.w = fmaf(e16[kk], u.w, acc.w);
+      }
+      *reinterpret_cast<float4*>(&Ar[lane * NS + 4 * t]) = acc;
     }
   }
 }
@@ -485,12 +597,19 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
                     const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                     int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
                     int64_t lde, hipStream_t s) {
-  const size_t shmem = size_t(B) * B * sizeof(float);
+  const size_t shmem = (size_t(B) * 4 * (B / 4 + 4) + size_t(64) * (B / 4)) * sizeof(float);
   if (shmem > 65536)
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+  // float4 paths need 16-byte alignment of every row start and of the block start
+  const bool vec = aligned16(W) && aligned16(F) && aligned16(U) && aligned16(Eb) &&
+                   (What == nullptr || aligned16(What)) &&
+                   ((reinterpret_cast<uintptr_t>(codes) & 3) == 0) && ldw % 4 == 0 &&
+                   ldf % 4 == 0 && ldu % 4 == 0 && ldc % 4 == 0 && ldwh % 4 == 0 &&
+                   lde % 4 == 0 && s0 % 4 == 0;
   hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(64), shmem, s, W, ldw,
-                     F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde);
+                     F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
+                     vec);
   return launch_check("ldlq_sweep_kernel");
 }
 
