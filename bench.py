@@ -41,7 +41,108 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of W in the oracle LDLQ sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with one plain device copy of COPY_MIB MiB (counter calibration)")
+    # summaries of rocprofv3 result databases (host only, no GPU)
+    ap.add_argument("--summarize-trace", metavar="DB")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--kernel", default=DOMINANT_KERNEL)
+    ap.add_argument("--command", default="")
+    ap.add_argument("--out")
     return ap.parse_args()
+
+
+DOMINANT_KERNEL = "gemm_kernel<128, 128, true, false, 0>"  # the Hessian contraction
+COPY_MIB = 256
+COPY_KERNEL = "MulFunctor"  # torch.mul(src, 1.0, out=dst): reads and writes COPY_MIB MiB
+
+
+def _kernel_rows(db):
+    import re
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    out = []
+    for name, start, end in con.execute("select name, start, end from kernels"):
+        nm = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        nm = re.sub(r"\(.*", "", nm)
+        out.append((nm, (end - start) / 1e3))
+    return out
+
+
+def summarize_trace(db, command, out):
+    rows = _kernel_rows(db)
+    agg = {}
+    for nm, d in rows:
+        a = agg.setdefault(nm, [0.0, 0])
+        a[0] += d
+        a[1] += 1
+    tot = sum(v[0] for v in agg.values())
+    lines = ["# rocprofv3 kernel trace: quantization pass, 4096 x 4096 layer (2-bit, RHT, B = 128)", "",
+             f"Command: `{command}`", "",
+             "| kernel | calls | total us | avg us | % |", "|---|---:|---:|---:|---:|"]
+    for k, (t, c) in sorted(agg.items(), key=lambda kv: -kv[1][0]):
+        lines.append(f"| `{k}` | {c} | {t:.1f} | {t / c:.2f} | {100 * t / tot:.1f} |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def _counter(db, counter):
+    import re
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    per = {}
+    for name, value in con.execute(
+            "select kernel_name, value from counters_collection where counter_name = ?", (counter,)):
+        nm = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        nm = re.sub(r"\(.*", "", nm)
+        per.setdefault(nm, []).append(float(value))
+    return per
+
+
+def summarize_counters(fetch_db, write_db, kernel, command, out):
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the counter reads for a plain copy of
+    COPY_MIB MiB (read and written once)."""
+    import hashlib
+
+    fetch = _counter(fetch_db, "FETCH_SIZE")
+    write = _counter(write_db, "WRITE_SIZE")
+
+    def pick(per, key):
+        hits = [v for k, v in per.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of {key} in the counter database")
+        vals = max(hits, key=len)
+        return float(np.mean(vals)), len(vals)
+
+    kf, nf = pick(fetch, kernel)
+    kw, nw = pick(write, kernel)
+    cf, _ = pick(fetch, COPY_KERNEL)
+    cw, _ = pick(write, COPY_KERNEL)
+    nbytes = COPY_MIB * 2 ** 20
+    f_read = nbytes / (cf * 1024.0)
+    f_write = nbytes / (cw * 1024.0)
+    rd = kf * 1024.0 * f_read
+    wr = kw * 1024.0 * f_write
+    src = os.path.join(ROOT, "post_weight_quantization_quip_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    d = {"kernel_prefix": "gemm_kernel", "kernel": kernel, "source_sha": sha,
+         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [nf, nw],
+         "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes_each_way": nbytes,
+         "scale_read": f_read, "scale_write": f_write,
+         "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+         "bytes_per_launch": rd + wr, "command": command}
+    text = json.dumps(d, indent=1)
+    if out:
+        with open(out, "w") as f:
+            f.write(text + "\n")
+    print(text)
 
 
 def traffic_from_profiles(kernel_prefix: str):
@@ -119,6 +220,12 @@ def cpu_baseline(cfg_name: str, rows: int) -> dict:
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command, args.out)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.kernel, args.command, args.out)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the pass is single-GPU here; see DESIGN.md for how it would shard)", file=sys.stderr)
@@ -186,9 +293,12 @@ def main():
     syrk_flops = cfg.N * cfg.n * (cfg.n + 1)
     achieved = syrk_flops / (syrk_ms / 1e3) / 1e12
     traffic = traffic_from_profiles("gemm_kernel")
+    if traffic is not None:
+        traffic = round(traffic / 1e6, 1)  # MB per launch
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "gemm_kernel<128,128,transA,!transB> (Hessian X^T X)",
+                "traffic": traffic, "traffic_unit": "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "kernel": "gemm_kernel<128,128,transA,!transB> (Hessian X^T X)",
                 "algorithmic_flops_per_launch": syrk_flops, "avg_launch_ms": round(syrk_ms, 4)}
 
     # RHT bandwidth per one-sided pass (W, 4096 x 4096)
@@ -238,6 +348,11 @@ def main():
         "rht": rht,
         "roofline": roofline,
     }
+    if args.calibrate_copy:
+        src = torch.ones(COPY_MIB * 2 ** 20 // 4, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_rows)
     print(json.dumps(line))
