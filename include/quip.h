@@ -232,7 +232,8 @@ quip_status quip_ldlq(const float* W, int64_t m, int64_t n, int64_t ldw, const f
 /*
  * quip_proxy_loss -- loss = tr((W^ - W) H (W^ - W)^T) ([QuIP] "Introduction":
  * the proxy objective), accumulated in float64.
- *   W, What: m x n, both with leading dim ld. H: n x n, leading dim ldh.
+ *   W, What: m x n, both with leading dim ld. H: n x n symmetric, leading
+ *   dim ldh; only its upper triangle is read.
  *   loss_dev: one device double, overwritten.
  *   ws: device workspace of quip_proxy_loss_workspace() bytes.
  * Errors: QUIP_ERR_ARG, QUIP_ERR_WORKSPACE.

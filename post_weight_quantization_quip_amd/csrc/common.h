@@ -86,7 +86,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 enum GemmEpi {
   EPI_STORE = 0,  // C_out = alpha * op(A) op(B) + beta * C_in
   EPI_DOT = 1,    // *dot += sum(alpha * op(A) op(B) .* E)  (float64 accumulate)
-  EPI_SPLIT = 2   // like STORE, columns >= split go to C2 (ldc2) at column - split
+  EPI_SPLIT = 2,  // like STORE, columns >= split go to C2 (ldc2) at column - split
+  EPI_DOT_SYM = 3 // like DOT with B symmetric (K == N): only B's upper triangle is read,
+                  // off-diagonal entries count twice, so output column j sums k <= j only
 };
 
 struct GemmArgs {

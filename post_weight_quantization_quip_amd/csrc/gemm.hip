@@ -10,8 +10,9 @@
 // {64, 128}); each wave owns a (BM/2) x (BN/2) sub-tile made of 32x32 blocks
 // computed with v_mfma_f32_32x32x2f32 (wave64: A operand lane = i + 32k,
 // B operand lane = j + 32k, D element (i, j) in lane j + 32*((i/4)%2),
-// register (i%4) + 4*(i/8)). K advances 16 at a time through double-buffered
+// register (i%4) + 4*(i/8)). K advances 32 at a time through double-buffered
 // LDS tiles stored K-major, so every operand read is 32 consecutive floats.
+// The beta term's C tile is read into registers before the K loop.
 // Work-group ids are remapped so that neighbouring tiles share an XCD's L2.
 #include "common.h"
 
@@ -20,7 +21,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 16;
+constexpr int BK = 32;
 constexpr int PAD = 4;
 
 __device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t col, int64_t ld,
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile coordinates
-  int bid = xcd_remap(blockIdx.x, total);
+  int bid = (EPI == EPI_DOT_SYM) ? int(blockIdx.x) : xcd_remap(blockIdx.x, total);
   int tm, tn;
   if (a.upper_tiles) {
     int rem = bid, r = 0;
@@ -65,6 +66,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
     }
     tm = r;
     tn = r + rem;
+  } else if (EPI == EPI_DOT_SYM) {
+    // column tile tn has K range [0, (tn+1) BN): longest tiles first, dealt
+    // round-robin over the XCDs, so the short ones fill the tail
+    tm = bid % tiles_m;
+    tn = tiles_n - 1 - bid / tiles_m;
   } else {
     const int G = 8;
     int per_group = G * tiles_n;
@@ -77,7 +83,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   }
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t bz = blockIdx.y;
-
   const float* A = a.A + bz * a.strideA;
   const float* B = a.B + bz * a.strideB;
 
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
         ra[i] = load4(A, k0 + k, m0 + m4, a.lda, a.K, a.M, vecA);
       } else {
-        int m = idx / 4, k4 = (idx % 4) * 4;
+        int m = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
         ra[i] = load4(A, m0 + m, k0 + k4, a.lda, a.M, a.K, vecA);
       }
     }
@@ -102,12 +107,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         int k = idx / (BN / 4), n4 = (idx % (BN / 4)) * 4;
         rb[i] = load4(B, k0 + k, n0 + n4, a.ldb, a.K, a.N, vecB);
       } else {
-        int n = idx / 4, k4 = (idx % 4) * 4;
+        int n = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
         rb[i] = load4(B, n0 + n, k0 + k4, a.ldb, a.N, a.K, vecB);
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int64_t kcur) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       int idx = tid + 256 * i;
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
         *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[i];
       } else {
-        int m = idx / 4, k4 = (idx % 4) * 4;
+        int m = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
         As[buf][k4 + 0][m] = ra[i].x;
         As[buf][k4 + 1][m] = ra[i].y;
         As[buf][k4 + 2][m] = ra[i].z;
@@ -127,9 +132,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       int idx = tid + 256 * i;
       if (!TB) {
         int k = idx / (BN / 4), n4 = (idx % (BN / 4)) * 4;
-        *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = rb[i];
+        float4 v = rb[i];
+        if (EPI == EPI_DOT_SYM) {
+          // upper triangle of B, off-diagonal entries doubled
+          const int kd = int(kcur - n0) + k - n4;  // row minus column of v.x
+          v.x = kd > 0 ? 0.f : (kd == 0 ? v.x : 2.f * v.x);
+          v.y = kd > 1 ? 0.f : (kd == 1 ? v.y : 2.f * v.y);
+          v.z = kd > 2 ? 0.f : (kd == 2 ? v.z : 2.f * v.z);
+          v.w = kd > 3 ? 0.f : (kd == 3 ? v.w : 2.f * v.w);
+        }
+        *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = v;
       } else {
-        int n = idx / 4, k4 = (idx % 4) * 4;
+        int n = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
         Bs[buf][k4 + 0][n] = rb[i].x;
         Bs[buf][k4 + 1][n] = rb[i].y;
         Bs[buf][k4 + 2][n] = rb[i].z;
@@ -146,13 +160,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int64_t nk = (a.K + BK - 1) / BK;
+  // C_in for the beta term, read before the K loop so its latency overlaps it
+  float* C = a.C + bz * a.strideC;
+  const float* Cin = a.Cin ? a.Cin + bz * a.strideCin : C;
+  const int64_t ldcin = a.Cin ? a.ldcin : a.ldc;
+  const int krow = lane >> 5, kcol = lane & 31;
+  f32x16 cpre[WBM][WBN];
+  const bool useC = (EPI == EPI_STORE || EPI == EPI_SPLIT) && a.beta != 0.f;
+  if (useC) {
+#pragma unroll
+    for (int i = 0; i < WBM; ++i)
+#pragma unroll
+      for (int j = 0; j < WBN; ++j) {
+        const int64_t col = n0 + wn * (BN / 2) + j * 32 + kcol;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * krow + (r % 4);
+          cpre[i][j][r] = (row < a.M && col < a.N) ? Cin[row * ldcin + col] : 0.f;
+        }
+      }
+  }
+
+  int64_t kend = a.K;
+  if (EPI == EPI_DOT_SYM) kend = (n0 + BN < a.K) ? n0 + BN : a.K;  // rows k <= last column
+  const int64_t nk = (kend + BK - 1) / BK;
   if (nk > 0) {
     gload(0);
-    sstore(0);
+    sstore(0, 0);
     __syncthreads();
   }
-  const int krow = lane >> 5, kcol = lane & 31;
   int buf = 0;
   for (int64_t kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) gload((kt + 1) * BK);
@@ -169,15 +205,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         for (int j = 0; j < WBN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + 1 < nk) sstore(buf ^ 1, (kt + 1) * BK);
     __syncthreads();
     buf ^= 1;
   }
 
   // ---- epilogue
-  float* C = a.C + bz * a.strideC;
-  const float* Cin = a.Cin ? a.Cin + bz * a.strideCin : C;
-  const int64_t ldcin = a.Cin ? a.ldcin : a.ldc;
   double dsum = 0.0;
 #pragma unroll
   for (int i = 0; i < WBM; ++i) {
@@ -189,10 +222,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         const int64_t row = m0 + wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * krow + (r % 4);
         if (row >= a.M || col >= a.N) continue;
         float v = a.alpha * acc[i][j][r];
-        if (EPI == EPI_DOT) {
+        if (EPI == EPI_DOT || EPI == EPI_DOT_SYM) {
           dsum += double(v) * double(a.E[row * a.lde + col]);
         } else {
-          if (a.beta != 0.f) v += a.beta * Cin[row * ldcin + col];
+          if (useC) v += a.beta * cpre[i][j][r];
           if (EPI == EPI_SPLIT && col >= a.split)
             a.C2[row * a.ldc2 + (col - a.split)] = v;
           else
@@ -206,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       }
     }
   }
-  if (EPI == EPI_DOT) {
+  if (EPI == EPI_DOT || EPI == EPI_DOT_SYM) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dsum += __shfl_down(dsum, off, 64);
     if (lane == 0) atomicAdd(a.dot, dsum);
@@ -259,6 +292,9 @@ quip_status gemm(const GemmArgs& a, hipStream_t s) {
     case EPI_STORE: return launch_epi<EPI_STORE>(a, s, vecA, vecB);
     case EPI_DOT: return launch_epi<EPI_DOT>(a, s, vecA, vecB);
     case EPI_SPLIT: return launch_epi<EPI_SPLIT>(a, s, vecA, vecB);
+    case EPI_DOT_SYM:
+      if (a.transB || a.K != a.N) return fail(QUIP_ERR_ARG, "gemm: symmetric dot needs B square, not transposed");
+      return launch_epi<EPI_DOT_SYM>(a, s, vecA, vecB);
   }
   return fail(QUIP_ERR_ARG, "gemm: bad epilogue");
 }

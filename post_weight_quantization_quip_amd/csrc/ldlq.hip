@@ -687,11 +687,22 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
 }
 
+// Trailing-update batch of the scalar sweep: the lazily updated block of B
+// columns is swept in sub-blocks of at most 128 columns (the sweep kernel), the
+// rest of each 512-column batch is updated after every sub-block, and the rest
+// of the matrix once per batch (one K = 512 product instead of four K = 128
+// ones: a quarter of the read-modify-write traffic of F).
+static int64_t outer_block(int64_t n, int g, int64_t B) {
+  if (g != 1) return B;
+  int64_t bo = B >= 512 ? B : B * (512 / B);
+  return bo < n ? bo : n;
+}
+
 size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_quantizer& q) {
   Carver c(nullptr, 0);
   c.take<float>(64);
   c.take<float>(size_t(m) * n);  // F
-  c.take<float>(size_t(m) * B);  // Eb
+  c.take<float>(size_t(m) * outer_block(n, g, B));  // Eb
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
     c.take<unsigned long long>(size_t(m));
@@ -710,7 +721,8 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   Carver c(ws, ws_bytes);
   float* fac = c.take<float>(64);
   float* F = c.take<float>(size_t(m) * n);
-  float* Eb = c.take<float>(size_t(m) * B);
+  const int64_t Bo = outer_block(n, g, B);
+  float* Eb = c.take<float>(size_t(m) * Bo);
   float hostf[64];
 
   if (q.kind == QUIP_Q_UNIFORM) {
@@ -723,17 +735,17 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
     }
     const int bi = B >= 128 ? 128 : (B >= 64 ? 64 : 32);
     uint8_t* cd = static_cast<uint8_t*>(codes);
-    for (int64_t j0 = 0; j0 < n; j0 += B) {
-      const int64_t bo = (n - j0 < B) ? n - j0 : B;
+    for (int64_t j0 = 0; j0 < n; j0 += Bo) {
+      const int64_t bo = (n - j0 < Bo) ? n - j0 : Bo;
       for (int64_t s0 = j0; s0 < j0 + bo; s0 += bi) {
         const int bw = int((j0 + bo - s0) < bi ? (j0 + bo - s0) : bi);
         QUIP_TRY(sweep(bi, W, ldw, F, n, s0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
-                       Eb + (s0 - j0), B, s));
-        // rest of this outer block
-        QUIP_TRY(feedback_gemm(Eb, B, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
+                       Eb + (s0 - j0), Bo, s));
+        // rest of this batch
+        QUIP_TRY(feedback_gemm(Eb, Bo, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
                                !(j0 == 0 && s0 == 0), s));
       }
-      QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
+      QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
     }
     return QUIP_OK;
   }

@@ -1,7 +1,9 @@
 // Proxy loss tr((W^ - W) H (W^ - W)^T) (QuIP, "Introduction": the quadratic
 // proxy objective): E = W^ - W, then the contraction E H on the matrix cores
 // with a fused epilogue that multiplies by E and sums in float64, so the
-// m x n product E H is never written to memory.
+// m x n product E H is never written to memory. H is symmetric, so only its
+// upper triangle is used (sum_{i<=j} E_ri H'_ij E_rj with H'_ij = 2 H_ij off the
+// diagonal): half the flops of the full product.
 #include "common.h"
 
 namespace quip {
@@ -28,7 +30,7 @@ quip_status proxy_loss(const float* W, const float* What, int64_t m, int64_t n, 
   g.lda = n;
   g.B = H;
   g.ldb = ldh;
-  g.epi = EPI_DOT;
+  g.epi = EPI_DOT_SYM;  // H symmetric: its upper triangle, off-diagonal counted twice
   g.E = E;
   g.lde = n;
   g.dot = loss;
