@@ -89,6 +89,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   float4 ra[LA], rb[LB];
 
   auto gload = [&](int64_t k0) {
+    const bool fullA = vecA && k0 + BK <= a.K && (TA ? (m0 + BM <= a.M) : (m0 + BM <= a.M));
+    const bool fullB = vecB && k0 + BK <= a.K && n0 + BN <= a.N;
+    if (fullA) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) {
+        int idx = tid + 256 * i;
+        if (TA) {
+          int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
+          ra[i] = *reinterpret_cast<const float4*>(A + (k0 + k) * a.lda + m0 + m4);
+        } else {
+          int m = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
+          ra[i] = *reinterpret_cast<const float4*>(A + (m0 + m) * a.lda + k0 + k4);
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       int idx = tid + 256 * i;
@@ -100,6 +115,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         ra[i] = load4(A, m0 + m, k0 + k4, a.lda, a.M, a.K, vecA);
       }
     }
+    }
+    if (fullB) {
+#pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        int idx = tid + 256 * i;
+        if (!TB) {
+          int k = idx / (BN / 4), n4 = (idx % (BN / 4)) * 4;
+          rb[i] = *reinterpret_cast<const float4*>(B + (k0 + k) * a.ldb + n0 + n4);
+        } else {
+          int n = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
+          rb[i] = *reinterpret_cast<const float4*>(B + (n0 + n) * a.ldb + k0 + k4);
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       int idx = tid + 256 * i;
@@ -110,6 +139,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         int n = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
         rb[i] = load4(B, n0 + n, k0 + k4, a.ldb, a.N, a.K, vecB);
       }
+    }
     }
   };
   auto sstore = [&](int buf, int64_t kcur) {

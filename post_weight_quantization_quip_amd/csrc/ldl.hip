@@ -4,23 +4,27 @@
 // page under "Builds on").
 //
 // Blocked right-looking algorithm working from the last column block to the
-// first, with NB = 64 columns per block:
-//   1. ldl_diag_kernel (one work-group): factor the NB x NB diagonal block
-//      A_KK = (I + U_KK) D_K (I + U_KK)^T in LDS, building on the way the
-//      inverse V = (I + U_KK)^{-1} as a product of elementary factors, and
-//      emit R = [V^T | V^T D_K^{-1}].
-//   2. Panel product on the matrix cores: [X | U_IK] = A_IK R for the rows
-//      above the block (X = U_IK D_K).
-//   3. Trailing update on the matrix cores, upper tiles only:
-//      A_IJ -= X_I U_JK^T for I, J above the block.
+// first, NB = 64 columns per block:
+//   1. ldl_block_kernel: every work-group takes PR rows above the block and
+//      the NB x NB diagonal block A_KK, factors A_KK (redundantly: each group
+//      computes bit-identical factors, so no group waits for another) and
+//      turns its rows into U_IK = A_IK (I + U_KK)^{-T} D_K^{-1} and
+//      X_IK = U_IK D_K.
+//   2. Trailing update on the matrix cores, upper tiles only:
+//      A_IJ -= X_I U_JK^T for I, J above the block (two levels: the columns of
+//      the current NO-wide outer block right away, the rest once per outer
+//      block with K = NO).
 // The input is never modified: the first trailing update reads H and writes
 // the workspace copy.
+#include <utility>
+
 #include "common.h"
 
 namespace quip {
 
-constexpr int LDL_NB = 64;   // columns per diagonal block (one register column per thread)
-constexpr int LDL_NO = 256;  // columns per outer block (K of the trailing update)
+constexpr int LDL_NB = 64;   // columns per diagonal block
+constexpr int LDL_NO = 256;  // columns per outer block (K of the outer trailing update)
+constexpr int LDL_PR = 64;   // rows above the diagonal block per work-group
 
 quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, float* D,
                        int32_t* info, void* ws, size_t ws_bytes, hipStream_t s);
@@ -28,251 +32,426 @@ size_t ldl_workspace_bytes(int64_t n);
 
 namespace {
 
-// Factor the w x w diagonal block at (k0, k0) of `src` (upper triangle read).
-//
-// Thread (j, q) holds rows [16q, 16q + 16) of column j of the block in
-// registers. A column that has not been pivoted yet holds the partially
-// reduced block S (full symmetric storage); once column j has been pivoted it
-// holds column j of V = (I + U_KK)^{-1}, built as a product of elementary
-// factors V <- (I - u_k e_k^T) V. Both updates of pivot k take the same form
-//     R[i] -= c_i * h_j   (i < k),   c_i = S[i][k],   h_j = R_j[k] / d,
-// except for the pivot column itself, which uses h = 1 + 1/d to turn its S
-// column into the V column (-u). Row k of every column is broadcast through
-// LDS by the row group that holds it (one barrier per pivot, double-buffered).
-// For 8x8 pivots (G = 8) c and h are 8-vectors and 1/d is D_K^{-1}, which one
-// thread computes (Cholesky) into LDS.
-// Outputs: U[k0.., k0..] (the whole w x w block), D, R = [V^T | V^T D^{-1}]
-// (w x 2w, row-major) and, on the first failing pivot, info.
-template <int NB, int G>
-__global__ __launch_bounds__(NB * NB / 16) void ldl_diag_kernel(const float* src, int64_t lds_,
-                                                                int64_t k0, int w, float* U,
-                                                                int64_t n, float* D, float* R,
-                                                                int32_t* info) {
-  constexpr int RG = 16;
-  constexpr int NT = NB * NB / RG;
-  __shared__ float tile[NB][NB + 1];  // input block, then the U block
-  __shared__ __align__(16) float colk[2][G][NB];
-  __shared__ float dsh[NB][G];
-  __shared__ float dinv[NB][G];
-  __shared__ float Dis[8][8];
-  __shared__ float Lsh[8][8], Lish[8][8];
-  __shared__ int bad_sh;
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_(f, std::make_integer_sequence<int, N>{});
+}
 
+// Value of lane J of this lane's 16-lane row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xF, 0xF, false));
+}
+
+// Cholesky of the 8x8 block P (upper triangle read) followed by its inverse;
+// every lane computes the same values. Returns false on a non-positive pivot.
+__device__ bool chol_inv8(const float (*P)[17], int r0, float (&Pinv)[8][8]) {
+  float L[8][8];
+  bool ok = true;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    float sd = P[r0 + a][r0 + a];
+#pragma unroll
+    for (int x = 0; x < a; ++x) sd = fmaf(-L[a][x], L[a][x], sd);
+    ok = ok && (sd > 0.f);
+    const float la = sqrtf(sd);
+    const float rla = 1.f / la;
+    L[a][a] = la;
+#pragma unroll
+    for (int b = a + 1; b < 8; ++b) {
+      float v = P[r0 + a][r0 + b];
+#pragma unroll
+      for (int x = 0; x < a; ++x) v = fmaf(-L[b][x], L[a][x], v);
+      L[b][a] = v * rla;
+    }
+  }
+  float Li[8][8];  // L^{-1}, lower triangular
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < c) {
+        Li[i][c] = 0.f;
+      } else {
+        float v = (i == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int x = c; x < i; ++x) v = fmaf(-L[i][x], Li[x][c], v);
+        Li[i][c] = v / L[i][i];
+      }
+    }
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      float v = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) v = fmaf(Li[x][a], Li[x][b], v);
+      Pinv[a][b] = v;
+    }
+  return ok;
+}
+
+// Moves a rows x 64 block between global memory (leading dimension ld, first
+// `cols` columns valid, rows below `nrows` absent) and an LDS tile with 65
+// floats per row; float4 accesses when `vec`.
+template <int NT, int R, bool LOAD>
+__device__ __forceinline__ void tile_io(float (*T)[65], const float* gsrc, float* gdst, int64_t ld,
+                                        int nrows, int cols, bool vec) {
   const int t = threadIdx.x;
-  const int j = t % NB, q = t / NB;
-  const int r0 = RG * q;
-  {
-    constexpr int NL = NB * NB / NT;  // loads per thread, all issued before the stores
-    float v[NL];
+  if (vec) {
+    constexpr int NV = (R * 16 + NT - 1) / NT;
+    float4 v[NV];
+    if (LOAD) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int e = t + NT * i;
-      const int r = e / NB, c = e % NB;
-      v[i] = (r < w && c < w && r <= c) ? src[(k0 + r) * lds_ + (k0 + c)] : 0.f;
-    }
+      for (int i = 0; i < NV; ++i) {
+        const int e = t + NT * i, a = e / 16, c4 = (e % 16) * 4;
+        v[i] = (e < R * 16 && a < nrows) ? *reinterpret_cast<const float4*>(gsrc + a * ld + c4)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int e = t + NT * i;
-      tile[e / NB][e % NB] = v[i];
-    }
-  }
-  if (t == 0) bad_sh = -1;
-  __syncthreads();
-  float Rr[RG];
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int i = r0 + r;
-    Rr[r] = (i <= j) ? tile[i][j] : tile[j][i];
-  }
-  __syncthreads();
-  for (int e = t; e < NB * NB; e += NT) tile[e / NB][e % NB] = 0.f;  // becomes the U block
-  __syncthreads();
-
-  if constexpr (G == 1) {
-    // pivots k = 16 qk + r, last to first; r is a compile-time register index
-    for (int qk = (w - 1) / RG; qk >= 0; --qk) {
-#pragma unroll
-      for (int r = RG - 1; r >= 0; --r) {
-        const int k = RG * qk + r;
-        if (k < w) {
-          float* ck = colk[k & 1][0];
-          if (q == qk) ck[j] = Rr[r];
-          __syncthreads();
-          // every LDS read of this pivot up front, one wait
-          const float d = ck[k];
-          const float rkj = ck[j];
-          float cc[RG];
-          {
-            const float4* c4 = reinterpret_cast<const float4*>(ck + r0);
-#pragma unroll
-            for (int v = 0; v < RG / 4; ++v) {
-              const float4 c = c4[v];
-              cc[4 * v + 0] = c.x;
-              cc[4 * v + 1] = c.y;
-              cc[4 * v + 2] = c.z;
-              cc[4 * v + 3] = c.w;
-            }
-          }
-          const float rd = __builtin_amdgcn_rcpf(d);  // pivot reciprocal (1 ulp)
-          const float h = (j == k) ? 1.f + rd : rd * rkj;
-          if (t == 0) {
-            if (!(d > 0.f) && bad_sh < 0) bad_sh = k;
-            dsh[k][0] = d;
-            dinv[k][0] = rd;
-          }
-          if (q == 0 && j < k) tile[j][k] = rkj * rd;
-          if (r0 + RG <= k) {  // whole row group above the pivot
-#pragma unroll
-            for (int rr = 0; rr < RG; ++rr) Rr[rr] = fmaf(-cc[rr], h, Rr[rr]);
-          } else if (r0 < k) {  // the row group of the pivot: rows below k are kept
-#pragma unroll
-            for (int rr = 0; rr < RG; ++rr) Rr[rr] = (rr < r) ? fmaf(-cc[rr], h, Rr[rr]) : Rr[rr];
-          }
-          if (j == k && q == qk) Rr[r] = 1.f;
+      for (int i = 0; i < NV; ++i) {
+        const int e = t + NT * i, a = e / 16, c4 = (e % 16) * 4;
+        if (e < R * 16) {
+          T[a][c4 + 0] = v[i].x;
+          T[a][c4 + 1] = v[i].y;
+          T[a][c4 + 2] = v[i].z;
+          T[a][c4 + 3] = v[i].w;
         }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = t + NT * i, a = e / 16, c4 = (e % 16) * 4;
+        if (e < R * 16 && a < nrows)
+          *reinterpret_cast<float4*>(gdst + a * ld + c4) =
+              make_float4(T[a][c4 + 0], T[a][c4 + 1], T[a][c4 + 2], T[a][c4 + 3]);
       }
     }
   } else {
-    for (int qk = (w - 1) / RG; qk >= 0; --qk) {
+    constexpr int NS = (R * 64 + NT - 1) / NT;
+    float v[NS];
+    if (LOAD) {
 #pragma unroll
-    for (int hb = 1; hb >= 0; --hb) {  // the two 8-row halves of row group qk
-      const int kb = 2 * qk + hb;
-      const int c0 = kb * 8;
-      if (c0 >= w) continue;
-      float(*ck)[NB] = colk[kb & 1];
-      if (q == qk) {
-#pragma unroll
-        for (int a = 0; a < 8; ++a) ck[a][j] = Rr[8 * hb + a];
+      for (int i = 0; i < NS; ++i) {
+        const int e = t + NT * i, a = e / 64, c = e % 64;
+        v[i] = (e < R * 64 && a < nrows && c < cols) ? gsrc[a * ld + c] : 0.f;
       }
-      __syncthreads();
-      if (t == 0) {
-        float(*Lc)[8] = Lsh;  // thread 0 works in LDS to keep registers free
-        bool ok = true;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          float sd = ck[a][c0 + a];
+      for (int i = 0; i < NS; ++i) {
+        const int e = t + NT * i;
+        if (e < R * 64) T[e / 64][e % 64] = v[i];
+      }
+    } else {
 #pragma unroll
-          for (int x = 0; x < a; ++x) sd -= Lc[a][x] * Lc[a][x];
-          ok = ok && (sd > 0.f);
-          const float la = sqrtf(sd);
-          Lc[a][a] = la;
+      for (int i = 0; i < NS; ++i) {
+        const int e = t + NT * i, a = e / 64, c = e % 64;
+        if (e < R * 64 && a < nrows && c < cols) gdst[a * ld + c] = T[a][c];
+      }
+    }
+  }
+}
+
+// One diagonal block and PR rows above it.
+//
+// Layout: thread t = ROWS * qt + r holds row r of the tall panel (rows
+// [0, PR): the rows prow0 + r of the matrix above the block; rows PR + i:
+// row i of the diagonal block, stored in full) restricted to the 16 columns
+// [16 qt, 16 qt + 16) of the block, in registers s[0..15]. Global reads and
+// writes go through LDS tiles so that they are coalesced.
+// Column groups of 16 are processed from the last (gq = 3) to the first:
+//   leaf  - the wave holding the group's 16 diagonal rows (one 16-lane DPP
+//           row) factors the 16 x 16 sub-block S_gg = (I + U_gg) D_g
+//           (I + U_gg)^T; for g = 1 the pivot row is broadcast with DPP, no
+//           barrier; for g = 8 the two 8 x 8 pivots are Cholesky-inverted by
+//           every lane;
+//   solve - every row above the group solves x (I + U_gg)^T = a on its 16
+//           columns (x = U D), then u = x D_g^{-1};
+//   update- rows above subtract x U_{c,g}^T from their columns c left of the
+//           group (U_{c,g} from the diagonal rows of the same pass).
+// Outputs: U and X rows above the block from every group; the diagonal block
+// of U, D and info from the first group.
+template <int PR, int G>
+__global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* src, int64_t lds_,
+                                                                  int64_t k0, int w, float* U,
+                                                                  int64_t n, float* D, float* Xp,
+                                                                  int64_t ldx, int32_t* info) {
+  constexpr int NB = 64, ROWS = PR + NB, NT = 4 * ROWS;
+  __shared__ float tile[NB][65];   // diagonal block (upper triangle), later U's diagonal block
+  __shared__ float ptile[PR][65];  // rows above, later their U
+  __shared__ float xtile[PR][65];  // X of the rows above
+  __shared__ __align__(16) float Xs[ROWS][20];
+  __shared__ __align__(16) float Us[NB][16];
+  __shared__ __align__(16) float Ut[16][16];  // Ut[l][j] = U[c0 + j][c0 + l]
+  __shared__ float dsh[NB][G];
+  __shared__ float dinv[NB][G];
+  __shared__ float L16[16][17];
+  __shared__ int bad_sh;
+
+  const int t = threadIdx.x;
+  const int qt = t / ROWS, r = t % ROWS;
+  const int lane = t & 63, wave = t >> 6;
+  const bool is_panel = r < PR;
+  const int64_t prow0 = int64_t(blockIdx.x) * PR;
+  const int64_t grow = prow0 + r;
+  const int npan = int(k0 - prow0 < PR ? (k0 - prow0 > 0 ? k0 - prow0 : 0) : PR);
+  const bool live = !is_panel || r < npan;
+  const int di = r - PR;  // row of the diagonal block (diagonal rows only)
+
+  const bool vin = (w == NB) && (lds_ % 4 == 0) && ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+  tile_io<NT, NB, true>(tile, src + k0 * lds_ + k0, nullptr, lds_, w, w, vin);
+  tile_io<NT, PR, true>(ptile, src + prow0 * lds_ + k0, nullptr, lds_, npan, w, vin);
+  if (t == 0) bad_sh = -1;
+  __syncthreads();
+  float s[16];
 #pragma unroll
-          for (int b = a + 1; b < 8; ++b) {
-            float v = ck[a][c0 + b];
+  for (int m = 0; m < 16; ++m) {
+    const int c = 16 * qt + m;
+    if (is_panel)
+      s[m] = ptile[r][c];
+    else
+      s[m] = (di >= w || c >= w) ? (di == c ? 1.f : 0.f) : (di <= c ? tile[di][c] : tile[c][di]);
+  }
+
+  static_for<4>([&](auto GI) {
+    constexpr int gq = 3 - decltype(GI)::value;
+    constexpr int c0 = 16 * gq;
+    constexpr int base = ROWS * gq + PR + c0;  // thread of diagonal row c0 in column group gq
+    constexpr int wl = base / 64, lb = base % 64;
+    static_assert(lb % 16 == 0, "leaf rows must form one DPP row");
+    const int il = lane - lb;
+    // ---- leaf
+    if (wave == wl) {
+      if constexpr (G == 1) {
+        // on a copy: the other lanes of this wave hold rows that still need s
+        float ls[16], uu[16], dd[16];
 #pragma unroll
-            for (int x = 0; x < a; ++x) v -= Lc[b][x] * Lc[a][x];
-            Lc[b][a] = v / la;
+        for (int k = 0; k < 16; ++k) ls[k] = s[k];
+        static_for<16>([&](auto KI) {
+          constexpr int k = 15 - decltype(KI)::value;
+          const float d = row_bcast<k>(ls[k]);
+          const float rd = __builtin_amdgcn_rcpf(d);  // pivot reciprocal (1 ulp)
+          const float u = ls[k] * rd;
+          const float nu = -u;
+          uu[k] = u;
+          dd[k] = d;
+          static_for<k>([&](auto JI) {
+            constexpr int j = decltype(JI)::value;
+            ls[j] = fmaf(row_bcast<k>(ls[j]), nu, ls[j]);
+          });
+        });
+        if (il >= 0 && il < 16) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const float v = k > il ? uu[k] : 0.f;
+            Ut[k][il] = v;
+            s[k] = v;
           }
         }
-        if (!ok && bad_sh < 0) bad_sh = c0;
-        float(*Li)[8] = Lish;
+        if (lane == lb) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if (i < c) {
-              Li[i][c] = 0.f;
-            } else {
-              float v = (i == c) ? 1.f : 0.f;
-#pragma unroll
-              for (int x = c; x < i; ++x) v -= Lc[i][x] * Li[x][c];
-              Li[i][c] = v / Lc[i][i];
-            }
+          for (int k = 15; k >= 0; --k) {
+            dsh[c0 + k][0] = dd[k];
+            dinv[c0 + k][0] = __builtin_amdgcn_rcpf(dd[k]);
+            if (!(dd[k] > 0.f) && bad_sh < 0) bad_sh = c0 + k;
           }
+        }
+      } else {
+        if (il >= 0 && il < 16) {
 #pragma unroll
-        for (int a = 0; a < 8; ++a)
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            float v = 0.f;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) v += Li[x][a] * Li[x][b];
-            Dis[a][b] = v;
-            dinv[c0 + a][b] = v;
-            dsh[c0 + a][b] = ck[b][c0 + a];
-          }
-      }
-      __syncthreads();
-      const bool piv = (j >= c0) && (j < c0 + 8);
-      const int jp = piv ? j - c0 : 0;
-      float h[8];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        float v = 0.f;
-#pragma unroll
-        for (int a = 0; a < 8; ++a) v = fmaf(Dis[b][a], ck[a][j], v);
-        h[b] = piv ? ((b == jp ? 1.f : 0.f) + Dis[b][jp]) : v;
-      }
-      if (q == 0 && j < c0) {
+          for (int k = 0; k < 16; ++k) L16[il][k] = s[k];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float Pinv[8][8];
+        // second 8-block first
+        const bool ok1 = chol_inv8(L16, 8, Pinv);
+        float u8[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           float v = 0.f;
 #pragma unroll
-          for (int a = 0; a < 8; ++a) v = fmaf(ck[a][j], Dis[a][b], v);
-          tile[j][c0 + b] = v;
+          for (int a = 0; a < 8; ++a) v = fmaf(s[8 + a], Pinv[a][b], v);
+          u8[b] = v;  // rows il < 8: U[c0 + il][c0 + 8 + b]
         }
-      }
-      if (r0 < c0) {
+        if (lane == lb) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const float4* c4 = reinterpret_cast<const float4*>(&ck[b][r0]);
+          for (int a = 0; a < 8; ++a)
 #pragma unroll
-          for (int v = 0; v < RG / 4; ++v) {
-            const float4 c = c4[v];
-            const float cc[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * v + e;
-              const float ci = (r0 + r < c0) ? cc[e] : 0.f;
-              Rr[r] = fmaf(-ci, h[b], Rr[r]);
+            for (int b = 0; b < 8; ++b) {
+              dsh[c0 + 8 + a][b] = a <= b ? L16[8 + a][8 + b] : L16[8 + b][8 + a];
+              dinv[c0 + 8 + a][b] = Pinv[a][b];
             }
+          if (!ok1 && bad_sh < 0) bad_sh = c0 + 8;
+        }
+        // Schur complement of the first 8 rows: S00 -= u S10
+        float s00[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v = s[j];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) v = fmaf(-u8[b], L16[j][8 + b], v);
+          s00[j] = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (il >= 0 && il < 8) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) L16[il][j] = s00[j];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const bool ok0 = chol_inv8(L16, 0, Pinv);
+        if (lane == lb) {
+#pragma unroll
+          for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+              dsh[c0 + a][b] = a <= b ? L16[a][b] : L16[b][a];
+              dinv[c0 + a][b] = Pinv[a][b];
+            }
+          if (!ok0 && ok1 && bad_sh < 0) bad_sh = c0;
+        }
+        if (il >= 0 && il < 16) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const float v = (il < 8 && k >= 8) ? u8[k - 8] : 0.f;
+            Ut[k][il] = v;
+            s[k] = v;
           }
         }
       }
-      if (piv && q == qk) {
+    }
+    __syncthreads();
+    const bool above = live && (is_panel || di < c0);
+    // ---- solve x (I + U_gg)^T = a, then u = x D_g^{-1}
+    if (gq > 0 || PR > 0) {
+      if (qt == gq && above) {
+        float4 cur[4];
 #pragma unroll
-        for (int a = 0; a < 8; ++a) Rr[8 * hb + a] = (a == jp) ? 1.f : 0.f;
+        for (int v = 0; v < 4; ++v) cur[v] = reinterpret_cast<const float4*>(Ut[15])[v];
+#pragma unroll
+        for (int l = 15; l > 0; --l) {
+          float4 nxt[4];
+          if (l > 1) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) nxt[v] = reinterpret_cast<const float4*>(Ut[l - 1])[v];
+          }
+          const float xl = s[l];
+          const float uc[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
+                                cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                                cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+#pragma unroll
+          for (int j = 0; j < l; ++j) s[j] = fmaf(-xl, uc[j], s[j]);
+          if (l > 1) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
+          }
+        }
+        float4* x4 = reinterpret_cast<float4*>(Xs[r]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          x4[v] = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+        if (is_panel) {
+#pragma unroll
+          for (int l = 0; l < 16; ++l) xtile[r][c0 + l] = s[l];
+        }
+        if constexpr (G == 1) {
+#pragma unroll
+          for (int l = 0; l < 16; ++l) s[l] *= dinv[c0 + l][0];
+        } else {
+          float x[16];
+#pragma unroll
+          for (int l = 0; l < 16; ++l) x[l] = s[l];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int a = 0; a < 8; ++a) {
+              float v = 0.f;
+#pragma unroll
+              for (int b = 0; b < 8; ++b) v = fmaf(x[8 * hb + b], dinv[c0 + 8 * hb + b][a], v);
+              s[8 * hb + a] = v;
+            }
+        }
+        if (!is_panel) {
+          float4* o4 = reinterpret_cast<float4*>(Us[di]);
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            o4[v] = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+        }
       }
     }
+    if constexpr (gq > 0) {
+      __syncthreads();
+      // ---- update the columns left of the group
+      if (qt < gq && above) {
+        float x[16];
+        const float4* x4 = reinterpret_cast<const float4*>(Xs[r]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 c = x4[v];
+          x[4 * v + 0] = c.x;
+          x[4 * v + 1] = c.y;
+          x[4 * v + 2] = c.z;
+          x[4 * v + 3] = c.w;
+        }
+        float4 cur[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cur[v] = reinterpret_cast<const float4*>(Us[16 * qt])[v];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          float4 nxt[4];
+          if (m < 15) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) nxt[v] = reinterpret_cast<const float4*>(Us[16 * qt + m + 1])[v];
+          }
+          float acc = s[m];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc = fmaf(-x[4 * v + 0], cur[v].x, acc);
+            acc = fmaf(-x[4 * v + 1], cur[v].y, acc);
+            acc = fmaf(-x[4 * v + 2], cur[v].z, acc);
+            acc = fmaf(-x[4 * v + 3], cur[v].w, acc);
+          }
+          s[m] = acc;
+          if (m < 15) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
+          }
+        }
+      }
+    }
+  });
+
+  // ---- outputs through the LDS tiles
+  if (is_panel) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) ptile[r][16 * qt + m] = s[m];
+  } else if (blockIdx.x == 0) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int c = 16 * qt + m;
+      const bool up = (G == 1) ? (c > di) : (c / 8 > di / 8);
+      tile[di][c] = up ? s[m] : 0.f;
     }
   }
   __syncthreads();
-
-  // U block
-  for (int e = t; e < w * w; e += NT) {
-    const int r = e / w, c = e % w;
-    U[(k0 + r) * n + (k0 + c)] = tile[r][c];
-  }
-  if (q == 0 && j < w) {
+  const bool vout = (w == NB) && (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
+  const bool vx = (w == NB) && (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(Xp) & 15) == 0);
+  tile_io<NT, PR, false>(ptile, nullptr, U + prow0 * n + k0, n, npan, w, vout);
+  tile_io<NT, PR, false>(xtile, nullptr, Xp + prow0 * ldx, ldx, npan, w, vx);
+  if (blockIdx.x == 0) {
+    tile_io<NT, NB, false>(tile, nullptr, U + k0 * n + k0, n, w, w, vout);
+    if (t < w) {
 #pragma unroll
-    for (int b = 0; b < G; ++b) D[(k0 + j) * G + b] = dsh[j][b];
-  }
-  // R[j][c] = V[c][j] for c < j (1 at c = j, 0 above); R[j][w + c] = sum_b V[b][j] Dinv[b][c]
-  if (j < w) {
-    float* Rrow = R + j * (2 * w);
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const int c = r0 + r;
-      if (c < w) {
-        const float v = c < j ? Rr[r] : (c == j ? 1.f : 0.f);
-        Rrow[c] = v;
-        float vd;
-        if constexpr (G == 1) {
-          vd = v * dinv[c][0];
-        } else {
-          const int rb = r & ~7;  // first row of c's 8-block inside this thread
-          vd = 0.f;
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const int cbb = r0 + rb + b;
-            const float vb = cbb < j ? Rr[rb + b] : (cbb == j ? 1.f : 0.f);
-            vd = fmaf(vb, dinv[cbb][c - (r0 + rb)], vd);
-          }
-        }
-        Rrow[w + c] = vd;
-      }
+      for (int b = 0; b < G; ++b) D[(k0 + t) * G + b] = dsh[t][b];
     }
+    if (t == 0 && bad_sh >= 0) atomicCAS(info, 0, int32_t(k0 + bad_sh + 1));
   }
-  if (t == 0 && bad_sh >= 0) atomicCAS(info, 0, int32_t(k0 + bad_sh + 1));
 }
 
 }  // namespace
@@ -280,8 +459,7 @@ __global__ __launch_bounds__(NB * NB / 16) void ldl_diag_kernel(const float* src
 size_t ldl_workspace_bytes(int64_t n) {
   Carver c(nullptr, 0);
   c.take<float>(size_t(n) * n);       // working copy of the upper triangle
-  c.take<float>(size_t(n) * LDL_NO);          // X panel of an outer block
-  c.take<float>(size_t(LDL_NB) * 2 * LDL_NB);  // R
+  c.take<float>(size_t(n) * LDL_NO);  // X panel of an outer block
   return c.used;
 }
 
@@ -291,17 +469,18 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
   float* Aw = c.take<float>(size_t(n) * n);
   constexpr int NB = LDL_NB;
   constexpr int NO = LDL_NO;
+  constexpr int PR = LDL_PR;
+  static_assert(NO % NB == 0 && NB % PR == 0, "block sizes");
   float* Xp = c.take<float>(size_t(n) * NO);
-  float* R = c.take<float>(size_t(NB) * 2 * NB);
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldl: workspace too small");
 
   QUIP_TRY(fill_matrix(U, n, n, n, 0.f, s));
   QUIP_TRY(fill_f32(reinterpret_cast<float*>(info), 1, 0.f, s));  // info <- 0 (bit pattern)
 
-  // Outer blocks of NO columns from the last to the first; inside each, inner
-  // blocks of NB columns (diagonal factor, panel product for every row above,
-  // update of the outer block's remaining columns); then one trailing update
-  // of the leading block with K = NO.
+  // Outer blocks of NO columns from the last to the first; inside each, blocks
+  // of NB columns (factor + rows above in one kernel, then the update of the
+  // outer block's remaining columns); then one trailing update of the leading
+  // block with K = NO.
   const int64_t nouter = cdiv(n, NO);
   // Which copy holds the current values: the leading block [0, o1)^2 is in Aw
   // once an outer trailing update has run (aw_lead); inside an outer block its
@@ -317,30 +496,15 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
       const int w = int((o1 - k0) < NB ? (o1 - k0) : NB);
       const float* src = aw_outer ? Aw : H;
       const int64_t lsrc = aw_outer ? n : ldh;
+      const dim3 grid(unsigned(k0 > 0 ? k0 / PR : 1));
       if (g == 1)
-        hipLaunchKernelGGL((ldl_diag_kernel<NB, 1>), dim3(1), dim3(NB * NB / 16), 0, s, src, lsrc,
-                           k0, w, U, n, D, R, info);
+        hipLaunchKernelGGL((ldl_block_kernel<PR, 1>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
+                           k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
       else
-        hipLaunchKernelGGL((ldl_diag_kernel<NB, 8>), dim3(1), dim3(NB * NB / 16), 0, s, src, lsrc,
-                           k0, w, U, n, D, R, info);
-      QUIP_TRY(launch_check("ldl_diag_kernel"));
+        hipLaunchKernelGGL((ldl_block_kernel<PR, 8>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
+                           k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
+      QUIP_TRY(launch_check("ldl_block_kernel"));
       if (k0 == 0) break;
-      // [X | U_IK] = A_IK R for all rows above the block
-      GemmArgs p;
-      p.M = k0;
-      p.N = 2 * w;
-      p.K = w;
-      p.A = src + k0;
-      p.lda = lsrc;
-      p.B = R;
-      p.ldb = 2 * w;
-      p.C = Xp + (k0 - o0);
-      p.ldc = NO;
-      p.epi = EPI_SPLIT;
-      p.split = w;
-      p.C2 = U + k0;
-      p.ldc2 = n;
-      QUIP_TRY(gemm(p, s));
       if (b > 0) {
         // the outer block's columns left of this one: A[:k0, o0:k0] -= X U[o0:k0, blk]^T
         GemmArgs t;
