@@ -204,8 +204,8 @@ quip_status quip_scales(const float* W, int64_t m, int64_t n, int64_t ldw, const
  * LDL factor; [QTIP] "Builds on": BlockLDLQ). Lazily blocked: B columns are
  * swept at a time and the rest of the matrix is updated once per block.
  *   W: m x n incoherence-processed weights, leading dim ldw (read only).
- *   U, D: from quip_ldl with the same g (D is read only for g = 8; pass it
- *     anyway for g = 1).
+ *   U, D: from quip_ldl with the same g (D is read for g = 8 and for the
+ *     loss outputs).
  *   B: lazy block size, a multiple of g, 8..4096.
  *   q: quantizer (UNIFORM needs g = 1; E8 needs g = 8).
  *   scales: as quip_scales; written when q->scale_mode is COMPUTE, read when
@@ -218,6 +218,13 @@ quip_status quip_scales(const float* W, int64_t m, int64_t n, int64_t ldw, const
  *     scaled back by their RMS.
  *   codebook: 65536 x 8 device floats for E8 (quip_e8_codebook order), else
  *     NULL.
+ *   row_loss, loss: optional (may be NULL) device float64 outputs, m values
+ *     and one value: the proxy loss tr((W^ - W) H (W^ - W)^T) ([QuIP]
+ *     "Introduction") per row and summed, in W's domain, for the H whose
+ *     factors U, D are passed. It is taken from the rounding itself: with
+ *     H = (I + U) D (I + U)^T, column K of (W - W^)(I + U) is the pre-rounding
+ *     target P_K minus W^_K, so the loss is sum_K (P_K - W^_K) D_K
+ *     (P_K - W^_K)^T, O(mn) instead of O(mn^2). Requires D.
  *   ws: device workspace of quip_ldlq_workspace() bytes.
  * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (n % g, B % g, B range),
  *   QUIP_ERR_WORKSPACE, QUIP_ERR_UNSUPPORTED (bits > 8).
@@ -226,8 +233,9 @@ quip_status quip_ldlq_workspace(int64_t m, int64_t n, int64_t g, int64_t B,
                                 const quip_quantizer* q, size_t* bytes);
 quip_status quip_ldlq(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
                       const float* D, int64_t g, int64_t B, const quip_quantizer* q,
-                      float* scales, void* codes, float* What, const float* codebook, void* ws,
-                      size_t ws_bytes, hipStream_t stream);
+                      float* scales, void* codes, float* What, const float* codebook,
+                      double* row_loss, double* loss, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
 
 /*
  * quip_proxy_loss -- loss = tr((W^ - W) H (W^ - W)^T) ([QuIP] "Introduction":

@@ -65,7 +65,8 @@ SYMBOLS = {
     "quip_ldlq_workspace": (c_int, [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(Quantizer),
                                     ctypes.POINTER(c_sz)]),
     "quip_ldlq": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_i64,
-                          ctypes.POINTER(Quantizer), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+                          ctypes.POINTER(Quantizer), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                          c_vp]),
     "quip_proxy_loss_workspace": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "quip_proxy_loss": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_sz,
                                 c_vp]),
@@ -200,12 +201,13 @@ def quip_scales(W, q: Quantizer, scales, mse_out=None, codebook=None, stream=Non
 
 
 def quip_ldlq(W, U, D, g: int, B: int, q: Quantizer, scales, codes, What=None, codebook=None,
-              stream=None, ws=None):
+              row_loss=None, loss=None, stream=None, ws=None):
     m, n = W.shape
     if ws is None:
         ws = _workspace(_ws_query(lib.quip_ldlq_workspace, m, n, g, B, ctypes.byref(q)), W.device)
     _check(lib.quip_ldlq(_p(W), m, n, _ld(W), _p(U), _p(D), g, B, ctypes.byref(q), _p(scales),
-                         _p(codes), _p(What), _p(codebook), _p(ws), ws.numel(), _stream(stream)),
+                         _p(codes), _p(What), _p(codebook), _p(row_loss), _p(loss), _p(ws),
+                         ws.numel(), _stream(stream)),
            "quip_ldlq")
 
 

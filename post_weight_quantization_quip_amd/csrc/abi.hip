@@ -22,8 +22,8 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
 size_t ldl_workspace_bytes(int64_t n);
 quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
                      const float* D, int g, int64_t B, const quip_quantizer& q, float* scales,
-                     void* codes, float* What, const float* codebook, void* ws, size_t ws_bytes,
-                     hipStream_t s);
+                     void* codes, float* What, const float* codebook, double* row_loss,
+                     double* loss, void* ws, size_t ws_bytes, hipStream_t s);
 size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_quantizer& q);
 quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const quip_quantizer& q,
                        float* scales, void* mse_out, const float* codebook, void* ws,
@@ -287,8 +287,9 @@ quip_status quip_ldlq_workspace(int64_t m, int64_t n, int64_t g, int64_t B,
 
 quip_status quip_ldlq(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
                       const float* D, int64_t g, int64_t B, const quip_quantizer* q,
-                      float* scales, void* codes, float* What, const float* codebook, void* ws,
-                      size_t ws_bytes, hipStream_t stream) {
+                      float* scales, void* codes, float* What, const float* codebook,
+                      double* row_loss, double* loss, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
   clear_error();
   QUIP_TRY(check_matrix(W, m, n, ldw, "quip_ldlq", "W"));
   QUIP_TRY(check_quantizer(q, n, codebook, "quip_ldlq"));
@@ -298,10 +299,10 @@ quip_status quip_ldlq(const float* W, int64_t m, int64_t n, int64_t ldw, const f
     return fail(QUIP_ERR_ARG, "quip_ldlq: the scalar grid needs g = 1 and the E8 codebook g = 8");
   if (n % g) return fail(QUIP_ERR_SHAPE, "quip_ldlq: n must be a multiple of g");
   if (B < 8 || B > 4096 || B % g) return fail(QUIP_ERR_SHAPE, "quip_ldlq: B must be a multiple of g in [8, 4096]");
-  if (q->kind == QUIP_Q_E8 && !D) return fail(QUIP_ERR_ARG, "quip_ldlq: D is null");
+  if ((q->kind == QUIP_Q_E8 || row_loss || loss) && !D) return fail(QUIP_ERR_ARG, "quip_ldlq: D is null");
   QUIP_TRY(check_ws(ws, ws_bytes, ldlq_workspace_bytes(m, n, int(g), B, *q), "quip_ldlq"));
-  return ldlq_run(W, m, n, ldw, U, D, int(g), B, *q, scales, codes, What, codebook, ws, ws_bytes,
-                  stream);
+  return ldlq_run(W, m, n, ldw, U, D, int(g), B, *q, scales, codes, What, codebook, row_loss, loss,
+                  ws, ws_bytes, stream);
 }
 
 quip_status quip_proxy_loss_workspace(int64_t m, int64_t n, size_t* bytes) {

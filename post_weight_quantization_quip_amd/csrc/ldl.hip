@@ -42,6 +42,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_(f, std::make_integer_sequence<int, N>{});
 }
 
+// First float4 slot of column l in the packed strictly-upper 16 x 16 factor.
+__host__ __device__ constexpr int ut_off(int l) {
+  int o = 0;
+  for (int c = 1; c < l; ++c) o += (c + 3) / 4;
+  return o;
+}
+static_assert(ut_off(16) == 36, "packed factor size");
+
 // Value of lane J of this lane's 16-lane row (DPP row_newbcast).
 template <int J>
 __device__ __forceinline__ float row_bcast(float v) {
@@ -186,7 +194,8 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
   __shared__ float xtile[PR][65];  // X of the rows above
   __shared__ __align__(16) float Xs[ROWS][20];
   __shared__ __align__(16) float Us[NB][16];
-  __shared__ __align__(16) float Ut[16][16];  // Ut[l][j] = U[c0 + j][c0 + l]
+  // column l of U_gg (rows j < l), packed: float4 slots ut_off(l) .. + ceil(l/4)
+  __shared__ __align__(16) float4 UtP[36];
   __shared__ float dsh[NB][G];
   __shared__ float dinv[NB][G];
   __shared__ float L16[16][17];
@@ -208,21 +217,29 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
   if (t == 0) bad_sh = -1;
   __syncthreads();
   float s[16];
+  {
+    // branch-free: every candidate is read (indices clamped), then selected
+    const int rp = is_panel ? r : 0;
+    const int dr = is_panel ? 0 : di;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int c = 16 * qt + m;
-    if (is_panel)
-      s[m] = ptile[r][c];
-    else
-      s[m] = (di >= w || c >= w) ? (di == c ? 1.f : 0.f) : (di <= c ? tile[di][c] : tile[c][di]);
+    for (int m = 0; m < 16; ++m) {
+      const int c = 16 * qt + m;
+      const float vp = ptile[rp][c];
+      const float va = tile[dr][c];
+      const float vb = tile[c][dr];
+      float vd = (dr <= c) ? va : vb;
+      vd = (dr >= w || c >= w) ? (dr == c ? 1.f : 0.f) : vd;
+      s[m] = is_panel ? vp : vd;
+    }
   }
 
-  static_for<4>([&](auto GI) {
-    constexpr int gq = 3 - decltype(GI)::value;
-    constexpr int c0 = 16 * gq;
-    constexpr int base = ROWS * gq + PR + c0;  // thread of diagonal row c0 in column group gq
-    constexpr int wl = base / 64, lb = base % 64;
-    static_assert(lb % 16 == 0, "leaf rows must form one DPP row");
+  static_assert((ROWS + 16) % 16 == 0 && PR % 16 == 0, "leaf rows must form one DPP row");
+  // a runtime loop: one copy of the group code stays in the instruction cache
+#pragma nounroll
+  for (int gq = 3; gq >= 0; --gq) {
+    const int c0 = 16 * gq;
+    const int base = ROWS * gq + PR + c0;  // thread of diagonal row c0 in column group gq
+    const int wl = base / 64, lb = base % 64;
     const int il = lane - lb;
     // ---- leaf
     if (wave == wl) {
@@ -248,17 +265,19 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             const float v = k > il ? uu[k] : 0.f;
-            Ut[k][il] = v;
+            if (k > il) reinterpret_cast<float*>(UtP)[4 * ut_off(k) + il] = v;
             s[k] = v;
           }
         }
         if (lane == lb) {
+          int bad = -1;  // first non-positive pivot in processing order (highest index)
 #pragma unroll
-          for (int k = 15; k >= 0; --k) {
+          for (int k = 0; k < 16; ++k) {
             dsh[c0 + k][0] = dd[k];
             dinv[c0 + k][0] = __builtin_amdgcn_rcpf(dd[k]);
-            if (!(dd[k] > 0.f) && bad_sh < 0) bad_sh = c0 + k;
+            bad = !(dd[k] > 0.f) ? c0 + k : bad;
           }
+          if (bad >= 0 && bad_sh < 0) bad_sh = bad;
         }
       } else {
         if (il >= 0 && il < 16) {
@@ -320,7 +339,7 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             const float v = (il < 8 && k >= 8) ? u8[k - 8] : 0.f;
-            Ut[k][il] = v;
+            if (k > il) reinterpret_cast<float*>(UtP)[4 * ut_off(k) + il] = v;
             s[k] = v;
           }
         }
@@ -329,28 +348,18 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
     __syncthreads();
     const bool above = live && (is_panel || di < c0);
     // ---- solve x (I + U_gg)^T = a, then u = x D_g^{-1}
-    if (gq > 0 || PR > 0) {
+    {
       if (qt == gq && above) {
-        float4 cur[4];
+        // every column of U_gg up front (144 floats), then the back substitution
+        float4 up[36];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) cur[v] = reinterpret_cast<const float4*>(Ut[15])[v];
+        for (int v = 0; v < 36; ++v) up[v] = UtP[v];
+        const float* uf = reinterpret_cast<const float*>(up);
 #pragma unroll
         for (int l = 15; l > 0; --l) {
-          float4 nxt[4];
-          if (l > 1) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) nxt[v] = reinterpret_cast<const float4*>(Ut[l - 1])[v];
-          }
           const float xl = s[l];
-          const float uc[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
-                                cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
-                                cur[3].x, cur[3].y, cur[3].z, cur[3].w};
 #pragma unroll
-          for (int j = 0; j < l; ++j) s[j] = fmaf(-xl, uc[j], s[j]);
-          if (l > 1) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
-          }
+          for (int j = 0; j < l; ++j) s[j] = fmaf(-xl, uf[4 * ut_off(l) + j], s[j]);
         }
         float4* x4 = reinterpret_cast<float4*>(Xs[r]);
 #pragma unroll
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
         }
       }
     }
-    if constexpr (gq > 0) {
+    if (gq > 0) {
       __syncthreads();
       // ---- update the columns left of the group
       if (qt < gq && above) {
@@ -399,33 +408,37 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
           x[4 * v + 2] = c.z;
           x[4 * v + 3] = c.w;
         }
-        float4 cur[4];
+        const float4* us = reinterpret_cast<const float4*>(Us[16 * qt]);
+        float4 cur[16], nxt[16];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) cur[v] = reinterpret_cast<const float4*>(Us[16 * qt])[v];
+        for (int v = 0; v < 16; ++v) cur[v] = us[v];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          float4 nxt[4];
-          if (m < 15) {
+        for (int ch = 0; ch < 4; ++ch) {  // columns 4 ch .. 4 ch + 3
+          if (ch < 3) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) nxt[v] = reinterpret_cast<const float4*>(Us[16 * qt + m + 1])[v];
+            for (int v = 0; v < 16; ++v) nxt[v] = us[16 * (ch + 1) + v];
           }
-          float acc = s[m];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            acc = fmaf(-x[4 * v + 0], cur[v].x, acc);
-            acc = fmaf(-x[4 * v + 1], cur[v].y, acc);
-            acc = fmaf(-x[4 * v + 2], cur[v].z, acc);
-            acc = fmaf(-x[4 * v + 3], cur[v].w, acc);
+          for (int mm = 0; mm < 4; ++mm) {
+            float acc = s[4 * ch + mm];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float4 c = cur[4 * mm + v];
+              acc = fmaf(-x[4 * v + 0], c.x, acc);
+              acc = fmaf(-x[4 * v + 1], c.y, acc);
+              acc = fmaf(-x[4 * v + 2], c.z, acc);
+              acc = fmaf(-x[4 * v + 3], c.w, acc);
+            }
+            s[4 * ch + mm] = acc;
           }
-          s[m] = acc;
-          if (m < 15) {
+          if (ch < 3) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
+            for (int v = 0; v < 16; ++v) cur[v] = nxt[v];
           }
         }
       }
     }
-  });
+  }
 
   // ---- outputs through the LDS tiles
   if (is_panel) {

@@ -29,8 +29,8 @@ namespace quip {
 
 quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
                      const float* D, int g, int64_t B, const quip_quantizer& q, float* scales,
-                     void* codes, float* What, const float* codebook, void* ws, size_t ws_bytes,
-                     hipStream_t s);
+                     void* codes, float* What, const float* codebook, double* row_loss,
+                     double* loss, void* ws, size_t ws_bytes, hipStream_t s);
 size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_quantizer& q);
 quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const quip_quantizer& q,
                        float* scales, void* mse_out, const float* codebook, void* ws,
@@ -145,13 +145,15 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
     const float* __restrict__ U, int64_t ldu, const float* __restrict__ scales, int L, int64_t m,
     int64_t s0, int bw, uint8_t* __restrict__ codes, int64_t ldcode, float* __restrict__ What,
-    int64_t ldwh, float* __restrict__ Eb, int64_t lde, bool vec) {
+    int64_t ldwh, float* __restrict__ Eb, int64_t lde, const float* __restrict__ Dg,
+    double* __restrict__ rowloss, bool vec) {
   constexpr int NT = B / 16;  // 16-column chunks
   constexpr int NS = B / 4;   // columns per lane over the whole block
   constexpr int PS = NS + 4;  // padded row of the permuted U block
   extern __shared__ __align__(16) float sm[];
   float* Us = sm;                  // [B][4][PS]: Us[(k*4 + g)*PS + 4t + e] = U[s0+k][s0+16t+4g+e]
   float* Ar = sm + B * 4 * PS;     // [64][NS]: per-lane accumulators of the later chunks
+  float* Ds = Ar + 64 * NS;        // [B]: D of the block (proxy loss)
 
   const int lane = threadIdx.x;
   const int g = lane & 3;
@@ -207,6 +209,9 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
     if (c + 3 < bw) v.w = p[3];
     return v;
   };
+  if (rowloss) {
+    for (int i = lane; i < B; i += 64) Ds[i] = i < bw ? Dg[s0 + i] : 0.f;
+  }
   {
     float4 fv[NT];
 #pragma unroll
@@ -222,6 +227,10 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
   const float half = L * 0.5f, cen = (L - 1) * 0.5f, hi = float(L - 1);
 
   float4 wn = load4(W, ldw, 4 * g);
+  // proxy loss of this row: with H = (I + U) D (I + U)^T and E = W - W^, the
+  // column j of E (I + U) is the target p_j minus its rounded value, so
+  // tr(E H E^T) = sum_j D_j (p_j - q_j)^2 over the columns this lane owns
+  double lsum = 0.0;
   for (int tk = 0; tk < NT; ++tk) {
     if (16 * tk >= bw) break;
     float wc[4] = {wn.x, wn.y, wn.z, wn.w};
@@ -234,6 +243,7 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
     const float* ub = Us + (64 * tk + g) * PS + 4 * tk;
     const int nk = (bw - 16 * tk) < 16 ? (bw - 16 * tk) : 16;
     float e16[16];
+    float res[4] = {0.f, 0.f, 0.f, 0.f};  // p - q of this lane's 4 columns (last pass)
     uint32_t cw = 0u;
     // One pass over the 16 columns of the chunk. EXACT = false rounds with
     // p * (1/s); it reports whether an owner lane came within 1e-4 of a
@@ -271,6 +281,7 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
         if (g == gk) {
           wc[ek] = qv;
           ac[ek] = err;
+          res[ek] = p - qv;
           cw |= uint32_t(kf) << (8 * ek);
         }
         // columns of this chunk after k (U is zero on and below the diagonal)
@@ -301,6 +312,12 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
     // outputs of this chunk: lane g's columns 16 tk + 4 g + e
     if (live) {
       const int c = 16 * tk + 4 * g;
+      if (rowloss) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&Ds[c]);  // zero past bw
+        const double r0 = res[0], r1 = res[1], r2 = res[2], r3 = res[3];
+        lsum += double(d4.x) * (r0 * r0) + double(d4.y) * (r1 * r1) + double(d4.z) * (r2 * r2) +
+                double(d4.w) * (r3 * r3);
+      }
       if (vec && c + 3 < bw) {
         *reinterpret_cast<uint32_t*>(codes + row * ldcode + s0 + c) = cw;
         if (What)
@@ -329,6 +346,11 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
       }
       *reinterpret_cast<float4*>(&Ar[lane * NS + 4 * t]) = acc;
     }
+  }
+  if (rowloss) {
+    lsum += __shfl_xor(lsum, 1, 64);
+    lsum += __shfl_xor(lsum, 2, 64);
+    if (live && g == 0) rowloss[row] += lsum;  // one work-group per row per launch
   }
 }
 
@@ -508,13 +530,17 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
   }
 }
 
-// Finish a group step: codes, quantized values, errors; reset the keys.
+// Finish a group step: codes, quantized values, errors; reset the keys. With
+// rowloss, also the group's proxy-loss term rms^2 (y - q) D_g (y - q)^T, y the
+// pre-rounding vector (normalized domain) recomputed as in e8_argmin_kernel.
 __global__ void e8_finish_kernel(const float* __restrict__ Wn, int64_t n, const float* __restrict__ C,
                                  const float* __restrict__ sp, const float* __restrict__ rms,
                                  int64_t c0, int64_t m,
                                  unsigned long long* __restrict__ keys, uint16_t* __restrict__ codes,
                                  int64_t ldcode, float* __restrict__ What, float* __restrict__ Eb,
-                                 int64_t lde, int ecol) {
+                                 int64_t lde, int ecol, const float* __restrict__ F, bool useF,
+                                 const float* __restrict__ U, int64_t s0,
+                                 const float* __restrict__ Dg, double* __restrict__ rowloss) {
   const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (row >= m) return;
   const float s = *sp;
@@ -522,12 +548,45 @@ __global__ void e8_finish_kernel(const float* __restrict__ Wn, int64_t n, const 
   keys[row] = ~0ull;
   codes[row * ldcode + c0 / 8] = uint16_t(code);
   const float r = rms[row];
+  double res[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const float qv = s * C[code * 8 + k];
+    if (rowloss) {
+      float y = Wn[row * n + c0 + k];
+      if (useF) y += F[row * n + c0 + k];
+      for (int c = 0; c < ecol; ++c) y = fmaf(Eb[row * lde + c], U[(s0 + c) * n + c0 + k], y);
+      res[k] = double(y) - double(qv);
+    }
     Eb[row * lde + ecol + k] = Wn[row * n + c0 + k] - qv;
     if (What) What[row * n + c0 + k] = r * qv;
   }
+  if (rowloss) {
+    double acc = 0.0;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      double t = 0.0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) t += double(Dg[(c0 + a) * 8 + b]) * res[b];
+      acc += res[a] * t;
+    }
+    rowloss[row] += double(r) * double(r) * acc;
+  }
+}
+
+// loss = sum of the row losses, in a fixed order (one work-group).
+__global__ __launch_bounds__(256) void sum_rows_kernel(const double* __restrict__ rowloss,
+                                                       int64_t m, double* __restrict__ out) {
+  __shared__ double part[256];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < m; i += 256) acc += rowloss[i];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (int(threadIdx.x) < h) part[threadIdx.x] += part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = part[0];
 }
 
 __global__ void fill_u64_kernel(unsigned long long* p, int64_t count, unsigned long long v) {
@@ -551,6 +610,12 @@ void host_grid_factors(int ncand, float* out) {
 }
 void host_e8_candidates(int ncand, float* out) {
   for (int c = 0; c < ncand; ++c) out[c] = float(0.5 * pow(4.0, double(c) / double(ncand - 1)));
+}
+
+quip_status finish_loss(const double* rl, int64_t m, double* loss, hipStream_t s) {
+  if (!loss) return QUIP_OK;
+  hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, s, rl, m, loss);
+  return launch_check("sum_rows_kernel");
 }
 
 struct E8Ws {
@@ -596,8 +661,8 @@ template <int B>
 quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
                     const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                     int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
-                    int64_t lde, hipStream_t s) {
-  const size_t shmem = (size_t(B) * 4 * (B / 4 + 4) + size_t(64) * (B / 4)) * sizeof(float);
+                    int64_t lde, const float* D, double* rowloss, hipStream_t s) {
+  const size_t shmem = (size_t(B) * 4 * (B / 4 + 4) + size_t(64) * (B / 4) + B) * sizeof(float);
   if (shmem > 65536)
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
@@ -609,18 +674,18 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
                    lde % 4 == 0 && s0 % 4 == 0;
   hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(64), shmem, s, W, ldw,
                      F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
-                     vec);
+                     D, rowloss, vec);
   return launch_check("ldlq_sweep_kernel");
 }
 
 quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
                   const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                   int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
-                  int64_t lde, hipStream_t s) {
+                  int64_t lde, const float* D, double* rowloss, hipStream_t s) {
   switch (b) {
-    case 32: return sweep_t<32>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, s);
-    case 64: return sweep_t<64>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, s);
-    case 128: return sweep_t<128>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, s);
+    case 32: return sweep_t<32>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
+    case 64: return sweep_t<64>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
+    case 128: return sweep_t<128>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
   }
   return fail(QUIP_ERR_UNSUPPORTED, "ldlq: inner block size");
 }
@@ -703,6 +768,7 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
   c.take<float>(64);
   c.take<float>(size_t(m) * n);  // F
   c.take<float>(size_t(m) * outer_block(n, g, B));  // Eb
+  c.take<double>(size_t(m));                         // per-row proxy loss
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
     c.take<unsigned long long>(size_t(m));
@@ -715,15 +781,18 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
 
 quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
                      const float* D, int g, int64_t B, const quip_quantizer& q, float* scales,
-                     void* codes, float* What, const float* codebook, void* ws, size_t ws_bytes,
-                     hipStream_t s) {
-  (void)D;
+                     void* codes, float* What, const float* codebook, double* row_loss,
+                     double* loss, void* ws, size_t ws_bytes, hipStream_t s) {
   Carver c(ws, ws_bytes);
   float* fac = c.take<float>(64);
   float* F = c.take<float>(size_t(m) * n);
   const int64_t Bo = outer_block(n, g, B);
   float* Eb = c.take<float>(size_t(m) * Bo);
+  double* rl_ws = c.take<double>(size_t(m));
   float hostf[64];
+  // per-row proxy loss: the caller's buffer, or the workspace when only the total is wanted
+  double* rl = row_loss ? row_loss : (loss ? rl_ws : nullptr);
+  if (rl && c.fits()) QUIP_TRY(fill_f64(rl, m, 0.0, s));
 
   if (q.kind == QUIP_Q_UNIFORM) {
     if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldlq: workspace too small");
@@ -740,14 +809,14 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       for (int64_t s0 = j0; s0 < j0 + bo; s0 += bi) {
         const int bw = int((j0 + bo - s0) < bi ? (j0 + bo - s0) : bi);
         QUIP_TRY(sweep(bi, W, ldw, F, n, s0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
-                       Eb + (s0 - j0), Bo, s));
+                       Eb + (s0 - j0), Bo, D, rl, s));
         // rest of this batch
         QUIP_TRY(feedback_gemm(Eb, Bo, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
                                !(j0 == 0 && s0 == 0), s));
       }
       QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
     }
-    return QUIP_OK;
+    return finish_loss(rl, m, loss, s);
   }
 
   // ---- E8, g = 8
@@ -786,12 +855,12 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       QUIP_TRY(launch_check("e8_argmin_kernel"));
       hipLaunchKernelGGL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
                          codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
-                         int(c0 - j0));
+                         int(c0 - j0), F, j0 > 0, U, j0, D, rl);
       QUIP_TRY(launch_check("e8_finish_kernel"));
     }
     QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
   }
-  return QUIP_OK;
+  return finish_loss(rl, m, loss, s);
 }
 
 }  // namespace quip

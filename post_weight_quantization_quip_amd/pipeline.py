@@ -7,9 +7,10 @@ allocates buffers once and sequences the calls on one HIP stream):
   quip_rht2 / quip_kron_orth (right, then left)   H~ = V H V^T   (in place)
   quip_rht2 / quip_kron_orth                      W~ = U W V^T
   quip_ldl                                        H~ = (I+U) D (I+U)^T
-  quip_ldlq                                       scales, codes, W^~
+  quip_ldlq                                       scales, codes, W^~ and the proxy
+                                                  loss tr((W^~ - W~) H~ (W^~ - W~)^T)
+                                                  per row and summed
   quip_rht2_inv / quip_kron_orth_inv              W^ = U^T W^~ V
-  quip_proxy_loss                                 tr((W^~ - W~) H~ (W^~ - W~)^T)
 """
 from __future__ import annotations
 
@@ -102,12 +103,12 @@ class LayerPass:
         b["What_t"] = torch.empty((m, n), **f32)
         b["What"] = torch.empty((m, n), **f32)
         b["loss"] = torch.zeros(1, dtype=torch.float64, device=dev)
+        b["row_loss"] = torch.zeros(m, dtype=torch.float64, device=dev)
         # workspaces, sized once
         need = [256]
         need.append(N._ws_query(N.lib.quip_ldl_workspace, n, self.g))
         import ctypes
         need.append(N._ws_query(N.lib.quip_ldlq_workspace, m, n, self.g, self.B, ctypes.byref(self.q)))
-        need.append(N._ws_query(N.lib.quip_proxy_loss_workspace, m, n))
         need.append(N._ws_query(N.lib.quip_kron_orth_workspace, max(m, n), max(m, n)))
         b["ws"] = N._workspace(max(need), dev)
 
@@ -133,13 +134,12 @@ class LayerPass:
         mark("ldl")
         N.quip_ldl(b["H"], self.g, b["U"], b["D"], b["info"], stream=stream, ws=ws)
         mark("ldlq")
+        # the proxy loss comes out of the rounding (per row and summed)
         N.quip_ldlq(b["Wt"], b["U"], b["D"], self.g, self.B, self.q, b["scales"], b["codes"],
-                    b["What_t"], self.codebook, stream=stream, ws=ws)
+                    b["What_t"], self.codebook, row_loss=b["row_loss"] if with_loss else None,
+                    loss=b["loss"] if with_loss else None, stream=stream, ws=ws)
         mark("postprocess")
         apply_two_sided(b["What_t"], b["What"], self.left, self.right, True, ws, stream)
-        mark("loss")
-        if with_loss:
-            N.quip_proxy_loss(b["Wt"], b["What_t"], b["H"], b["loss"], stream=stream, ws=ws)
         mark("end")
         return b
 

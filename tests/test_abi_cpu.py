@@ -86,25 +86,28 @@ def test_ldlq_and_scales_validation():
     q = N.quantizer(N.Q_UNIFORM, 2)
     big = fake(0x100000)
     st = lib.quip_ldlq(fake(), 4, 16, 16, fake(), fake(), 8, 8, ctypes.byref(q), fake(), fake(), None,
-                       None, big, 1 << 40, None)
+                       None, None, None, big, 1 << 40, None)
     assert st == N.QUIP_ERR_ARG  # scalar grid with g = 8
     qe = N.quantizer(N.Q_E8, 2)
     st = lib.quip_ldlq(fake(), 4, 20, 20, fake(), fake(), 8, 8, ctypes.byref(qe), fake(), fake(), None,
-                       fake(), big, 1 << 40, None)
+                       fake(), None, None, big, 1 << 40, None)
     assert st == N.QUIP_ERR_SHAPE  # n % 8
     st = lib.quip_ldlq(fake(), 4, 16, 16, fake(), fake(), 8, 8, ctypes.byref(qe), fake(), fake(), None,
-                       None, big, 1 << 40, None)
+                       None, None, None, big, 1 << 40, None)
     assert st == N.QUIP_ERR_ARG  # no codebook
     q9 = N.quantizer(N.Q_UNIFORM, 9)
     st = lib.quip_ldlq(fake(), 4, 16, 16, fake(), fake(), 1, 8, ctypes.byref(q9), fake(), fake(), None,
-                       None, big, 1 << 40, None)
+                       None, None, None, big, 1 << 40, None)
     assert st == N.QUIP_ERR_UNSUPPORTED
     qb = N.quantizer(N.Q_UNIFORM, 2, 1)
     assert lib.quip_scales(fake(), 4, 16, 16, ctypes.byref(qb), fake(), None, None, big, 1 << 40,
                            None) == N.QUIP_ERR_ARG  # n_cand < 2
     st = lib.quip_ldlq(fake(), 4, 16, 16, fake(), fake(), 1, 4, ctypes.byref(q), fake(), fake(), None,
-                       None, big, 1 << 40, None)
+                       None, None, None, big, 1 << 40, None)
     assert st == N.QUIP_ERR_SHAPE  # B < 8
+    st = lib.quip_ldlq(fake(), 4, 16, 16, fake(), None, 1, 8, ctypes.byref(q), fake(), fake(), None,
+                       None, fake(), None, big, 1 << 40, None)
+    assert st == N.QUIP_ERR_ARG  # per-row loss needs D
 
 
 def test_hessian_and_loss_validation():

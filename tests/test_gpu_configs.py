@@ -146,6 +146,16 @@ def check_ldl(b, g, rng, nent=4000):
     return Uh, Dh
 
 
+def check_fused_rows(b, rows, Wt_rows, What_rows, Hh):
+    """The per-row proxy loss LDLQ returns, against e H e^T in float64."""
+    E = What_rows.astype(np.float64) - Wt_rows.astype(np.float64)
+    want = np.einsum("ij,ij->i", E @ Hh.astype(np.float64), E)
+    got = host(b["row_loss"])[rows]
+    assert np.allclose(got, want, rtol=2e-5), np.abs(got / want - 1).max()
+    tot = float(host(b["loss"])[0])
+    assert abs(tot - host(b["row_loss"]).sum()) <= 1e-12 * tot
+
+
 def replay_rows(Wt_rows, U, What_rows, block=2048):
     """P = W~ + (W~ - W^~) U for a few rows, U float32 (n x n), in column blocks."""
     n = U.shape[0]
@@ -192,8 +202,10 @@ def test_config_uniform(name):
     Ht = b["H"]
     loss = torch.empty(1, dtype=torch.float64, device=DEV)
     Q.quip_proxy_loss(torch.from_numpy(Wt).to(DEV), torch.from_numpy(What).to(DEV), Ht, loss)
-    want_loss = O.proxy_loss(Wt, What, host(Ht))
+    Hh = host(Ht)
+    want_loss = O.proxy_loss(Wt, What, Hh)
     assert abs(float(host(loss)[0]) - want_loss) <= 1e-4 * want_loss
+    check_fused_rows(b, rows, Wt, What, Hh)
     # post-processing rows: row i of U^T W^~ V = (column i of U)^T W^~ V
     ri = rows[:4]
     back = O.incoherence_side(side_cols(L.left, cfg.m, ri) @ host(b["What_t"]).astype(np.float64),
@@ -231,3 +243,4 @@ def test_config_e8():
         assert np.all(dg - dbest[mism] <= tol)
     assert mism.sum() <= max(1, P.MAX_MISMATCH * cg.size)
     assert np.allclose(What, rms_all[rows][:, None] * s * C[codes].reshape(NSAMP, -1), rtol=1e-6, atol=1e-7)
+    check_fused_rows(b, rows, host(b["Wt"])[rows], host(b["What_t"])[rows], host(b["H"]))

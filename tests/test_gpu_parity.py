@@ -261,6 +261,65 @@ def ldlq_gpu(Wt32, U32, D32, g, B, bits, scales=None, codebook=None, kind=None):
     return host(sd), host(codes), host(What)
 
 
+def ldlq_gpu_loss(Wt32, U32, D32, g, B, bits, codebook=None):
+    """LDLQ with the fused proxy-loss outputs: (What, row_loss, loss)."""
+    m, n = Wt32.shape
+    kind = Q.Q_UNIFORM if g == 1 else Q.Q_E8
+    q = Q.quantizer(kind, bits if kind == Q.Q_UNIFORM else 2, 32, Q.SCALE_COMPUTE)
+    sd = torch.empty(m + (1 if kind == Q.Q_E8 else 0), device=DEV)
+    codes = torch.empty((m, n) if g == 1 else (m, n // 8), dtype=torch.uint8 if g == 1 else torch.int16,
+                        device=DEV)
+    What = torch.empty((m, n), device=DEV)
+    rl = torch.full((m,), -1.0, dtype=torch.float64, device=DEV)
+    tot = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    Q.quip_ldlq(dev(Wt32), dev(U32), dev(D32), g, B, q, sd, codes, What,
+                None if codebook is None else dev(codebook), row_loss=rl, loss=tot)
+    return host(What), host(rl), float(host(tot)[0])
+
+
+# The fused loss sums D_K |P_K - W^_K|^2 with the GPU's float32 factors and
+# targets; the oracle evaluates tr(E H E^T) in float64 on the same W^ and the
+# float32 H. They differ by the LDL's backward error (a few 1e-7 relative to
+# H's entries) and the float32 feedback sums, i.e. ~1e-6 of the loss; 2e-5
+# per row and 1e-5 in total leave an order of magnitude.
+FUSED_LOSS_RTOL_ROW = 2e-5
+FUSED_LOSS_RTOL = 1e-5
+
+
+def check_fused_loss(Wt, What, H, row_loss, loss):
+    E = What.astype(np.float64) - Wt.astype(np.float64)
+    want = np.einsum("ij,ij->i", E @ H.astype(np.float64), E)
+    assert np.all(row_loss >= 0)
+    assert np.allclose(row_loss, want, rtol=FUSED_LOSS_RTOL_ROW, atol=1e-12 * want.max())
+    assert abs(loss - want.sum()) <= FUSED_LOSS_RTOL * want.sum()
+    assert abs(loss - row_loss.sum()) <= 1e-12 * loss
+
+
+@pytest.mark.parametrize("m,n,B,bits", [(256, 256, 32, 2), (37, 200, 64, 3), (300, 384, 128, 4),
+                                        (1, 8, 8, 2), (70, 1100, 256, 2)])
+def test_ldlq_fused_loss(m, n, B, bits):
+    H = spd32(m + 3 * n, n)
+    Wt = (rng(m + n).standard_normal((m, n)) * 0.7).astype(np.float32)
+    U, D, info = ldl_gpu(H, 1)
+    assert info == 0
+    What, rl, loss = ldlq_gpu_loss(Wt, U, D, 1, B, bits)
+    check_fused_loss(Wt, What, H, rl, loss)
+
+
+def test_ldlq_fused_loss_diagonal_H():
+    # H diagonal: U = 0, P = W, the loss is sum_j d_j (w_j - q_j)^2; the kernel
+    # forms w_j - q_j in float32 (one rounding, relative 2^-24), squares and
+    # weights it in float64, so each term is within 2^-23 relative
+    m, n = 40, 96
+    Wt = rng(31).standard_normal((m, n)).astype(np.float32)
+    d = rng(32).uniform(0.5, 2.0, n).astype(np.float32)
+    U, D, _ = ldl_gpu(np.diag(d), 1)
+    What, rl, loss = ldlq_gpu_loss(Wt, U, D, 1, 32, 2)
+    E = What.astype(np.float64) - Wt.astype(np.float64)
+    want = (E * E * d.astype(np.float64)[None, :]).sum(axis=1)
+    assert np.allclose(rl, want, rtol=2.0 ** -23)
+
+
 def check_uniform_replay(Wt, U, What, s, codes, L):
     mism, bad, tot = P.replay_uniform(Wt, U, What, s, codes, L)
     assert bad == 0, f"{bad} codes differ outside the boundary band"
@@ -360,6 +419,16 @@ def test_block_ldlq_e8_replay(m, n, B, codebook):
     assert np.allclose(What, rms[:, None] * float(s[0]) * cw, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("m,n,B", [(64, 128, 64), (33, 256, 128)])
+def test_block_ldlq_e8_fused_loss(m, n, B, codebook):
+    H = spd32(m + n + 5, n)
+    Wt = (rng(n + 1).standard_normal((m, n)) * np.exp(0.3 * rng(m + 1).standard_normal(m))[:, None]).astype(np.float32)
+    U, D, info = ldl_gpu(H, 8)
+    assert info == 0
+    What, rl, loss = ldlq_gpu_loss(Wt, U, D, 8, B, 2, codebook=codebook)
+    check_fused_loss(Wt, What, H, rl, loss)
+
+
 # ------------------------------------------------------------------ end to end
 
 def check_independent_run(Wt, What_t, codes, Ht, ref, loss):
@@ -393,6 +462,7 @@ def test_layer_pass_end_to_end_c1():
     # near-tie, after which LDLQ follows another (equally valid) path, so the
     # total is compared with a bound for a few diverged rows.
     loss = float(host(b["loss"])[0])
+    check_fused_loss(host(b["Wt"]), host(b["What_t"]), host(b["H"]), host(b["row_loss"]), loss)
     check_independent_run(host(b["Wt"]), host(b["What_t"]), host(b["codes"]), host(b["H"]),
                           ref, loss)
     # post-processing inverts the incoherence transforms
