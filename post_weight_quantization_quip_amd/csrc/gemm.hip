@@ -289,11 +289,14 @@ quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
 
 template <bool TA, bool TB, int EPI>
 quip_status launch_tiles(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
-  // Prefer 128x128 tiles; drop to 64 along a dimension that is small, or when
-  // the 128-tile grid would leave most of the 256 CUs idle.
+  // Prefer 128x128 tiles; 64x64 when the 128-tile grid would not give every
+  // CU two work-groups (small launches are latency-bound: more, smaller tiles
+  // finish sooner); 64 along one dimension when only that one is small.
   int64_t t128 = cdiv(a.M, 128) * cdiv(a.N, 128) * a.batch;
-  bool smallM = a.M <= 64 || (t128 < 256 && a.M <= a.N);
-  bool smallN = a.N <= 64 || (t128 < 256 && a.N < a.M);
+  if (a.upper_tiles) t128 = cdiv(a.M, 128) * (cdiv(a.M, 128) + 1) / 2 * a.batch;
+  if (t128 < 512) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
+  bool smallM = a.M <= 64;
+  bool smallN = a.N <= 64;
   if (a.upper_tiles) smallN = smallM;  // square tiles for the triangular grid
   if (smallM && smallN) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
   if (smallM) return launch_t<64, 128, TA, TB, EPI>(a, s, vecA, vecB);
