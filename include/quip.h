@@ -91,10 +91,19 @@ const char* quip_last_error(void);
  *   accumulate: 0 overwrites H with X^T X, 1 adds X^T X to H (stream X in
  *   chunks of rows and call quip_hessian_finalize once with the total N).
  *   N may be 0 (H is zeroed, or left as is when accumulating).
- * Errors: QUIP_ERR_ARG (null pointer, ldx < n, ldh < n, n <= 0, N < 0).
+ *   ws: optional (may be NULL) 16-byte aligned device workspace of
+ *   quip_hessian_workspace() bytes (0 bytes when none is needed). With it,
+ *   the output tiles that would otherwise run alone in a last round of
+ *   work-groups are split along N and their pieces summed in a fixed order:
+ *   the result is deterministic either way, and bitwise the same for every
+ *   call with the same sizes and workspace choice.
+ * Errors: QUIP_ERR_ARG (null pointer, ldx < n, ldh < n, n <= 0, N < 0,
+ *   misaligned ws).
  */
+quip_status quip_hessian_workspace(int64_t N, int64_t n, size_t* bytes);
 quip_status quip_hessian(const float* X, int64_t N, int64_t n, int64_t ldx, float* H,
-                         int64_t ldh, int accumulate, hipStream_t stream);
+                         int64_t ldh, int accumulate, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
  * quip_hessian_finalize -- H <- H / N_total + alpha * mean(diag(H / N_total)) * I

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("QUIP_LIB", os.path.join(_HERE, "libquip.so"))
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libquip.so not found at {LIB_PATH}; build it with "
-        "`python -m post_weight_quantization_quip_amd.build` (hipcc, gfx950)")
+        "`python post_weight_quantization_quip_amd/build.py` (hipcc, gfx950)")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -46,7 +46,8 @@ SYMBOLS = {
     "quip_version": (ctypes.c_int32, []),
     "quip_status_string": (ctypes.c_char_p, [c_int]),
     "quip_last_error": (ctypes.c_char_p, []),
-    "quip_hessian": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_vp]),
+    "quip_hessian_workspace": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
+    "quip_hessian": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_int, c_vp, c_sz, c_vp]),
     "quip_hessian_finalize": (c_int, [c_vp, c_i64, c_i64, c_i64, c_f, c_vp, c_sz, c_vp]),
     "quip_rht": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_vp]),
     "quip_rht_inv": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_int, c_vp]),
@@ -126,9 +127,13 @@ def version() -> int:
 
 # ---------------------------------------------------------------- entry points
 
-def quip_hessian(X: torch.Tensor, H: torch.Tensor, accumulate: bool = False, stream=None):
+def quip_hessian(X: torch.Tensor, H: torch.Tensor, accumulate: bool = False, stream=None, ws=None):
     N, n = X.shape
-    _check(lib.quip_hessian(_p(X), N, n, _ld(X), _p(H), _ld(H), int(accumulate), _stream(stream)),
+    if ws is None:
+        need = _ws_query(lib.quip_hessian_workspace, N, n)
+        ws = _workspace(need, X.device) if need > 0 else None
+    _check(lib.quip_hessian(_p(X), N, n, _ld(X), _p(H), _ld(H), int(accumulate), _p(ws),
+                            0 if ws is None else ws.numel(), _stream(stream)),
            "quip_hessian")
 
 

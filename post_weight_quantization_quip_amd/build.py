@@ -1,6 +1,9 @@
 """Build libquip.so (HIP, gfx950) in the package directory.
 
-    python -m post_weight_quantization_quip_amd.build
+    python post_weight_quantization_quip_amd/build.py
+
+(run as a script: importing the package would first load the library it
+builds).
 
 Every source under csrc/ is compiled with hipcc for gfx950 only and linked
 into one shared library next to this file. Packed-FP32 instruction selection

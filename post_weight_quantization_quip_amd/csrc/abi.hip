@@ -10,7 +10,8 @@ namespace quip {
 
 // implemented in the other translation units
 quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx, float* H,
-                               int64_t ldh, bool accumulate, hipStream_t s);
+                               int64_t ldh, bool accumulate, float* P, size_t P_floats,
+                               hipStream_t s);
 quip_status hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,
                              double* scratch, hipStream_t s);
 quip_status kron_apply(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
@@ -143,13 +144,24 @@ const char* quip_status_string(quip_status st) {
 
 const char* quip_last_error(void) { return last_error_cstr(); }
 
+quip_status quip_hessian_workspace(int64_t N, int64_t n, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(QUIP_ERR_ARG, "quip_hessian_workspace: null pointer");
+  if (N < 0 || n <= 0) return fail(QUIP_ERR_ARG, "quip_hessian_workspace: need N >= 0 and n > 0");
+  *bytes = N > 0 ? gemm_upper_tail_floats(n, N) * sizeof(float) : 0;
+  return QUIP_OK;
+}
+
 quip_status quip_hessian(const float* X, int64_t N, int64_t n, int64_t ldx, float* H, int64_t ldh,
-                         int accumulate, hipStream_t stream) {
+                         int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   if (N < 0 || n <= 0) return fail(QUIP_ERR_ARG, "quip_hessian: need N >= 0 and n > 0");
   if (N > 0) QUIP_TRY(check_matrix(X, N, n, ldx, "quip_hessian", "X"));
   QUIP_TRY(check_matrix(H, n, n, ldh, "quip_hessian", "H"));
-  return hessian_accumulate(X, N, n, ldx, H, ldh, accumulate != 0, stream);
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 15))
+    return fail(QUIP_ERR_ARG, "quip_hessian: workspace must be 16-byte aligned");
+  return hessian_accumulate(X, N, n, ldx, H, ldh, accumulate != 0, static_cast<float*>(ws),
+                            ws ? ws_bytes / sizeof(float) : 0, stream);
 }
 
 quip_status quip_hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,

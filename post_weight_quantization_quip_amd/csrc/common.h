@@ -113,7 +113,20 @@ struct GemmArgs {
   int64_t split = 0;  // EPI_SPLIT
   float* C2 = nullptr;
   int64_t ldc2 = 0;
+  // upper_tiles + EPI_STORE: when the tile count does not fill the last round
+  // of work-groups, the leftover tiles are split along K into pieces written
+  // to P (float count P_floats) and summed in a fixed order (deterministic).
+  float* P = nullptr;
+  size_t P_floats = 0;
+  // internal: tiles [tile0, tile0 + grid / kpieces) of the grid, K in pieces of kchunk
+  int tile0 = 0;
+  int kpieces = 1;
+  int64_t kchunk = 0;
 };
+
+// Partial-tile workspace (floats) that gemm() uses for the leftover tiles of
+// the Hessian's upper-tile product X^T X (X: K x n); 0 when there are none.
+size_t gemm_upper_tail_floats(int64_t n, int64_t K);
 
 quip_status gemm(const GemmArgs& a, hipStream_t stream);
 

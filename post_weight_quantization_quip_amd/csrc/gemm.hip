@@ -57,6 +57,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
 
   // ---- tile coordinates
   int bid = (EPI == EPI_DOT_SYM) ? int(blockIdx.x) : xcd_remap(blockIdx.x, total);
+  int piece = 0;
+  if (a.kpieces > 1) {
+    piece = bid % a.kpieces;
+    bid /= a.kpieces;
+  }
+  bid += a.tile0;
   int tm, tn;
   if (a.upper_tiles) {
     int rem = bid, r = 0;
@@ -88,9 +94,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
 
   float4 ra[LA], rb[LB];
 
+  // K range of this work-group: [kbeg, kend)
+  int64_t kbeg = 0, kend = a.K;
+  if (a.kpieces > 1) {
+    kbeg = piece * a.kchunk;
+    kend = (kbeg + a.kchunk < a.K) ? kbeg + a.kchunk : a.K;
+  }
+  if (EPI == EPI_DOT_SYM) kend = (n0 + BN < a.K) ? n0 + BN : a.K;  // rows k <= last column
+  const int64_t klim = kend;
+
   auto gload = [&](int64_t k0) {
-    const bool fullA = vecA && k0 + BK <= a.K && (TA ? (m0 + BM <= a.M) : (m0 + BM <= a.M));
-    const bool fullB = vecB && k0 + BK <= a.K && n0 + BN <= a.N;
+    const bool fullA = vecA && k0 + BK <= klim && m0 + BM <= a.M;
+    const bool fullB = vecB && k0 + BK <= klim && n0 + BN <= a.N;
     if (fullA) {
 #pragma unroll
       for (int i = 0; i < LA; ++i) {
@@ -109,10 +124,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       int idx = tid + 256 * i;
       if (TA) {
         int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
-        ra[i] = load4(A, k0 + k, m0 + m4, a.lda, a.K, a.M, vecA);
+        ra[i] = load4(A, k0 + k, m0 + m4, a.lda, klim, a.M, vecA);
       } else {
         int m = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
-        ra[i] = load4(A, m0 + m, k0 + k4, a.lda, a.M, a.K, vecA);
+        ra[i] = load4(A, m0 + m, k0 + k4, a.lda, a.M, klim, vecA);
       }
     }
     }
@@ -134,10 +149,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       int idx = tid + 256 * i;
       if (!TB) {
         int k = idx / (BN / 4), n4 = (idx % (BN / 4)) * 4;
-        rb[i] = load4(B, k0 + k, n0 + n4, a.ldb, a.K, a.N, vecB);
+        rb[i] = load4(B, k0 + k, n0 + n4, a.ldb, klim, a.N, vecB);
       } else {
         int n = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
-        rb[i] = load4(B, n0 + n, k0 + k4, a.ldb, a.N, a.K, vecB);
+        rb[i] = load4(B, n0 + n, k0 + k4, a.ldb, a.N, klim, vecB);
       }
     }
     }
@@ -211,17 +226,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       }
   }
 
-  int64_t kend = a.K;
-  if (EPI == EPI_DOT_SYM) kend = (n0 + BN < a.K) ? n0 + BN : a.K;  // rows k <= last column
-  const int64_t nk = (kend + BK - 1) / BK;
+  const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
-    gload(0);
-    sstore(0, 0);
+    gload(kbeg);
+    sstore(0, kbeg);
     __syncthreads();
   }
   int buf = 0;
   for (int64_t kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK / 2; ++kk) {
       float av[WBM], bv[WBN];
@@ -235,12 +248,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
         for (int j = 0; j < WBN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1, (kt + 1) * BK);
+    if (kt + 1 < nk) sstore(buf ^ 1, kbeg + (kt + 1) * BK);
     __syncthreads();
     buf ^= 1;
   }
 
   // ---- epilogue
+  if (a.kpieces > 1) {  // raw partial tile, summed later by tail_reduce_kernel
+    float* Pt = a.P + (size_t((bid - a.tile0) * a.kpieces + piece) * BM * BN);
+#pragma unroll
+    for (int i = 0; i < WBM; ++i)
+#pragma unroll
+      for (int j = 0; j < WBN; ++j) {
+        const int c = wn * (BN / 2) + j * 32 + kcol;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * krow + (r % 4);
+          Pt[rr * BN + c] = acc[i][j][r];
+        }
+      }
+    return;
+  }
   double dsum = 0.0;
 #pragma unroll
   for (int i = 0; i < WBM; ++i) {
@@ -276,11 +304,124 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   }
 }
 
+// Sums the K pieces of the leftover tiles (fixed order) and applies alpha,
+// beta and the mirror like the regular epilogue.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a, int tiles_m) {
+  const int r = blockIdx.x;  // leftover tile
+  int rem = a.tile0 + r, tr = 0;
+  while (rem >= tiles_m - tr) {
+    rem -= tiles_m - tr;
+    ++tr;
+  }
+  const int tm = tr, tn = tr + rem;
+  const int e4 = (int(blockIdx.y) * 256 + int(threadIdx.x)) * 4;  // 4 consecutive elements
+  if (e4 >= BM * BN) return;
+  const int i = e4 / BN, j0 = e4 % BN;
+  const float* Pr = a.P + size_t(r) * a.kpieces * BM * BN + e4;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < a.kpieces; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(Pr + size_t(p) * BM * BN);
+    v.x += x.x;
+    v.y += x.y;
+    v.z += x.z;
+    v.w += x.w;
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  const int64_t row = int64_t(tm) * BM + i;
+  const float* Cin = a.Cin ? a.Cin : a.C;
+  const int64_t ldcin = a.Cin ? a.ldcin : a.ldc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t col = int64_t(tn) * BN + j0 + e;
+    if (row >= a.M || col >= a.N) continue;
+    float o = a.alpha * vv[e];
+    if (a.beta != 0.f) o += a.beta * Cin[row * ldcin + col];
+    a.C[row * a.ldc + col] = o;
+    if (a.mirror && tm != tn) {
+      float w = a.alpha * vv[e];
+      if (a.beta != 0.f) w += a.beta * Cin[col * ldcin + row];
+      a.C[col * a.ldc + row] = w;
+    }
+  }
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+struct TailPlan {
+  int T = 0, R = 0, kp = 1;
+  int64_t kchunk = 0;
+  size_t floats = 0;
+};
+
+// Leftover-tile split of an upper-tile grid: T tiles, `slots` resident
+// work-groups; the T mod slots tiles of the last round are cut into K pieces
+// so that they fill (at most) one round.
+template <int BM, int BN, bool TA, bool TB, int EPI>
+TailPlan plan_tail(int64_t M, int64_t K) {
+  TailPlan pl;
+  const int tiles_m = int(cdiv(M, BM));
+  pl.T = tiles_m * (tiles_m + 1) / 2;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&gemm_kernel<BM, BN, TA, TB, EPI>), 256, 0) !=
+          hipSuccess ||
+      per_cu <= 0)
+    return pl;
+  const int slots = per_cu * device_cus();
+  pl.R = pl.T % slots;
+  if (pl.R == 0) return pl;
+  int kp = slots / pl.R;
+  const int64_t kchunk = cdiv(cdiv(K, kp), BK) * BK;
+  kp = int(cdiv(K, kchunk));
+  if (kp < 2) return pl;
+  pl.kp = kp;
+  pl.kchunk = kchunk;
+  pl.floats = size_t(pl.R) * kp * BM * BN;
+  return pl;
+}
+
 template <int BM, int BN, bool TA, bool TB, int EPI>
 quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
   int tiles_m = int(cdiv(a.M, BM)), tiles_n = int(cdiv(a.N, BN));
   int total = a.upper_tiles ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
   if (total == 0 || a.batch == 0) return QUIP_OK;
+  if (EPI == EPI_STORE && a.upper_tiles && a.P && a.batch == 1) {
+    const TailPlan pl = plan_tail<BM, BN, TA, TB, EPI>(a.M, a.K);
+    if (pl.kp > 1 && pl.floats <= a.P_floats) {
+      const int full = pl.T - pl.R;
+      if (full > 0) {
+        GemmArgs f = a;
+        f.tile0 = 0;
+        f.kpieces = 1;
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(full, 1), dim3(256), 0, s, f,
+                           tiles_m, tiles_n, full, vecA, vecB);
+        QUIP_TRY(launch_check("gemm_kernel"));
+      }
+      GemmArgs t = a;
+      t.tile0 = full;
+      t.kpieces = pl.kp;
+      t.kchunk = pl.kchunk;
+      const int np = pl.R * pl.kp;
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(np, 1), dim3(256), 0, s, t,
+                         tiles_m, tiles_n, np, vecA, vecB);
+      QUIP_TRY(launch_check("gemm_kernel"));
+      hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(pl.R, BM * BN / 1024), dim3(256), 0, s,
+                         t, tiles_m);
+      return launch_check("tail_reduce_kernel");
+    }
+  }
   dim3 grid(total, a.batch);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), grid, dim3(256), 0, s, a, tiles_m,
                      tiles_n, total, vecA, vecB);
@@ -315,6 +456,13 @@ quip_status launch_epi(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
 }
 
 }  // namespace
+
+size_t gemm_upper_tail_floats(int64_t n, int64_t K) {
+  // the Hessian product: upper tiles, op(A) = X^T, op(B) = X, tile size as launch_tiles picks it
+  const int64_t t = cdiv(n, 128) * (cdiv(n, 128) + 1) / 2;
+  if (t < 512) return plan_tail<64, 64, true, false, EPI_STORE>(n, K).floats;
+  return plan_tail<128, 128, true, false, EPI_STORE>(n, K).floats;
+}
 
 quip_status gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return QUIP_OK;

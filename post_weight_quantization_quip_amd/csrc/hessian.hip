@@ -1,7 +1,9 @@
 // Proxy Hessian H = X^T X (QuIP, "Adaptive Rounding Step": the second moment
 // of the layer inputs) as a symmetric rank-N update on the fp32 matrix cores:
 // only output tiles on or above the diagonal are computed, and each is also
-// written to its mirror position. Damping (QuIP, "Experiments / Methods"):
+// written to its mirror position. The tiles that would run alone in a last
+// round of work-groups are split along N (the calibration rows) into pieces
+// summed in a fixed order, when the caller passes the workspace for them. Damping (QuIP, "Experiments / Methods"):
 // H <- H / N + alpha * mean(diag(H / N)) * I.
 #include "common.h"
 
@@ -38,7 +40,8 @@ __global__ void finalize_kernel(float* H, int64_t n, int64_t ldh, const double* 
 }  // namespace
 
 quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx, float* H,
-                               int64_t ldh, bool accumulate, hipStream_t s) {
+                               int64_t ldh, bool accumulate, float* P, size_t P_floats,
+                               hipStream_t s) {
   if (N == 0) {
     if (!accumulate) return fill_matrix(H, n, n, ldh, 0.f, s);
     return QUIP_OK;
@@ -59,6 +62,8 @@ quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx
   g.beta = accumulate ? 1.f : 0.f;
   g.upper_tiles = true;
   g.mirror = true;
+  g.P = P;  // leftover tiles split along K when the workspace holds their pieces
+  g.P_floats = P_floats;
   return gemm(g, s);
 }
 

@@ -112,6 +112,16 @@ class LayerPass:
         need.append(N._ws_query(N.lib.quip_kron_orth_workspace, max(m, n), max(m, n)))
         b["ws"] = N._workspace(max(need), dev)
 
+    def _hessian_ws(self, n_rows: int):
+        """Workspace for the split leftover tiles of X^T X; kept for the largest
+        calibration size seen (allocated on the first pass of that size)."""
+        need = N._ws_query(N.lib.quip_hessian_workspace, n_rows, self.n)
+        ws = self.buffers.get("ws_h")
+        if need > 0 and (ws is None or ws.numel() < need):
+            ws = N._workspace(need, self.device)
+            self.buffers["ws_h"] = ws
+        return ws if need > 0 else None
+
     def run(self, W: torch.Tensor, X: torch.Tensor, events: dict | None = None, stream=None,
             with_loss: bool = True) -> dict:
         """One pass. ``events`` (optional) receives torch.cuda.Event pairs per phase."""
@@ -125,7 +135,7 @@ class LayerPass:
                 events.setdefault(name, []).append(ev)
 
         mark("hessian")
-        N.quip_hessian(X, b["H"], accumulate=False, stream=stream)
+        N.quip_hessian(X, b["H"], accumulate=False, stream=stream, ws=self._hessian_ws(X.shape[0]))
         N.quip_hessian_finalize(b["H"], X.shape[0], self.alpha, stream=stream, ws=ws)
         mark("incoherence_H")
         apply_two_sided(b["H"], b["H"], self.right, self.right, False, ws, stream)

@@ -112,8 +112,9 @@ def test_ldlq_and_scales_validation():
 
 def test_hessian_and_loss_validation():
     lib = N.lib
-    assert lib.quip_hessian(fake(), -1, 4, 4, fake(), 4, 0, None) == N.QUIP_ERR_ARG
-    assert lib.quip_hessian(fake(), 8, 4, 3, fake(), 4, 0, None) == N.QUIP_ERR_ARG
+    assert lib.quip_hessian(fake(), -1, 4, 4, fake(), 4, 0, None, 0, None) == N.QUIP_ERR_ARG
+    assert lib.quip_hessian(fake(), 8, 4, 3, fake(), 4, 0, None, 0, None) == N.QUIP_ERR_ARG
+    assert lib.quip_hessian(fake(), 8, 4, 4, fake(), 4, 0, fake(0x10008), 64, None) == N.QUIP_ERR_ARG  # misaligned ws
     assert lib.quip_hessian_finalize(fake(), 4, 4, 0, 0.01, fake(0x10000), 256, None) == N.QUIP_ERR_ARG
     assert lib.quip_hessian_finalize(fake(), 4, 4, 8, -1.0, fake(0x10000), 256, None) == N.QUIP_ERR_ARG
     assert lib.quip_hessian_finalize(fake(), 4, 4, 8, 0.01, fake(0x10000), 8, None) == N.QUIP_ERR_WORKSPACE

@@ -63,6 +63,37 @@ def test_hessian_parity(N, n):
     assert np.array_equal(got, got.T)
 
 
+def hessian_raw(Xd, n, ws):
+    """X^T X through the C ABI, with or without the leftover-tile workspace."""
+    N = Xd.shape[0]
+    H = torch.empty((n, n), device=DEV)
+    Q.native._check(Q.native.lib.quip_hessian(
+        Xd.data_ptr(), N, n, n, H.data_ptr(), n, 0, None if ws is None else ws.data_ptr(),
+        0 if ws is None else ws.numel(), torch.cuda.current_stream().cuda_stream), "quip_hessian")
+    return host(H)
+
+
+@pytest.mark.parametrize("N,n", [(4096, 4096), (2048, 256), (333, 1100)])
+def test_hessian_leftover_split(N, n):
+    # the leftover tiles split along N (with the workspace) and the plain grid
+    # both match float64 sums; each path is bitwise reproducible
+    X = (rng(N + n).standard_normal((N, n)) * np.exp(0.5 * rng(n + 1).standard_normal(n))).astype(np.float32)
+    Xd = dev(X)
+    need = Q.native._ws_query(Q.native.lib.quip_hessian_workspace, N, n)
+    ws = Q.native._workspace(need, DEV) if need else None
+    a = hessian_raw(Xd, n, ws)
+    a2 = hessian_raw(Xd, n, ws)
+    b = hessian_raw(Xd, n, None)
+    assert np.array_equal(a, a2)
+    assert np.array_equal(a, a.T) and np.array_equal(b, b.T)
+    cols = rng(5).choice(n, min(n, 64), replace=False)
+    ref = X[:, cols].astype(np.float64).T @ X.astype(np.float64)  # rows `cols` of X^T X
+    d = np.sqrt(np.einsum("ij,ij->j", X.astype(np.float64), X.astype(np.float64)))
+    tol = 2e-5 * d[cols][:, None] * d[None, :]
+    assert (np.abs(a[cols] - ref) <= tol).all()
+    assert (np.abs(b[cols] - ref) <= tol).all()
+
+
 def test_hessian_accumulates_in_chunks():
     X = rng(3).standard_normal((700, 130)).astype(np.float32)
     H = torch.empty((130, 130), device=DEV)
