@@ -30,7 +30,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FP32_MFMA_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix cores
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CUs x 2.4 GHz x 256 fp32 flop/clock (vector ALUs)
+
+# source file of each kernel family (the counter summaries are tied to its hash)
+FAMILY_SOURCES = [("gemm:", "gemm.hip"), ("gemm_tail_reduce", "gemm.hip"),
+                  ("ldl_block_kernel", "ldl.hip"), ("ldlq_sweep_kernel", "ldlq.hip"),
+                  ("grid_scale_kernel", "ldlq.hip"), ("rht_", "rht.hip")]
 
 
 def parse():
@@ -46,13 +52,13 @@ def parse():
     # summaries of rocprofv3 result databases (host only, no GPU)
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
-    ap.add_argument("--kernel", default=DOMINANT_KERNEL)
+    ap.add_argument("--kernel", help="rocprofv3 kernel-name substring of the family's dispatches")
+    ap.add_argument("--family", help="library timing family the counters belong to")
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
     return ap.parse_args()
 
 
-DOMINANT_KERNEL = "gemm_kernel<128, 128, true, false, 0>"  # the Hessian contraction
 COPY_MIB = 256
 COPY_KERNEL = "MulFunctor"  # torch.mul(src, 1.0, out=dst): reads and writes COPY_MIB MiB
 
@@ -104,12 +110,27 @@ def _counter(db, counter):
     return per
 
 
-def summarize_counters(fetch_db, write_db, kernel, command, out):
-    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by what the counter reads for a plain copy of
-    COPY_MIB MiB (read and written once)."""
-    import hashlib
+def family_source(family: str) -> str:
+    for prefix, src in FAMILY_SOURCES:
+        if family.startswith(prefix):
+            return src
+    raise SystemExit(f"no source file known for kernel family {family}")
 
+
+def source_sha(src: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "post_weight_quantization_quip_amd", "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counters_path(family: str) -> str:
+    return os.path.join(ROOT, "profiles", "counters_" + family.replace(":", "_") + "_c2.json")
+
+
+def summarize_counters(fetch_db, write_db, kernel, family, command, out):
+    """HBM bytes per launch of `kernel` (rocprofv3 name substring) from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the counter
+    reads for a plain copy of COPY_MIB MiB (read and written once)."""
     fetch = _counter(fetch_db, "FETCH_SIZE")
     write = _counter(write_db, "WRITE_SIZE")
 
@@ -129,39 +150,44 @@ def summarize_counters(fetch_db, write_db, kernel, command, out):
     f_write = nbytes / (cw * 1024.0)
     rd = kf * 1024.0 * f_read
     wr = kw * 1024.0 * f_write
-    src = os.path.join(ROOT, "post_weight_quantization_quip_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    d = {"kernel_prefix": "gemm_kernel", "kernel": kernel, "source_sha": sha,
+    src = family_source(family)
+    d = {"family": family, "kernel": kernel, "source": src, "source_sha": source_sha(src),
          "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [nf, nw],
          "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes_each_way": nbytes,
          "scale_read": f_read, "scale_write": f_write,
          "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
          "bytes_per_launch": rd + wr, "command": command}
     text = json.dumps(d, indent=1)
-    if out:
-        with open(out, "w") as f:
-            f.write(text + "\n")
+    out = out or counters_path(family)
+    with open(out, "w") as f:
+        f.write(text + "\n")
     print(text)
 
 
-def traffic_from_profiles(kernel_prefix: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (profiles/hessian_syrk_c2_counters.json), or None."""
-    path = os.path.join(ROOT, "profiles", "hessian_syrk_c2_counters.json")
+def traffic_from_profiles(family: str):
+    """HBM bytes per launch of a kernel family from its committed counter
+    summary under profiles/, or None (absent, or the kernel's source changed
+    since the counters were taken)."""
+    path = counters_path(family)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_prefix") != kernel_prefix or d.get("source_sha") is None:
+    if d.get("family") != family or d.get("source_sha") != source_sha(family_source(family)):
         return None
-    src = os.path.join(ROOT, "post_weight_quantization_quip_amd", "csrc", "gemm.hip")
-    import hashlib
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    if sha != d["source_sha"]:
-        return None  # the kernel changed since the counters were taken
     return d.get("bytes_per_launch")
+
+
+def kernel_bound(name: str):
+    """(bound, peak, unit) of a kernel family: the matrix-core products against
+    the fp32 MFMA peak, the two latency-bound sequential kernels (LDL block
+    factor, LDLQ sweep) against the fp32 vector-ALU peak, the streaming kernels
+    against HBM bandwidth."""
+    if name.startswith("gemm:"):
+        return "mfma", FP32_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    if name in ("ldl_block_kernel", "ldlq_sweep_kernel", "e8_argmin_kernel", "e8_scale_kernel"):
+        return "alu", FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
+    return "hbm", HBM_PEAK_GBS, "GB/s"
 
 
 def cpu_baseline(cfg_name: str, rows: int) -> dict:
@@ -224,7 +250,9 @@ def main():
         summarize_trace(args.summarize_trace, args.command, args.out)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.kernel, args.command, args.out)
+        if not args.kernel or not args.family:
+            raise SystemExit("--summarize-counters needs --kernel and --family")
+        summarize_counters(*args.summarize_counters, args.kernel, args.family, args.command, args.out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -267,7 +295,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    order = ["hessian", "incoherence_H", "incoherence_W", "ldl", "ldlq", "postprocess", "loss", "end"]
+    order = ["hessian", "incoherence_H", "incoherence_W", "ldl", "ldlq", "postprocess", "end"]
     phases = {}
     for a, b in zip(order[:-1], order[1:]):
         phases[a] = float(np.mean([ea.elapsed_time(eb) for ea, eb in zip(events[a], events[b])]))
@@ -278,28 +306,43 @@ def main():
     from_resident = (phases["incoherence_H"] + phases["incoherence_W"] + phases["ldl"]
                      + phases["ldlq"])
 
-    # dominant kernel: the Hessian contraction (one launch per step, events around it)
-    syrk_ms = phases["hessian"]
-    hs = []
+    # per-kernel figures: the same passes again with the library's event timing
+    # on (two HIP events around every launch, on the pass's stream); the
+    # roofline is that of the kernel family with the most time per step
+    Q.timing_reset()
+    Q.timing_enable(True)
     for _ in range(args.steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        Q.quip_hessian(X, lp.buffers["H"])
-        e1.record(stream)
-        hs.append((e0, e1))
+        lp.run(W, X)
     torch.cuda.synchronize()
-    syrk_ms = float(np.mean([a.elapsed_time(b) for a, b in hs]))
-    syrk_flops = cfg.N * cfg.n * (cfg.n + 1)
-    achieved = syrk_flops / (syrk_ms / 1e3) / 1e12
-    traffic = traffic_from_profiles("gemm_kernel")
+    Q.timing_enable(False)
+    rep = Q.timing_report()
+    Q.timing_reset()
+    kernels = {}
+    for name, (launches, ms, flops, nbytes) in rep.items():
+        bound, peak, unit = kernel_bound(name)
+        per_step = ms / args.steps
+        if bound == "hbm":
+            achieved = nbytes / (ms / 1e3) / 1e9 if ms > 0 else 0.0
+        else:
+            achieved = flops / (ms / 1e3) / 1e12 if ms > 0 else 0.0
+        kernels[name] = {"ms_per_step": round(per_step, 4), "launches_per_step": launches / args.steps,
+                         "avg_launch_us": round(1e3 * ms / launches, 2), "bound": bound,
+                         "achieved": round(achieved, 3), "unit": unit, "peak": peak,
+                         "frac": round(achieved / peak, 4),
+                         "algorithmic_flops_per_launch": round(flops / launches),
+                         "algorithmic_bytes_per_launch": round(nbytes / launches)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    k = kernels[dom]
+    traffic = traffic_from_profiles(dom)
     if traffic is not None:
-        traffic = round(traffic / 1e6, 1)  # MB per launch
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic, "traffic_unit": "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "kernel": "gemm_kernel<128,128,transA,!transB> (Hessian X^T X)",
-                "algorithmic_flops_per_launch": syrk_flops, "avg_launch_ms": round(syrk_ms, 4)}
+        traffic = round(traffic / 1e6, 3)  # MB per launch
+    roofline = {"bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"], "unit": k["unit"],
+                "frac": k["frac"], "traffic": traffic,
+                "traffic_unit": "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "kernel": dom, "avg_launch_ms": round(k["avg_launch_us"] / 1e3, 5),
+                "launches_per_step": k["launches_per_step"],
+                "algorithmic_flops_per_launch": k["algorithmic_flops_per_launch"],
+                "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"]}
 
     # RHT bandwidth per one-sided pass (W, 4096 x 4096)
     def timed(fn, reps):
@@ -347,6 +390,7 @@ def main():
         "weights_per_s_from_resident_H_W": round(mn / (from_resident / 1e3), 1),
         "rht": rht,
         "roofline": roofline,
+        "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])),
     }
     if args.calibrate_copy:
         src = torch.ones(COPY_MIB * 2 ** 20 // 4, device=dev)

@@ -261,6 +261,28 @@ quip_status quip_proxy_loss(const float* W, const float* What, int64_t m, int64_
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Kernel timing (measurement support; not a step of the method). While
+ * enabled, every kernel the library launches is bracketed by two HIP events
+ * recorded on the caller's stream and filed under its kernel family (GEMMs by
+ * call site: "gemm:hessian", "gemm:ldl_inner", "gemm:ldl_outer",
+ * "gemm:ldlq_inner", "gemm:ldlq_outer", "gemm:kron", "gemm:proxy_loss").
+ * Process-wide, off by default; enabling adds two event records per launch.
+ *   quip_timing_enable(on): 1 on, 0 off.
+ *   quip_timing_reset(): waits for recorded events, then clears all sums.
+ *   quip_timing_report(buf, len, needed): waits for recorded events, adds them
+ *     to the sums and writes one text line "name launches total_ms flops
+ *     bytes" per family into buf (NUL-terminated, truncated to len), where
+ *     flops and bytes are the summed algorithmic work of the launches (useful
+ *     floating-point operations, compulsory global-memory bytes; 0 where not
+ *     modelled); *needed receives the full size. buf may be NULL to query the
+ *     size.
+ * Errors: QUIP_ERR_HIP (an event could not be waited on).
+ */
+quip_status quip_timing_enable(int on);
+quip_status quip_timing_reset(void);
+quip_status quip_timing_report(char* buf, size_t len, size_t* needed);
+
+/*
  * quip_e8_codebook -- fills HOST memory with the 65536 smallest-norm points of
  * the E8 lattice (D8 together with D8 + 1/2) ordered by squared norm, then by
  * coordinates ascending with the first coordinate most significant; 65536 x 8

@@ -72,6 +72,9 @@ SYMBOLS = {
     "quip_proxy_loss": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_sz,
                                 c_vp]),
     "quip_e8_codebook": (c_int, [c_vp]),
+    "quip_timing_enable": (c_int, [c_int]),
+    "quip_timing_reset": (c_int, []),
+    "quip_timing_report": (c_int, [ctypes.c_char_p, c_sz, ctypes.POINTER(c_sz)]),
 }
 
 for _name, (_res, _args) in SYMBOLS.items():
@@ -230,4 +233,26 @@ def quip_e8_codebook() -> torch.Tensor:
     """The 65536 x 8 codebook in host memory (float32)."""
     out = torch.empty((65536, 8), dtype=torch.float32)
     _check(lib.quip_e8_codebook(c_vp(out.data_ptr())), "quip_e8_codebook")
+    return out
+
+
+def timing_enable(on: bool = True) -> None:
+    """Per-kernel event timing inside the library (measurement support)."""
+    _check(lib.quip_timing_enable(int(on)), "quip_timing_enable")
+
+
+def timing_reset() -> None:
+    _check(lib.quip_timing_reset(), "quip_timing_reset")
+
+
+def timing_report() -> dict:
+    """{kernel family: (launches, total_ms, flops, bytes)} since the last reset."""
+    need = c_sz(0)
+    _check(lib.quip_timing_report(None, 0, ctypes.byref(need)), "quip_timing_report")
+    buf = ctypes.create_string_buffer(need.value + 64)
+    _check(lib.quip_timing_report(buf, len(buf), ctypes.byref(need)), "quip_timing_report")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, count, ms, flops, nbytes = line.split()
+        out[name] = (int(count), float(ms), float(flops), float(nbytes))
     return out

@@ -21,6 +21,9 @@ size_t kron_workspace_bytes(int64_t rows, int64_t cols);
 quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, float* D,
                        int32_t* info, void* ws, size_t ws_bytes, hipStream_t s);
 size_t ldl_workspace_bytes(int64_t n);
+void timing_enable(bool on);
+quip_status timing_reset();
+quip_status timing_report(std::string& out);
 quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const float* U,
                      const float* D, int g, int64_t B, const quip_quantizer& q, float* scales,
                      void* codes, float* What, const float* codebook, double* row_loss,
@@ -335,6 +338,30 @@ quip_status quip_proxy_loss(const float* W, const float* What, int64_t m, int64_
   if (!loss_dev) return fail(QUIP_ERR_ARG, "quip_proxy_loss: loss is null");
   QUIP_TRY(check_ws(ws, ws_bytes, loss_workspace_bytes(m, n), "quip_proxy_loss"));
   return proxy_loss(W, What, m, n, ld, H, ldh, loss_dev, ws, ws_bytes, stream);
+}
+
+quip_status quip_timing_enable(int on) {
+  clear_error();
+  timing_enable(on != 0);
+  return QUIP_OK;
+}
+
+quip_status quip_timing_reset(void) {
+  clear_error();
+  return timing_reset();
+}
+
+quip_status quip_timing_report(char* buf, size_t len, size_t* needed) {
+  clear_error();
+  std::string out;
+  const quip_status st = timing_report(out);
+  if (needed) *needed = out.size() + 1;
+  if (buf && len > 0) {
+    const size_t k = out.size() < len - 1 ? out.size() : len - 1;
+    std::memcpy(buf, out.data(), k);
+    buf[k] = 0;
+  }
+  return st;
 }
 
 quip_status quip_e8_codebook(float* host_out) {

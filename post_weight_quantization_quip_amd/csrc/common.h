@@ -42,6 +42,25 @@ quip_status fail(quip_status st, const std::string& msg);
 // Checks the last launch on this thread.
 quip_status launch_check(const char* what);
 
+// ---------------------------------------------------------------- kernel timing
+
+// While timing is on (quip_timing_enable), every launch is bracketed by two
+// HIP events on its stream, filed under `name` (timing.cpp).
+// `flops` and `bytes` are the launch's algorithmic work (useful floating-point
+// operations, compulsory global-memory bytes), summed with the times.
+bool timing_on();
+int timing_begin(const char* name, hipStream_t s, double flops, double bytes);  // -1 when off
+void timing_end(int token, hipStream_t s);
+
+template <typename F>
+quip_status timed_launch(const char* name, hipStream_t s, F&& launch, double flops = 0.0,
+                         double bytes = 0.0) {
+  const int tok = timing_on() ? timing_begin(name, s, flops, bytes) : -1;
+  launch();
+  if (tok >= 0) timing_end(tok, s);
+  return launch_check(name);
+}
+
 // ---------------------------------------------------------------- workspace
 
 // Carves 256-byte aligned sub-buffers out of a caller workspace. With a null
@@ -118,6 +137,7 @@ struct GemmArgs {
   // to P (float count P_floats) and summed in a fixed order (deterministic).
   float* P = nullptr;
   size_t P_floats = 0;
+  const char* tag = "gemm";  // name under which launches are timed
   // internal: tiles [tile0, tile0 + grid / kpieces) of the grid, K in pieces of kchunk
   int tile0 = 0;
   int kpieces = 1;

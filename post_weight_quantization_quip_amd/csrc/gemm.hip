@@ -392,8 +392,27 @@ TailPlan plan_tail(int64_t M, int64_t K) {
   return pl;
 }
 
+// Algorithmic work of one gemm() call: useful flops (the upper triangle only
+// for upper tiles, k <= j only for the symmetric dot) and compulsory bytes.
+void gemm_work(const GemmArgs& a, double& flops, double& bytes) {
+  const double M = double(a.M), N = double(a.N), K = double(a.K), b = double(a.batch);
+  if (a.upper_tiles) {
+    flops = M * (M + 1.0) * K * b;
+    bytes = 4.0 * b * (K * M * (a.A == a.B ? 1.0 : 2.0) + M * M * (a.beta != 0.f ? 2.0 : 1.0));
+  } else if (a.epi == EPI_DOT_SYM) {
+    flops = M * N * (N + 1.0) * b + 2.0 * M * N * b;
+    bytes = 4.0 * b * (M * K + N * (N + 1.0) / 2.0 + M * N);
+  } else {
+    flops = 2.0 * M * N * K * b + (a.epi == EPI_DOT ? 2.0 * M * N * b : 0.0);
+    bytes = 4.0 * b * (M * K + K * N +
+                       (a.epi == EPI_DOT ? M * N : M * N * (a.beta != 0.f ? 2.0 : 1.0)));
+  }
+}
+
 template <int BM, int BN, bool TA, bool TB, int EPI>
 quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
+  double wf = 0.0, wb = 0.0;  // attributed to the call's first launch
+  if (timing_on()) gemm_work(a, wf, wb);
   int tiles_m = int(cdiv(a.M, BM)), tiles_n = int(cdiv(a.N, BN));
   int total = a.upper_tiles ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
   if (total == 0 || a.batch == 0) return QUIP_OK;
@@ -405,27 +424,32 @@ quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
         GemmArgs f = a;
         f.tile0 = 0;
         f.kpieces = 1;
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(full, 1), dim3(256), 0, s, f,
-                           tiles_m, tiles_n, full, vecA, vecB);
-        QUIP_TRY(launch_check("gemm_kernel"));
+        QUIP_TRY(timed_launch(a.tag, s, [&] {
+          hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(full, 1), dim3(256), 0, s, f,
+                             tiles_m, tiles_n, full, vecA, vecB);
+        }, wf, wb));
+        wf = wb = 0.0;
       }
       GemmArgs t = a;
       t.tile0 = full;
       t.kpieces = pl.kp;
       t.kchunk = pl.kchunk;
       const int np = pl.R * pl.kp;
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(np, 1), dim3(256), 0, s, t,
-                         tiles_m, tiles_n, np, vecA, vecB);
-      QUIP_TRY(launch_check("gemm_kernel"));
-      hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(pl.R, BM * BN / 1024), dim3(256), 0, s,
-                         t, tiles_m);
-      return launch_check("tail_reduce_kernel");
+      QUIP_TRY(timed_launch(a.tag, s, [&] {
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(np, 1), dim3(256), 0, s, t,
+                           tiles_m, tiles_n, np, vecA, vecB);
+      }, wf, wb));
+      return timed_launch("gemm_tail_reduce", s, [&] {
+        hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(pl.R, BM * BN / 1024), dim3(256), 0, s,
+                           t, tiles_m);
+      });
     }
   }
   dim3 grid(total, a.batch);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), grid, dim3(256), 0, s, a, tiles_m,
-                     tiles_n, total, vecA, vecB);
-  return launch_check("gemm_kernel");
+  return timed_launch(a.tag, s, [&] {
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), grid, dim3(256), 0, s, a, tiles_m,
+                       tiles_n, total, vecA, vecB);
+  }, wf, wb);
 }
 
 template <bool TA, bool TB, int EPI>

@@ -62,6 +62,7 @@ quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx
   g.beta = accumulate ? 1.f : 0.f;
   g.upper_tiles = true;
   g.mirror = true;
+  g.tag = "gemm:hessian";
   g.P = P;  // leftover tiles split along K when the workspace holds their pieces
   g.P_floats = P_floats;
   return gemm(g, s);
@@ -69,14 +70,16 @@ quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx
 
 quip_status hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,
                              double* scratch, hipStream_t s) {
-  hipLaunchKernelGGL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
-  QUIP_TRY(launch_check("trace_kernel"));
+  QUIP_TRY(timed_launch("trace_kernel", s, [&] {
+    hipLaunchKernelGGL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
+  }));
   int64_t gx = cdiv(n, 256);
   if (gx > 16) gx = 16;
   dim3 grid(unsigned(gx), unsigned(n < 65535 ? n : 65535));
-  hipLaunchKernelGGL(finalize_kernel, grid, dim3(256), 0, s, H, n, ldh, scratch,
-                     1.0 / double(N_total), double(alpha));
-  return launch_check("finalize_kernel");
+  return timed_launch("finalize_kernel", s, [&] {
+    hipLaunchKernelGGL(finalize_kernel, grid, dim3(256), 0, s, H, n, ldh, scratch,
+                       1.0 / double(N_total), double(alpha));
+  });
 }
 
 }  // namespace quip

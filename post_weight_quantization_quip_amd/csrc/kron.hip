@@ -44,6 +44,7 @@ quip_status kron_apply(const float* A, float* out, int64_t rows, int64_t cols, i
     g1.C = T;
     g1.ldc = q;
     g1.strideC = p * q;
+    g1.tag = "gemm:kron";
     QUIP_TRY(gemm(g1, s));
     // out_r[a, b] = sum_a' F1[a][a'] T_r[a', b]  (inverse: F1^T)
     GemmArgs g2;
@@ -60,6 +61,7 @@ quip_status kron_apply(const float* A, float* out, int64_t rows, int64_t cols, i
     g2.ldc = q;
     g2.strideC = ld;
     g2.batch = int(rows);
+    g2.tag = "gemm:kron";
     return gemm(g2, s);
   }
   // LEFT: T_a = F2 A_a (q x cols), a = 0..p-1
@@ -77,6 +79,7 @@ quip_status kron_apply(const float* A, float* out, int64_t rows, int64_t cols, i
   g1.ldc = cols;
   g1.strideC = q * cols;
   g1.batch = int(p);
+  g1.tag = "gemm:kron";
   QUIP_TRY(gemm(g1, s));
   // out[(a, b), :] = sum_a' F1[a][a'] T[(a', b), :] : batched over b (row stride q*ld)
   GemmArgs g2;
@@ -101,6 +104,7 @@ quip_status kron_apply(const float* A, float* out, int64_t rows, int64_t cols, i
     g2.strideC = ld;
     g2.batch = int(q);
   }
+  g2.tag = "gemm:kron";
   return gemm(g2, s);
 }
 

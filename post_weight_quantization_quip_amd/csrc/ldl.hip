@@ -510,13 +510,18 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
       const float* src = aw_outer ? Aw : H;
       const int64_t lsrc = aw_outer ? n : ldh;
       const dim3 grid(unsigned(k0 > 0 ? k0 / PR : 1));
-      if (g == 1)
-        hipLaunchKernelGGL((ldl_block_kernel<PR, 1>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
-                           k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
-      else
-        hipLaunchKernelGGL((ldl_block_kernel<PR, 8>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
-                           k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
-      QUIP_TRY(launch_check("ldl_block_kernel"));
+      // work: the w x w factorization, then per row above a triangular solve
+      // and the D^{-1} scaling; reads the block column, writes U, X and D
+      const double wd = double(w), kd = double(k0);
+      QUIP_TRY(timed_launch("ldl_block_kernel", s, [&] {
+        if (g == 1)
+          hipLaunchKernelGGL((ldl_block_kernel<PR, 1>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
+                             k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
+        else
+          hipLaunchKernelGGL((ldl_block_kernel<PR, 8>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
+                             k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
+      }, 2.0 / 3.0 * wd * wd * wd + kd * (wd * wd + wd),
+         4.0 * ((kd + wd) * wd + 2.0 * kd * wd + wd * wd + wd * g)));
       if (k0 == 0) break;
       if (b > 0) {
         // the outer block's columns left of this one: A[:k0, o0:k0] -= X U[o0:k0, blk]^T
@@ -535,6 +540,7 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
         t.ldcin = lsrc;
         t.alpha = -1.f;
         t.beta = 1.f;
+        t.tag = "gemm:ldl_inner";
         QUIP_TRY(gemm(t, s));
         aw_outer = true;
       }
@@ -559,6 +565,7 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
     t.alpha = -1.f;
     t.beta = 1.f;
     t.upper_tiles = true;
+    t.tag = "gemm:ldl_outer";
     QUIP_TRY(gemm(t, s));
     aw_lead = true;
   }

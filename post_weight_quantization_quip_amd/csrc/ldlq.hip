@@ -614,8 +614,9 @@ void host_e8_candidates(int ncand, float* out) {
 
 quip_status finish_loss(const double* rl, int64_t m, double* loss, hipStream_t s) {
   if (!loss) return QUIP_OK;
-  hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, s, rl, m, loss);
-  return launch_check("sum_rows_kernel");
+  return timed_launch("sum_rows_kernel", s, [&] {
+    hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, s, rl, m, loss);
+  });
 }
 
 struct E8Ws {
@@ -630,13 +631,17 @@ struct E8Ws {
 
 quip_status grid_scales(const float* W, int64_t m, int64_t n, int64_t ldw, int L, int ncand,
                         float* factors_dev, float* scales, float* mse, hipStream_t s) {
-  if (ncand <= 32)
-    hipLaunchKernelGGL((grid_scale_kernel<32>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
-                       ncand, factors_dev, scales, mse);
-  else
-    hipLaunchKernelGGL((grid_scale_kernel<64>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
-                       ncand, factors_dev, scales, mse);
-  return launch_check("grid_scale_kernel");
+  // work: every candidate step rounds every weight of the row once
+  const double gfl = double(m) * double(n) * double(ncand) * 6.0;
+  const double gby = 4.0 * double(m) * double(n) + 4.0 * double(m);
+  return timed_launch("grid_scale_kernel", s, [&] {
+    if (ncand <= 32)
+      hipLaunchKernelGGL((grid_scale_kernel<32>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
+                         ncand, factors_dev, scales, mse);
+    else
+      hipLaunchKernelGGL((grid_scale_kernel<64>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
+                         ncand, factors_dev, scales, mse);
+  }, gfl, gby);
 }
 
 quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, const E8Ws& e,
@@ -644,15 +649,17 @@ quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, con
   QUIP_TRY(fill_f64(e.sse, 64, 0.0, s));
   const int64_t nvec = m * (n / 8);
   dim3 grid(unsigned(cdiv(nvec, 128)));
-  if (ncand <= 32)
-    hipLaunchKernelGGL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
-                       ncand, e.sse);
-  else
-    hipLaunchKernelGGL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
-                       ncand, e.sse);
-  QUIP_TRY(launch_check("e8_scale_kernel"));
-  hipLaunchKernelGGL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
-  QUIP_TRY(launch_check("e8_pick_scale_kernel"));
+  QUIP_TRY(timed_launch("e8_scale_kernel", s, [&] {
+    if (ncand <= 32)
+      hipLaunchKernelGGL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+                         ncand, e.sse);
+    else
+      hipLaunchKernelGGL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+                         ncand, e.sse);
+  }));
+  QUIP_TRY(timed_launch("e8_pick_scale_kernel", s, [&] {
+    hipLaunchKernelGGL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
+  }));
   if (sse_out) QUIP_HIP(hipMemcpyAsync(sse_out, e.sse, sizeof(double) * ncand, hipMemcpyDeviceToDevice, s));
   return QUIP_OK;
 }
@@ -672,10 +679,17 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
                    ((reinterpret_cast<uintptr_t>(codes) & 3) == 0) && ldw % 4 == 0 &&
                    ldf % 4 == 0 && ldu % 4 == 0 && ldc % 4 == 0 && ldwh % 4 == 0 &&
                    lde % 4 == 0 && s0 % 4 == 0;
-  hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(64), shmem, s, W, ldw,
-                     F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
-                     D, rowloss, vec);
-  return launch_check("ldlq_sweep_kernel");
+  // work: per row the in-block feedback (bw (bw - 1) flops) and the rounding;
+  // reads W, F and the U block, writes codes, W^ and the errors
+  const double md = double(m), bd = double(bw);
+  const double flops = md * (bd * (bd - 1.0) + 6.0 * bd);
+  const double bytes = md * bd * (4.0 + (useF ? 4.0 : 0.0) + 1.0 + (What ? 4.0 : 0.0) + 4.0) +
+                       4.0 * bd * bd + (rowloss ? 16.0 * md : 0.0);
+  return timed_launch("ldlq_sweep_kernel", s, [&] {
+    hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(64), shmem, s, W, ldw,
+                       F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
+                       D, rowloss, vec);
+  }, flops, bytes);
 }
 
 quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
@@ -693,7 +707,7 @@ quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ld
 // F[:, c0:c1] (+)= Eb[:, e0:e0+K] U[r0:r0+K, c0:c1]
 quip_status feedback_gemm(const float* Eb, int64_t lde, int64_t e0, int64_t K, const float* U,
                           int64_t n, int64_t r0, int64_t c0, int64_t c1, float* F, int64_t m,
-                          bool accumulate, hipStream_t s) {
+                          bool accumulate, const char* tag, hipStream_t s) {
   if (c1 <= c0 || K <= 0) return QUIP_OK;
   GemmArgs a;
   a.M = m;
@@ -707,6 +721,7 @@ quip_status feedback_gemm(const float* Eb, int64_t lde, int64_t e0, int64_t K, c
   a.ldc = n;
   a.alpha = 1.f;
   a.beta = accumulate ? 1.f : 0.f;
+  a.tag = tag;
   return gemm(a, s);
 }
 
@@ -744,11 +759,13 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_scales: workspace too small");
   host_e8_candidates(q.n_cand, hostf);
   QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
-  hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
-                     true);
-  QUIP_TRY(launch_check("rownorm_kernel"));
-  hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
-  QUIP_TRY(launch_check("e8_norms_kernel"));
+  QUIP_TRY(timed_launch("rownorm_kernel", s, [&] {
+    hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
+                       true);
+  }));
+  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&] {
+    hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+  }));
   return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
 }
 
@@ -812,9 +829,9 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
                        Eb + (s0 - j0), Bo, D, rl, s));
         // rest of this batch
         QUIP_TRY(feedback_gemm(Eb, Bo, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
-                               !(j0 == 0 && s0 == 0), s));
+                               !(j0 == 0 && s0 == 0), "gemm:ldlq_inner", s));
       }
-      QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
+      QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
     }
     return finish_loss(rl, m, loss, s);
   }
@@ -830,11 +847,13 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   e.Eb = Eb;
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldlq: workspace too small");
   const bool compute = q.scale_mode == QUIP_SCALE_COMPUTE;
-  hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
-                     compute);
-  QUIP_TRY(launch_check("rownorm_kernel"));
-  hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
-  QUIP_TRY(launch_check("e8_norms_kernel"));
+  QUIP_TRY(timed_launch("rownorm_kernel", s, [&] {
+    hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
+                       compute);
+  }));
+  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&] {
+    hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+  }));
   if (compute) {
     host_e8_candidates(q.n_cand, hostf);
     QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
@@ -842,23 +861,26 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   }
   // the global scale stays on the device (scales[0]); the step kernels read it there
   const float* sglob = scales;
-  hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
-  QUIP_TRY(launch_check("fill_u64_kernel"));
+  QUIP_TRY(timed_launch("fill_u64_kernel", s, [&] {
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
+  }));
   uint16_t* cd = static_cast<uint16_t*>(codes);
   const int chunk = 4096;
   for (int64_t j0 = 0; j0 < n; j0 += B) {
     const int64_t bo = (n - j0 < B) ? n - j0 : B;
     for (int64_t c0 = j0; c0 < j0 + bo; c0 += 8) {
       dim3 grid(unsigned(cdiv(m, 32)), unsigned(65536 / chunk));
-      hipLaunchKernelGGL(e8_argmin_kernel, grid, dim3(256), 0, s, e.Wn, n, F, j0 > 0, Eb, B,
-                         int(c0 - j0), U, c0, j0, codebook, e.c2, sglob, m, chunk, e.keys);
-      QUIP_TRY(launch_check("e8_argmin_kernel"));
-      hipLaunchKernelGGL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
-                         codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
-                         int(c0 - j0), F, j0 > 0, U, j0, D, rl);
-      QUIP_TRY(launch_check("e8_finish_kernel"));
+      QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&] {
+        hipLaunchKernelGGL(e8_argmin_kernel, grid, dim3(256), 0, s, e.Wn, n, F, j0 > 0, Eb, B,
+                           int(c0 - j0), U, c0, j0, codebook, e.c2, sglob, m, chunk, e.keys);
+      }));
+      QUIP_TRY(timed_launch("e8_finish_kernel", s, [&] {
+        hipLaunchKernelGGL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
+                           codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
+                           int(c0 - j0), F, j0 > 0, U, j0, D, rl);
+      }));
     }
-    QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, s));
+    QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
   }
   return finish_loss(rl, m, loss, s);
 }

@@ -35,6 +35,7 @@ quip_status proxy_loss(const float* W, const float* What, int64_t m, int64_t n, 
   g.lde = n;
   g.dot = loss;
   g.C = nullptr;
+  g.tag = "gemm:proxy_loss";
   return gemm(g, s);
 }
 

@@ -54,39 +54,44 @@ quip_status fill_f32(float* p, int64_t count, float v, hipStream_t s) {
   if (count <= 0) return QUIP_OK;
   int64_t blocks = cdiv(count, 256);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(fill_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
-  return launch_check("fill_f32");
+  return timed_launch("fill_f32", s, [&] {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
+  });
 }
 
 quip_status fill_f64(double* p, int64_t count, double v, hipStream_t s) {
   if (count <= 0) return QUIP_OK;
   int64_t blocks = cdiv(count, 256);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(fill_f64_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
-  return launch_check("fill_f64");
+  return timed_launch("fill_f64", s, [&] {
+    hipLaunchKernelGGL(fill_f64_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
+  });
 }
 
 quip_status fill_matrix(float* p, int64_t rows, int64_t cols, int64_t ld, float v, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return QUIP_OK;
   if (ld == cols) return fill_f32(p, rows * cols, v, s);
-  hipLaunchKernelGGL(fill_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, p, rows, cols, ld, v);
-  return launch_check("fill_matrix");
+  return timed_launch("fill_matrix", s, [&] {
+    hipLaunchKernelGGL(fill_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, p, rows, cols, ld, v);
+  });
 }
 
 quip_status sub_matrix(const float* a, const float* b, float* out, int64_t rows, int64_t cols,
                        int64_t lda, int64_t ldb, int64_t ldo, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return QUIP_OK;
-  hipLaunchKernelGGL(sub_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, a, b, out, rows,
-                     cols, lda, ldb, ldo);
-  return launch_check("sub_matrix");
+  return timed_launch("sub_matrix", s, [&] {
+    hipLaunchKernelGGL(sub_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, a, b, out, rows,
+                       cols, lda, ldb, ldo);
+  });
 }
 
 quip_status copy_matrix(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows,
                         int64_t cols, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return QUIP_OK;
-  hipLaunchKernelGGL(copy_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, src, lds, dst, ldd,
-                     rows, cols);
-  return launch_check("copy_matrix");
+  return timed_launch("copy_matrix", s, [&] {
+    hipLaunchKernelGGL(copy_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, src, lds, dst, ldd,
+                       rows, cols);
+  });
 }
 
 }  // namespace quip

@@ -297,44 +297,48 @@ quip_status rows_t(const float* A, float* out, int64_t rows, int64_t ld, const f
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_rows_kernel<LOGN, LE>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
   dim3 grid(unsigned(cdiv(rows, RW)));
-  hipLaunchKernelGGL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
-                     s, scale, inverse, vec);
-  return launch_check("rht_rows_kernel");
+  return timed_launch("rht_rows_kernel", st, [&] {
+    hipLaunchKernelGGL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
+                       s, scale, inverse, vec);
+  }, double(rows) * N * (LOGN + 2), 8.0 * double(rows) * N);
 }
 
 template <int N>
 quip_status rows_small_t(const float* A, float* out, int64_t rows, int64_t ld, const float* s,
                          bool inverse, hipStream_t st) {
   const float scale = 1.0f / sqrtf(float(N));
-  hipLaunchKernelGGL((rht_rows_small_kernel<N>), dim3(unsigned(cdiv(rows, 256))), dim3(256), 0, st,
-                     A, out, rows, ld, s, scale, inverse);
-  return launch_check("rht_rows_small_kernel");
+  return timed_launch("rht_rows_small_kernel", st, [&] {
+    hipLaunchKernelGGL((rht_rows_small_kernel<N>), dim3(unsigned(cdiv(rows, 256))), dim3(256), 0, st,
+                       A, out, rows, ld, s, scale, inverse);
+  });
 }
 
 template <int D>
 quip_status cols_small_t(const float* A, float* out, int64_t cols, int64_t ld, const float* s,
                          bool inverse, hipStream_t st) {
   const float scale = 1.0f / sqrtf(float(D));
-  hipLaunchKernelGGL((rht_cols_small_kernel<D>), dim3(unsigned(cdiv(cols, 256))), dim3(256), 0, st,
-                     A, out, cols, ld, s, scale, inverse);
-  return launch_check("rht_cols_small_kernel");
+  return timed_launch("rht_cols_small_kernel", st, [&] {
+    hipLaunchKernelGGL((rht_cols_small_kernel<D>), dim3(unsigned(cdiv(cols, 256))), dim3(256), 0, st,
+                       A, out, cols, ld, s, scale, inverse);
+  });
 }
 
 quip_status cols_pass(int kr, const float* A, float* out, int64_t d, int64_t cols, int64_t ld,
                       int lo, const float* s, float scale, int mode, hipStream_t st) {
   dim3 grid(unsigned(d >> kr), unsigned(cdiv(cols, 64)));
-  switch (kr) {
-#define CASE(K)                                                                              \
-  case K:                                                                                    \
-    hipLaunchKernelGGL((rht_cols_pass<K>), grid, dim3(256), 0, st, A, out, cols, ld, lo, s, \
-                       scale, mode);                                                         \
+  if (kr < 4 || kr > 7) return fail(QUIP_ERR_UNSUPPORTED, "rht_cols: pass size");
+  // one pass reads and writes the whole matrix once (kr butterfly levels)
+  return timed_launch("rht_cols_pass", st, [&] {
+    switch (kr) {
+#define CASE(K)                                                                                \
+  case K:                                                                                      \
+    hipLaunchKernelGGL((rht_cols_pass<K>), grid, dim3(256), 0, st, A, out, cols, ld, lo, s,   \
+                       scale, mode);                                                           \
     break;
-    CASE(4) CASE(5) CASE(6) CASE(7)
+      CASE(4) CASE(5) CASE(6) CASE(7)
 #undef CASE
-    default:
-      return fail(QUIP_ERR_UNSUPPORTED, "rht_cols: pass size");
-  }
-  return launch_check("rht_cols_pass");
+    }
+  }, double(d) * double(cols) * (kr + 1), 8.0 * double(d) * double(cols));
 }
 
 }  // namespace
