@@ -23,6 +23,8 @@
 // (order-preserving distance bits, index) 64-bit key and atomicMin.
 #include <type_traits>
 
+#include <utility>
+
 #include "common.h"
 
 namespace quip {
@@ -126,59 +128,70 @@ __global__ __launch_bounds__(256) void grid_scale_kernel(const float* __restrict
   }
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value of lane J of this lane's 16-lane row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xF, 0xF, false));
+}
+
 // ------------------------------------------------------------------ scalar LDLQ sweep
 
-// Scalar LDLQ sweep of one block of B columns for 16 rows per wave.
+// Scalar LDLQ sweep of one block of B columns for 16 rows per work-group.
 //
-// Lanes: row r = lane / 4 of the wave, quad position g = lane % 4. The block is
-// walked in chunks of 16 columns; inside the current chunk lane g owns the 4
-// columns 16 tk + 4 g + e. A column is rounded by its owner, the error is sent
-// to the other lanes of the quad with one DPP quad_perm, and the 4 current-chunk
-// accumulators of every lane are updated at once (rank-1, registers). The later
-// chunks of the block get one rank-16 update per chunk from the 16 broadcast
-// errors; their accumulators live in per-lane LDS (so the code stays a short
-// loop and every register index is static). U's block is staged in LDS,
-// permuted so that each lane's 4 columns are one float4 and padded so that the
-// 4 lanes of a quad hit different banks.
+// 4 waves x 4 rows; each row is one 16-lane DPP row of its wave, and lane j of
+// the row owns column 16 tk + j of the current 16-column chunk tk. Every lane
+// evaluates the rounding on its own target; the owner's error of column kk is
+// sent to the row with one DPP row_newbcast and every lane adds its share of
+// the feedback (rank-1, one FMA; U is zero on and below the diagonal, so the
+// columns already rounded are left alone). After a chunk, each lane adds the
+// chunk's rank-16 feedback to one accumulator per later chunk; those live in
+// registers, shifted down by one chunk per step so that every register index
+// is static. U's block is staged transposed in LDS (row c = column c of U),
+// so that a lane's 16 coefficients of a chunk are four float4 reads.
 template <int B>
-__global__ __launch_bounds__(64) void ldlq_sweep_kernel(
+__global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
     const float* __restrict__ U, int64_t ldu, const float* __restrict__ scales, int L, int64_t m,
     int64_t s0, int bw, uint8_t* __restrict__ codes, int64_t ldcode, float* __restrict__ What,
     int64_t ldwh, float* __restrict__ Eb, int64_t lde, const float* __restrict__ Dg,
     double* __restrict__ rowloss, bool vec) {
   constexpr int NT = B / 16;  // 16-column chunks
-  constexpr int NS = B / 4;   // columns per lane over the whole block
-  constexpr int PS = NS + 4;  // padded row of the permuted U block
+  constexpr int UP = B + 4;   // padded row of the transposed U block
   extern __shared__ __align__(16) float sm[];
-  float* Us = sm;                  // [B][4][PS]: Us[(k*4 + g)*PS + 4t + e] = U[s0+k][s0+16t+4g+e]
-  float* Ar = sm + B * 4 * PS;     // [64][NS]: per-lane accumulators of the later chunks
-  float* Ds = Ar + 64 * NS;        // [B]: D of the block (proxy loss)
+  float* Ut = sm;            // [B][UP]: Ut[c * UP + k] = U[s0 + k][s0 + c]
+  float* Ds = sm + B * UP;   // [B]: D of the block (proxy loss)
 
-  const int lane = threadIdx.x;
-  const int g = lane & 3;
-  const int64_t row = int64_t(blockIdx.x) * 16 + (lane >> 2);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = lane & 15;  // column of the chunk owned by this lane
+  const int64_t row = int64_t(blockIdx.x) * 16 + (tid >> 4);
   const bool live = row < m;
 
-  // U block -> LDS in batches: all loads of a batch are issued before any store
+  // U block -> LDS, transposed; lanes walk k so that the LDS writes are
+  // consecutive; every load of a batch is issued before its stores
   {
-    constexpr int NL = B * (B / 4) / 64;  // float4 per lane
-    constexpr int BATCH = NL < 16 ? NL : 16;
+    constexpr int NL = B * (B / 4) / 256;  // float4 per thread
+    constexpr int BATCH = NL < 8 ? NL : 8;
     const bool fast = vec && bw == B;
     for (int b0 = 0; b0 < NL; b0 += BATCH) {
       float4 v[BATCH];
-      if (fast) {
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-          const int e = lane + 64 * (b0 + i);
-          const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
+      for (int i = 0; i < BATCH; ++i) {
+        const int e = tid + 256 * (b0 + i);
+        const int k = e % B, c4 = (e / B) * 4;
+        if (fast) {
           v[i] = *reinterpret_cast<const float4*>(U + (s0 + k) * ldu + s0 + c4);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-          const int e = lane + 64 * (b0 + i);
-          const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
+        } else {
           v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (k < bw) {
             const float* src = U + (s0 + k) * ldu + s0 + c4;
@@ -191,78 +204,78 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
       }
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
-        const int e = lane + 64 * (b0 + i);
-        const int k = e / (B / 4), c4 = (e % (B / 4)) * 4;
-        const int gg = (c4 >> 2) & 3, t16 = c4 >> 4;
-        *reinterpret_cast<float4*>(&Us[(k * 4 + gg) * PS + 4 * t16]) = v[i];
+        const int e = tid + 256 * (b0 + i);
+        const int k = e % B, c4 = (e / B) * 4;
+        Ut[(c4 + 0) * UP + k] = v[i].x;
+        Ut[(c4 + 1) * UP + k] = v[i].y;
+        Ut[(c4 + 2) * UP + k] = v[i].z;
+        Ut[(c4 + 3) * UP + k] = v[i].w;
       }
     }
   }
-  auto load4 = [&](const float* base, int64_t ld, int c) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!live) return v;
-    const float* p = base + row * ld + s0 + c;
-    if (vec && c + 3 < bw) return *reinterpret_cast<const float4*>(p);
-    if (c + 0 < bw) v.x = p[0];
-    if (c + 1 < bw) v.y = p[1];
-    if (c + 2 < bw) v.z = p[2];
-    if (c + 3 < bw) v.w = p[3];
-    return v;
-  };
   if (rowloss) {
-    for (int i = lane; i < B; i += 64) Ds[i] = i < bw ? Dg[s0 + i] : 0.f;
+    for (int i = tid; i < B; i += 256) Ds[i] = i < bw ? Dg[s0 + i] : 0.f;
   }
-  {
-    float4 fv[NT];
+  // accumulators: `acc` for the current chunk, ar[i] for chunk tk + 1 + i
+  float acc = 0.f, ar[NT > 1 ? NT - 1 : 1];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      fv[t] = useF ? load4(F, ldf, 16 * t + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < NT - 1; ++i) ar[i] = 0.f;
+  if (useF && live) {
+    if (j < bw) acc = F[row * ldf + s0 + j];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<float4*>(&Ar[lane * NS + 4 * t]) = fv[t];
+    for (int i = 0; i < NT - 1; ++i) {
+      const int c = 16 * (i + 1) + j;
+      if (c < bw) ar[i] = F[row * ldf + s0 + c];
+    }
   }
   __syncthreads();
 
   const float s = live ? scales[row] : 1.f;
   const float inv = 1.f / s;
   const float half = L * 0.5f, cen = (L - 1) * 0.5f, hi = float(L - 1);
-
-  float4 wn = load4(W, ldw, 4 * g);
   // proxy loss of this row: with H = (I + U) D (I + U)^T and E = W - W^, the
   // column j of E (I + U) is the target p_j minus its rounded value, so
   // tr(E H E^T) = sum_j D_j (p_j - q_j)^2 over the columns this lane owns
   double lsum = 0.0;
+
+  float wnext = (live && j < bw) ? W[row * ldw + s0 + j] : 0.f;
   for (int tk = 0; tk < NT; ++tk) {
     if (16 * tk >= bw) break;
-    float wc[4] = {wn.x, wn.y, wn.z, wn.w};
-    const float4 a4 = *reinterpret_cast<const float4*>(&Ar[lane * NS + 4 * tk]);
-    float ac[4] = {a4.x, a4.y, a4.z, a4.w};
-    if (tk + 1 < NT) wn = load4(W, ldw, 16 * (tk + 1) + 4 * g);
-    const float w0[4] = {wc[0], wc[1], wc[2], wc[3]};
-    const float a0[4] = {ac[0], ac[1], ac[2], ac[3]};
-    // row k = 16 tk + kk of the permuted U block, this lane's 4 columns of chunk tk
-    const float* ub = Us + (64 * tk + g) * PS + 4 * tk;
-    const int nk = (bw - 16 * tk) < 16 ? (bw - 16 * tk) : 16;
+    const int c = 16 * tk + j;  // this lane's column in the block
+    const bool own = live && c < bw;
+    const float w = wnext;
+    if (tk + 1 < NT) {
+      const int cn = c + 16;
+      wnext = (live && cn < bw) ? W[row * ldw + s0 + cn] : 0.f;
+    }
+    // the chunk's 16 coefficients U[16 tk + kk][c] of this lane's column
+    float u16[16];
+    {
+      const float4* up = reinterpret_cast<const float4*>(Ut + c * UP + 16 * tk);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 x = up[v];
+        u16[4 * v + 0] = x.x;
+        u16[4 * v + 1] = x.y;
+        u16[4 * v + 2] = x.z;
+        u16[4 * v + 3] = x.w;
+      }
+    }
+    const float a0 = acc;
     float e16[16];
-    float res[4] = {0.f, 0.f, 0.f, 0.f};  // p - q of this lane's 4 columns (last pass)
-    uint32_t cw = 0u;
+    float q = 0.f, err = 0.f, res = 0.f;
+    uint32_t code = 0u;
     // One pass over the 16 columns of the chunk. EXACT = false rounds with
     // p * (1/s); it reports whether an owner lane came within 1e-4 of a
     // decision boundary, where p * (1/s) and the IEEE quotient p / s might
     // differ, and then the chunk is redone with EXACT = true.
-    auto pass = [&](auto exact_tag, auto full_tag) -> bool {
+    auto pass = [&](auto exact_tag) -> bool {
       constexpr bool EXACT = decltype(exact_tag)::value;
-      constexpr bool FULL = decltype(full_tag)::value;
       bool near = false;
-      float4 u16[16];  // the chunk's 16 rows of U, read up front (off the rounding chain)
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) u16[kk] = *reinterpret_cast<const float4*>(ub + kk * 4 * PS);
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const int gk = kk >> 2, ek = kk & 3;
-        e16[kk] = 0.f;
-        if (!FULL && kk >= nk) continue;
-        const float4 u = u16[kk];
-        const float p = wc[ek] + ac[ek];
+      float a = acc;
+      static_for<16>([&](auto KI) {
+        constexpr int kk = decltype(KI)::value;
+        const float p = w + a;
         float y;
         if constexpr (EXACT) {
           y = p / s + half;
@@ -270,87 +283,68 @@ __global__ __launch_bounds__(64) void ldlq_sweep_kernel(
           y = fmaf(p, inv, half);
         }
         const float kfl = floorf(y);
+        const bool mine = (j == kk);
         if constexpr (!EXACT) {
           const float fr = y - kfl;
-          near = near | (live & (g == gk) & ((fr < 1e-4f) | (fr > 0.9999f)));
+          near = near | (own & mine & ((fr < 1e-4f) | (fr > 0.9999f)));
         }
         const float kf = __builtin_amdgcn_fmed3f(kfl, 0.f, hi);
         const float qv = (kf - cen) * s;
-        const float err = wc[ek] - qv;
-        const float errb = quad_bcast(err, gk);
-        if (g == gk) {
-          wc[ek] = qv;
-          ac[ek] = err;
-          res[ek] = p - qv;
-          cw |= uint32_t(kf) << (8 * ek);
+        const float ev = w - qv;
+        const float eb = row_bcast<kk>(ev);
+        if (mine) {
+          q = qv;
+          err = ev;
+          res = p - qv;
+          code = uint32_t(kf);
         }
-        // columns of this chunk after k (U is zero on and below the diagonal)
-        ac[0] = fmaf(errb, u.x, ac[0]);
-        ac[1] = fmaf(errb, u.y, ac[1]);
-        ac[2] = fmaf(errb, u.z, ac[2]);
-        ac[3] = fmaf(errb, u.w, ac[3]);
-        e16[kk] = errb;
-      }
+        e16[kk] = eb;
+        a = fmaf(eb, u16[kk], a);  // zero coefficient on and below the diagonal
+      });
       return near;
     };
-    using T = std::true_type;
-    using Fz = std::false_type;
-    const bool fullchunk = nk == 16;
-    const bool near = fullchunk ? pass(Fz{}, T{}) : pass(Fz{}, Fz{});
+    const bool near = pass(std::false_type{});
     if (__builtin_amdgcn_ballot_w64(near)) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wc[e] = w0[e];
-        ac[e] = a0[e];
-      }
-      cw = 0u;
-      if (fullchunk)
-        pass(T{}, T{});
-      else
-        pass(T{}, Fz{});
+      acc = a0;
+      pass(std::true_type{});
     }
-    // outputs of this chunk: lane g's columns 16 tk + 4 g + e
-    if (live) {
-      const int c = 16 * tk + 4 * g;
+    // outputs of this chunk: one column per lane
+    if (own) {
+      codes[row * ldcode + s0 + c] = uint8_t(code);
+      if (What) What[row * ldwh + s0 + c] = q;
+      Eb[row * lde + c] = err;
       if (rowloss) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&Ds[c]);  // zero past bw
-        const double r0 = res[0], r1 = res[1], r2 = res[2], r3 = res[3];
-        lsum += double(d4.x) * (r0 * r0) + double(d4.y) * (r1 * r1) + double(d4.z) * (r2 * r2) +
-                double(d4.w) * (r3 * r3);
-      }
-      if (vec && c + 3 < bw) {
-        *reinterpret_cast<uint32_t*>(codes + row * ldcode + s0 + c) = cw;
-        if (What)
-          *reinterpret_cast<float4*>(What + row * ldwh + s0 + c) = make_float4(wc[0], wc[1], wc[2], wc[3]);
-        *reinterpret_cast<float4*>(Eb + row * lde + c) = make_float4(ac[0], ac[1], ac[2], ac[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (c + e >= bw) continue;
-          codes[row * ldcode + s0 + c + e] = uint8_t((cw >> (8 * e)) & 0xFF);
-          if (What) What[row * ldwh + s0 + c + e] = wc[e];
-          Eb[row * lde + c + e] = ac[e];
-        }
+        const double r = res;
+        lsum += double(Ds[c]) * (r * r);
       }
     }
-    // rank-16 update of the later chunks
-    for (int t = tk + 1; t < NT; ++t) {
-      float4 acc = *reinterpret_cast<const float4*>(&Ar[lane * NS + 4 * t]);
+    // rank-16 update of the later chunks, then shift them down by one
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const float4 u = *reinterpret_cast<const float4*>(ub + kk * 4 * PS + 4 * (t - tk));
-        acc.x = fmaf(e16[kk], u.x, acc.x);
-        acc.y = fmaf(e16[kk], u.y, acc.y);
-        acc.z = fmaf(e16[kk], u.z, acc.z);
-        acc.w = fmaf(e16[kk], u.w, acc.w);
+    for (int i = 0; i < NT - 1; ++i) {
+      if (i < NT - 1 - tk) {
+        const float4* up = reinterpret_cast<const float4*>(Ut + (c + 16 * (i + 1)) * UP + 16 * tk);
+        float t = ar[i];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 x = up[v];
+          t = fmaf(e16[4 * v + 0], x.x, t);
+          t = fmaf(e16[4 * v + 1], x.y, t);
+          t = fmaf(e16[4 * v + 2], x.z, t);
+          t = fmaf(e16[4 * v + 3], x.w, t);
+        }
+        ar[i] = t;
       }
-      *reinterpret_cast<float4*>(&Ar[lane * NS + 4 * t]) = acc;
+    }
+    if (NT > 1) {
+      acc = ar[0];
+#pragma unroll
+      for (int i = 0; i + 1 < NT - 1; ++i) ar[i] = ar[i + 1];
     }
   }
   if (rowloss) {
-    lsum += __shfl_xor(lsum, 1, 64);
-    lsum += __shfl_xor(lsum, 2, 64);
-    if (live && g == 0) rowloss[row] += lsum;  // one work-group per row per launch
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+    if (live && j == 0) rowloss[row] += lsum;  // one work-group per row per launch
   }
 }
 
@@ -669,7 +663,7 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
                     const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                     int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
                     int64_t lde, const float* D, double* rowloss, hipStream_t s) {
-  const size_t shmem = (size_t(B) * 4 * (B / 4 + 4) + size_t(64) * (B / 4) + B) * sizeof(float);
+  const size_t shmem = (size_t(B) * (B + 4) + B) * sizeof(float);
   if (shmem > 65536)
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
@@ -686,7 +680,7 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
   const double bytes = md * bd * (4.0 + (useF ? 4.0 : 0.0) + 1.0 + (What ? 4.0 : 0.0) + 4.0) +
                        4.0 * bd * bd + (rowloss ? 16.0 * md : 0.0);
   return timed_launch("ldlq_sweep_kernel", s, [&] {
-    hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(64), shmem, s, W, ldw,
+    hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s, W, ldw,
                        F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
                        D, rowloss, vec);
   }, flops, bytes);
