@@ -157,7 +157,8 @@ __device__ __forceinline__ float row_bcast(float v) {
 // chunk's rank-16 feedback to one accumulator per later chunk; those live in
 // registers, shifted down by one chunk per step so that every register index
 // is static. U's block is staged transposed in LDS (row c = column c of U),
-// so that a lane's 16 coefficients of a chunk are four float4 reads.
+// one 16-row chunk ahead of its use, so that a lane's 16 coefficients of a
+// chunk are four float4 reads.
 template <int B>
 __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
@@ -177,42 +178,63 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
   const int64_t row = int64_t(blockIdx.x) * 16 + (tid >> 4);
   const bool live = row < m;
 
-  // U block -> LDS, transposed; lanes walk k so that the LDS writes are
-  // consecutive; every load of a batch is issued before its stores
-  {
-    constexpr int NL = B * (B / 4) / 256;  // float4 per thread
-    constexpr int BATCH = NL < 8 ? NL : 8;
-    const bool fast = vec && bw == B;
-    for (int b0 = 0; b0 < NL; b0 += BATCH) {
-      float4 v[BATCH];
+  // U's rows are staged chunk by chunk: rows [16 t, 16 t + 16) are loaded
+  // (coalesced) while chunk t - 1 is processed and written transposed, with
+  // the float4 slot of (c, k) swizzled by c so that the writes spread over the
+  // banks: Ut[c * UP + 4 * ((k / 4) ^ ((c / 4) & 7)) + k % 4] = U[s0 + k][s0 + c]
+  constexpr int RV = 16 * (B / 4);                 // float4 of one row chunk
+  constexpr int NV = (RV + 255) / 256;             // per thread
+  const bool fastU = vec && bw == B;
+  auto load_rows = [&](int t, float4 (&v)[NV]) {
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int e = tid + 256 * (b0 + i);
-        const int k = e % B, c4 = (e / B) * 4;
-        if (fast) {
-          v[i] = *reinterpret_cast<const float4*>(U + (s0 + k) * ldu + s0 + c4);
-        } else {
-          v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (k < bw) {
-            const float* src = U + (s0 + k) * ldu + s0 + c4;
-            if (c4 + 0 < bw) v[i].x = src[0];
-            if (c4 + 1 < bw) v[i].y = src[1];
-            if (c4 + 2 < bw) v[i].z = src[2];
-            if (c4 + 3 < bw) v[i].w = src[3];
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int e = tid + 256 * (b0 + i);
-        const int k = e % B, c4 = (e / B) * 4;
-        Ut[(c4 + 0) * UP + k] = v[i].x;
-        Ut[(c4 + 1) * UP + k] = v[i].y;
-        Ut[(c4 + 2) * UP + k] = v[i].z;
-        Ut[(c4 + 3) * UP + k] = v[i].w;
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i;
+      const int k = 16 * t + e / (B / 4), c4 = (e % (B / 4)) * 4;
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e >= RV) continue;
+      const float* src = U + (s0 + k) * ldu + s0 + c4;
+      if (fastU) {
+        v[i] = *reinterpret_cast<const float4*>(src);
+      } else if (k < bw) {
+        if (c4 + 0 < bw) v[i].x = src[0];
+        if (c4 + 1 < bw) v[i].y = src[1];
+        if (c4 + 2 < bw) v[i].z = src[2];
+        if (c4 + 3 < bw) v[i].w = src[3];
       }
     }
+  };
+  auto store_rows = [&](int t, const float4 (&v)[NV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i;
+      if (e >= RV) continue;
+      const int k = 16 * t + e / (B / 4), c4 = (e % (B / 4)) * 4;
+      const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int c = c4 + x;
+        Ut[c * UP + 4 * ((k >> 2) ^ ((c >> 2) & 7)) + (k & 3)] = vv[x];
+      }
+    }
+  };
+  float4 upre[NV];
+  load_rows(0, upre);
+  {
+    // Warm this XCD's L2 with U's block: work-groups are dealt round-robin to
+    // the 8 XCDs, and every group reads the whole block, so each takes its
+    // share of the rows of the block once here; the chunk loads then hit L2.
+    const int per_xcd = int((gridDim.x + 7) / 8);
+    const int share = (B + per_xcd - 1) / per_xcd;  // rows per work-group
+    const int r0 = int(blockIdx.x / 8) * share;
+    const int e = tid;  // one float4 per thread
+    const int k = r0 + e / (B / 4), c4 = (e % (B / 4)) * 4;
+    if (e < share * (B / 4) && k < bw && k < r0 + share) {
+      const float* src = U + (s0 + k) * ldu + s0 + c4;
+      const float v = *src;  // one float per 16 bytes touches the line
+      if (v != v && tid > 4096) Ds[0] = v;  // never taken: keeps the load
+    }
   }
+  store_rows(0, upre);
   if (rowloss) {
     for (int i = tid; i < B; i += 256) Ds[i] = i < bw ? Dg[s0 + i] : 0.f;
   }
@@ -249,29 +271,32 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
       wnext = (live && cn < bw) ? W[row * ldw + s0 + cn] : 0.f;
     }
     // the chunk's 16 coefficients U[16 tk + kk][c] of this lane's column
+    if (tk + 1 < NT) load_rows(tk + 1, upre);  // next chunk's rows, stored after this chunk
     float u16[16];
     {
-      const float4* up = reinterpret_cast<const float4*>(Ut + c * UP + 16 * tk);
+      const float4* up = reinterpret_cast<const float4*>(Ut + c * UP);
+      const int sw = (c >> 2) & 7;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float4 x = up[v];
+        const float4 x = up[(4 * tk + v) ^ sw];
         u16[4 * v + 0] = x.x;
         u16[4 * v + 1] = x.y;
         u16[4 * v + 2] = x.z;
         u16[4 * v + 3] = x.w;
       }
     }
-    const float a0 = acc;
     float e16[16];
-    float q = 0.f, err = 0.f, res = 0.f;
-    uint32_t code = 0u;
-    // One pass over the 16 columns of the chunk. EXACT = false rounds with
-    // p * (1/s); it reports whether an owner lane came within 1e-4 of a
-    // decision boundary, where p * (1/s) and the IEEE quotient p / s might
-    // differ, and then the chunk is redone with EXACT = true.
-    auto pass = [&](auto exact_tag) -> bool {
+    // One pass over the 16 columns of the chunk; returns this lane's
+    // accumulator as it stood at its own column (it does not change after: the
+    // remaining coefficients lie below the diagonal and are zero), so the
+    // owner's rounding is redone once afterwards with the same arithmetic.
+    // EXACT = false rounds with p * (1/s); when an owner lane lands within 1e-4
+    // of a decision boundary, where p * (1/s) and the IEEE quotient p / s might
+    // differ, the chunk is redone with EXACT = true. The error sent to the row
+    // is w - q with q = (k - c) * s, each rounded once (no contraction), the
+    // same values the outputs store.
+    auto pass = [&](auto exact_tag) -> float {
       constexpr bool EXACT = decltype(exact_tag)::value;
-      bool near = false;
       float a = acc;
       static_for<16>([&](auto KI) {
         constexpr int kk = decltype(KI)::value;
@@ -282,32 +307,31 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
         } else {
           y = fmaf(p, inv, half);
         }
-        const float kfl = floorf(y);
-        const bool mine = (j == kk);
-        if constexpr (!EXACT) {
-          const float fr = y - kfl;
-          near = near | (own & mine & ((fr < 1e-4f) | (fr > 0.9999f)));
-        }
-        const float kf = __builtin_amdgcn_fmed3f(kfl, 0.f, hi);
-        const float qv = (kf - cen) * s;
-        const float ev = w - qv;
+        const float kf = __builtin_amdgcn_fmed3f(floorf(y), 0.f, hi);
+        const float ev = __fsub_rn(w, __fmul_rn(kf - cen, s));
         const float eb = row_bcast<kk>(ev);
-        if (mine) {
-          q = qv;
-          err = ev;
-          res = p - qv;
-          code = uint32_t(kf);
-        }
         e16[kk] = eb;
         a = fmaf(eb, u16[kk], a);  // zero coefficient on and below the diagonal
       });
-      return near;
+      return a;
     };
-    const bool near = pass(std::false_type{});
-    if (__builtin_amdgcn_ballot_w64(near)) {
-      acc = a0;
-      pass(std::true_type{});
+    float af = pass(std::false_type{});
+    float p = w + af;
+    float y = fmaf(p, inv, half);
+    {
+      const float fr = y - floorf(y);
+      const bool near = own && ((fr < 1e-4f) | (fr > 0.9999f));
+      if (__builtin_amdgcn_ballot_w64(near)) {
+        af = pass(std::true_type{});
+        p = w + af;
+        y = p / s + half;
+      }
     }
+    const float kf = __builtin_amdgcn_fmed3f(floorf(y), 0.f, hi);
+    const float q = __fmul_rn(kf - cen, s);
+    const float err = __fsub_rn(w, q);
+    const float res = p - q;
+    const uint32_t code = uint32_t(kf);
     // outputs of this chunk: one column per lane
     if (own) {
       codes[row * ldcode + s0 + c] = uint8_t(code);
@@ -322,11 +346,13 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
 #pragma unroll
     for (int i = 0; i < NT - 1; ++i) {
       if (i < NT - 1 - tk) {
-        const float4* up = reinterpret_cast<const float4*>(Ut + (c + 16 * (i + 1)) * UP + 16 * tk);
+        const int cc = c + 16 * (i + 1);
+        const float4* up = reinterpret_cast<const float4*>(Ut + cc * UP);
+        const int sw = (cc >> 2) & 7;
         float t = ar[i];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float4 x = up[v];
+          const float4 x = up[(4 * tk + v) ^ sw];
           t = fmaf(e16[4 * v + 0], x.x, t);
           t = fmaf(e16[4 * v + 1], x.y, t);
           t = fmaf(e16[4 * v + 2], x.z, t);
@@ -339,6 +365,10 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
       acc = ar[0];
 #pragma unroll
       for (int i = 0; i + 1 < NT - 1; ++i) ar[i] = ar[i + 1];
+    }
+    if (tk + 1 < NT) {  // rows of the next chunk (other k than this chunk's reads)
+      store_rows(tk + 1, upre);
+      __syncthreads();
     }
   }
   if (rowloss) {
