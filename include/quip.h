@@ -262,11 +262,12 @@ quip_status quip_proxy_loss(const float* W, const float* What, int64_t m, int64_
 
 /*
  * Kernel timing (measurement support; not a step of the method). While
- * enabled, every kernel the library launches is bracketed by two HIP events
- * recorded on the caller's stream and filed under its kernel family (GEMMs by
+ * enabled, every kernel the library launches carries two HIP events that its
+ * own dispatch stamps with the kernel's start and end (hipExtLaunchKernel;
+ * no extra work on the stream), filed under its kernel family (GEMMs by
  * call site: "gemm:hessian", "gemm:ldl_inner", "gemm:ldl_outer",
  * "gemm:ldlq_inner", "gemm:ldlq_outer", "gemm:kron", "gemm:proxy_loss").
- * Process-wide, off by default; enabling adds two event records per launch.
+ * Process-wide, off by default.
  *   quip_timing_enable(on): 1 on, 0 off.
  *   quip_timing_reset(): waits for recorded events, then clears all sums.
  *   quip_timing_report(buf, len, needed): waits for recorded events, adds them

@@ -1,6 +1,7 @@
 // Internal helpers shared by the libquip translation units (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -46,18 +47,26 @@ quip_status launch_check(const char* what);
 
 // While timing is on (quip_timing_enable), every launch is bracketed by two
 // HIP events on its stream, filed under `name` (timing.cpp).
-// `flops` and `bytes` are the launch's algorithmic work (useful floating-point
-// operations, compulsory global-memory bytes), summed with the times.
+// The launch lambda receives a start / stop event pair (null when timing is
+// off) and launches with QUIP_KERNEL, which hands the pair to the dispatch
+// itself (hipExtLaunchKernelGGL): the events carry the kernel's own start and
+// end times, with no extra packets on the stream. `flops` and `bytes` are the
+// launch's algorithmic work (useful floating-point operations, compulsory
+// global-memory bytes), summed with the times.
 bool timing_on();
-int timing_begin(const char* name, hipStream_t s, double flops, double bytes);  // -1 when off
-void timing_end(int token, hipStream_t s);
+bool timing_begin(const char* name, double flops, double bytes, hipEvent_t* start,
+                  hipEvent_t* stop);
+
+#define QUIP_KERNEL(kernel, grid, block, shmem, stream, ...) \
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev_start_, ev_stop_, 0, __VA_ARGS__)
 
 template <typename F>
 quip_status timed_launch(const char* name, hipStream_t s, F&& launch, double flops = 0.0,
                          double bytes = 0.0) {
-  const int tok = timing_on() ? timing_begin(name, s, flops, bytes) : -1;
-  launch();
-  if (tok >= 0) timing_end(tok, s);
+  (void)s;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (timing_on() && !timing_begin(name, flops, bytes, &a, &b)) a = b = nullptr;
+  launch(a, b);
   return launch_check(name);
 }
 

@@ -205,7 +205,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // C_in for the beta term, read before the K loop so its latency overlaps it
+  const int64_t nk = (kend - kbeg + BK - 1) / BK;
+  if (nk > 0) gload(kbeg);
+  // C_in for the beta term, read after the first A/B tiles (loads retire in
+  // order) and before the K loop, so its latency overlaps the loop
   float* C = a.C + bz * a.strideC;
   const float* Cin = a.Cin ? a.Cin + bz * a.strideCin : C;
   const int64_t ldcin = a.Cin ? a.ldcin : a.ldc;
@@ -226,9 +229,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       }
   }
 
-  const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
-    gload(kbeg);
     sstore(0, kbeg);
     __syncthreads();
   }
@@ -424,8 +425,8 @@ quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
         GemmArgs f = a;
         f.tile0 = 0;
         f.kpieces = 1;
-        QUIP_TRY(timed_launch(a.tag, s, [&] {
-          hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(full, 1), dim3(256), 0, s, f,
+        QUIP_TRY(timed_launch(a.tag, s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+          QUIP_KERNEL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(full, 1), dim3(256), 0, s, f,
                              tiles_m, tiles_n, full, vecA, vecB);
         }, wf, wb));
         wf = wb = 0.0;
@@ -435,19 +436,19 @@ quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
       t.kpieces = pl.kp;
       t.kchunk = pl.kchunk;
       const int np = pl.R * pl.kp;
-      QUIP_TRY(timed_launch(a.tag, s, [&] {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(np, 1), dim3(256), 0, s, t,
+      QUIP_TRY(timed_launch(a.tag, s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(np, 1), dim3(256), 0, s, t,
                            tiles_m, tiles_n, np, vecA, vecB);
       }, wf, wb));
-      return timed_launch("gemm_tail_reduce", s, [&] {
-        hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(pl.R, BM * BN / 1024), dim3(256), 0, s,
+      return timed_launch("gemm_tail_reduce", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL((tail_reduce_kernel<BM, BN>), dim3(pl.R, BM * BN / 1024), dim3(256), 0, s,
                            t, tiles_m);
       });
     }
   }
   dim3 grid(total, a.batch);
-  return timed_launch(a.tag, s, [&] {
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, TA, TB, EPI>), grid, dim3(256), 0, s, a, tiles_m,
+  return timed_launch(a.tag, s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL((gemm_kernel<BM, BN, TA, TB, EPI>), grid, dim3(256), 0, s, a, tiles_m,
                        tiles_n, total, vecA, vecB);
   }, wf, wb);
 }

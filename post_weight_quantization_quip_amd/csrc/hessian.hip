@@ -70,14 +70,14 @@ quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx
 
 quip_status hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,
                              double* scratch, hipStream_t s) {
-  QUIP_TRY(timed_launch("trace_kernel", s, [&] {
-    hipLaunchKernelGGL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
+  QUIP_TRY(timed_launch("trace_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
   }));
   int64_t gx = cdiv(n, 256);
   if (gx > 16) gx = 16;
   dim3 grid(unsigned(gx), unsigned(n < 65535 ? n : 65535));
-  return timed_launch("finalize_kernel", s, [&] {
-    hipLaunchKernelGGL(finalize_kernel, grid, dim3(256), 0, s, H, n, ldh, scratch,
+  return timed_launch("finalize_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(finalize_kernel, grid, dim3(256), 0, s, H, n, ldh, scratch,
                        1.0 / double(N_total), double(alpha));
   });
 }

@@ -513,12 +513,12 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
       // work: the w x w factorization, then per row above a triangular solve
       // and the D^{-1} scaling; reads the block column, writes U, X and D
       const double wd = double(w), kd = double(k0);
-      QUIP_TRY(timed_launch("ldl_block_kernel", s, [&] {
+      QUIP_TRY(timed_launch("ldl_block_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
         if (g == 1)
-          hipLaunchKernelGGL((ldl_block_kernel<PR, 1>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
+          QUIP_KERNEL((ldl_block_kernel<PR, 1>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
                              k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
         else
-          hipLaunchKernelGGL((ldl_block_kernel<PR, 8>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
+          QUIP_KERNEL((ldl_block_kernel<PR, 8>), grid, dim3(4 * (PR + NB)), 0, s, src, lsrc,
                              k0, w, U, n, D, Xp + (k0 - o0), int64_t(NO), info);
       }, 2.0 / 3.0 * wd * wd * wd + kd * (wd * wd + wd),
          4.0 * ((kd + wd) * wd + 2.0 * kd * wd + wd * wd + wd * g)));

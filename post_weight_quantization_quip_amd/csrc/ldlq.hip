@@ -638,8 +638,8 @@ void host_e8_candidates(int ncand, float* out) {
 
 quip_status finish_loss(const double* rl, int64_t m, double* loss, hipStream_t s) {
   if (!loss) return QUIP_OK;
-  return timed_launch("sum_rows_kernel", s, [&] {
-    hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, s, rl, m, loss);
+  return timed_launch("sum_rows_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(sum_rows_kernel, dim3(1), dim3(256), 0, s, rl, m, loss);
   });
 }
 
@@ -658,12 +658,12 @@ quip_status grid_scales(const float* W, int64_t m, int64_t n, int64_t ldw, int L
   // work: every candidate step rounds every weight of the row once
   const double gfl = double(m) * double(n) * double(ncand) * 6.0;
   const double gby = 4.0 * double(m) * double(n) + 4.0 * double(m);
-  return timed_launch("grid_scale_kernel", s, [&] {
+  return timed_launch("grid_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (ncand <= 32)
-      hipLaunchKernelGGL((grid_scale_kernel<32>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
+      QUIP_KERNEL((grid_scale_kernel<32>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
                          ncand, factors_dev, scales, mse);
     else
-      hipLaunchKernelGGL((grid_scale_kernel<64>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
+      QUIP_KERNEL((grid_scale_kernel<64>), dim3(unsigned(m)), dim3(256), 0, s, W, m, n, ldw, L,
                          ncand, factors_dev, scales, mse);
   }, gfl, gby);
 }
@@ -673,16 +673,16 @@ quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, con
   QUIP_TRY(fill_f64(e.sse, 64, 0.0, s));
   const int64_t nvec = m * (n / 8);
   dim3 grid(unsigned(cdiv(nvec, 128)));
-  QUIP_TRY(timed_launch("e8_scale_kernel", s, [&] {
+  QUIP_TRY(timed_launch("e8_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (ncand <= 32)
-      hipLaunchKernelGGL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
                          ncand, e.sse);
     else
-      hipLaunchKernelGGL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
                          ncand, e.sse);
   }));
-  QUIP_TRY(timed_launch("e8_pick_scale_kernel", s, [&] {
-    hipLaunchKernelGGL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
+  QUIP_TRY(timed_launch("e8_pick_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
   }));
   if (sse_out) QUIP_HIP(hipMemcpyAsync(sse_out, e.sse, sizeof(double) * ncand, hipMemcpyDeviceToDevice, s));
   return QUIP_OK;
@@ -709,8 +709,8 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
   const double flops = md * (bd * (bd - 1.0) + 6.0 * bd);
   const double bytes = md * bd * (4.0 + (useF ? 4.0 : 0.0) + 1.0 + (What ? 4.0 : 0.0) + 4.0) +
                        4.0 * bd * bd + (rowloss ? 16.0 * md : 0.0);
-  return timed_launch("ldlq_sweep_kernel", s, [&] {
-    hipLaunchKernelGGL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s, W, ldw,
+  return timed_launch("ldlq_sweep_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s, W, ldw,
                        F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
                        D, rowloss, vec);
   }, flops, bytes);
@@ -783,12 +783,12 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_scales: workspace too small");
   host_e8_candidates(q.n_cand, hostf);
   QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
-  QUIP_TRY(timed_launch("rownorm_kernel", s, [&] {
-    hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
+  QUIP_TRY(timed_launch("rownorm_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
                        true);
   }));
-  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&] {
-    hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
   }));
   return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
 }
@@ -871,12 +871,12 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   e.Eb = Eb;
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldlq: workspace too small");
   const bool compute = q.scale_mode == QUIP_SCALE_COMPUTE;
-  QUIP_TRY(timed_launch("rownorm_kernel", s, [&] {
-    hipLaunchKernelGGL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
+  QUIP_TRY(timed_launch("rownorm_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
                        compute);
   }));
-  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&] {
-    hipLaunchKernelGGL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
   }));
   if (compute) {
     host_e8_candidates(q.n_cand, hostf);
@@ -885,8 +885,8 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   }
   // the global scale stays on the device (scales[0]); the step kernels read it there
   const float* sglob = scales;
-  QUIP_TRY(timed_launch("fill_u64_kernel", s, [&] {
-    hipLaunchKernelGGL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
+  QUIP_TRY(timed_launch("fill_u64_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
   }));
   uint16_t* cd = static_cast<uint16_t*>(codes);
   const int chunk = 4096;
@@ -894,12 +894,12 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
     const int64_t bo = (n - j0 < B) ? n - j0 : B;
     for (int64_t c0 = j0; c0 < j0 + bo; c0 += 8) {
       dim3 grid(unsigned(cdiv(m, 32)), unsigned(65536 / chunk));
-      QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&] {
-        hipLaunchKernelGGL(e8_argmin_kernel, grid, dim3(256), 0, s, e.Wn, n, F, j0 > 0, Eb, B,
+      QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, e.Wn, n, F, j0 > 0, Eb, B,
                            int(c0 - j0), U, c0, j0, codebook, e.c2, sglob, m, chunk, e.keys);
       }));
-      QUIP_TRY(timed_launch("e8_finish_kernel", s, [&] {
-        hipLaunchKernelGGL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
+      QUIP_TRY(timed_launch("e8_finish_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
                            codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
                            int(c0 - j0), F, j0 > 0, U, j0, D, rl);
       }));

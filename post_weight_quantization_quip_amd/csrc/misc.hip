@@ -54,8 +54,8 @@ quip_status fill_f32(float* p, int64_t count, float v, hipStream_t s) {
   if (count <= 0) return QUIP_OK;
   int64_t blocks = cdiv(count, 256);
   if (blocks > 8192) blocks = 8192;
-  return timed_launch("fill_f32", s, [&] {
-    hipLaunchKernelGGL(fill_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
+  return timed_launch("fill_f32", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(fill_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
   });
 }
 
@@ -63,24 +63,24 @@ quip_status fill_f64(double* p, int64_t count, double v, hipStream_t s) {
   if (count <= 0) return QUIP_OK;
   int64_t blocks = cdiv(count, 256);
   if (blocks > 8192) blocks = 8192;
-  return timed_launch("fill_f64", s, [&] {
-    hipLaunchKernelGGL(fill_f64_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
+  return timed_launch("fill_f64", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(fill_f64_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, v);
   });
 }
 
 quip_status fill_matrix(float* p, int64_t rows, int64_t cols, int64_t ld, float v, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return QUIP_OK;
   if (ld == cols) return fill_f32(p, rows * cols, v, s);
-  return timed_launch("fill_matrix", s, [&] {
-    hipLaunchKernelGGL(fill_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, p, rows, cols, ld, v);
+  return timed_launch("fill_matrix", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(fill_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, p, rows, cols, ld, v);
   });
 }
 
 quip_status sub_matrix(const float* a, const float* b, float* out, int64_t rows, int64_t cols,
                        int64_t lda, int64_t ldb, int64_t ldo, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return QUIP_OK;
-  return timed_launch("sub_matrix", s, [&] {
-    hipLaunchKernelGGL(sub_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, a, b, out, rows,
+  return timed_launch("sub_matrix", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(sub_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, a, b, out, rows,
                        cols, lda, ldb, ldo);
   });
 }
@@ -88,8 +88,8 @@ quip_status sub_matrix(const float* a, const float* b, float* out, int64_t rows,
 quip_status copy_matrix(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows,
                         int64_t cols, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return QUIP_OK;
-  return timed_launch("copy_matrix", s, [&] {
-    hipLaunchKernelGGL(copy_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, src, lds, dst, ldd,
+  return timed_launch("copy_matrix", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(copy_matrix_kernel, grid2d(rows, cols), dim3(1024), 0, s, src, lds, dst, ldd,
                        rows, cols);
   });
 }

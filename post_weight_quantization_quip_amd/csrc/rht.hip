@@ -297,8 +297,8 @@ quip_status rows_t(const float* A, float* out, int64_t rows, int64_t ld, const f
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_rows_kernel<LOGN, LE>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
   dim3 grid(unsigned(cdiv(rows, RW)));
-  return timed_launch("rht_rows_kernel", st, [&] {
-    hipLaunchKernelGGL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
+  return timed_launch("rht_rows_kernel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
                        s, scale, inverse, vec);
   }, double(rows) * N * (LOGN + 2), 8.0 * double(rows) * N);
 }
@@ -307,8 +307,8 @@ template <int N>
 quip_status rows_small_t(const float* A, float* out, int64_t rows, int64_t ld, const float* s,
                          bool inverse, hipStream_t st) {
   const float scale = 1.0f / sqrtf(float(N));
-  return timed_launch("rht_rows_small_kernel", st, [&] {
-    hipLaunchKernelGGL((rht_rows_small_kernel<N>), dim3(unsigned(cdiv(rows, 256))), dim3(256), 0, st,
+  return timed_launch("rht_rows_small_kernel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL((rht_rows_small_kernel<N>), dim3(unsigned(cdiv(rows, 256))), dim3(256), 0, st,
                        A, out, rows, ld, s, scale, inverse);
   });
 }
@@ -317,8 +317,8 @@ template <int D>
 quip_status cols_small_t(const float* A, float* out, int64_t cols, int64_t ld, const float* s,
                          bool inverse, hipStream_t st) {
   const float scale = 1.0f / sqrtf(float(D));
-  return timed_launch("rht_cols_small_kernel", st, [&] {
-    hipLaunchKernelGGL((rht_cols_small_kernel<D>), dim3(unsigned(cdiv(cols, 256))), dim3(256), 0, st,
+  return timed_launch("rht_cols_small_kernel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL((rht_cols_small_kernel<D>), dim3(unsigned(cdiv(cols, 256))), dim3(256), 0, st,
                        A, out, cols, ld, s, scale, inverse);
   });
 }
@@ -328,11 +328,11 @@ quip_status cols_pass(int kr, const float* A, float* out, int64_t d, int64_t col
   dim3 grid(unsigned(d >> kr), unsigned(cdiv(cols, 64)));
   if (kr < 4 || kr > 7) return fail(QUIP_ERR_UNSUPPORTED, "rht_cols: pass size");
   // one pass reads and writes the whole matrix once (kr butterfly levels)
-  return timed_launch("rht_cols_pass", st, [&] {
+  return timed_launch("rht_cols_pass", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     switch (kr) {
 #define CASE(K)                                                                                \
   case K:                                                                                      \
-    hipLaunchKernelGGL((rht_cols_pass<K>), grid, dim3(256), 0, st, A, out, cols, ld, lo, s,   \
+    QUIP_KERNEL((rht_cols_pass<K>), grid, dim3(256), 0, st, A, out, cols, ld, lo, s,   \
                        scale, mode);                                                           \
     break;
       CASE(4) CASE(5) CASE(6) CASE(7)

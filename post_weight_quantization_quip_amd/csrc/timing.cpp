@@ -1,6 +1,7 @@
 // Per-kernel launch timing with HIP events, off by default. While on, every
-// launch made through timed_launch records an event pair on its stream; a
-// report waits for the recorded pairs and sums their durations per name.
+// launch made through timed_launch gets an event pair that its dispatch
+// stamps with the kernel's start and end; a report waits for the pairs and
+// sums their durations per name.
 #include <atomic>
 #include <cstdio>
 #include <map>
@@ -74,7 +75,8 @@ quip_status drain(Registry& r) {
 
 bool timing_on() { return g_on.load(std::memory_order_relaxed); }
 
-int timing_begin(const char* name, hipStream_t s, double flops, double bytes) {
+bool timing_begin(const char* name, double flops, double bytes, hipEvent_t* start,
+                  hipEvent_t* stop) {
   Registry& r = reg();
   std::lock_guard<std::mutex> lk(r.mu);
   Pending p;
@@ -83,19 +85,15 @@ int timing_begin(const char* name, hipStream_t s, double flops, double bytes) {
   p.bytes = bytes;
   p.a = take_event(r);
   p.b = take_event(r);
-  if (!p.a || !p.b || hipEventRecord(p.a, s) != hipSuccess) {
+  if (!p.a || !p.b) {
     if (p.a) r.pool.push_back(p.a);
     if (p.b) r.pool.push_back(p.b);
-    return -1;
+    return false;
   }
   r.pending.push_back(p);
-  return int(r.pending.size()) - 1;
-}
-
-void timing_end(int token, hipStream_t s) {
-  Registry& r = reg();
-  std::lock_guard<std::mutex> lk(r.mu);
-  if (token >= 0 && token < int(r.pending.size())) (void)hipEventRecord(r.pending[token].b, s);
+  *start = p.a;
+  *stop = p.b;
+  return true;
 }
 
 void timing_enable(bool on) { g_on.store(on); }
