@@ -3,16 +3,18 @@
 
 A step is one whole pass over one synthetic layer with everything resident in
 HBM when the timed region starts: proxy Hessian + damping, two-sided random
-Hadamard transform of H and of W, LDL, per-row scale search, LDLQ, inverse
-transforms and the proxy loss. The workload is the 4096 x 4096 attention
+Hadamard transform of H and of W, LDL, per-row scale search, LDLQ with the
+proxy loss, inverse transforms. The workload is the 4096 x 4096 attention
 projection layer (2-bit grid, RHT on both sides, lazy block 128, 4096
 calibration rows); the metric is quantized weights per second.
 
-Also reported: per-phase times (HIP events on the pass's stream), the RHT
-bandwidth per one-sided pass, the roofline of the dominant kernel (the fp32
-matrix-core Hessian contraction, one launch per step, bracketed by its own
-events), HBM traffic from rocprofv3 counters when a counter summary is
-present under profiles/, and the CPU oracle timed on a bounded sample.
+Also reported: per-phase times (HIP events on the pass's stream), per-kernel
+family times and algorithmic work from the library's own timing (the dispatch
+of every kernel stamps an event pair; the same figures rocprofv3 reports), the
+roofline of the family with the most time per step, HBM traffic from the
+committed rocprofv3 counter summary of that family (when its source is
+unchanged), the RHT bandwidth per one-sided pass, and the CPU oracle timed on
+a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
