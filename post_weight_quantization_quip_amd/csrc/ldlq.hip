@@ -156,9 +156,10 @@ __device__ __forceinline__ float row_bcast(float v) {
 // columns already rounded are left alone). After a chunk, each lane adds the
 // chunk's rank-16 feedback to one accumulator per later chunk; those live in
 // registers, shifted down by one chunk per step so that every register index
-// is static. U's block is staged transposed in LDS (row c = column c of U),
-// one 16-row chunk ahead of its use, so that a lane's 16 coefficients of a
-// chunk are four float4 reads.
+// is static. U's rows are staged transposed in LDS (row c = column c of U) in
+// a two-chunk ring, one 16-row chunk ahead of their use, so that a lane's 16
+// coefficients of a chunk are four float4 reads and the LDS footprint does not
+// grow with B.
 template <int B>
 __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
@@ -167,9 +168,9 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     int64_t ldwh, float* __restrict__ Eb, int64_t lde, const float* __restrict__ Dg,
     double* __restrict__ rowloss, bool vec) {
   constexpr int NT = B / 16;  // 16-column chunks
-  constexpr int UP = B + 4;   // padded row of the transposed U block
+  constexpr int UP = 36;      // two 16-row chunks of U (a ring) and a pad, per column
   extern __shared__ __align__(16) float sm[];
-  float* Ut = sm;            // [B][UP]: Ut[c * UP + k] = U[s0 + k][s0 + c]
+  float* Ut = sm;            // [B][UP]: column c of U's rows of the current and next chunk
   float* Ds = sm + B * UP;   // [B]: D of the block (proxy loss)
 
   const int tid = threadIdx.x;
@@ -179,9 +180,10 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
   const bool live = row < m;
 
   // U's rows are staged chunk by chunk: rows [16 t, 16 t + 16) are loaded
-  // (coalesced) while chunk t - 1 is processed and written transposed, with
-  // the float4 slot of (c, k) swizzled by c so that the writes spread over the
-  // banks: Ut[c * UP + 4 * ((k / 4) ^ ((c / 4) & 7)) + k % 4] = U[s0 + k][s0 + c]
+  // (coalesced) while chunk t - 1 is processed and written transposed into a
+  // two-chunk ring (k mod 32), with the float4 slot swizzled by c so that the
+  // writes spread over the banks:
+  //   Ut[c * UP + 4 * (((k / 4) & 7) ^ ((c / 4) & 7)) + k % 4] = U[s0 + k][s0 + c]
   constexpr int RV = 16 * (B / 4);                 // float4 of one row chunk
   constexpr int NV = (RV + 255) / 256;             // per thread
   const bool fastU = vec && bw == B;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int c = c4 + x;
-        Ut[c * UP + 4 * ((k >> 2) ^ ((c >> 2) & 7)) + (k & 3)] = vv[x];
+        Ut[c * UP + 4 * (((k >> 2) & 7) ^ ((c >> 2) & 7)) + (k & 3)] = vv[x];
       }
     }
   };
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
       const int sw = (c >> 2) & 7;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float4 x = up[(4 * tk + v) ^ sw];
+        const float4 x = up[((4 * tk + v) & 7) ^ sw];
         u16[4 * v + 0] = x.x;
         u16[4 * v + 1] = x.y;
         u16[4 * v + 2] = x.z;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
         float t = ar[i];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float4 x = up[(4 * tk + v) ^ sw];
+          const float4 x = up[((4 * tk + v) & 7) ^ sw];
           t = fmaf(e16[4 * v + 0], x.x, t);
           t = fmaf(e16[4 * v + 1], x.y, t);
           t = fmaf(e16[4 * v + 2], x.z, t);
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
 #pragma unroll
       for (int i = 0; i + 1 < NT - 1; ++i) ar[i] = ar[i + 1];
     }
-    if (tk + 1 < NT) {  // rows of the next chunk (other k than this chunk's reads)
+    if (tk + 1 < NT) {  // rows of the next chunk, into the other half of the ring
       store_rows(tk + 1, upre);
       __syncthreads();
     }
@@ -693,7 +695,7 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
                     const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                     int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
                     int64_t lde, const float* D, double* rowloss, hipStream_t s) {
-  const size_t shmem = (size_t(B) * (B + 4) + B) * sizeof(float);
+  const size_t shmem = (size_t(B) * 36 + B) * sizeof(float);
   if (shmem > 65536)
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
@@ -724,6 +726,7 @@ quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ld
     case 32: return sweep_t<32>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
     case 64: return sweep_t<64>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
     case 128: return sweep_t<128>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
+    case 256: return sweep_t<256>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
   }
   return fail(QUIP_ERR_UNSUPPORTED, "ldlq: inner block size");
 }
@@ -843,7 +846,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
       QUIP_TRY(grid_scales(W, m, n, ldw, L, q.n_cand, fac, scales, nullptr, s));
     }
-    const int bi = B >= 128 ? 128 : (B >= 64 ? 64 : 32);
+    const int bi = B >= 256 ? 256 : (B >= 128 ? 128 : (B >= 64 ? 64 : 32));
     uint8_t* cd = static_cast<uint8_t*>(codes);
     for (int64_t j0 = 0; j0 < n; j0 += Bo) {
       const int64_t bo = (n - j0 < Bo) ? n - j0 : Bo;
