@@ -236,18 +236,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   int buf = 0;
   for (int64_t kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
+    // operands of step kk + 1 are read while step kk's MFMAs run
+    float av[2][WBM], bv[2][WBN];
+#pragma unroll
+    for (int i = 0; i < WBM; ++i) av[0][i] = As[buf][krow][wm * (BM / 2) + i * 32 + kcol];
+#pragma unroll
+    for (int j = 0; j < WBN; ++j) bv[0][j] = Bs[buf][krow][wn * (BN / 2) + j * 32 + kcol];
+    // one ds_read2 serves two operands 32 floats apart
+    constexpr int kReads = (WBM + 1) / 2 + (WBN + 1) / 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 2; ++kk) {
-      float av[WBM], bv[WBN];
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 2) {
 #pragma unroll
-      for (int i = 0; i < WBM; ++i) av[i] = As[buf][2 * kk + krow][wm * (BM / 2) + i * 32 + kcol];
+        for (int i = 0; i < WBM; ++i)
+          av[cur ^ 1][i] = As[buf][2 * kk + 2 + krow][wm * (BM / 2) + i * 32 + kcol];
 #pragma unroll
-      for (int j = 0; j < WBN; ++j) bv[j] = Bs[buf][2 * kk + krow][wn * (BN / 2) + j * 32 + kcol];
+        for (int j = 0; j < WBN; ++j)
+          bv[cur ^ 1][j] = Bs[buf][2 * kk + 2 + krow][wn * (BN / 2) + j * 32 + kcol];
+      }
 #pragma unroll
       for (int i = 0; i < WBM; ++i)
 #pragma unroll
         for (int j = 0; j < WBN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+      // keep the order: the next step's LDS reads, then this step's MFMAs
+      if (kk + 1 < BK / 2) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WBM * WBN, 0);
     }
     if (kt + 1 < nk) sstore(buf ^ 1, kbeg + (kt + 1) * BK);
     __syncthreads();
