@@ -11,7 +11,15 @@
 // computed with v_mfma_f32_32x32x2f32 (wave64: A operand lane = i + 32k,
 // B operand lane = j + 32k, D element (i, j) in lane j + 32*((i/4)%2),
 // register (i%4) + 4*(i/8)). K advances 32 at a time through double-buffered
-// LDS tiles stored K-major, so every operand read is 32 consecutive floats.
+// LDS tiles kept in the operand's own memory order, so every store is one
+// float4: a k-contiguous operand (A not transposed, B transposed) as rows of
+// 32 k values padded to 36 floats, an m/n-contiguous one as 32 rows of BM
+// (BN) floats padded by 8. Inside a 32-wide K step, sub-step kk (0..15) of
+// lane half h sums k = 8 (kk / 4) + 4 h + kk % 4, so a k-contiguous operand
+// gives four sub-steps per 128-bit LDS read, and the two lane halves of an
+// m/n-contiguous read are 4 rows apart (a shift of 32 banks with these pads).
+// The reads of the next four sub-steps are issued before the current four
+// sub-steps' MFMAs.
 // The beta term's C tile is read into registers before the K loop.
 // Work-group ids are remapped so that neighbouring tiles share an XCD's L2.
 #include "common.h"
@@ -22,7 +30,8 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 32;
-constexpr int PAD = 4;
+constexpr int KC_LD = BK + 4;  // row length of a k-contiguous LDS tile
+constexpr int MC_PAD = 8;      // row padding of an m/n-contiguous LDS tile
 
 __device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t col, int64_t ld,
                                         int64_t rows, int64_t cols, bool vec) {
@@ -43,8 +52,11 @@ __device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t 
 template <int BM, int BN, bool TA, bool TB, int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n,
                                                       int total, bool vecA, bool vecB) {
-  __shared__ __align__(16) float As[2][BK][BM + PAD];
-  __shared__ __align__(16) float Bs[2][BK][BN + PAD];
+  constexpr bool KCA = !TA, KCB = TB;  // operand tiles stored k-contiguous
+  constexpr int LDA_S = KCA ? KC_LD : BM + MC_PAD;
+  constexpr int LDB_S = KCB ? KC_LD : BN + MC_PAD;
+  __shared__ __align__(16) float As[2][KCA ? BM * KC_LD : BK * (BM + MC_PAD)];
+  __shared__ __align__(16) float Bs[2][KCB ? BN * KC_LD : BK * (BN + MC_PAD)];
 
   constexpr int WBM = BM / 64;  // 32x32 blocks per wave along M
   constexpr int WBN = BN / 64;
@@ -163,13 +175,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       int idx = tid + 256 * i;
       if (TA) {
         int k = idx / (BM / 4), m4 = (idx % (BM / 4)) * 4;
-        *reinterpret_cast<float4*>(&As[buf][k][m4]) = ra[i];
+        *reinterpret_cast<float4*>(&As[buf][k * LDA_S + m4]) = ra[i];
       } else {
         int m = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
-        As[buf][k4 + 0][m] = ra[i].x;
-        As[buf][k4 + 1][m] = ra[i].y;
-        As[buf][k4 + 2][m] = ra[i].z;
-        As[buf][k4 + 3][m] = ra[i].w;
+        *reinterpret_cast<float4*>(&As[buf][m * LDA_S + k4]) = ra[i];
       }
     }
 #pragma unroll
@@ -186,13 +195,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
           v.z = kd > 2 ? 0.f : (kd == 2 ? v.z : 2.f * v.z);
           v.w = kd > 3 ? 0.f : (kd == 3 ? v.w : 2.f * v.w);
         }
-        *reinterpret_cast<float4*>(&Bs[buf][k][n4]) = v;
+        *reinterpret_cast<float4*>(&Bs[buf][k * LDB_S + n4]) = v;
       } else {
         int n = idx / (BK / 4), k4 = (idx % (BK / 4)) * 4;
-        Bs[buf][k4 + 0][n] = rb[i].x;
-        Bs[buf][k4 + 1][n] = rb[i].y;
-        Bs[buf][k4 + 2][n] = rb[i].z;
-        Bs[buf][k4 + 3][n] = rb[i].w;
+        *reinterpret_cast<float4*>(&Bs[buf][n * LDB_S + k4]) = rb[i];
       }
     }
   };
@@ -229,45 +235,92 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
       }
   }
 
-  if (nk > 0) {
-    sstore(0, kbeg);
-    __syncthreads();
-  }
-  int buf = 0;
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
-    // operands of step kk + 1 are read while step kk's MFMAs run
-    float av[2][WBM], bv[2][WBN];
+  // sub-steps 4q .. 4q+3 of LDS buffer bf: aq[s][i] / bq[s][j] are the
+  // operands of sub-step 4q + s
+  auto read_quad = [&](int bf, int q, float (&aq)[4][WBM], float (&bq)[4][WBN]) {
+    const int kq = 8 * q + 4 * krow;
 #pragma unroll
-    for (int i = 0; i < WBM; ++i) av[0][i] = As[buf][krow][wm * (BM / 2) + i * 32 + kcol];
+    for (int i = 0; i < WBM; ++i) {
+      const int m = wm * (BM / 2) + i * 32 + kcol;
+      if (KCA) {
+        const float4 v = *reinterpret_cast<const float4*>(&As[bf][m * LDA_S + kq]);
+        aq[0][i] = v.x;
+        aq[1][i] = v.y;
+        aq[2][i] = v.z;
+        aq[3][i] = v.w;
+      } else {
 #pragma unroll
-    for (int j = 0; j < WBN; ++j) bv[0][j] = Bs[buf][krow][wn * (BN / 2) + j * 32 + kcol];
-    // one ds_read2 serves two operands 32 floats apart
-    constexpr int kReads = (WBM + 1) / 2 + (WBN + 1) / 2;
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 2; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 2) {
-#pragma unroll
-        for (int i = 0; i < WBM; ++i)
-          av[cur ^ 1][i] = As[buf][2 * kk + 2 + krow][wm * (BM / 2) + i * 32 + kcol];
-#pragma unroll
-        for (int j = 0; j < WBN; ++j)
-          bv[cur ^ 1][j] = Bs[buf][2 * kk + 2 + krow][wn * (BN / 2) + j * 32 + kcol];
+        for (int st = 0; st < 4; ++st) aq[st][i] = As[bf][(kq + st) * LDA_S + m];
       }
+    }
+#pragma unroll
+    for (int j = 0; j < WBN; ++j) {
+      const int n = wn * (BN / 2) + j * 32 + kcol;
+      if (KCB) {
+        const float4 v = *reinterpret_cast<const float4*>(&Bs[bf][n * LDB_S + kq]);
+        bq[0][j] = v.x;
+        bq[1][j] = v.y;
+        bq[2][j] = v.z;
+        bq[3][j] = v.w;
+      } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bq[st][j] = Bs[bf][(kq + st) * LDB_S + n];
+      }
+    }
+  };
+  // MFMAs of sub-steps s0 .. s1-1 of a quad
+  auto mfma_quad = [&](const float (&aq)[4][WBM], const float (&bq)[4][WBN], int s0, int s1) {
+#pragma unroll
+    for (int st = s0; st < s1; ++st)
 #pragma unroll
       for (int i = 0; i < WBM; ++i)
 #pragma unroll
         for (int j = 0; j < WBN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
-      // keep the order: the next step's LDS reads, then this step's MFMAs
-      if (kk + 1 < BK / 2) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, WBM * WBN, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1, kbeg + (kt + 1) * BK);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(aq[st][i], bq[st][j], acc[i][j], 0, 0, 0);
+  };
+  // LDS read instructions per quad (pairs 32 floats apart share a ds_read2)
+  constexpr int kReads = (KCA ? WBM : 4 * ((WBM + 1) / 2)) + (KCB ? WBN : 4 * ((WBN + 1) / 2));
+  constexpr int kQuads = BK / 8;
+  static_assert(kQuads % 2 == 0, "quads alternate between the two operand register sets");
+
+  // Software pipeline: the reads of quad q + 1 are issued before the MFMAs of
+  // quad q; at a step boundary half of the last quad's MFMAs go before the
+  // LDS stores and the barrier, the other half after the next step's first
+  // reads, so that they cover the read latency.
+  float aq[2][4][WBM], bq[2][4][WBN];
+  int buf = 0;
+  if (nk > 0) {
+    sstore(0, kbeg);
     __syncthreads();
+    read_quad(0, 0, aq[0], bq[0]);
+  }
+  // quads 0 .. kQuads-2 of the current step, each after the next one's reads
+  auto step_quads = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+    for (int q = 0; q + 1 < kQuads; ++q) {
+      const int cur = q & 1;
+      read_quad(buf, q + 1, aq[cur ^ 1], bq[cur ^ 1]);
+      mfma_quad(aq[cur], bq[cur], 0, 4);
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * WBM * WBN, 0);
+    }
+  };
+  constexpr int last = (kQuads - 1) & 1;
+  // every step but the last (no branch inside, so the accumulators stay in place)
+  for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+    gload(kbeg + (kt + 1) * BK);
+    step_quads();
+    mfma_quad(aq[last], bq[last], 0, 2);
+    sstore(buf ^ 1, kbeg + (kt + 1) * BK);
+    __syncthreads();
+    read_quad(buf ^ 1, 0, aq[last ^ 1], bq[last ^ 1]);
+    mfma_quad(aq[last], bq[last], 2, 4);
     buf ^= 1;
+  }
+  if (nk > 0) {
+    step_quads();
+    mfma_quad(aq[last], bq[last], 0, 4);
   }
 
   // ---- epilogue
