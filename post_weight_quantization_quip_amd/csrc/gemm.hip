@@ -213,15 +213,29 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
 
   const int64_t nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) gload(kbeg);
-  // C_in for the beta term, read after the first A/B tiles (loads retire in
-  // order) and before the K loop, so its latency overlaps the loop
+  // C_in for the beta term: read at the start of the last K step, when no
+  // tile loads are in flight (their registers are free) and the step's MFMAs
+  // cover the latency
   float* C = a.C + bz * a.strideC;
   const float* Cin = a.Cin ? a.Cin + bz * a.strideCin : C;
   const int64_t ldcin = a.Cin ? a.ldcin : a.ldc;
   const int krow = lane >> 5, kcol = lane & 31;
   f32x16 cpre[WBM][WBN];
   const bool useC = (EPI == EPI_STORE || EPI == EPI_SPLIT) && a.beta != 0.f;
-  if (useC) {
+  auto load_c = [&]() {
+    if (!useC) return;
+    if (m0 + BM <= a.M && n0 + BN <= a.N) {  // interior tile: no per-element checks
+#pragma unroll
+      for (int i = 0; i < WBM; ++i)
+#pragma unroll
+        for (int j = 0; j < WBN; ++j) {
+          const float* cp = Cin + (m0 + wm * (BM / 2) + i * 32 + 4 * krow) * ldcin + n0 +
+                            wn * (BN / 2) + j * 32 + kcol;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cpre[i][j][r] = cp[(8 * (r / 4) + (r % 4)) * ldcin];
+        }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < WBM; ++i)
 #pragma unroll
@@ -233,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
           cpre[i][j][r] = (row < a.M && col < a.N) ? Cin[row * ldcin + col] : 0.f;
         }
       }
-  }
+  };
 
   // sub-steps 4q .. 4q+3 of LDS buffer bf: aq[s][i] / bq[s][j] are the
   // operands of sub-step 4q + s
@@ -318,6 +332,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
     mfma_quad(aq[last], bq[last], 2, 4);
     buf ^= 1;
   }
+  load_c();
   if (nk > 0) {
     step_quads();
     mfma_quad(aq[last], bq[last], 0, 4);
