@@ -85,7 +85,12 @@ __global__ __launch_bounds__(256) void grid_scale_kernel(const float* __restrict
       for (int c = tid; c < ncand; c += 256) mse_out[row * ncand + c] = 0.f;
     return;
   }
-  const float cen = (L - 1) * 0.5f, half = L * 0.5f, hi = float(L - 1);
+  // Error in units of the candidate step: t = x / s + (L-1)/2 (one fma),
+  // code k = clamp(round(t), 0, L-1), e / s = t - k (exact for in-range codes,
+  // Sterbenz); the sum over the row is scaled by s^2 once at the end. Round
+  // half to even differs from floor(t + 1/2) only at exact ties, where both
+  // codes leave |e / s| = 1/2.
+  const float cen = (L - 1) * 0.5f, hi = float(L - 1);
   const float smax = gmax / cen;
   float sc[NC], inv[NC], acc[NC];
 #pragma unroll
@@ -98,12 +103,14 @@ __global__ __launch_bounds__(256) void grid_scale_kernel(const float* __restrict
     const float x = w[j];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      float k = floorf(x * inv[c] + half);
-      k = fminf(fmaxf(k, 0.f), hi);
-      float e = x - (k - cen) * sc[c];
+      const float t = fmaf(x, inv[c], cen);
+      const float k = __builtin_amdgcn_fmed3f(rintf(t), 0.f, hi);
+      const float e = t - k;
       acc[c] = fmaf(e, e, acc[c]);
     }
   }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] *= sc[c] * sc[c];
   __syncthreads();
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
