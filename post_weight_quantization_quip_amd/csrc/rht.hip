@@ -7,16 +7,24 @@
 // butterfly round runs on what each thread loaded (index bits {0,1} and the
 // top bits, so that every load is a lane-contiguous float4); the remaining
 // index bits are covered by rounds of E-point butterflies in registers, with an
-// LDS transpose between rounds (double-buffered, one barrier per round, XOR
-// swizzle on bits 2..4 so the strided round patterns hit distinct banks). A
-// last transpose brings the data back to the float4 layout for the store.
+// LDS transpose between rounds (one buffer per row, so that more work-groups
+// fit on a CU; XOR swizzle on bits 2..4 so the strided round patterns hit
+// distinct banks). A last transpose brings the data back to the float4 layout
+// for the store. As many work-groups as fit at once, each looping over rows
+// with the next row's loads issued before the current row's transform.
 //
-// LEFT side (along a column, strided by the row pitch): rht_cols_pass. The
-// d-point transform is split H_d = H_{2^k1} (x) H_{2^k2} (x) ... into passes
-// that each transform 2^KR rows spaced 2^lo apart, for 64 consecutive columns
-// per work-group (lanes run along the columns, so every access is a 256-byte
-// row segment). Inside a pass: butterflies on the rows a thread holds, one LDS
-// transpose, butterflies on the rest.
+// LEFT side (along a column, strided by the row pitch). For d = 4096 and
+// float4-aligned rows, one pass over memory: rht_cols_panel holds all d rows
+// of 8 columns in LDS (128 KB + padding), does the top four index bits in
+// registers right after the load, the middle four through one LDS round
+// trip, the low four in registers right before the store; column blocks are
+// dealt out so that the four work-groups sharing a 128-byte line run on one
+// XCD. Otherwise rht_cols_pass: the d-point transform is split
+// H_d = H_{2^k1} (x) H_{2^k2} (x) ... into passes that each transform 2^KR
+// rows spaced 2^lo apart, for 64 consecutive columns per work-group (lanes run
+// along the columns, so every access is a 256-byte row segment). Inside a
+// pass: butterflies on the rows a thread holds, one LDS transpose, butterflies
+// on the rest.
 #include "common.h"
 
 namespace quip {
@@ -42,14 +50,17 @@ __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* ou
   constexpr int REM = MID % LE;
   constexpr int NR = NFULL + (REM ? 1 : 0);
 
-  extern __shared__ __align__(16) float lds[];  // 2 * RW * N floats
+  extern __shared__ __align__(16) float lds[];  // RW * N floats
 
   const int tid = threadIdx.x;
   const int rw = tid / T, p = tid % T;
-  const int64_t row = int64_t(blockIdx.x) * RW + rw;
-  const bool live = row < rows;
+  // rows of this work-group: (blockIdx.x + k gridDim.x) RW + rw, k = 0, 1, ...;
+  // the next row's loads are issued before the current row's transform
+  int64_t row = int64_t(blockIdx.x) * RW + rw;
+  int64_t wbase = int64_t(blockIdx.x) * RW;  // uniform over the work-group
+  const int64_t wstep = int64_t(gridDim.x) * RW;
 
-  float x[E];
+  float x[E], xn[E];
 
   // round-0 layout: i = (r & 3) | (p << 2) | ((r >> 2) << MID_HI)
   auto idx0 = [&](int r) { return (r & 3) | (p << 2) | ((r >> 2) << MID_HI); };
@@ -57,73 +68,48 @@ __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* ou
     return (p & ((1 << a) - 1)) | (r << a) | ((p >> a) << (a + LE));
   };
 
-  const float* src = A + row * ld;
-#pragma unroll
-  for (int c = 0; c < E / 4; ++c) {
-    int i = idx0(4 * c);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (live) {
-      if (vec) {
-        v = *reinterpret_cast<const float4*>(src + i);
-      } else {
-        v.x = src[i];
-        v.y = src[i + 1];
-        v.z = src[i + 2];
-        v.w = src[i + 3];
-      }
-    }
-    x[4 * c + 0] = v.x;
-    x[4 * c + 1] = v.y;
-    x[4 * c + 2] = v.z;
-    x[4 * c + 3] = v.w;
-  }
-  if (!inverse) {
+  auto load_row = [&](int64_t r, float (&y)[E]) {
+    const float* src = A + r * ld;
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
-      float4 s = *reinterpret_cast<const float4*>(signs + idx0(4 * c));
-      x[4 * c + 0] *= s.x;
-      x[4 * c + 1] *= s.y;
-      x[4 * c + 2] *= s.z;
-      x[4 * c + 3] *= s.w;
+      int i = idx0(4 * c);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < rows) {
+        if (vec) {
+          v = *reinterpret_cast<const float4*>(src + i);
+        } else {
+          v.x = src[i];
+          v.y = src[i + 1];
+          v.z = src[i + 2];
+          v.w = src[i + 3];
+        }
+      }
+      y[4 * c + 0] = v.x;
+      y[4 * c + 1] = v.y;
+      y[4 * c + 2] = v.z;
+      y[4 * c + 3] = v.w;
     }
-  }
-  // round 0: every register bit is a new index bit
+  };
+  load_row(row, xn);
+  for (;;) {
+    const bool live = row < rows;
 #pragma unroll
-  for (int t = 0; t < LE; ++t) {
+    for (int e = 0; e < E; ++e) x[e] = xn[e];
+    const bool more = wbase + wstep < rows;
+    if (more) load_row(row + wstep, xn);
+    if (!inverse) {
 #pragma unroll
-    for (int r = 0; r < E; ++r) {
-      if (r & (1 << t)) continue;
-      float u = x[r], w = x[r | (1 << t)];
-      x[r] = u + w;
-      x[r | (1 << t)] = u - w;
+      for (int c = 0; c < E / 4; ++c) {
+        float4 s = *reinterpret_cast<const float4*>(signs + idx0(4 * c));
+        x[4 * c + 0] *= s.x;
+        x[4 * c + 1] *= s.y;
+        x[4 * c + 2] *= s.z;
+        x[4 * c + 3] *= s.w;
+      }
     }
-  }
-
-  float* base[2] = {lds + rw * N, lds + (RW + rw) * N};
-  int buf = 0;
-  int prev = -1;  // -1: round-0 layout, else base bit of the previous round
-#pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    const int a = j < NFULL ? MID_LO + j * LE : (MID_HI - LE > 0 ? MID_HI - LE : 0);
-    const int new_lo = j < NFULL ? a : MID_LO + NFULL * LE;
-    const int new_hi = j < NFULL ? a + LE : MID_HI;
-    float* L = base[buf];
-    if (prev < 0) {
-#pragma unroll
-      for (int c = 0; c < E / 4; ++c)
-        *reinterpret_cast<float4*>(L + swz(idx0(4 * c))) =
-            make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < E; ++r) L[swz(idxa(prev, r))] = x[r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < E; ++r) x[r] = L[swz(idxa(a, r))];
-    buf ^= 1;
+    // round 0: every register bit is a new index bit
 #pragma unroll
     for (int t = 0; t < LE; ++t) {
-      if (a + t < new_lo || a + t >= new_hi) continue;
 #pragma unroll
       for (int r = 0; r < E; ++r) {
         if (r & (1 << t)) continue;
@@ -132,46 +118,83 @@ __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* ou
         x[r | (1 << t)] = u - w;
       }
     }
-    prev = a;
-  }
-  if (NR > 0) {
-    float* L = base[buf];
+
+    float* const L = lds + rw * N;  // one transpose buffer per row
+    int prev = -1;  // -1: round-0 layout, else base bit of the previous round
 #pragma unroll
-    for (int r = 0; r < E; ++r) L[swz(idxa(prev, r))] = x[r];
-    __syncthreads();
+    for (int j = 0; j < NR; ++j) {
+      const int a = j < NFULL ? MID_LO + j * LE : (MID_HI - LE > 0 ? MID_HI - LE : 0);
+      const int new_lo = j < NFULL ? a : MID_LO + NFULL * LE;
+      const int new_hi = j < NFULL ? a + LE : MID_HI;
+      if (j > 0) __syncthreads();  // the previous round's reads are done
+      if (prev < 0) {
 #pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-      float4 v = *reinterpret_cast<const float4*>(L + swz(idx0(4 * c)));
-      x[4 * c + 0] = v.x;
-      x[4 * c + 1] = v.y;
-      x[4 * c + 2] = v.z;
-      x[4 * c + 3] = v.w;
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < E / 4; ++c) {
-    float4 s = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (inverse) s = *reinterpret_cast<const float4*>(signs + idx0(4 * c));
-    x[4 * c + 0] *= s.x * scale;
-    x[4 * c + 1] *= s.y * scale;
-    x[4 * c + 2] *= s.z * scale;
-    x[4 * c + 3] *= s.w * scale;
-  }
-  if (live) {
-    float* dst = out + row * ld;
-#pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-      int i = idx0(4 * c);
-      if (vec) {
-        *reinterpret_cast<float4*>(dst + i) =
-            make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+        for (int c = 0; c < E / 4; ++c)
+          *reinterpret_cast<float4*>(L + swz(idx0(4 * c))) =
+              make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
       } else {
-        dst[i] = x[4 * c];
-        dst[i + 1] = x[4 * c + 1];
-        dst[i + 2] = x[4 * c + 2];
-        dst[i + 3] = x[4 * c + 3];
+#pragma unroll
+        for (int r = 0; r < E; ++r) L[swz(idxa(prev, r))] = x[r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < E; ++r) x[r] = L[swz(idxa(a, r))];
+#pragma unroll
+      for (int t = 0; t < LE; ++t) {
+        if (a + t < new_lo || a + t >= new_hi) continue;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          if (r & (1 << t)) continue;
+          float u = x[r], w = x[r | (1 << t)];
+          x[r] = u + w;
+          x[r | (1 << t)] = u - w;
+        }
+      }
+      prev = a;
+    }
+    if (NR > 0) {
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < E; ++r) L[swz(idxa(prev, r))] = x[r];
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        float4 v = *reinterpret_cast<const float4*>(L + swz(idx0(4 * c)));
+        x[4 * c + 0] = v.x;
+        x[4 * c + 1] = v.y;
+        x[4 * c + 2] = v.z;
+        x[4 * c + 3] = v.w;
       }
     }
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      float4 s = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (inverse) s = *reinterpret_cast<const float4*>(signs + idx0(4 * c));
+      x[4 * c + 0] *= s.x * scale;
+      x[4 * c + 1] *= s.y * scale;
+      x[4 * c + 2] *= s.z * scale;
+      x[4 * c + 3] *= s.w * scale;
+    }
+    if (live) {
+      float* dst = out + row * ld;
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        int i = idx0(4 * c);
+        if (vec) {
+          *reinterpret_cast<float4*>(dst + i) =
+              make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+        } else {
+          dst[i] = x[4 * c];
+          dst[i + 1] = x[4 * c + 1];
+          dst[i + 2] = x[4 * c + 2];
+          dst[i + 3] = x[4 * c + 3];
+        }
+      }
+    }
+    if (!more) break;
+    __syncthreads();  // the LDS buffer is reused by the next row
+    row += wstep;
+    wbase += wstep;
   }
 }
 
@@ -261,6 +284,102 @@ __global__ __launch_bounds__(256) void rht_cols_pass(const float* A, float* out,
   }
 }
 
+// In-register butterflies over the index bits of v[0..15] (one float4 of
+// four columns per index).
+__device__ __forceinline__ void fwht16_f4(float4 (&v)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float4 u = v[i], w = v[i | h];
+      v[i] = make_float4(u.x + w.x, u.y + w.y, u.z + w.z, u.w + w.w);
+      v[i | h] = make_float4(u.x - w.x, u.y - w.y, u.z - w.z, u.w - w.w);
+    }
+}
+
+// Column transform of length 4096 for 8 consecutive columns per work-group,
+// in one pass over memory (see the file header). 512 threads; the panel sits
+// in LDS as float4 slots: row r, column group cg (4 columns) at
+// 2 r + cg + r / 16 (one slot of padding per 16 rows keeps every phase's
+// 16-lane groups on distinct banks). Needs ld % 4 == 0 and 16-byte aligned
+// A and out; A == out is allowed (each column block is read and written by
+// one work-group only, and read in full before it is written).
+constexpr int PANEL_SLOTS = 2 * 4096 + 4096 / 16;
+
+__global__ __launch_bounds__(512) void rht_cols_panel(const float* A, float* out, int64_t cols,
+                                                      int64_t ld,
+                                                      const float* __restrict__ signs,
+                                                      float scale, bool inverse) {
+  extern __shared__ __align__(16) float4 P[];
+  auto slot = [](int r, int cg) { return 2 * r + cg + (r >> 4); };
+  const int t = threadIdx.x;
+  const int cg = t & 1;
+  const int nblk = int((cols + 7) / 8);
+  const int64_t c = int64_t(xcd_remap(int(blockIdx.x), nblk)) * 8 + 4 * cg;  // first of 4 columns
+  const int ncol = cols - c >= 4 ? 4 : (cols - c > 0 ? int(cols - c) : 0);
+  float4 v[16];
+
+  // ---- load rows rb + 256 i, i = 0..15; bits 8..11 in registers
+  {
+    const int rb = t >> 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* p = A + int64_t(rb + 256 * i) * ld + c;
+      if (ncol == 4) {
+        v[i] = *reinterpret_cast<const float4*>(p);
+      } else {
+        v[i] = make_float4(ncol > 0 ? p[0] : 0.f, ncol > 1 ? p[1] : 0.f, ncol > 2 ? p[2] : 0.f, 0.f);
+      }
+    }
+    if (!inverse) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float sg = signs[rb + 256 * i];
+        v[i] = make_float4(v[i].x * sg, v[i].y * sg, v[i].z * sg, v[i].w * sg);
+      }
+    }
+    fwht16_f4(v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) P[slot(rb + 256 * i, cg)] = v[i];
+  }
+  __syncthreads();
+  // ---- rows lo + 16 i + 256 hi: bits 4..7
+  {
+    const int lo = (t >> 1) & 15, hi = t >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = P[slot(lo + 16 * i + 256 * hi, cg)];
+    fwht16_f4(v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) P[slot(lo + 16 * i + 256 * hi, cg)] = v[i];
+  }
+  __syncthreads();
+  // ---- rows i + 16 mid + 256 hi: bits 0..3, then the store
+  {
+    const int mid = (t >> 1) & 15, hi = t >> 5;
+    const int r0 = 16 * mid + 256 * hi;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = P[slot(r0 + i, cg)];
+    fwht16_f4(v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float sg = scale * (inverse ? signs[r0 + i] : 1.f);
+      v[i] = make_float4(v[i].x * sg, v[i].y * sg, v[i].z * sg, v[i].w * sg);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float* p = out + int64_t(r0 + i) * ld + c;
+      if (ncol == 4) {
+        *reinterpret_cast<float4*>(p) = v[i];
+      } else {
+        if (ncol > 0) p[0] = v[i].x;
+        if (ncol > 1) p[1] = v[i].y;
+        if (ncol > 2) p[2] = v[i].z;
+      }
+    }
+  }
+}
+
 // Column transform of length 2, 4 or 8: one thread per column.
 template <int D>
 __global__ void rht_cols_small_kernel(const float* A, float* out, int64_t cols, int64_t ld,
@@ -292,11 +411,21 @@ quip_status rows_t(const float* A, float* out, int64_t rows, int64_t ld, const f
   constexpr int RW = T >= 256 ? 1 : 256 / T;
   const float scale = 1.0f / sqrtf(float(N));
   bool vec = aligned16(A) && aligned16(out) && ld % 4 == 0;
-  size_t shmem = size_t(2) * RW * N * sizeof(float);
+  size_t shmem = size_t(RW) * N * sizeof(float);
   if (shmem > 65536)
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_rows_kernel<LOGN, LE>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
-  dim3 grid(unsigned(cdiv(rows, RW)));
+  // as many work-groups as fit at once (each loops over rows), at most one per row group
+  int64_t nwg = cdiv(rows, RW);
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&rht_rows_kernel<LOGN, LE>), T * RW, shmem) ==
+          hipSuccess &&
+      hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      per_cu > 0 && cus > 0 && int64_t(per_cu) * cus < nwg)
+    nwg = int64_t(per_cu) * cus;
+  const dim3 grid{unsigned(nwg)};
   return timed_launch("rht_rows_kernel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
                        s, scale, inverse, vec);
@@ -368,6 +497,17 @@ quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int
     case 3: return cols_small_t<8>(A, out, cols, ld, signs, inverse, st);
   }
   if (k < 4 || k > 14) return fail(QUIP_ERR_SHAPE, "rht: the transform length must be a power of two in [2, 16384]");
+  if (k == 12 && aligned16(A) && aligned16(out) && ld % 4 == 0) {
+    const size_t shmem = size_t(PANEL_SLOTS) * sizeof(float4);
+    QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+    const float scale = 1.0f / 64.0f;  // 1 / sqrt(4096)
+    const dim3 grid{unsigned(cdiv(cols, 8))};
+    return timed_launch("rht_cols_panel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+      QUIP_KERNEL(rht_cols_panel, grid, dim3(512), shmem, st, A, out, cols, ld, signs, scale,
+                  inverse);
+    }, double(rows) * double(cols) * 14.0, 8.0 * double(rows) * double(cols));
+  }
   const int npass = (k + 6) / 7;
   int lo = 0;
   const float* src = A;

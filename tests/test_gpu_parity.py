@@ -124,8 +124,11 @@ def test_rht_right(rows, d):
     assert np.array_equal(host(Ad), host(out))
 
 
+# d = 4096 with aligned rows takes the one-pass panel kernel (8 columns per
+# work-group): 13 and 1030 columns leave ragged last blocks
 @pytest.mark.parametrize("d,cols", [(2, 5), (4, 65), (8, 1), (16, 64), (64, 130), (128, 64), (256, 300),
-                                    (512, 64), (2048, 65), (4096, 128), (8192, 64)])
+                                    (512, 64), (2048, 65), (4096, 128), (4096, 13), (4096, 1030),
+                                    (8192, 64)])
 def test_rht_left(d, cols):
     A = rng(d * 3 + cols).standard_normal((d, cols)).astype(np.float32)
     s = signs(d + 1, d)
@@ -136,7 +139,22 @@ def test_rht_left(d, cols):
     assert P.rel_rows(host(out).T, ref.T) <= 1e-5
     back = torch.empty_like(Ad)
     Q.quip_rht_inv(out, back, sd, Q.LEFT)
+    assert P.rel_rows(host(back).T, O.rht_inv(host(out), s, "left").T) <= 1e-5
     assert P.rel_rows(host(back).T, A.T) <= 1e-5
+    Q.quip_rht(Ad, Ad, sd, Q.LEFT)  # in place
+    assert np.array_equal(host(Ad), host(out))
+
+
+def test_rht_left_unaligned_rows():
+    # row pitch 131 floats: not float4-aligned, so d = 4096 goes through the
+    # multi-pass column kernels; it must agree with the oracle all the same
+    base = rng(11).standard_normal((4096, 131)).astype(np.float32)
+    A = dev(base)[:, :130]
+    s = signs(12, 4096)
+    out = torch.zeros((4096, 131), device=DEV)[:, :130]
+    Q.quip_rht(A, out, dev(s), Q.LEFT)
+    ref = O.rht(base[:, :130], s, "left")
+    assert P.rel_rows(host(out).T, ref.T) <= 1e-5
 
 
 def test_rht_leading_dimension():
