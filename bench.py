@@ -182,12 +182,14 @@ def traffic_from_profiles(family: str):
 
 def kernel_bound(name: str):
     """(bound, peak, unit) of a kernel family: the matrix-core products against
-    the fp32 MFMA peak, the two latency-bound sequential kernels (LDL block
-    factor, LDLQ sweep) against the fp32 vector-ALU peak, the streaming kernels
-    against HBM bandwidth."""
+    the fp32 MFMA peak; the latency-bound sequential kernels (LDL block factor,
+    LDLQ sweep) and the vector-ALU-bound searches (scale candidates, E8
+    codewords) against the fp32 vector-ALU peak; the streaming kernels against
+    HBM bandwidth."""
     if name.startswith("gemm:"):
         return "mfma", FP32_MFMA_PEAK_TFLOPS, "TFLOP/s"
-    if name in ("ldl_block_kernel", "ldlq_sweep_kernel", "e8_argmin_kernel", "e8_scale_kernel"):
+    if name in ("ldl_block_kernel", "ldlq_sweep_kernel", "grid_scale_kernel", "e8_argmin_kernel",
+                "e8_scale_kernel"):
         return "alu", FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
     return "hbm", HBM_PEAK_GBS, "GB/s"
 
@@ -346,18 +348,20 @@ def main():
                 "algorithmic_flops_per_launch": k["algorithmic_flops_per_launch"],
                 "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"]}
 
-    # RHT bandwidth per one-sided pass (W, 4096 x 4096)
+    # RHT bandwidth per one-sided pass (W, 4096 x 4096): `reps` calls back to
+    # back between one pair of events (per-call events would also count the
+    # host's time to issue each call)
     def timed(fn, reps):
-        es = []
-        for _ in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            es.append((a, b))
+        fn()
         torch.cuda.synchronize()
-        return float(np.mean([x.elapsed_time(y) for x, y in es]))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
     tmp = torch.empty_like(W)
     rht = {}
