@@ -14,12 +14,14 @@
 // with the next row's loads issued before the current row's transform.
 //
 // LEFT side (along a column, strided by the row pitch). For d = 4096 and
-// float4-aligned rows, one pass over memory: rht_cols_panel holds all d rows
-// of 8 columns in LDS (128 KB + padding), does the top four index bits in
-// registers right after the load, the middle four through one LDS round
-// trip, the low four in registers right before the store; column blocks are
-// dealt out so that the four work-groups sharing a 128-byte line run on one
-// XCD. Otherwise rht_cols_pass: the d-point transform is split
+// float4-aligned rows, one pass over memory, a work-group per column block:
+// rht_cols_panel16 (16 columns, 64-byte row segments, the panel in registers,
+// two LDS exchanges in halves) when the column count is a multiple of 16, else
+// rht_cols_panel (8 columns in LDS, 128 KB + padding: the top four index bits
+// in registers right after the load, the middle four through one LDS round
+// trip, the low four in registers right before the store). Row segments
+// narrower than a 128-byte line cost per-CU throughput, so column blocks are
+// dealt out such that the work-groups sharing a line run on one XCD. Otherwise rht_cols_pass: the d-point transform is split
 // H_d = H_{2^k1} (x) H_{2^k2} (x) ... into passes that each transform 2^KR
 // rows spaced 2^lo apart, for 64 consecutive columns per work-group (lanes run
 // along the columns, so every access is a 256-byte row segment). Inside a
@@ -380,6 +382,104 @@ __global__ __launch_bounds__(512) void rht_cols_panel(const float* A, float* out
   }
 }
 
+// In-register butterflies over the index bits of v[0..31] (float4 of four
+// columns per index).
+__device__ __forceinline__ void fwht32_f4(float4 (&v)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i & h) continue;
+      const float4 u = v[i], w = v[i | h];
+      v[i] = make_float4(u.x + w.x, u.y + w.y, u.z + w.z, u.w + w.w);
+      v[i | h] = make_float4(u.x - w.x, u.y - w.y, u.z - w.z, u.w - w.w);
+    }
+}
+
+// Column transform of length 4096 for 16 consecutive columns per work-group
+// (64-byte row segments: four lanes per row), in one pass over memory. 512
+// threads; thread t holds column group g = t % 4 (4 columns) of 32 rows in
+// registers (the 256 KB panel lives in registers). Index bits 7..11 are done
+// right after the load (rows k + 128 i), bits 2..6 after one exchange (rows
+// l + 4 i + 128 h), bits 0..1 after a second one (rows 32 k + i), then the
+// store. Each exchange goes through LDS in two halves of 8 columns (128 KB +
+// padding: slot 2 r + g' + r / 16 of a half). Needs cols % 16 == 0, ld % 4 ==
+// 0 and 16-byte aligned A and out; A == out is allowed.
+__global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* out, int64_t ld,
+                                                        int nblk,
+                                                        const float* __restrict__ signs,
+                                                        float scale, bool inverse) {
+  extern __shared__ __align__(16) float4 P[];
+  auto slot = [](int r, int g2) { return 2 * r + g2 + (r >> 4); };
+  const int t = threadIdx.x;
+  const int g = t & 3, k = t >> 2;  // column group, row index of the thread (0..127)
+  const int64_t c = int64_t(xcd_remap(int(blockIdx.x), nblk)) * 16 + 4 * g;
+  float4 v[32];
+
+  // ---- rows k + 128 i: bits 7..11
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    v[i] = *reinterpret_cast<const float4*>(A + int64_t(k + 128 * i) * ld + c);
+  if (!inverse) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float sg = signs[k + 128 * i];
+      v[i] = make_float4(v[i].x * sg, v[i].y * sg, v[i].z * sg, v[i].w * sg);
+    }
+  }
+  fwht32_f4(v);
+  // ---- exchange to rows l + 4 i + 128 h (l = k % 4, h = k / 4): bits 2..6
+  const int l = k & 3, h = k >> 2;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const bool mine = (g >> 1) == half;
+    if (half) __syncthreads();  // the first half's reads are done
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) P[slot(k + 128 * i, g & 1)] = v[i];
+    }
+    __syncthreads();
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = P[slot(l + 4 * i + 128 * h, g & 1)];
+    }
+  }
+  fwht32_f4(v);
+  // ---- exchange to rows 32 k + i: bits 0..1 (and the store layout)
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const bool mine = (g >> 1) == half;
+    __syncthreads();  // the previous reads of the buffer are done
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) P[slot(l + 4 * i + 128 * h, g & 1)] = v[i];
+    }
+    __syncthreads();
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = P[slot(32 * k + i, g & 1)];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 32; q += 4) {  // bits 0..1: groups of four consecutive rows
+#pragma unroll
+    for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i & hb) continue;
+        const float4 u = v[q + i], w = v[q + (i | hb)];
+        v[q + i] = make_float4(u.x + w.x, u.y + w.y, u.z + w.z, u.w + w.w);
+        v[q + (i | hb)] = make_float4(u.x - w.x, u.y - w.y, u.z - w.z, u.w - w.w);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float sg = scale * (inverse ? signs[32 * k + i] : 1.f);
+    *reinterpret_cast<float4*>(out + int64_t(32 * k + i) * ld + c) =
+        make_float4(v[i].x * sg, v[i].y * sg, v[i].z * sg, v[i].w * sg);
+  }
+}
+
 // Column transform of length 2, 4 or 8: one thread per column.
 template <int D>
 __global__ void rht_cols_small_kernel(const float* A, float* out, int64_t cols, int64_t ld,
@@ -502,6 +602,15 @@ quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
     const float scale = 1.0f / 64.0f;  // 1 / sqrt(4096)
+    if (cols % 16 == 0) {  // 64-byte row segments
+      QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel16),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+      const int nblk = int(cols / 16);
+      return timed_launch("rht_cols_panel16", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL(rht_cols_panel16, dim3(unsigned(nblk)), dim3(512), shmem, st, A, out, ld,
+                    nblk, signs, scale, inverse);
+      }, double(rows) * double(cols) * 14.0, 8.0 * double(rows) * double(cols));
+    }
     const dim3 grid{unsigned(cdiv(cols, 8))};
     return timed_launch("rht_cols_panel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
       QUIP_KERNEL(rht_cols_panel, grid, dim3(512), shmem, st, A, out, cols, ld, signs, scale,

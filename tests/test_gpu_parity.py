@@ -124,11 +124,12 @@ def test_rht_right(rows, d):
     assert np.array_equal(host(Ad), host(out))
 
 
-# d = 4096 with aligned rows takes the one-pass panel kernel (8 columns per
-# work-group): 13 and 1030 columns leave ragged last blocks
+# d = 4096 with aligned rows takes a one-pass panel kernel: 16 columns per
+# work-group when the count is a multiple of 16 (128, 16, 4096), else 8 (13
+# and 1030 leave ragged last blocks)
 @pytest.mark.parametrize("d,cols", [(2, 5), (4, 65), (8, 1), (16, 64), (64, 130), (128, 64), (256, 300),
-                                    (512, 64), (2048, 65), (4096, 128), (4096, 13), (4096, 1030),
-                                    (8192, 64)])
+                                    (512, 64), (2048, 65), (4096, 128), (4096, 16), (4096, 13),
+                                    (4096, 1030), (8192, 64)])
 def test_rht_left(d, cols):
     A = rng(d * 3 + cols).standard_normal((d, cols)).astype(np.float32)
     s = signs(d + 1, d)
