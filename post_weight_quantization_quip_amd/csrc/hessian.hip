@@ -25,16 +25,32 @@ __global__ void trace_kernel(const float* H, int64_t n, int64_t ldh, double* out
   }
 }
 
-__global__ void finalize_kernel(float* H, int64_t n, int64_t ldh, const double* trace,
-                                double inv_n_total, double alpha) {
+// One row per work-group; float4 accesses when every row start is 16-byte
+// aligned.
+__global__ __launch_bounds__(256) void finalize_kernel(float* H, int64_t n, int64_t ldh,
+                                                       const double* trace, double inv_n_total,
+                                                       double alpha, bool vec) {
   const float shift = float(alpha * (*trace) * inv_n_total / double(n));
   const float scale = float(inv_n_total);
-  for (int64_t r = blockIdx.y; r < n; r += gridDim.y)
-    for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < n; c += int64_t(gridDim.x) * 256) {
-      float v = H[r * ldh + c] * scale;
-      if (r == c) v += shift;
-      H[r * ldh + c] = v;
+  const int64_t r = blockIdx.x;
+  float* row = H + r * ldh;
+  if (vec) {
+    for (int64_t c = int64_t(threadIdx.x) * 4; c < n; c += 1024) {
+      float4 v = *reinterpret_cast<const float4*>(row + c);
+      v = make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
+      if (r == c + 0) v.x += shift;
+      if (r == c + 1) v.y += shift;
+      if (r == c + 2) v.z += shift;
+      if (r == c + 3) v.w += shift;
+      *reinterpret_cast<float4*>(row + c) = v;
     }
+  } else {
+    for (int64_t c = threadIdx.x; c < n; c += 256) {
+      float v = row[c] * scale;
+      if (r == c) v += shift;
+      row[c] = v;
+    }
+  }
 }
 
 }  // namespace
@@ -73,13 +89,11 @@ quip_status hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, 
   QUIP_TRY(timed_launch("trace_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
   }));
-  int64_t gx = cdiv(n, 256);
-  if (gx > 16) gx = 16;
-  dim3 grid(unsigned(gx), unsigned(n < 65535 ? n : 65535));
+  const bool vec = aligned16(H) && ldh % 4 == 0 && n % 4 == 0;
   return timed_launch("finalize_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(finalize_kernel, grid, dim3(256), 0, s, H, n, ldh, scratch,
-                       1.0 / double(N_total), double(alpha));
-  });
+    QUIP_KERNEL(finalize_kernel, dim3(unsigned(n)), dim3(256), 0, s, H, n, ldh, scratch,
+                1.0 / double(N_total), double(alpha), vec);
+  }, 2.0 * double(n) * double(n), 8.0 * double(n) * double(n));
 }
 
 }  // namespace quip
