@@ -21,6 +21,7 @@ a bounded sample.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -376,6 +377,26 @@ def main():
                "right_ms": round(r_ms, 4), "left_ms": round(l_ms, 4), "two_sided_ms": round(t_ms, 4),
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
+    # The E8 codebook at 2 bits per weight on an i.i.d. N(0,1) source (1024 x
+    # 4096 weights, 524288 8-vectors), through the search of the E8
+    # configuration's scale step: the best mean squared error per weight over
+    # the 32 scale candidates, against the Gaussian distortion-rate bound 2^-4;
+    # the QTIP page's figures (E8P 0.089, 256-D TCQ 0.068-0.071) are context
+    gm, gn = 1024, 4096
+    G = torch.from_numpy(wl.gaussian_rows(1, gm, gn)).to(dev)
+    cb = Q.quip_e8_codebook().to(dev)
+    q8 = Q.quantizer(Q.Q_E8, 2)
+    gsc = torch.empty(gm + 1, device=dev)
+    gsse = torch.empty(32, dtype=torch.float64, device=dev)
+    gws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_scales_workspace, gm, gn,
+                                                 ctypes.byref(q8)), dev)
+    g_ms = timed(lambda: Q.quip_scales(G, q8, gsc, mse_out=gsse, codebook=cb, ws=gws), 3)
+    nvec = gm * gn // 8
+    gaussian_vq = {"mse_per_weight": round(float(gsse.min().item()) / (gm * gn), 5),
+                   "distortion_rate_bound": 0.0625, "printed_e8p": 0.089,
+                   "printed_tcq_256d": [0.068, 0.071], "vectors": nvec, "ms": round(g_ms, 3),
+                   "candidate_distances_per_s": round(nvec * 65536 * 32 / (g_ms / 1e3), 1)}
+
     line = {
         "metric": "quantized weights/sec for a 4096x4096 layer (LDLQ+RHT, 2-bit); RHT GB/s",
         "value": round(value, 1),
@@ -395,6 +416,7 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in phases.items()},
         "weights_per_s_from_resident_H_W": round(mn / (from_resident / 1e3), 1),
         "rht": rht,
+        "gaussian_vq": gaussian_vq,
         "roofline": roofline,
         "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])),
     }

@@ -518,3 +518,43 @@ def test_layer_pass_end_to_end_c1():
     # post-processing inverts the incoherence transforms
     back = O.incoherence_W_inv(host(b["What_t"]), L.left, L.right)
     assert P.rel_rows(host(b["What"]), back) <= 1e-5
+
+
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
+def test_e8_gaussian_source_mse(codebook):
+    # The E8 codebook at 2 bits per weight on an i.i.d. N(0,1) source, through
+    # the GPU search (the scale search of the E8 configuration). Per-candidate
+    # squared errors match the oracle on a small sample; on a large sample the
+    # best mean squared error lies between the Gaussian distortion-rate bound
+    # 2^-4 (the QTIP page prints 0.063) and the best 2-bit scalar grid (Max
+    # 1960), and agrees with the oracle's estimate within sampling error.
+    gd = _golden("qtip_gaussian_2bit_mse.json")
+    scalar = _golden("max1960_uniform_gaussian.json")["levels"]["4"]["mse"]
+    q = Q.quantizer(Q.Q_E8, 2)
+
+    def gpu_sse(W):
+        m = W.shape[0]
+        scales = torch.empty(m + 1, device=DEV)
+        sse = torch.empty(32, dtype=torch.float64, device=DEV)
+        Q.quip_scales(dev(W), q, scales, mse_out=sse, codebook=dev(codebook))
+        return host(scales), host(sse)
+
+    small = wl.gaussian_rows(11, 64, 256)  # 2048 8-vectors
+    sg, eg = gpu_sse(small)
+    Wn = small / sg[1:, None].astype(np.float64)
+    _, c_ref, sse_ref = O.e8_scale_search(Wn, codebook)
+    assert np.allclose(eg, sse_ref, rtol=1e-4)
+    mse_oracle = sse_ref[c_ref] / small.size
+
+    large = wl.gaussian_rows(12, 1024, 1024)  # 131072 8-vectors
+    _, el = gpu_sse(large)
+    mse = el.min() / large.size
+    assert 2.0 ** -4 <= mse < scalar
+    assert abs(mse - mse_oracle) <= 0.005
+    assert 0 < int(np.argmin(el)) < 31
