@@ -22,10 +22,8 @@
  *     that must be >= the number of columns.
  *   - The caller owns all memory: inputs, outputs and workspace. Workspace
  *     sizes come from the quip_*_workspace queries; a workspace must be 256-byte
- *     aligned. The library allocates no device memory. Its only host state is
- *     the timing registry (off by default) and, per device, one side stream
- *     with two events, created on the first quip_ldlq with the scalar grid
- *     (see there); calls on different streams are otherwise independent.
+ *     aligned. The library allocates nothing and keeps no global mutable state;
+ *     calls on different streams are independent.
  *   - Every call only enqueues work on `stream` (asynchronous) and returns at
  *     once. Argument and shape errors are detected on the host before any
  *     launch, and then nothing is enqueued. A failure found on the device (a
@@ -237,17 +235,8 @@ quip_status quip_scales(const float* W, int64_t m, int64_t n, int64_t ldw, const
  *     target P_K minus W^_K, so the loss is sum_K (P_K - W^_K) D_K
  *     (P_K - W^_K)^T, O(mn) instead of O(mn^2). Requires D.
  *   ws: device workspace of quip_ldlq_workspace() bytes.
- * Streams (scalar grid): after each outer block (the largest multiple of B
- *   up to 512 columns, or B when larger), the feedback to the next outer
- *   block is enqueued on `stream`, the feedback to the columns
- *   beyond it on the device's side stream (non-blocking, default priority),
- *   ordered by events; the side stream is joined back into `stream` before
- *   the call returns, so all of the call's work is complete when work
- *   enqueued on `stream` afterwards starts. Concurrent calls from several
- *   host threads on one device take turns enqueueing (a lock per device).
  * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (n % g, B % g, B range),
- *   QUIP_ERR_WORKSPACE, QUIP_ERR_UNSUPPORTED (bits > 8), QUIP_ERR_HIP (side
- *   stream or event creation).
+ *   QUIP_ERR_WORKSPACE, QUIP_ERR_UNSUPPORTED (bits > 8).
  */
 quip_status quip_ldlq_workspace(int64_t m, int64_t n, int64_t g, int64_t B,
                                 const quip_quantizer* q, size_t* bytes);

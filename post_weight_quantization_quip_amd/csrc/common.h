@@ -6,7 +6,6 @@
 
 #include <cstddef>
 #include <cstdint>
-#include <mutex>
 #include <string>
 
 #include "quip.h"
@@ -110,22 +109,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return start + local;
 }
 
-// ---------------------------------------------------------------- streams (streams.cpp)
-
-// The current device's side stream and its two ordering events (`fwd`:
-// caller -> side, `back`: side -> caller). `lock` holds the device's side
-// stream for the caller until the SideStream goes out of scope, so that the
-// event records and waits of concurrent host threads do not interleave.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fwd = nullptr, back = nullptr;
-  std::unique_lock<std::mutex> lock;
-};
-quip_status side_stream(SideStream* out);
-// Work enqueued on `waiter` from now on starts after the work enqueued on
-// `signaler` so far (event `ev` recorded on signaler, waited on by waiter).
-quip_status stream_after(hipStream_t waiter, hipStream_t signaler, hipEvent_t ev);
-
 // ---------------------------------------------------------------- GEMM (gemm.hip)
 
 enum GemmEpi {
@@ -164,9 +147,6 @@ struct GemmArgs {
   float* P = nullptr;
   size_t P_floats = 0;
   const char* tag = "gemm";  // name under which launches are timed
-  // > 0: the tiles go out in launches of at most this many work-groups (one
-  // after another), so that work on another stream keeps CUs to run on
-  int max_wgs = 0;
   // internal: tiles [tile0, tile0 + grid / kpieces) of the grid, K in pieces of kchunk
   int tile0 = 0;
   int kpieces = 1;

@@ -49,22 +49,14 @@ __device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t 
   return v;
 }
 
-template <int BM, int BN, bool TA, bool TB>
-struct GemmSmem {
-  static constexpr bool KCA = !TA, KCB = TB;  // operand tiles stored k-contiguous
-  static constexpr int SA = KCA ? BM * KC_LD : BK * (BM + MC_PAD);
-  static constexpr int SB = KCB ? BN * KC_LD : BK * (BN + MC_PAD);
-};
-
-// One output tile: grid slot `wg` of `total` (batch entry blockIdx.y).
 template <int BM, int BN, bool TA, bool TB, int EPI>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int wg, int tiles_m, int tiles_n,
-                                          int total, bool vecA, bool vecB,
-                                          float (&As)[2][GemmSmem<BM, BN, TA, TB>::SA],
-                                          float (&Bs)[2][GemmSmem<BM, BN, TA, TB>::SB]) {
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n,
+                                                      int total, bool vecA, bool vecB) {
   constexpr bool KCA = !TA, KCB = TB;  // operand tiles stored k-contiguous
   constexpr int LDA_S = KCA ? KC_LD : BM + MC_PAD;
   constexpr int LDB_S = KCB ? KC_LD : BN + MC_PAD;
+  __shared__ __align__(16) float As[2][KCA ? BM * KC_LD : BK * (BM + MC_PAD)];
+  __shared__ __align__(16) float Bs[2][KCB ? BN * KC_LD : BK * (BN + MC_PAD)];
 
   constexpr int WBM = BM / 64;  // 32x32 blocks per wave along M
   constexpr int WBN = BN / 64;
@@ -76,7 +68,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int wg, int tiles_m
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile coordinates
-  int bid = (EPI == EPI_DOT_SYM) ? wg : xcd_remap(wg, total);
+  int bid = (EPI == EPI_DOT_SYM) ? int(blockIdx.x) : xcd_remap(blockIdx.x, total);
   int piece = 0;
   if (a.kpieces > 1) {
     piece = bid % a.kpieces;
@@ -397,15 +389,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int wg, int tiles_m
   }
 }
 
-template <int BM, int BN, bool TA, bool TB, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n,
-                                                      int total, bool vecA, bool vecB) {
-  using S = GemmSmem<BM, BN, TA, TB>;
-  __shared__ __align__(16) float As[2][S::SA];
-  __shared__ __align__(16) float Bs[2][S::SB];
-  gemm_tile<BM, BN, TA, TB, EPI>(a, int(blockIdx.x), tiles_m, tiles_n, total, vecA, vecB, As, Bs);
-}
-
 // Sums the K pieces of the leftover tiles (fixed order) and applies alpha,
 // beta and the mirror like the regular epilogue.
 template <int BM, int BN>
@@ -546,22 +529,6 @@ quip_status launch_t(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
                            t, tiles_m);
       });
     }
-  }
-  if (a.max_wgs > 0 && a.max_wgs < total) {
-    // launches of at most max_wgs work-groups over consecutive tiles, so that
-    // work on another stream keeps CUs to run on
-    const int G = a.max_wgs;
-    for (int t0 = 0; t0 < total; t0 += G) {
-      GemmArgs c = a;
-      c.tile0 = a.tile0 + t0;
-      const int cnt = total - t0 < G ? total - t0 : G;
-      QUIP_TRY(timed_launch(a.tag, s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL((gemm_kernel<BM, BN, TA, TB, EPI>), dim3(cnt, a.batch), dim3(256), 0, s, c,
-                    tiles_m, tiles_n, cnt, vecA, vecB);
-      }, wf, wb));
-      wf = wb = 0.0;
-    }
-    return QUIP_OK;
   }
   dim3 grid(total, a.batch);
   return timed_launch(a.tag, s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {

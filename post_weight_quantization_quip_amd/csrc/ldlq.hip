@@ -43,10 +43,6 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// work-groups of one side-stream launch (one per CU when spread): a sweep
-// work-group still fits beside each
-constexpr int LDLQ_SIDE_WGS = 256;
-
 __device__ __forceinline__ float quad_bcast(float v, int src) {
   // quad_perm [src, src, src, src]
   const int ctrl = src * 0x55;
@@ -745,7 +741,7 @@ quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ld
 // F[:, c0:c1] (+)= Eb[:, e0:e0+K] U[r0:r0+K, c0:c1]
 quip_status feedback_gemm(const float* Eb, int64_t lde, int64_t e0, int64_t K, const float* U,
                           int64_t n, int64_t r0, int64_t c0, int64_t c1, float* F, int64_t m,
-                          bool accumulate, const char* tag, hipStream_t s, int max_wgs = 0) {
+                          bool accumulate, const char* tag, hipStream_t s) {
   if (c1 <= c0 || K <= 0) return QUIP_OK;
   GemmArgs a;
   a.M = m;
@@ -760,7 +756,6 @@ quip_status feedback_gemm(const float* Eb, int64_t lde, int64_t e0, int64_t K, c
   a.alpha = 1.f;
   a.beta = accumulate ? 1.f : 0.f;
   a.tag = tag;
-  a.max_wgs = max_wgs;
   return gemm(a, s);
 }
 
@@ -823,7 +818,7 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
   Carver c(nullptr, 0);
   c.take<float>(64);
   c.take<float>(size_t(m) * n);  // F
-  c.take<float>(size_t(m) * outer_block(n, g, B) * 2);  // Eb, two outer blocks
+  c.take<float>(size_t(m) * outer_block(n, g, B));  // Eb
   c.take<double>(size_t(m));                         // per-row proxy loss
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
@@ -843,8 +838,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   float* fac = c.take<float>(64);
   float* F = c.take<float>(size_t(m) * n);
   const int64_t Bo = outer_block(n, g, B);
-  float* Ebuf = c.take<float>(size_t(m) * Bo * 2);
-  float* Eb = Ebuf;
+  float* Eb = c.take<float>(size_t(m) * Bo);
   double* rl_ws = c.take<double>(size_t(m));
   float hostf[64];
   // per-row proxy loss: the caller's buffer, or the workspace when only the total is wanted
@@ -861,19 +855,8 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
     }
     const int bi = B >= 256 ? 256 : (B >= 128 ? 128 : (B >= 64 ? 64 : 32));
     uint8_t* cd = static_cast<uint8_t*>(codes);
-    // The feedback of an outer block to the columns right of it goes out in
-    // two parts: the next outer block's columns on the caller's stream (its
-    // sweeps need them), the rest on the side stream, where it overlaps the
-    // next outer block's sweeps and inner updates (which touch only that
-    // block's columns of F). The next look-ahead part waits for it (it
-    // accumulates into the same columns); the errors of consecutive outer
-    // blocks go to alternate buffers.
-    SideStream side;
-    QUIP_TRY(side_stream(&side));
-    bool side_pending = false;
     for (int64_t j0 = 0; j0 < n; j0 += Bo) {
       const int64_t bo = (n - j0 < Bo) ? n - j0 : Bo;
-      Eb = Ebuf + size_t((j0 / Bo) % 2) * m * Bo;
       for (int64_t s0 = j0; s0 < j0 + bo; s0 += bi) {
         const int bw = int((j0 + bo - s0) < bi ? (j0 + bo - s0) : bi);
         QUIP_TRY(sweep(bi, W, ldw, F, n, s0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
@@ -882,20 +865,8 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
         QUIP_TRY(feedback_gemm(Eb, Bo, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
                                !(j0 == 0 && s0 == 0), "gemm:ldlq_inner", s));
       }
-      const int64_t c1 = j0 + bo, c2 = (c1 + Bo < n) ? c1 + Bo : n;
-      if (side_pending) {
-        QUIP_TRY(stream_after(s, side.s, side.back));
-        side_pending = false;
-      }
-      if (c2 < n) QUIP_TRY(stream_after(side.s, s, side.fwd));
-      QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, c1, c2, F, m, j0 > 0, "gemm:ldlq_outer", s));
-      if (c2 < n) {
-        QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, c2, n, F, m, j0 > 0,
-                               "gemm:ldlq_outer_side", side.s, LDLQ_SIDE_WGS));
-        side_pending = true;
-      }
+      QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
     }
-    if (side_pending) QUIP_TRY(stream_after(s, side.s, side.back));
     return finish_loss(rl, m, loss, s);
   }
 
