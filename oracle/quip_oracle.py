@@ -580,6 +580,62 @@ def e8_quantizer(C, s: float, nearest=None):
 
 
 # --------------------------------------------------------------------------
+# Inference with the quantized layer
+# --------------------------------------------------------------------------
+
+def code_container_bits(bits: int) -> int:
+    """Bits each code occupies in the packed format: the smallest of 2, 4, 8
+    that holds `bits` (so that a code never straddles a byte)."""
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be in 1..8")
+    return 2 if bits <= 2 else (4 if bits <= 4 else 8)
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Row-wise packed codes: code j of a row occupies bits
+    [(j w) mod 8, (j w) mod 8 + w) of byte (j w) / 8 of that row (w the
+    container width, least significant bits first); a row takes
+    ceil(n w / 8) bytes. Written out element by element."""
+    codes = np.asarray(codes, dtype=np.int64)
+    m, n = codes.shape
+    w = code_container_bits(bits)
+    per = 8 // w
+    nbytes = (n + per - 1) // per
+    out = np.zeros((m, nbytes), dtype=np.uint8)
+    for r in range(m):
+        for j in range(n):
+            c = int(codes[r, j])
+            if not 0 <= c < (1 << bits):
+                raise ValueError("code out of range")
+            out[r, j // per] |= np.uint8(c << ((j % per) * w))
+    return out
+
+
+def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
+    """Inverse of ``pack_codes`` for rows of n codes."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    w = code_container_bits(bits)
+    per = 8 // w
+    j = np.arange(n)
+    return ((packed[:, j // per].astype(np.int64) >> ((j % per) * w)) & ((1 << w) - 1))
+
+
+def qmatvec_rht(codes, scales, L: int, signs_left, signs_right, x) -> np.ndarray:
+    """Product of the quantized layer with a full-precision vector at
+    inference: [QuIP] "Experiments", "Throughput Comparison" (a
+    quantized-matrix full-precision-vector product with the incoherence
+    transforms applied around it), with random-sign Hadamard sides ([QuIP#]
+    abstract). With W^~ the dequantized incoherent weights (code - (L-1)/2) s_r
+    and the transforms of ``rht`` (Q_L on the m side, Q_R on the n side), the
+    layer in the original basis is W^ = Q_L^T W^~ Q_R, and y = W^ x is taken
+    as x' = Q_R x, y' = W^~ x', y = Q_L^T y' (the vectors as rows below)."""
+    x = np.asarray(x, dtype=F64)
+    xp = rht(x[None, :], signs_right, "right")[0]
+    yp = uniform_level(codes, np.asarray(scales)[:, None], L) @ xp
+    return rht_inv(yp[None, :], signs_left, "right")[0]
+
+
+# --------------------------------------------------------------------------
 # The whole pass (small layers)
 # --------------------------------------------------------------------------
 

@@ -482,3 +482,40 @@ def test_workloads_are_deterministic_and_shaped():
     assert set(np.unique(a.left["signs"]).tolist()) == {-1.0, 1.0}
     frac = np.mean(np.abs(a.W) > 5)
     assert 0.002 < frac < 0.02  # ~1% outliers x10
+
+
+# ---------------------------------------------------------------- inference product
+
+def test_pack_codes_matches_handwritten_bytes():
+    for case in golden("packed_codes_example.json")["cases"]:
+        codes = np.array(case["codes"])
+        got = O.pack_codes(codes, case["bits"])
+        assert got.tolist() == case["packed"]
+        assert O.unpack_codes(got, codes.shape[1], case["bits"]).tolist() == case["codes"]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_pack_codes_round_trip(bits):
+    codes = rng(bits).integers(0, 1 << bits, size=(7, 37))
+    assert np.array_equal(O.unpack_codes(O.pack_codes(codes, bits), 37, bits), codes)
+
+
+@pytest.mark.parametrize("m,n,bits", [(64, 32, 2), (16, 128, 3), (32, 64, 4)])
+def test_qmatvec_rht_equals_the_dense_layer(m, n, bits):
+    r = rng(m + n + bits)
+    L = 1 << bits
+    codes = r.integers(0, L, size=(m, n))
+    scales = np.exp(r.standard_normal(m)).astype(np.float32)
+    sl = r.choice([-1.0, 1.0], m)
+    sr = r.choice([-1.0, 1.0], n)
+    x = r.standard_normal(n)
+    y = O.qmatvec_rht(codes, scales, L, sl, sr, x)
+    What_t = O.uniform_level(codes, scales[:, None], L)
+    tol = 1e-12 * np.abs(What_t).sum(axis=1).max() * np.abs(x).max()
+    # the pass's own post-processing: the inverse two-sided transform of the matrix
+    What = O.incoherence_W_inv(What_t, {"signs": sl}, {"signs": sr})
+    assert np.allclose(y, What @ x, rtol=0, atol=tol)
+    # explicit matrices: Q = H diag(s) / sqrt(d), W^ = Q_L^T W^~ Q_R
+    QL = O.sylvester(m) * sl[None, :] / np.sqrt(m)
+    QR = O.sylvester(n) * sr[None, :] / np.sqrt(n)
+    assert np.allclose(y, QL.T @ What_t @ QR @ x, rtol=0, atol=tol)
