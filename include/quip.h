@@ -284,6 +284,48 @@ quip_status quip_timing_reset(void);
 quip_status quip_timing_report(char* buf, size_t len, size_t* needed);
 
 /*
+ * quip_pack_codes -- packs the per-weight codes of the scalar grid (as
+ * quip_ldlq writes them) for inference: row by row, code j of a row occupies
+ * bits [(j w) mod 8, (j w) mod 8 + w) of byte (j w) / 8 of that row, least
+ * significant bits first, with w = 2, 4 or 8 the smallest container that
+ * holds `bits` (no code straddles a byte); a row takes
+ * quip_packed_row_bytes(n, bits) bytes and the rows follow each other without
+ * padding.
+ *   codes: m x n uint8 (device), leading dim ldc; values below 2^bits (higher
+ *     bits are dropped).
+ *   packed: m x quip_packed_row_bytes(n, bits) bytes (device, caller-owned).
+ * Errors: QUIP_ERR_ARG (null pointer, sizes, ldc < n, bits outside 1..8).
+ */
+quip_status quip_packed_row_bytes(int64_t n, int32_t bits, int64_t* bytes);
+quip_status quip_pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int32_t bits,
+                            uint8_t* packed, hipStream_t stream);
+
+/*
+ * quip_qmatvec_rht -- product of the quantized layer with a full-precision
+ * vector at inference: the quantized-matrix full-precision-vector product with
+ * the incoherence transforms applied around it ([QuIP] "Experiments",
+ * "Throughput Comparison"), with random-sign Hadamard sides ([QuIP#]
+ * abstract). With W^~[r][j] = scales[r] (code[r][j] - (2^bits - 1)/2) and
+ * Q_L = H_m diag(signs_left)/sqrt(m), Q_R = H_n diag(signs_right)/sqrt(n) (the
+ * transforms of quip_rht), it computes y = Q_L^T W^~ Q_R x, the layer W^ =
+ * Q_L^T W^~ Q_R in the original basis times x, without forming W^.
+ *   packed: m x quip_packed_row_bytes(n, bits) bytes from quip_pack_codes.
+ *   scales: m floats (the grid step of every row, as quip_ldlq uses them).
+ *   signs_left: m floats, signs_right: n floats (+1 / -1), as passed to
+ *     quip_rht for the two sides of W.
+ *   x: n floats in; y: m floats out (device). m: a power of two in
+ *     [2, 16384]; n: a power of two in [1024, 16384]. packed, x, y and the
+ *     signs 16-byte aligned.
+ *   ws: device workspace of quip_qmatvec_rht_workspace() bytes.
+ * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (m, n), QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_qmatvec_rht_workspace(int64_t m, int64_t n, size_t* bytes);
+quip_status quip_qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int32_t bits,
+                             const float* scales, const float* signs_left,
+                             const float* signs_right, const float* x, float* y, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
  * quip_e8_codebook -- fills HOST memory with the 65536 smallest-norm points of
  * the E8 lattice (D8 together with D8 + 1/2) ordered by squared norm, then by
  * coordinates ascending with the first coordinate most significant; 65536 x 8

@@ -72,6 +72,11 @@ SYMBOLS = {
     "quip_proxy_loss": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_sz,
                                 c_vp]),
     "quip_e8_codebook": (c_int, [c_vp]),
+    "quip_packed_row_bytes": (c_int, [c_i64, ctypes.c_int32, ctypes.POINTER(c_i64)]),
+    "quip_pack_codes": (c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp]),
+    "quip_qmatvec_rht_workspace": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
+    "quip_qmatvec_rht": (c_int, [c_vp, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                 c_vp, c_sz, c_vp]),
     "quip_timing_enable": (c_int, [c_int]),
     "quip_timing_reset": (c_int, []),
     "quip_timing_report": (c_int, [ctypes.c_char_p, c_sz, ctypes.POINTER(c_sz)]),
@@ -234,6 +239,29 @@ def quip_e8_codebook() -> torch.Tensor:
     out = torch.empty((65536, 8), dtype=torch.float32)
     _check(lib.quip_e8_codebook(c_vp(out.data_ptr())), "quip_e8_codebook")
     return out
+
+
+def quip_packed_row_bytes(n: int, bits: int) -> int:
+    out = c_i64(0)
+    _check(lib.quip_packed_row_bytes(n, bits, ctypes.byref(out)), "quip_packed_row_bytes")
+    return out.value
+
+
+def quip_pack_codes(codes, bits: int, packed, stream=None):
+    m, n = codes.shape
+    _check(lib.quip_pack_codes(_p(codes), m, n, _ld(codes), bits, _p(packed), _stream(stream)),
+           "quip_pack_codes")
+
+
+def quip_qmatvec_rht(packed, n: int, bits: int, scales, signs_left, signs_right, x, y,
+                     stream=None, ws=None):
+    m = scales.numel()
+    if ws is None:
+        ws = _workspace(_ws_query(lib.quip_qmatvec_rht_workspace, m, n), x.device)
+    _check(lib.quip_qmatvec_rht(_p(packed), m, n, bits, _p(scales), _p(signs_left),
+                                _p(signs_right), _p(x), _p(y), _p(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)),
+           "quip_qmatvec_rht")
 
 
 def timing_enable(on: bool = True) -> None:

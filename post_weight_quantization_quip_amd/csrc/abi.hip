@@ -320,6 +320,53 @@ quip_status quip_ldlq(const float* W, int64_t m, int64_t n, int64_t ldw, const f
                   ws, ws_bytes, stream);
 }
 
+quip_status quip_pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int32_t bits,
+                            uint8_t* packed, hipStream_t stream) {
+  clear_error();
+  QUIP_TRY(check_matrix(codes, m, n, ldc, "quip_pack_codes", "codes"));
+  if (!packed) return fail(QUIP_ERR_ARG, "quip_pack_codes: packed is null");
+  if (bits < 1 || bits > 8) return fail(QUIP_ERR_ARG, "quip_pack_codes: bits must be in [1, 8]");
+  return pack_codes(codes, m, n, ldc, bits, packed, stream);
+}
+
+quip_status quip_packed_row_bytes(int64_t n, int32_t bits, int64_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(QUIP_ERR_ARG, "quip_packed_row_bytes: bytes is null");
+  if (n <= 0) return fail(QUIP_ERR_ARG, "quip_packed_row_bytes: n must be positive");
+  if (bits < 1 || bits > 8) return fail(QUIP_ERR_ARG, "quip_packed_row_bytes: bits must be in [1, 8]");
+  *bytes = (n * code_container_bits(bits) + 7) / 8;
+  return QUIP_OK;
+}
+
+quip_status quip_qmatvec_rht_workspace(int64_t m, int64_t n, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(QUIP_ERR_ARG, "quip_qmatvec_rht_workspace: bytes is null");
+  if (m <= 0 || n <= 0) return fail(QUIP_ERR_ARG, "quip_qmatvec_rht_workspace: sizes must be positive");
+  *bytes = qmatvec_workspace_bytes(m, n);
+  return QUIP_OK;
+}
+
+quip_status quip_qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int32_t bits,
+                             const float* scales, const float* signs_left,
+                             const float* signs_right, const float* x, float* y, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  const char* who = "quip_qmatvec_rht";
+  if (!packed || !scales || !signs_left || !signs_right || !x || !y)
+    return fail(QUIP_ERR_ARG, std::string(who) + ": null pointer");
+  if (bits < 1 || bits > 8) return fail(QUIP_ERR_ARG, std::string(who) + ": bits must be in [1, 8]");
+  if (!is_pow2(m) || m < 2 || m > 16384)
+    return fail(QUIP_ERR_SHAPE, std::string(who) + ": m must be a power of two in [2, 16384]");
+  if (!is_pow2(n) || n < 1024 || n > 16384)
+    return fail(QUIP_ERR_SHAPE, std::string(who) + ": n must be a power of two in [1024, 16384]");
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(y) || !aligned16(signs_left) ||
+      !aligned16(signs_right))
+    return fail(QUIP_ERR_ARG, std::string(who) + ": packed, x, y and the signs must be 16-byte aligned");
+  QUIP_TRY(check_ws(ws, ws_bytes, qmatvec_workspace_bytes(m, n), who));
+  return qmatvec_rht(packed, m, n, bits, scales, signs_left, signs_right, x, y, ws, ws_bytes,
+                     stream);
+}
+
 quip_status quip_proxy_loss_workspace(int64_t m, int64_t n, size_t* bytes) {
   clear_error();
   if (!bytes) return fail(QUIP_ERR_ARG, "quip_proxy_loss_workspace: bytes is null");

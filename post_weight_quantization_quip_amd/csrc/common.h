@@ -109,6 +109,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return start + local;
 }
 
+// ---------------------------------------------------------------- inference (qmatvec.hip)
+
+int code_container_bits(int bits);
+quip_status pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, int bits,
+                       uint8_t* packed, hipStream_t s);
+size_t qmatvec_workspace_bytes(int64_t m, int64_t n);
+quip_status qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int bits, const float* scales,
+                        const float* signs_left, const float* signs_right, const float* x,
+                        float* y, void* ws, size_t ws_bytes, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMM (gemm.hip)
 
 enum GemmEpi {

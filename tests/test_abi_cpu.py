@@ -126,3 +126,31 @@ def test_e8_codebook_matches_oracle_enumeration():
     cb = Q.quip_e8_codebook().numpy().astype(np.float64)
     assert np.array_equal(cb, O.e8_codebook())
     assert N.lib.quip_e8_codebook(None) == N.QUIP_ERR_ARG
+
+
+def test_packed_codes_and_inference_product_validation():
+    lib = N.lib
+    # row sizes: 2-, 4- or 8-bit containers
+    assert [Q.quip_packed_row_bytes(13, b) for b in (1, 2, 3, 4, 5, 8)] == [4, 4, 7, 7, 13, 13]
+    out = ctypes.c_int64(0)
+    assert lib.quip_packed_row_bytes(13, 0, ctypes.byref(out)) == N.QUIP_ERR_ARG
+    assert lib.quip_packed_row_bytes(0, 2, ctypes.byref(out)) == N.QUIP_ERR_ARG
+    assert lib.quip_pack_codes(fake(), 4, 16, 8, 2, fake(), None) == N.QUIP_ERR_ARG  # ldc < n
+    assert lib.quip_pack_codes(fake(), 4, 16, 16, 9, fake(), None) == N.QUIP_ERR_ARG
+    assert lib.quip_pack_codes(fake(), 4, 16, 16, 2, None, None) == N.QUIP_ERR_ARG
+    ws = ctypes.c_size_t(0)
+    assert lib.quip_qmatvec_rht_workspace(4096, 4096, ctypes.byref(ws)) == N.QUIP_OK
+    assert ws.value >= 4 * (4096 + 4096)
+    big = fake(0x100000)
+
+    def call(m, n, bits, x=fake(), wsp=big, wsb=1 << 20):
+        return lib.quip_qmatvec_rht(fake(), m, n, bits, fake(), fake(), fake(), x, fake(), wsp, wsb,
+                                    None)
+    assert call(6, 1024, 2) == N.QUIP_ERR_SHAPE        # m not a power of two
+    assert call(64, 512, 2) == N.QUIP_ERR_SHAPE        # n below 1024
+    assert call(64, 32768, 2) == N.QUIP_ERR_SHAPE      # n above 16384
+    assert call(64, 1024, 0) == N.QUIP_ERR_ARG         # bits
+    assert call(64, 1024, 2, x=None) == N.QUIP_ERR_ARG
+    assert call(64, 1024, 2, x=fake(0x1004)) == N.QUIP_ERR_ARG  # x not 16-byte aligned
+    assert call(64, 1024, 2, wsb=16) == N.QUIP_ERR_WORKSPACE
+    assert call(64, 1024, 2, wsp=fake(0x100010)) == N.QUIP_ERR_WORKSPACE  # not 256-byte aligned

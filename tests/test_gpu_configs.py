@@ -211,6 +211,17 @@ def test_config_uniform(name):
     back = O.incoherence_side(side_cols(L.left, cfg.m, ri) @ host(b["What_t"]).astype(np.float64),
                               "right", L.right, inverse=True)
     assert P.rel_rows(host(b["What"])[ri], back) <= 1e-5
+    # inference: the packed codes and scales of this pass times a vector equal
+    # the post-processed layer W^ times that vector
+    if "signs" in L.left and "signs" in L.right and cfg.n >= 1024:
+        packed = torch.empty((cfg.m, Q.quip_packed_row_bytes(cfg.n, cfg.bits)), dtype=torch.uint8,
+                             device=DEV)
+        Q.quip_pack_codes(b["codes"], cfg.bits, packed)
+        x = torch.from_numpy(wl.gaussian_rows(77, 1, cfg.n)[0]).to(DEV)
+        y = torch.empty(cfg.m, device=DEV)
+        Q.quip_qmatvec_rht(packed, cfg.n, cfg.bits, b["scales"], lp.left.signs, lp.right.signs, x, y)
+        ref = (b["What"].double() @ x.double()).cpu().numpy()
+        assert np.linalg.norm(host(y) - ref) <= 1e-5 * np.linalg.norm(ref)
 
 
 def test_config_e8():

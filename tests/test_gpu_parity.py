@@ -558,3 +558,51 @@ def test_e8_gaussian_source_mse(codebook):
     assert 2.0 ** -4 <= mse < scalar
     assert abs(mse - mse_oracle) <= 0.005
     assert 0 < int(np.argmin(el)) < 31
+
+
+# ------------------------------------------------------------------ inference product
+
+@pytest.mark.parametrize("m,n,bits", [(3, 5, 2), (7, 37, 3), (16, 1024, 2), (5, 33, 1), (9, 19, 4),
+                                      (4, 7, 8)])
+def test_pack_codes_bit_exact(m, n, bits):
+    codes = rng(m * n + bits).integers(0, 1 << bits, size=(m, n)).astype(np.uint8)
+    rb = Q.quip_packed_row_bytes(n, bits)
+    packed = torch.zeros((m, rb), dtype=torch.uint8, device=DEV)
+    Q.quip_pack_codes(torch.from_numpy(codes).to(DEV), bits, packed)
+    assert np.array_equal(host(packed), O.pack_codes(codes, bits))
+
+
+def qmatvec_gpu(codes, scales, bits, sl, sr, x):
+    m, n = codes.shape
+    packed = torch.empty((m, Q.quip_packed_row_bytes(n, bits)), dtype=torch.uint8, device=DEV)
+    Q.quip_pack_codes(torch.from_numpy(codes).to(DEV), bits, packed)
+    y = torch.empty(m, device=DEV)
+    Q.quip_qmatvec_rht(packed, n, bits, dev(scales), dev(sl), dev(sr), dev(x), y)
+    return host(y).astype(np.float64)
+
+
+@pytest.mark.parametrize("m,n,bits", [(256, 1024, 2), (1024, 4096, 2), (64, 2048, 3), (128, 8192, 4),
+                                      (32, 16384, 2), (2, 1024, 8), (4096, 1024, 3)])
+def test_qmatvec_rht_parity(m, n, bits):
+    r = rng(m + 3 * n + bits)
+    L = 1 << bits
+    codes = r.integers(0, L, size=(m, n)).astype(np.uint8)
+    scales = np.exp(0.5 * r.standard_normal(m)).astype(np.float32)
+    sl = r.choice([-1.0, 1.0], m).astype(np.float32)
+    sr = r.choice([-1.0, 1.0], n).astype(np.float32)
+    x = r.standard_normal(n).astype(np.float32)
+    y = qmatvec_gpu(codes, scales, bits, sl, sr, x)
+    ref = O.qmatvec_rht(codes, scales, L, sl, sr, x)
+    # float32 sums of n terms: bounded by the product of absolute values
+    xp = O.rht(x.astype(np.float64)[None, :], sr, "right")[0]
+    absprod = np.abs(O.uniform_level(codes, scales[:, None], L)) @ np.abs(xp)
+    assert np.linalg.norm(y - ref) <= 1e-5 * np.linalg.norm(ref)
+    assert np.linalg.norm(y - ref) <= 2e-6 * np.sqrt(n) * np.linalg.norm(absprod)
+
+
+def test_qmatvec_rht_rejects_unsupported_shapes():
+    z = torch.zeros(1024, device=DEV)
+    packed = torch.zeros((6, 256), dtype=torch.uint8, device=DEV)
+    with pytest.raises(Q.QuipError, match="QUIP_ERR_SHAPE"):  # m = 6 is not a power of two
+        Q.quip_qmatvec_rht(packed, 1024, 2, torch.ones(6, device=DEV), torch.ones(8, device=DEV),
+                           z, z, torch.empty(6, device=DEV))
