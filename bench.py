@@ -397,6 +397,59 @@ def main():
                    "printed_tcq_256d": [0.068, 0.071], "vectors": nvec, "ms": round(g_ms, 3),
                    "candidate_distances_per_s": round(nvec * 65536 * 32 / (g_ms / 1e3), 1)}
 
+    # Inference with the quantized layer, y = Q_L^T W^~ Q_R x: the pass's own
+    # codes packed at 2 bits, then 16384 x 16384 layers of random codes at 2 and
+    # 4 bits, four distinct copies cycled so that the packed codes read per
+    # cycle (256 or 512 MB) exceed the 256 MB last-level cache
+    inference = {}
+    if left.is_rht and right.is_rht:
+        def qmv_case(codes_list, scales, sl, sr, bits, reps):
+            m, n = codes_list[0].shape
+            rb = Q.quip_packed_row_bytes(n, bits)
+            packs = []
+            for c in codes_list:
+                p = torch.empty((m, rb), dtype=torch.uint8, device=dev)
+                Q.quip_pack_codes(c, bits, p)
+                packs.append(p)
+            x = torch.from_numpy(wl.gaussian_rows(7, 1, n)[0]).to(dev)
+            y = torch.empty(m, device=dev)
+            ws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_qmatvec_rht_workspace, m, n),
+                                     dev)
+            it = [0]
+
+            def call():
+                Q.quip_qmatvec_rht(packs[it[0] % len(packs)], n, bits, scales, sl, sr, x, y, ws=ws)
+                it[0] += 1
+            ms = timed(call, reps)
+            Q.timing_reset()
+            Q.timing_enable(True)
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            Q.timing_enable(False)
+            launches, kms, _, kbytes = Q.timing_report()["qmatvec_kernel"]
+            Q.timing_reset()
+            gbps = kbytes / (kms / 1e3) / 1e9
+            return {"m": m, "n": n, "bits": bits, "packed_MB": round(m * rb / 1e6, 2),
+                    "copies": len(packs), "product_us": round(1e3 * ms, 2),
+                    "qmatvec_kernel_us": round(1e3 * kms / launches, 2),
+                    "qmatvec_kernel_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 3),
+                    "weights_per_s": round(m * n / (ms / 1e3), 1)}
+
+        inference["pass_layer"] = qmv_case([lp.buffers["codes"]], lp.buffers["scales"], left.signs,
+                                           right.signs, cfg.bits, 50)
+        big = 16384
+        gen = torch.Generator(device=dev).manual_seed(11)
+        sgn = lambda: (torch.randint(0, 2, (big,), device=dev, generator=gen).float() * 2 - 1)
+        bsl, bsr = sgn(), sgn()
+        bsc = torch.rand(big, device=dev, generator=gen) + 0.5
+        for bits in (2, 4):
+            cl = [torch.randint(0, 1 << bits, (big, big), dtype=torch.uint8, device=dev, generator=gen)
+                  for _ in range(4)]
+            inference[f"{big}x{big}_{bits}bit"] = qmv_case(cl, bsc, bsl, bsr, bits, 40)
+            del cl
+        torch.cuda.empty_cache()
+
     line = {
         "metric": "quantized weights/sec for a 4096x4096 layer (LDLQ+RHT, 2-bit); RHT GB/s",
         "value": round(value, 1),
@@ -417,6 +470,7 @@ def main():
         "weights_per_s_from_resident_H_W": round(mn / (from_resident / 1e3), 1),
         "rht": rht,
         "gaussian_vq": gaussian_vq,
+        "inference": inference,
         "roofline": roofline,
         "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])),
     }
