@@ -154,12 +154,53 @@ def kron_apply(A, K1, K2, side: str, inverse: bool = False) -> np.ndarray:
     raise ValueError(side)
 
 
+def permute_gather(A, rows=None, cols=None) -> np.ndarray:
+    """out[i][j] = A[rows[i]][cols[j]] (an absent index list is the identity).
+    With P_p the permutation matrix (P_p x)_i = x_{p(i)}, this is
+    P_rows A P_cols^T."""
+    A = np.asarray(A)
+    out = A if rows is None else A[np.asarray(rows, dtype=np.int64), :]
+    return out if cols is None else out[:, np.asarray(cols, dtype=np.int64)]
+
+
+def permute_scatter(A, rows=None, cols=None) -> np.ndarray:
+    """out[rows[i]][cols[j]] = A[i][j]: the inverse of ``permute_gather``,
+    i.e. P_rows^T A P_cols."""
+    A = np.asarray(A)
+    out = np.empty_like(A)
+    r = np.arange(A.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    c = np.arange(A.shape[1]) if cols is None else np.asarray(cols, dtype=np.int64)
+    out[np.ix_(r, c)] = A
+    return out
+
+
+def diag_order(H) -> np.ndarray:
+    """LDLQ-RG's quantization order, [QuIP] "Experiments / Methods" (the
+    weights re-ordered by diag(H)): column indices by decreasing H_jj, equal
+    values in increasing index (a reading: the pages give no direction or tie
+    rule). Position k of the result is the column quantized k-th."""
+    d = np.diag(np.asarray(H, dtype=F64))
+    return np.array(sorted(range(d.size), key=lambda j: (-d[j], j)), dtype=np.int32)
+
+
 def incoherence_side(A, side: str, spec: dict, inverse: bool = False) -> np.ndarray:
     """One side of incoherence processing with either a sign vector
-    (``{"signs": s}``, RHT) or two Kronecker factors (``{"A": K1, "B": K2}``)."""
+    (``{"signs": s}``, RHT) or two Kronecker factors (``{"A": K1, "B": K2}``),
+    optionally composed with a random permutation ``"perm": p`` of the
+    coordinates ([QuIP] "Further Ablation", Table 5: a permutation step inside
+    the fast orthogonal multiplication). With K the sign/Kronecker transform
+    the side's orthogonal matrix is Q = K P_p: the coordinates are permuted
+    first, then mixed. Left: Q A (inverse Q^T A); right: A Q^T (inverse A Q)."""
+    perm = spec.get("perm")
+    if not inverse and perm is not None:
+        A = permute_gather(A, rows=perm) if side == "left" else permute_gather(A, cols=perm)
     if "signs" in spec:
-        return (rht_inv if inverse else rht)(A, spec["signs"], side)
-    return kron_apply(A, spec["A"], spec["B"], side, inverse=inverse)
+        out = (rht_inv if inverse else rht)(A, spec["signs"], side)
+    else:
+        out = kron_apply(A, spec["A"], spec["B"], side, inverse=inverse)
+    if inverse and perm is not None:
+        out = permute_scatter(out, rows=perm) if side == "left" else permute_scatter(out, cols=perm)
+    return out
 
 
 def incoherence_H(H, right_spec: dict) -> np.ndarray:
@@ -641,16 +682,29 @@ def qmatvec_rht(codes, scales, L: int, signs_left, signs_right, x) -> np.ndarray
 
 def quantize_layer(W, X, left_spec: dict, right_spec: dict, *, quant: str = "uniform",
                    bits: int = 2, g: int = 1, alpha: float = 0.01, ncand: int = 32,
-                   codebook=None, use_cholesky: bool = False) -> dict:
+                   codebook=None, use_cholesky: bool = False, rg_order: bool = False) -> dict:
     """Hessian -> damping -> incoherence -> LDL -> scale -> LDLQ -> post-processing,
     returning every intermediate. ``quant`` is "uniform" (2^bits-level grid,
     per-row scale) or "e8" (rows of W~ normalized to unit RMS, one global scale,
-    BlockLDLQ with g = 8)."""
+    BlockLDLQ with g = 8).
+
+    ``rg_order``: LDLQ-RG's re-ordering by diag(H) ([QuIP] "Experiments /
+    Methods"; its further greedy passes are not described there and are not
+    done). The order r = ``diag_order(H~)`` is taken after incoherence
+    processing; H~ and W~ become P_r H~ P_r^T and W~ P_r^T, the LDL, the scales,
+    LDLQ, the codes and W^~ are in that order, and the post-processing scatters
+    W^~'s columns back (W^~ P_r) before the inverse transforms. "Ht", "Wt" and
+    "What_t" are returned in the quantization order, with "order"."""
     H = damp(proxy_hessian(X), alpha)
     Ht = incoherence_H(H, right_spec)
     Wt = incoherence_W(W, left_spec, right_spec)
+    order = None
+    if rg_order:
+        order = diag_order(Ht)
+        Ht = permute_gather(Ht, rows=order, cols=order)
+        Wt = permute_gather(Wt, cols=order)
     U, D = (udu_cholesky if use_cholesky else udu)(Ht, g)
-    out = {"H": H, "Ht": Ht, "Wt": Wt, "U": U, "D": D}
+    out = {"H": H, "Ht": Ht, "Wt": Wt, "U": U, "D": D, "order": order}
     if quant == "uniform":
         L = 1 << bits
         s, choice, _ = uniform_scale_search(Wt, L, ncand)
@@ -668,7 +722,8 @@ def quantize_layer(W, X, left_spec: dict, right_spec: dict, *, quant: str = "uni
     else:
         raise ValueError(quant)
     out["What_t"] = What_t
-    out["What"] = incoherence_W_inv(What_t, left_spec, right_spec)
+    back = What_t if order is None else permute_scatter(What_t, cols=order)
+    out["What"] = incoherence_W_inv(back, left_spec, right_spec)
     out["loss_t"] = proxy_loss(Wt, What_t, Ht)
     out["loss"] = proxy_loss(W, out["What"], H)
     return out

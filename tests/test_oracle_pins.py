@@ -519,3 +519,111 @@ def test_qmatvec_rht_equals_the_dense_layer(m, n, bits):
     QL = O.sylvester(m) * sl[None, :] / np.sqrt(m)
     QR = O.sylvester(n) * sr[None, :] / np.sqrt(n)
     assert np.allclose(y, QL.T @ What_t @ QR @ x, rtol=0, atol=tol)
+
+
+# ---------------------------------------------------------------- QuIP variants: permutations
+
+def perm_matrix(p):
+    """(P x)_i = x_{p(i)}: row i of P is e_{p(i)}."""
+    return np.eye(len(p))[np.asarray(p)]
+
+
+def test_permute_gather_and_scatter_are_permutation_matrix_products():
+    r = rng(41)
+    A = r.standard_normal((5, 7))
+    pr = r.permutation(5)
+    pc = r.permutation(7)
+    Pr, Pc = perm_matrix(pr), perm_matrix(pc)
+    assert np.array_equal(O.permute_gather(A, pr, pc), Pr @ A @ Pc.T)
+    assert np.array_equal(O.permute_scatter(A, pr, pc), Pr.T @ A @ Pc)
+    assert np.array_equal(O.permute_scatter(O.permute_gather(A, pr, pc), pr, pc), A)
+    assert np.array_equal(O.permute_gather(A, cols=pc), A @ Pc.T)
+    assert np.array_equal(O.permute_gather(A, rows=pr), Pr @ A)
+    # element by element for one entry
+    assert O.permute_gather(A, pr, pc)[2, 3] == A[pr[2], pc[3]]
+    assert O.permute_scatter(A, pr, pc)[pr[2], pc[3]] == A[2, 3]
+
+
+@pytest.mark.parametrize("kind", ["rht", "kron"])
+@pytest.mark.parametrize("side", ["left", "right"])
+def test_permutation_inside_the_orthogonal_multiply_is_K_times_P(kind, side):
+    r = rng(43)
+    d = 16 if kind == "rht" else 12
+    if kind == "rht":
+        s = np.where(r.random(d) < 0.5, -1.0, 1.0)
+        K = O.sylvester(d) @ np.diag(s) / np.sqrt(d)
+        spec = {"signs": s}
+    else:
+        K1 = np.linalg.qr(r.standard_normal((3, 3)))[0]
+        K2 = np.linalg.qr(r.standard_normal((4, 4)))[0]
+        K = np.kron(K1, K2)
+        spec = {"A": K1, "B": K2}
+    spec["perm"] = r.permutation(d)
+    Q = K @ perm_matrix(spec["perm"])
+    assert np.allclose(Q @ Q.T, np.eye(d), atol=1e-13)
+    A = r.standard_normal((d, d)) if side == "left" else r.standard_normal((5, d))
+    want = Q @ A if side == "left" else A @ Q.T
+    got = O.incoherence_side(A, side, spec)
+    assert np.allclose(got, want, atol=1e-12)
+    inv_want = Q.T @ A if side == "left" else A @ Q
+    assert np.allclose(O.incoherence_side(A, side, spec, inverse=True), inv_want, atol=1e-12)
+    # without the permutation the result differs (the step is not a no-op)
+    plain = {k: v for k, v in spec.items() if k != "perm"}
+    assert not np.allclose(O.incoherence_side(A, side, plain), want)
+
+
+def test_diag_order_hand_worked_with_ties():
+    # diag 2, 5, 5, 1, 3 -> decreasing, equal values by index: 1, 2, 4, 0, 3
+    H = np.diag([2.0, 5.0, 5.0, 1.0, 3.0])
+    assert O.diag_order(H).tolist() == [1, 2, 4, 0, 3]
+
+
+def test_diag_order_is_the_rank_count():
+    r = rng(47)
+    d = r.integers(0, 6, 40).astype(np.float64)  # many ties
+    H = np.diag(d) + 0.01 * np.ones((40, 40))
+    o = O.diag_order(H)
+    hd = np.diag(H)
+    # position of j = #{i : d_i > d_j} + #{i < j : d_i == d_j}
+    for j in range(40):
+        rank = int(np.sum(hd > hd[j]) + np.sum(hd[:j] == hd[j]))
+        assert o[rank] == j
+    assert sorted(o.tolist()) == list(range(40))
+
+
+def test_rg_order_pass_loss_in_both_domains_and_sorted_diagonal():
+    cfg = wl.custom_config("rg", 901, 16, 32, 256, left=wl.RHT, right=wl.KRON(4, 8, perm=True),
+                           bits=2, rg_order=True)
+    L = wl.make_layer(cfg)
+    assert sorted(L.right["perm"].tolist()) == list(range(32))
+    r = O.quantize_layer(L.W, L.X, L.left, L.right, quant="uniform", bits=2, rg_order=True)
+    dg = np.diag(r["Ht"])
+    assert np.all(np.diff(dg) <= 0)
+    # a wrong scatter back would scramble W^ and break this equality (the
+    # float32-drawn Kronecker factors are orthogonal to ~1e-7 only)
+    assert np.isclose(r["loss_t"], r["loss"], rtol=1e-6)
+    # the order is a relabelling: H~ in quantization order is P_r H~ P_r^T
+    Ht0 = O.incoherence_H(r["H"], L.right)
+    assert np.allclose(r["Ht"], perm_matrix(r["order"]) @ Ht0 @ perm_matrix(r["order"]).T)
+
+
+def test_rg_order_on_an_already_sorted_diagonal_changes_nothing():
+    r = rng(53)
+    n = 16
+    # column scales halving from column to column: diag(H) falls by ~4x per
+    # column, far beyond the sampling noise of 64 calibration rows
+    Xc = r.standard_normal((64, n)) * 0.5 ** np.arange(n)[None, :]
+    W = r.standard_normal((6, n))
+    ident = {"A": np.eye(1), "B": np.eye(n)}  # identity transform: diag(H~) = diag(H)
+    a = O.quantize_layer(W, Xc, {"A": np.eye(1), "B": np.eye(6)}, ident, bits=2)
+    b = O.quantize_layer(W, Xc, {"A": np.eye(1), "B": np.eye(6)}, ident, bits=2, rg_order=True)
+    assert np.array_equal(b["order"], np.arange(n))
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["What"], b["What"])
+    # reversed column scales: the order is reversed, and the pass equals the
+    # natural-order pass on the column-reversed layer, scattered back
+    Xr = Xc[:, ::-1].copy()
+    c = O.quantize_layer(W[:, ::-1].copy(), Xr, {"A": np.eye(1), "B": np.eye(6)}, ident, bits=2,
+                         rg_order=True)
+    assert np.array_equal(c["order"], np.arange(n)[::-1])
+    assert np.array_equal(c["codes"], a["codes"])
+    assert np.allclose(c["What"], a["What"][:, ::-1], atol=1e-12)

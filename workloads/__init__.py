@@ -40,6 +40,8 @@ STREAMS = {
     "kron_left_b": 8,
     "kron_right_a": 9,
     "kron_right_b": 10,
+    "perm_left": 11,
+    "perm_right": 12,
 }
 
 
@@ -49,11 +51,13 @@ def rng_for(cfg_id: int, stream: int) -> np.random.Generator:
 
 @dataclass(frozen=True)
 class Side:
-    """How one side of W is made incoherent: ``("rht",)`` or ``("kron", p, q)``."""
+    """How one side of W is made incoherent: ``("rht",)`` or ``("kron", p, q)``;
+    ``perm``: a random permutation of the coordinates before the transform."""
 
     kind: str
     p: int = 0
     q: int = 0
+    perm: bool = False
 
     def __post_init__(self):
         if self.kind not in ("rht", "kron", "none"):
@@ -63,8 +67,8 @@ class Side:
 RHT = Side("rht")
 
 
-def KRON(p: int, q: int) -> Side:
-    return Side("kron", p, q)
+def KRON(p: int, q: int, perm: bool = False) -> Side:
+    return Side("kron", p, q, perm)
 
 
 @dataclass(frozen=True)
@@ -85,6 +89,7 @@ class LayerConfig:
     w_outlier_mult: float = 10.0
     w_row_sigma: float = 0.0  # log-normal sigma of per-row std (0: none)
     x_col_sigma: float = 1.0  # log-normal sigma of per-column scale of X
+    rg_order: bool = False  # quantize the columns in decreasing diag(H~) order
     description: str = ""
 
 
@@ -104,6 +109,10 @@ CONFIGS = {
                        description="large 28672x8192, 4-bit, Kron 128x224 left, RHT right"),
     "c4c": LayerConfig("c4c", 43, 8192, 28672, 16384, RHT, KRON(128, 224), "uniform", 4, 256,
                        description="large 8192x28672, 4-bit, RHT left, Kron 128x224 right"),
+    "c3p": LayerConfig("c3p", 33, 4096, 11008, 8192, RHT, KRON(64, 172, perm=True), "uniform", 3,
+                       128, rg_order=True,
+                       description="MLP 4096x11008, 3-bit, RHT left, Kron 64x172 right with a random "
+                                   "permutation, LDLQ-RG order"),
     "c5": LayerConfig("c5", 5, 4096, 4096, 4096, RHT, RHT, "e8", 2, 128, g=8,
                       description="vector BlockLDLQ 4096x4096, E8 2^16 codebook, g=8, B=128"),
 }
@@ -155,15 +164,24 @@ def activations(cfg: LayerConfig, N: Optional[int] = None, n: Optional[int] = No
     return X
 
 
+def random_permutation(rng: np.random.Generator, n: int) -> np.ndarray:
+    """A uniformly random permutation of 0..n-1, as int32."""
+    return rng.permutation(n).astype(np.int32)
+
+
 def side_inputs(cfg: LayerConfig, side: Side, dim: int, which: str) -> dict:
     if side.kind == "rht":
-        return {"signs": rademacher(rng_for(cfg.cfg_id, STREAMS[f"sign_{which}"]), dim)}
-    if side.kind == "kron":
+        out = {"signs": rademacher(rng_for(cfg.cfg_id, STREAMS[f"sign_{which}"]), dim)}
+    elif side.kind == "kron":
         if side.p * side.q != dim:
             raise ValueError(f"kron {side.p}x{side.q} does not match dimension {dim}")
-        return {"A": haar_orthogonal(rng_for(cfg.cfg_id, STREAMS[f"kron_{which}_a"]), side.p),
-                "B": haar_orthogonal(rng_for(cfg.cfg_id, STREAMS[f"kron_{which}_b"]), side.q)}
-    return {}
+        out = {"A": haar_orthogonal(rng_for(cfg.cfg_id, STREAMS[f"kron_{which}_a"]), side.p),
+               "B": haar_orthogonal(rng_for(cfg.cfg_id, STREAMS[f"kron_{which}_b"]), side.q)}
+    else:
+        return {}
+    if side.perm:
+        out["perm"] = random_permutation(rng_for(cfg.cfg_id, STREAMS[f"perm_{which}"]), dim)
+    return out
 
 
 def make_layer(name_or_cfg, with_x: bool = True) -> Layer:
