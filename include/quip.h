@@ -326,6 +326,46 @@ quip_status quip_qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int32_
                              size_t ws_bytes, hipStream_t stream);
 
 /*
+ * quip_permute -- moves the rows and columns of a matrix by index vectors:
+ * the permutation step inside the fast orthogonal multiplication ([QuIP]
+ * "Further Ablation", Table 5: the side transform becomes Q = K P, the
+ * coordinates permuted before they are mixed) and LDLQ-RG's re-ordering of the
+ * weights ([QuIP] "Experiments / Methods").
+ *   scatter = 0 (gather): out[i][j] = A[row_index[i]][col_index[j]], i.e.
+ *     out = P_r A P_c^T with (P_p x)_i = x_{p(i)}.
+ *   scatter = 1: out[row_index[i]][col_index[j]] = A[i][j], i.e.
+ *     out = P_r^T A P_c (the inverse of the gather with the same vectors).
+ *   A, out: rows x cols float32 (device), leading dims lda, ldo >= cols; they
+ *     must not overlap (no in-place use).
+ *   row_index: rows int32 (device) or NULL (identity); col_index: cols int32
+ *     (device) or NULL (identity). The vectors should be permutations of
+ *     0..rows-1 and 0..cols-1; they are not checked on the host. Gather: an
+ *     index outside the matrix yields NaN. Scatter: an entry with such an index
+ *     is dropped, and entries of out that no index reaches are unspecified.
+ *     No access leaves the matrices either way.
+ * Errors: QUIP_ERR_ARG (null pointer with a non-empty matrix, negative sizes,
+ * leading dimension < cols, overlapping A and out, scatter not 0 or 1),
+ * QUIP_ERR_SHAPE (cols > 32768 with a column index: the row is staged in LDS).
+ */
+quip_status quip_permute(const float* A, int64_t lda, float* out, int64_t ldo, int64_t rows,
+                         int64_t cols, const int32_t* row_index, const int32_t* col_index,
+                         int32_t scatter, hipStream_t stream);
+
+/*
+ * quip_diag_order -- LDLQ-RG's quantization order ([QuIP] "Experiments /
+ * Methods": the weights re-ordered by diag(H)): order[k] is the column
+ * quantized k-th, the columns taken by decreasing H[j][j], equal values by
+ * increasing j (NaN after every number; +0 and -0 equal). Deterministic.
+ *   H: n x n float32 (device), leading dim ldh >= n; only the diagonal is read.
+ *   order: n int32 (device).
+ *   ws: quip_diag_order_workspace(n) bytes, 256-byte aligned.
+ * Errors: QUIP_ERR_ARG (null pointer, n <= 0, ldh < n), QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_diag_order_workspace(int64_t n, size_t* bytes);
+quip_status quip_diag_order(const float* H, int64_t n, int64_t ldh, int32_t* order, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
  * quip_e8_codebook -- fills HOST memory with the 65536 smallest-norm points of
  * the E8 lattice (D8 together with D8 + 1/2) ordered by squared norm, then by
  * coordinates ascending with the first coordinate most significant; 65536 x 8

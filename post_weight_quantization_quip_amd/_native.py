@@ -77,6 +77,10 @@ SYMBOLS = {
     "quip_qmatvec_rht_workspace": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "quip_qmatvec_rht": (c_int, [c_vp, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_sz, c_vp]),
+    "quip_permute": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, ctypes.c_int32,
+                             c_vp]),
+    "quip_diag_order_workspace": (c_int, [c_i64, ctypes.POINTER(c_sz)]),
+    "quip_diag_order": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "quip_timing_enable": (c_int, [c_int]),
     "quip_timing_reset": (c_int, []),
     "quip_timing_report": (c_int, [ctypes.c_char_p, c_sz, ctypes.POINTER(c_sz)]),
@@ -262,6 +266,23 @@ def quip_qmatvec_rht(packed, n: int, bits: int, scales, signs_left, signs_right,
                                 _p(signs_right), _p(x), _p(y), _p(ws),
                                 0 if ws is None else ws.numel(), _stream(stream)),
            "quip_qmatvec_rht")
+
+
+def quip_permute(A, out, row_index=None, col_index=None, scatter: bool = False, stream=None):
+    """Gather out = A[row_index][:, col_index], or scatter out[row_index][:, col_index] = A
+    (int32 index tensors on the device; None is the identity)."""
+    r, c = A.shape
+    _check(lib.quip_permute(_p(A), _ld(A), _p(out), _ld(out), r, c, _p(row_index), _p(col_index),
+                            int(scatter), _stream(stream)), "quip_permute")
+
+
+def quip_diag_order(H, order, stream=None, ws=None):
+    """order = the columns of H by decreasing H[j][j], ties by index (int32)."""
+    n = H.shape[0]
+    if ws is None:
+        ws = _workspace(_ws_query(lib.quip_diag_order_workspace, n), H.device)
+    _check(lib.quip_diag_order(_p(H), n, _ld(H), _p(order), _p(ws), 0 if ws is None else ws.numel(),
+                               _stream(stream)), "quip_diag_order")
 
 
 def timing_enable(on: bool = True) -> None:

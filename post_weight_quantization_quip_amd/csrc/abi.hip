@@ -367,6 +367,43 @@ quip_status quip_qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int32_
                      stream);
 }
 
+quip_status quip_permute(const float* A, int64_t lda, float* out, int64_t ldo, int64_t rows,
+                         int64_t cols, const int32_t* row_index, const int32_t* col_index,
+                         int32_t scatter, hipStream_t stream) {
+  clear_error();
+  const char* who = "quip_permute";
+  if (rows < 0 || cols < 0) return fail(QUIP_ERR_ARG, std::string(who) + ": negative size");
+  if (scatter != 0 && scatter != 1) return fail(QUIP_ERR_ARG, std::string(who) + ": scatter must be 0 or 1");
+  if (rows == 0 || cols == 0) return QUIP_OK;
+  if (!A || !out) return fail(QUIP_ERR_ARG, std::string(who) + ": null matrix");
+  if (lda < cols || ldo < cols)
+    return fail(QUIP_ERR_ARG, std::string(who) + ": leading dimension smaller than cols");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t a1 = a0 + sizeof(float) * size_t((rows - 1) * lda + cols);
+  const uintptr_t o1 = o0 + sizeof(float) * size_t((rows - 1) * ldo + cols);
+  if (a0 < o1 && o0 < a1) return fail(QUIP_ERR_ARG, std::string(who) + ": A and out overlap");
+  if (col_index && cols > permute_max_cols())
+    return fail(QUIP_ERR_SHAPE, std::string(who) + ": at most 32768 columns with a column index");
+  return permute(A, lda, out, ldo, rows, cols, row_index, col_index, scatter != 0, stream);
+}
+
+quip_status quip_diag_order_workspace(int64_t n, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(QUIP_ERR_ARG, "quip_diag_order_workspace: bytes is null");
+  if (n <= 0) return fail(QUIP_ERR_ARG, "quip_diag_order_workspace: n must be positive");
+  *bytes = diag_order_workspace_bytes(n);
+  return QUIP_OK;
+}
+
+quip_status quip_diag_order(const float* H, int64_t n, int64_t ldh, int32_t* order, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  QUIP_TRY(check_matrix(H, n, n, ldh, "quip_diag_order", "H"));
+  if (!order) return fail(QUIP_ERR_ARG, "quip_diag_order: order is null");
+  QUIP_TRY(check_ws(ws, ws_bytes, diag_order_workspace_bytes(n), "quip_diag_order"));
+  return diag_order(H, n, ldh, order, ws, ws_bytes, stream);
+}
+
 quip_status quip_proxy_loss_workspace(int64_t m, int64_t n, size_t* bytes) {
   clear_error();
   if (!bytes) return fail(QUIP_ERR_ARG, "quip_proxy_loss_workspace: bytes is null");

@@ -119,6 +119,16 @@ quip_status qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int bits, c
                         const float* signs_left, const float* signs_right, const float* x,
                         float* y, void* ws, size_t ws_bytes, hipStream_t s);
 
+// ---------------------------------------------------------------- permutations (permute.hip)
+
+int64_t permute_max_cols();
+quip_status permute(const float* A, int64_t lda, float* out, int64_t ldo, int64_t rows,
+                    int64_t cols, const int32_t* ridx, const int32_t* cidx, bool scatter,
+                    hipStream_t s);
+size_t diag_order_workspace_bytes(int64_t n);
+quip_status diag_order(const float* H, int64_t n, int64_t ldh, int32_t* order, void* ws,
+                       size_t ws_bytes, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMM (gemm.hip)
 
 enum GemmEpi {

@@ -11,6 +11,15 @@ allocates buffers once and sequences the calls on one HIP stream):
                                                   loss tr((W^~ - W~) H~ (W^~ - W~)^T)
                                                   per row and summed
   quip_rht2_inv / quip_kron_orth_inv              W^ = U^T W^~ V
+
+Variants ([QuIP] "Further Ablation" and "Experiments / Methods"):
+  * a side with a permutation p: its transform is K P_p. quip_permute gathers
+    the coordinates before the transform (H on both sides, W on that side)
+    and scatters them back after the inverse transform;
+  * rg_order (LDLQ-RG's order): quip_diag_order gives the order of decreasing
+    diag(H~); quip_permute gathers H~ (both sides) and W~'s columns in that
+    order before the LDL, and scatters W^~'s columns back before the inverse
+    transforms. H, Wt, What_t, codes and scales stay in quantization order.
 """
 from __future__ import annotations
 
@@ -28,6 +37,7 @@ class SideSpec:
     signs: torch.Tensor | None = None
     F1: torch.Tensor | None = None
     F2: torch.Tensor | None = None
+    perm: torch.Tensor | None = None  # int32: coordinates permuted before the transform
 
     @property
     def is_rht(self) -> bool:
@@ -35,10 +45,15 @@ class SideSpec:
 
     @staticmethod
     def from_numpy(spec: dict, device) -> "SideSpec":
+        perm = None
+        if spec.get("perm") is not None:
+            perm = torch.as_tensor(spec["perm"], dtype=torch.int32).to(device).contiguous()
         if "signs" in spec:
-            return SideSpec(signs=torch.as_tensor(spec["signs"], dtype=torch.float32).to(device))
+            return SideSpec(signs=torch.as_tensor(spec["signs"], dtype=torch.float32).to(device),
+                            perm=perm)
         return SideSpec(F1=torch.as_tensor(spec["A"], dtype=torch.float32).to(device).contiguous(),
-                        F2=torch.as_tensor(spec["B"], dtype=torch.float32).to(device).contiguous())
+                        F2=torch.as_tensor(spec["B"], dtype=torch.float32).to(device).contiguous(),
+                        perm=perm)
 
 
 def apply_side(A: torch.Tensor, out: torch.Tensor, side: int, spec: SideSpec, inverse: bool,
@@ -79,6 +94,7 @@ class LayerPass:
     n_cand: int = 32
     device: str = "cuda"
     codebook: torch.Tensor | None = None
+    rg_order: bool = False
     buffers: dict = field(default_factory=dict)
 
     def __post_init__(self):
@@ -104,6 +120,14 @@ class LayerPass:
         b["What"] = torch.empty((m, n), **f32)
         b["loss"] = torch.zeros(1, dtype=torch.float64, device=dev)
         b["row_loss"] = torch.zeros(m, dtype=torch.float64, device=dev)
+        self.side_perm = self.left.perm is not None or self.right.perm is not None
+        if self.right.perm is not None or self.rg_order:
+            b["Htmp"] = torch.empty((n, n), **f32)
+        if self.side_perm or self.rg_order:
+            b["Wtmp"] = torch.empty((m, n), **f32)
+        if self.rg_order:
+            b["order"] = torch.empty(n, dtype=torch.int32, device=dev)
+            b["ws_order"] = N._workspace(N._ws_query(N.lib.quip_diag_order_workspace, n), dev)
         # workspaces, sized once
         need = [256]
         need.append(N._ws_query(N.lib.quip_ldl_workspace, n, self.g))
@@ -138,9 +162,25 @@ class LayerPass:
         N.quip_hessian(X, b["H"], accumulate=False, stream=stream, ws=self._hessian_ws(X.shape[0]))
         N.quip_hessian_finalize(b["H"], X.shape[0], self.alpha, stream=stream, ws=ws)
         mark("incoherence_H")
-        apply_two_sided(b["H"], b["H"], self.right, self.right, False, ws, stream)
+        rp = self.right.perm
+        if rp is not None:  # V = K P: permute both sides of H, then transform
+            N.quip_permute(b["H"], b["Htmp"], rp, rp, stream=stream)
+            apply_two_sided(b["Htmp"], b["H"], self.right, self.right, False, ws, stream)
+        else:
+            apply_two_sided(b["H"], b["H"], self.right, self.right, False, ws, stream)
+        if self.rg_order:
+            N.quip_diag_order(b["H"], b["order"], stream=stream, ws=b["ws_order"])
+            N.quip_permute(b["H"], b["Htmp"], b["order"], b["order"], stream=stream)
+            b["H"], b["Htmp"] = b["Htmp"], b["H"]
         mark("incoherence_W")
-        apply_two_sided(W, b["Wt"], self.left, self.right, False, ws, stream)
+        if self.side_perm:
+            N.quip_permute(W, b["Wtmp"], self.left.perm, rp, stream=stream)
+            apply_two_sided(b["Wtmp"], b["Wt"], self.left, self.right, False, ws, stream)
+        else:
+            apply_two_sided(W, b["Wt"], self.left, self.right, False, ws, stream)
+        if self.rg_order:
+            N.quip_permute(b["Wt"], b["Wtmp"], None, b["order"], stream=stream)
+            b["Wt"], b["Wtmp"] = b["Wtmp"], b["Wt"]
         mark("ldl")
         N.quip_ldl(b["H"], self.g, b["U"], b["D"], b["info"], stream=stream, ws=ws)
         mark("ldlq")
@@ -149,7 +189,14 @@ class LayerPass:
                     b["What_t"], self.codebook, row_loss=b["row_loss"] if with_loss else None,
                     loss=b["loss"] if with_loss else None, stream=stream, ws=ws)
         mark("postprocess")
-        apply_two_sided(b["What_t"], b["What"], self.left, self.right, True, ws, stream)
+        src = b["What_t"]
+        if self.rg_order:  # back to the transformed basis's column order
+            N.quip_permute(src, b["Wtmp"], None, b["order"], scatter=True, stream=stream)
+            src = b["Wtmp"]
+        apply_two_sided(src, b["What"], self.left, self.right, True, ws, stream)
+        if self.side_perm:  # undo the permutations of the sides: P_L^T (.) P_R
+            N.quip_permute(b["What"], b["Wtmp"], self.left.perm, rp, scatter=True, stream=stream)
+            b["What"], b["Wtmp"] = b["Wtmp"], b["What"]
         mark("end")
         return b
 

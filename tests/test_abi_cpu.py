@@ -154,3 +154,23 @@ def test_packed_codes_and_inference_product_validation():
     assert call(64, 1024, 2, x=fake(0x1004)) == N.QUIP_ERR_ARG  # x not 16-byte aligned
     assert call(64, 1024, 2, wsb=16) == N.QUIP_ERR_WORKSPACE
     assert call(64, 1024, 2, wsp=fake(0x100010)) == N.QUIP_ERR_WORKSPACE  # not 256-byte aligned
+
+
+def test_permute_and_diag_order_validation():
+    lib = N.lib
+    A, O_ = fake(0x1000), fake(0x100000)
+    assert lib.quip_permute(A, 8, O_, 8, 0, 8, None, None, 0, None) == N.QUIP_OK  # empty
+    assert lib.quip_permute(A, 8, O_, 8, -1, 8, None, None, 0, None) == N.QUIP_ERR_ARG
+    assert lib.quip_permute(None, 8, O_, 8, 4, 8, None, None, 0, None) == N.QUIP_ERR_ARG
+    assert lib.quip_permute(A, 4, O_, 8, 4, 8, None, None, 0, None) == N.QUIP_ERR_ARG  # lda < cols
+    assert lib.quip_permute(A, 8, O_, 8, 4, 8, None, None, 2, None) == N.QUIP_ERR_ARG  # scatter flag
+    assert lib.quip_permute(A, 8, fake(0x1010), 8, 4, 8, None, None, 0, None) == N.QUIP_ERR_ARG
+    assert lib.quip_permute(A, 40000, O_, 40000, 1, 40000, None, fake(0x5000), 0,
+                            None) == N.QUIP_ERR_SHAPE
+    ws = ctypes.c_size_t(0)
+    assert lib.quip_diag_order_workspace(4096, ctypes.byref(ws)) == N.QUIP_OK
+    assert ws.value >= 4 * 4096 * 8
+    assert lib.quip_diag_order_workspace(0, ctypes.byref(ws)) == N.QUIP_ERR_ARG
+    assert lib.quip_diag_order(A, 16, 8, fake(), fake(0x100000), 1 << 20, None) == N.QUIP_ERR_ARG
+    assert lib.quip_diag_order(A, 16, 16, None, fake(0x100000), 1 << 20, None) == N.QUIP_ERR_ARG
+    assert lib.quip_diag_order(A, 16, 16, fake(), fake(0x100000), 4, None) == N.QUIP_ERR_WORKSPACE

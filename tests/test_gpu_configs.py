@@ -32,22 +32,32 @@ def host(t):
 
 
 def side_rows(spec, d, idx):
-    """Rows `idx` of the d x d orthogonal matrix of one side (float64)."""
+    """Rows `idx` of the d x d orthogonal matrix of one side (float64); with a
+    permutation p the matrix is K P_p, whose row i is row i of K scattered by p."""
     idx = np.asarray(idx)
     if "signs" in spec:
         s = np.asarray(spec["signs"], np.float64)
         j = np.arange(d)
         pc = np.bitwise_count(idx[:, None] & j[None, :])  # Sylvester entry (-1)^popcount(i & j)
-        return np.where(pc % 2 == 1, -1.0, 1.0) * s[None, :] / np.sqrt(d)
-    K1 = np.asarray(spec["A"], np.float64)
-    K2 = np.asarray(spec["B"], np.float64)
-    q = K2.shape[0]
-    return np.stack([np.kron(K1[i // q], K2[i % q]) for i in idx])
+        K = np.where(pc % 2 == 1, -1.0, 1.0) * s[None, :] / np.sqrt(d)
+    else:
+        K1 = np.asarray(spec["A"], np.float64)
+        K2 = np.asarray(spec["B"], np.float64)
+        q = K2.shape[0]
+        K = np.stack([np.kron(K1[i // q], K2[i % q]) for i in idx])
+    if spec.get("perm") is not None:
+        K = O.permute_scatter(K, cols=spec["perm"])
+    return K
 
 
 def side_cols(spec, d, idx):
-    """Columns `idx` of the d x d orthogonal matrix of one side, as rows (float64)."""
+    """Columns `idx` of the d x d orthogonal matrix of one side, as rows (float64);
+    column c of K P_p is column p^-1(c) of K."""
     idx = np.asarray(idx)
+    if spec.get("perm") is not None:
+        inv = np.argsort(spec["perm"])
+        plain = {k: v for k, v in spec.items() if k != "perm"}
+        return side_cols(plain, d, inv[idx])
     if "signs" in spec:
         s = np.asarray(spec["signs"], np.float64)
         j = np.arange(d)
@@ -71,14 +81,28 @@ def run_config(name, seed=0):
     X = torch.from_numpy(L.X).to(DEV)
     lp = Q.LayerPass(cfg.m, cfg.n, Q.SideSpec.from_numpy(L.left, DEV),
                      Q.SideSpec.from_numpy(L.right, DEV), quant=cfg.quant, bits=cfg.bits, B=cfg.B,
-                     g=cfg.g, alpha=cfg.alpha, device=DEV)
+                     g=cfg.g, alpha=cfg.alpha, device=DEV, rg_order=cfg.rg_order)
     b = lp.run(W, X)
     torch.cuda.synchronize()
     rng = np.random.default_rng(seed + cfg.cfg_id)
     return L, lp, b, rng
 
 
-def check_hessian_and_transforms(L, b, rng):
+def check_order(b):
+    """LDLQ-RG's order: diag(H~) in quantization order is non-increasing, and
+    equal entries keep increasing column index (this fixes the order)."""
+    order = host(b["order"]).astype(np.int64)
+    n = order.size
+    assert np.array_equal(np.sort(order), np.arange(n))
+    dg = np.diag(host(b["H"]))
+    assert np.all(dg[:-1] >= dg[1:])
+    tie = dg[:-1] == dg[1:]
+    assert np.all(order[:-1][tie] < order[1:][tie])
+    return order
+
+
+def check_hessian_and_transforms(L, b, rng, order=None):
+    """``order``: LDLQ-RG's order (H~ and W~ in quantization order), or None."""
     cfg = L.cfg
     n, m, N = cfg.n, cfg.m, cfg.N
     X64 = L.X.astype(np.float64)
@@ -87,11 +111,14 @@ def check_hessian_and_transforms(L, b, rng):
     shift = cfg.alpha * Hd_diag.mean()
     # H~ rows: H~[i, :] = (v_i^T H) V^T with H the damped Hessian recomputed here
     rows = rng.choice(n, NSAMP, replace=False)
-    Vr = side_rows(L.right, n, rows)  # rows of V
+    orig = rows if order is None else order[rows]
+    Vr = side_rows(L.right, n, orig)  # rows of V
     # v_i^T H = ((X v_i)^T X) / N + shift v_i
     XV = X64 @ Vr.T  # N x NSAMP
     vH = (XV.T @ X64) / N + shift * Vr
     Ht_rows = right_apply_rows(vH, L.right)
+    if order is not None:
+        Ht_rows = Ht_rows[:, order]
     got = host(b["H"])[rows].astype(np.float64)
     # normwise per row (transform tolerance on top of the float32 Hessian sums)
     assert P.rel_rows(got, Ht_rows) <= 2e-5
@@ -99,6 +126,8 @@ def check_hessian_and_transforms(L, b, rng):
     rw = rng.choice(m, NSAMP, replace=False)
     Ur = side_rows(L.left, m, rw)
     Wt_rows = right_apply_rows(Ur @ L.W.astype(np.float64), L.right)
+    if order is not None:
+        Wt_rows = Wt_rows[:, order]
     assert P.rel_rows(host(b["Wt"])[rw], Wt_rows) <= 1e-5
     return rw
 
@@ -167,12 +196,13 @@ def replay_rows(Wt_rows, U, What_rows, block=2048):
     return P_
 
 
-@pytest.mark.parametrize("name", ["c2", "c3a", "c3b", "c4a", "c4b", "c4c"])
+@pytest.mark.parametrize("name", ["c2", "c3a", "c3b", "c4a", "c4b", "c4c", "c3p"])
 def test_config_uniform(name):
     L, lp, b, rng = run_config(name)
     cfg = L.cfg
     Lv = 1 << cfg.bits
-    check_hessian_and_transforms(L, b, rng)
+    order = check_order(b) if cfg.rg_order else None
+    check_hessian_and_transforms(L, b, rng, order)
     Uh, Dh = check_ldl(b, 1, rng)
     rows = np.sort(rng.choice(cfg.m, NSAMP, replace=False))
     Wt = host(b["Wt"])[rows]
@@ -208,7 +238,10 @@ def test_config_uniform(name):
     check_fused_rows(b, rows, Wt, What, Hh)
     # post-processing rows: row i of U^T W^~ V = (column i of U)^T W^~ V
     ri = rows[:4]
-    back = O.incoherence_side(side_cols(L.left, cfg.m, ri) @ host(b["What_t"]).astype(np.float64),
+    What_t = host(b["What_t"])
+    if order is not None:  # back to the transform's column order
+        What_t = O.permute_scatter(What_t, cols=order)
+    back = O.incoherence_side(side_cols(L.left, cfg.m, ri) @ What_t.astype(np.float64),
                               "right", L.right, inverse=True)
     assert P.rel_rows(host(b["What"])[ri], back) <= 1e-5
     # inference: the packed codes and scales of this pass times a vector equal

@@ -606,3 +606,110 @@ def test_qmatvec_rht_rejects_unsupported_shapes():
     with pytest.raises(Q.QuipError, match="QUIP_ERR_SHAPE"):  # m = 6 is not a power of two
         Q.quip_qmatvec_rht(packed, 1024, 2, torch.ones(6, device=DEV), torch.ones(8, device=DEV),
                            z, z, torch.empty(6, device=DEV))
+
+
+# ------------------------------------------------------------------ QuIP variants: permutations
+
+@pytest.mark.parametrize("rows,cols,lda,ldo,use_r,use_c", [
+    (7, 13, 13, 13, True, True),        # scalar path, ragged
+    (64, 256, 256, 256, True, True),    # float4 path
+    (33, 4100, 4104, 4100, True, True),  # padded leading dimension
+    (5, 11, 16, 12, False, True),       # columns only, scalar path
+    (100, 64, 64, 64, True, False),     # rows only
+    (2, 32768, 32768, 32768, True, True),  # longest staged row
+    (1, 1, 1, 1, True, True),
+])
+def test_permute_bit_exact(rows, cols, lda, ldo, use_r, use_c):
+    r = rng(rows * 7 + cols)
+    A = r.standard_normal((rows, lda)).astype(np.float32)
+    pr = r.permutation(rows).astype(np.int32) if use_r else None
+    pc = r.permutation(cols).astype(np.int32) if use_c else None
+    Ad = dev(A)[:, :cols] if lda > cols else dev(A)
+    for scatter in (False, True):
+        out = torch.full((rows, ldo), -7.0, device=DEV)
+        o = out[:, :cols] if ldo > cols else out
+        Q.quip_permute(Ad, o, None if pr is None else dev(pr, torch.int32),
+                       None if pc is None else dev(pc, torch.int32), scatter=scatter)
+        f = O.permute_scatter if scatter else O.permute_gather
+        want = f(A[:, :cols], pr, pc)
+        got = host(out)
+        assert np.array_equal(got[:, :cols], want)
+        assert np.all(got[:, cols:] == -7.0)  # nothing written past the row
+
+
+def test_permute_gather_out_of_range_index_gives_nan():
+    A = np.arange(12, dtype=np.float32).reshape(3, 4)
+    pc = np.array([3, 9, 0, -1], dtype=np.int32)
+    pr = np.array([2, 0, 5], dtype=np.int32)
+    out = torch.empty((3, 4), device=DEV)
+    Q.quip_permute(dev(A), out, dev(pr, torch.int32), dev(pc, torch.int32))
+    got = host(out)
+    assert np.array_equal(got[0], [11.0, np.nan, 8.0, np.nan], equal_nan=True)
+    assert np.array_equal(got[1], [3.0, np.nan, 0.0, np.nan], equal_nan=True)
+    assert np.all(np.isnan(got[2]))
+
+
+def test_permute_rejects_overlap_and_long_staged_rows():
+    A = torch.zeros((4, 8), device=DEV)
+    with pytest.raises(Q.QuipError):
+        Q.quip_permute(A, A, None, dev(np.arange(8, dtype=np.int32), torch.int32))
+    big = torch.zeros((1, 32769), device=DEV)
+    with pytest.raises(Q.QuipError):
+        Q.quip_permute(big, torch.zeros_like(big), None,
+                       dev(np.arange(32769, dtype=np.int32), torch.int32))
+
+
+@pytest.mark.parametrize("n", [1, 5, 511, 512, 513, 4099, 11008])
+def test_diag_order_bit_exact(n):
+    r = rng(n)
+    # integer-valued diagonal: many exact ties; plus a few signed zeros
+    d = r.integers(0, max(2, n // 8), n).astype(np.float32)
+    if n > 4:
+        d[1], d[3] = 0.0, -0.0
+    H = np.zeros((n, n + 3), dtype=np.float32)
+    H[np.arange(n), np.arange(n)] = d
+    Hd = dev(H)[:, :n]
+    order = torch.empty(n, dtype=torch.int32, device=DEV)
+    Q.quip_diag_order(Hd, order)
+    assert np.array_equal(host(order), O.diag_order(H[:, :n]))
+    # distinct random values
+    H2 = np.diag(r.standard_normal(n).astype(np.float32)) + 1.0
+    Q.quip_diag_order(dev(H2), order)
+    assert np.array_equal(host(order), O.diag_order(H2))
+
+
+def test_layer_pass_with_permutations_and_rg_order():
+    cfg = wl.custom_config("perm-rg", 902, 64, 96, 512, left=wl.Side("rht", perm=True),
+                           right=wl.KRON(8, 12, perm=True), bits=2, B=32, rg_order=True)
+    L = wl.make_layer(cfg)
+    W, X = dev(L.W), dev(L.X)
+    lp = Q.LayerPass(cfg.m, cfg.n, Q.SideSpec.from_numpy(L.left, DEV),
+                     Q.SideSpec.from_numpy(L.right, DEV), bits=2, B=32, rg_order=True)
+    b = lp.run(W, X)
+    assert int(host(b["info"])[0]) == 0
+    order = host(b["order"]).astype(np.int64)
+    H = host(b["H"])
+    # the GPU's order is the diag order of its own transformed H (bit-exact)
+    H0 = O.permute_scatter(H, order, order)
+    assert np.array_equal(order, O.diag_order(H0))
+    # H~ and W~ against the oracle's transforms (permutation inside), in the GPU's order
+    ref = O.quantize_layer(L.W, L.X, L.left, L.right, quant="uniform", bits=2, rg_order=True)
+    Ht_ref = O.permute_gather(O.incoherence_H(ref["H"], L.right), order, order)
+    d = np.sqrt(np.diag(Ht_ref))
+    assert np.abs(H - Ht_ref).max() <= 1e-5 * d.max() ** 2
+    Wt_ref = O.permute_gather(O.incoherence_W(L.W, L.left, L.right), cols=order)
+    assert P.rel_rows(host(b["Wt"]), Wt_ref) <= 1e-5
+    # the oracle's own order agrees except between near-equal diagonal entries
+    dref = np.diag(O.incoherence_H(ref["H"], L.right))
+    diff = ref["order"] != order
+    assert np.all(np.abs(dref[ref["order"][diff]] - dref[order[diff]]) <= 1e-5 * dref.max())
+    check_uniform_replay(host(b["Wt"]), host(b["U"]), host(b["What_t"]), host(b["scales"]),
+                         host(b["codes"]), 4)
+    loss = float(host(b["loss"])[0])
+    check_fused_loss(host(b["Wt"]), host(b["What_t"]), H, host(b["row_loss"]), loss)
+    if not diff.any():
+        check_independent_run(host(b["Wt"]), host(b["What_t"]), host(b["codes"]), H, ref, loss)
+    # post-processing: columns back to the transform's order, inverse transforms
+    # (permutations inside)
+    back = O.incoherence_W_inv(O.permute_scatter(host(b["What_t"]), cols=order), L.left, L.right)
+    assert P.rel_rows(host(b["What"]), back) <= 1e-5
