@@ -14,9 +14,12 @@ of every kernel stamps an event pair; the same figures rocprofv3 reports), the
 roofline of the family with the most time per step, HBM traffic from the
 committed rocprofv3 counter summary of that family (when its source is
 unchanged), the RHT bandwidth per one-sided pass, and the CPU oracle timed on
-a bounded sample.
+a bounded sample. Beside the pass: the E8 codebook's MSE on a Gaussian source,
+the inference product's rates on packed codes, and the QuIP variants (the
+permutation inside the Kronecker multiply, LDLQ-RG's order) on a 4096 x 11008
+layer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-variants]
 """
 from __future__ import annotations
 
@@ -49,6 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the QuIP-variant passes")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of W in the oracle LDLQ sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain device copy of COPY_MIB MiB (counter calibration)")
@@ -193,6 +197,56 @@ def kernel_bound(name: str):
                 "e8_scale_kernel"):
         return "alu", FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
     return "hbm", HBM_PEAK_GBS, "GB/s"
+
+
+def variants_bench(Q, wl, dev, steps: int) -> dict:
+    """The QuIP variants on the 4096 x 11008 MLP layer (3-bit, RHT left,
+    Kronecker 64 x 172 right): without them, with the random permutation inside
+    the Kronecker multiply, with LDLQ-RG's diag(H) order, and with both. Per
+    variant: time per pass (wall clock over `steps` passes), the proxy loss, and
+    the permutation kernels' own times and rates from the library timing."""
+    import torch
+
+    L = wl.make_layer("c3p")
+    cfg = L.cfg
+    W = torch.from_numpy(L.W).to(dev)
+    X = torch.from_numpy(L.X).to(dev)
+    out = {"workload": f"{cfg.m}x{cfg.n}, {cfg.bits}-bit, RHT left, Kron 64x172 right, N = {cfg.N}"}
+    for name, perm, rg in (("plain", False, False), ("perm", True, False), ("rg", False, True),
+                           ("perm_rg", True, True)):
+        right = dict(L.right)
+        if not perm:
+            right.pop("perm")
+        lp = Q.LayerPass(cfg.m, cfg.n, Q.SideSpec.from_numpy(L.left, dev),
+                         Q.SideSpec.from_numpy(right, dev), quant=cfg.quant, bits=cfg.bits, B=cfg.B,
+                         alpha=cfg.alpha, device=dev, rg_order=rg)
+        lp.run(W, X)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            lp.run(W, X)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        Q.timing_reset()
+        Q.timing_enable(True)
+        lp.run(W, X)
+        torch.cuda.synchronize()
+        Q.timing_enable(False)
+        rep = Q.timing_report()
+        Q.timing_reset()
+        v = {"ms_per_pass": round(ms, 3), "proxy_loss": float(lp.buffers["loss"].item()),
+             "info": int(lp.buffers["info"].item())}
+        for k in ("permute_gather_kernel", "permute_scatter_kernel", "diag_rank_kernel",
+                  "diag_order_finish_kernel"):
+            if k in rep:
+                launches, kms, _, kbytes = rep[k]
+                v[k] = {"launches": launches, "us": round(1e3 * kms, 2)}
+                if k.startswith("permute"):
+                    v[k]["GBps"] = round(kbytes / (kms / 1e3) / 1e9, 1)
+        out[name] = v
+        del lp
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(cfg_name: str, rows: int) -> dict:
@@ -450,6 +504,8 @@ def main():
             del cl
         torch.cuda.empty_cache()
 
+    variants = {} if args.no_variants else variants_bench(Q, wl, dev, max(2, args.steps // 3))
+
     line = {
         "metric": "quantized weights/sec for a 4096x4096 layer (LDLQ+RHT, 2-bit); RHT GB/s",
         "value": round(value, 1),
@@ -471,6 +527,7 @@ def main():
         "rht": rht,
         "gaussian_vq": gaussian_vq,
         "inference": inference,
+        "variants": variants,
         "roofline": roofline,
         "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])),
     }
