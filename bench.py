@@ -19,7 +19,7 @@ the inference product's rates on packed codes, and the QuIP variants (the
 permutation inside the Kronecker multiply, LDLQ-RG's order) on a 4096 x 11008
 layer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-variants]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-variants] [--no-extras]
 """
 from __future__ import annotations
 
@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the QuIP-variant passes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="the pass only: skip the Gaussian-source VQ, inference and variant figures "
+                         "(profiled runs, whose per-kernel means must cover the pass's launches only)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of W in the oracle LDLQ sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain device copy of COPY_MIB MiB (counter calibration)")
@@ -197,6 +200,91 @@ def kernel_bound(name: str):
                 "e8_scale_kernel"):
         return "alu", FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
     return "hbm", HBM_PEAK_GBS, "GB/s"
+
+
+def gaussian_vq_bench(Q, wl, dev, timed) -> dict:
+    """The E8 codebook at 2 bits per weight on an i.i.d. N(0,1) source (1024 x
+    4096 weights, 524288 8-vectors), through the search of the E8
+    configuration's scale step: the best mean squared error per weight over the
+    32 scale candidates, against the Gaussian distortion-rate bound 2^-4; the
+    QTIP page's figures (E8P 0.089, 256-D TCQ 0.068-0.071) are context."""
+    import torch
+
+    gm, gn = 1024, 4096
+    G = torch.from_numpy(wl.gaussian_rows(1, gm, gn)).to(dev)
+    cb = Q.quip_e8_codebook().to(dev)
+    q8 = Q.quantizer(Q.Q_E8, 2)
+    gsc = torch.empty(gm + 1, device=dev)
+    gsse = torch.empty(32, dtype=torch.float64, device=dev)
+    gws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_scales_workspace, gm, gn,
+                                                 ctypes.byref(q8)), dev)
+    g_ms = timed(lambda: Q.quip_scales(G, q8, gsc, mse_out=gsse, codebook=cb, ws=gws), 3)
+    nvec = gm * gn // 8
+    return {"mse_per_weight": round(float(gsse.min().item()) / (gm * gn), 5),
+            "distortion_rate_bound": 0.0625, "printed_e8p": 0.089,
+            "printed_tcq_256d": [0.068, 0.071], "vectors": nvec, "ms": round(g_ms, 3),
+            "candidate_distances_per_s": round(nvec * 65536 * 32 / (g_ms / 1e3), 1)}
+
+
+def inference_bench(Q, wl, dev, timed, lp, left, right, cfg) -> dict:
+    """Inference with the quantized layer, y = Q_L^T W^~ Q_R x: the pass's own
+    codes packed at 2 bits, then 16384 x 16384 layers of random codes at 2 and
+    4 bits, four distinct copies cycled so that the packed codes read per cycle
+    (268 or 537 MB) exceed the 256 MB last-level cache."""
+    import torch
+
+    if not (left.is_rht and right.is_rht):
+        return {}
+
+    def qmv_case(codes_list, scales, sl, sr, bits, reps):
+        m, n = codes_list[0].shape
+        rb = Q.quip_packed_row_bytes(n, bits)
+        packs = []
+        for c in codes_list:
+            p = torch.empty((m, rb), dtype=torch.uint8, device=dev)
+            Q.quip_pack_codes(c, bits, p)
+            packs.append(p)
+        x = torch.from_numpy(wl.gaussian_rows(7, 1, n)[0]).to(dev)
+        y = torch.empty(m, device=dev)
+        ws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_qmatvec_rht_workspace, m, n),
+                                 dev)
+        it = [0]
+
+        def call():
+            Q.quip_qmatvec_rht(packs[it[0] % len(packs)], n, bits, scales, sl, sr, x, y, ws=ws)
+            it[0] += 1
+        ms = timed(call, reps)
+        Q.timing_reset()
+        Q.timing_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        Q.timing_enable(False)
+        launches, kms, _, kbytes = Q.timing_report()["qmatvec_kernel"]
+        Q.timing_reset()
+        gbps = kbytes / (kms / 1e3) / 1e9
+        return {"m": m, "n": n, "bits": bits, "packed_MB": round(m * rb / 1e6, 2),
+                "copies": len(packs), "product_us": round(1e3 * ms, 2),
+                "qmatvec_kernel_us": round(1e3 * kms / launches, 2),
+                "qmatvec_kernel_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 3),
+                "weights_per_s": round(m * n / (ms / 1e3), 1)}
+
+    out = {"pass_layer": qmv_case([lp.buffers["codes"]], lp.buffers["scales"], left.signs,
+                                  right.signs, cfg.bits, 50)}
+    big = 16384
+    gen = torch.Generator(device=dev).manual_seed(11)
+
+    def sgn():
+        return torch.randint(0, 2, (big,), device=dev, generator=gen).float() * 2 - 1
+    bsl, bsr = sgn(), sgn()
+    bsc = torch.rand(big, device=dev, generator=gen) + 0.5
+    for bits in (2, 4):
+        cl = [torch.randint(0, 1 << bits, (big, big), dtype=torch.uint8, device=dev, generator=gen)
+              for _ in range(4)]
+        out[f"{big}x{big}_{bits}bit"] = qmv_case(cl, bsc, bsl, bsr, bits, 40)
+        del cl
+    torch.cuda.empty_cache()
+    return out
 
 
 def variants_bench(Q, wl, dev, steps: int) -> dict:
@@ -431,80 +519,13 @@ def main():
                "right_ms": round(r_ms, 4), "left_ms": round(l_ms, 4), "two_sided_ms": round(t_ms, 4),
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
-    # The E8 codebook at 2 bits per weight on an i.i.d. N(0,1) source (1024 x
-    # 4096 weights, 524288 8-vectors), through the search of the E8
-    # configuration's scale step: the best mean squared error per weight over
-    # the 32 scale candidates, against the Gaussian distortion-rate bound 2^-4;
-    # the QTIP page's figures (E8P 0.089, 256-D TCQ 0.068-0.071) are context
-    gm, gn = 1024, 4096
-    G = torch.from_numpy(wl.gaussian_rows(1, gm, gn)).to(dev)
-    cb = Q.quip_e8_codebook().to(dev)
-    q8 = Q.quantizer(Q.Q_E8, 2)
-    gsc = torch.empty(gm + 1, device=dev)
-    gsse = torch.empty(32, dtype=torch.float64, device=dev)
-    gws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_scales_workspace, gm, gn,
-                                                 ctypes.byref(q8)), dev)
-    g_ms = timed(lambda: Q.quip_scales(G, q8, gsc, mse_out=gsse, codebook=cb, ws=gws), 3)
-    nvec = gm * gn // 8
-    gaussian_vq = {"mse_per_weight": round(float(gsse.min().item()) / (gm * gn), 5),
-                   "distortion_rate_bound": 0.0625, "printed_e8p": 0.089,
-                   "printed_tcq_256d": [0.068, 0.071], "vectors": nvec, "ms": round(g_ms, 3),
-                   "candidate_distances_per_s": round(nvec * 65536 * 32 / (g_ms / 1e3), 1)}
-
-    # Inference with the quantized layer, y = Q_L^T W^~ Q_R x: the pass's own
-    # codes packed at 2 bits, then 16384 x 16384 layers of random codes at 2 and
-    # 4 bits, four distinct copies cycled so that the packed codes read per
-    # cycle (256 or 512 MB) exceed the 256 MB last-level cache
-    inference = {}
-    if left.is_rht and right.is_rht:
-        def qmv_case(codes_list, scales, sl, sr, bits, reps):
-            m, n = codes_list[0].shape
-            rb = Q.quip_packed_row_bytes(n, bits)
-            packs = []
-            for c in codes_list:
-                p = torch.empty((m, rb), dtype=torch.uint8, device=dev)
-                Q.quip_pack_codes(c, bits, p)
-                packs.append(p)
-            x = torch.from_numpy(wl.gaussian_rows(7, 1, n)[0]).to(dev)
-            y = torch.empty(m, device=dev)
-            ws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_qmatvec_rht_workspace, m, n),
-                                     dev)
-            it = [0]
-
-            def call():
-                Q.quip_qmatvec_rht(packs[it[0] % len(packs)], n, bits, scales, sl, sr, x, y, ws=ws)
-                it[0] += 1
-            ms = timed(call, reps)
-            Q.timing_reset()
-            Q.timing_enable(True)
-            for _ in range(reps):
-                call()
-            torch.cuda.synchronize()
-            Q.timing_enable(False)
-            launches, kms, _, kbytes = Q.timing_report()["qmatvec_kernel"]
-            Q.timing_reset()
-            gbps = kbytes / (kms / 1e3) / 1e9
-            return {"m": m, "n": n, "bits": bits, "packed_MB": round(m * rb / 1e6, 2),
-                    "copies": len(packs), "product_us": round(1e3 * ms, 2),
-                    "qmatvec_kernel_us": round(1e3 * kms / launches, 2),
-                    "qmatvec_kernel_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 3),
-                    "weights_per_s": round(m * n / (ms / 1e3), 1)}
-
-        inference["pass_layer"] = qmv_case([lp.buffers["codes"]], lp.buffers["scales"], left.signs,
-                                           right.signs, cfg.bits, 50)
-        big = 16384
-        gen = torch.Generator(device=dev).manual_seed(11)
-        sgn = lambda: (torch.randint(0, 2, (big,), device=dev, generator=gen).float() * 2 - 1)
-        bsl, bsr = sgn(), sgn()
-        bsc = torch.rand(big, device=dev, generator=gen) + 0.5
-        for bits in (2, 4):
-            cl = [torch.randint(0, 1 << bits, (big, big), dtype=torch.uint8, device=dev, generator=gen)
-                  for _ in range(4)]
-            inference[f"{big}x{big}_{bits}bit"] = qmv_case(cl, bsc, bsl, bsr, bits, 40)
-            del cl
-        torch.cuda.empty_cache()
-
-    variants = {} if args.no_variants else variants_bench(Q, wl, dev, max(2, args.steps // 3))
+    # beside the pass: Gaussian-source VQ, the inference product, the variants
+    gaussian_vq, inference, variants = {}, {}, {}
+    if not args.no_extras:
+        gaussian_vq = gaussian_vq_bench(Q, wl, dev, timed)
+        inference = inference_bench(Q, wl, dev, timed, lp, left, right, cfg)
+        if not args.no_variants:
+            variants = variants_bench(Q, wl, dev, max(2, args.steps // 3))
 
     line = {
         "metric": "quantized weights/sec for a 4096x4096 layer (LDLQ+RHT, 2-bit); RHT GB/s",
