@@ -677,6 +677,96 @@ def qmatvec_rht(codes, scales, L: int, signs_left, signs_right, x) -> np.ndarray
 
 
 # --------------------------------------------------------------------------
+# Trellis-coded quantization with a bitshift trellis ([QTIP] summary)
+# --------------------------------------------------------------------------
+
+TCQ_LCG_MUL = 1664525       # the multiplier and increment of the classic
+TCQ_LCG_ADD = 1013904223    # 32-bit linear congruential generator (Numerical Recipes)
+TCQ_SUM_MEAN = 510.0        # four uniform bytes: mean 4 * 255 / 2
+TCQ_SUM_STD = float(np.sqrt(4.0 * (256.0 ** 2 - 1.0) / 12.0))  # and standard deviation
+
+
+def tcq_code_constants(scale: float = 1.0):
+    """(alpha, beta) as float32: reconstruction = fma(bytesum, alpha, beta)."""
+    a = F32(scale / TCQ_SUM_STD)
+    b = F32(-TCQ_SUM_MEAN * scale / TCQ_SUM_STD)
+    return a, b
+
+
+def tcq_code(states, scale: float = 1.0) -> np.ndarray:
+    """The reconstruction value of each trellis state: a computed pseudorandom
+    Gaussian code in the sense of [QTIP] (values generated from the state by a
+    few integer instructions, no stored codebook; the page names such codes
+    but gives no formula, so this one is a reading): one multiply-add of the
+    32-bit LCG, h = (1664525 s + 1013904223) mod 2^32, then the sum of h's four
+    bytes (an Irwin-Hall approximation of a Gaussian), centred and scaled to
+    unit variance times ``scale``. The last step is one float32 fused
+    multiply-add, fma(sum, alpha, beta), reproduced exactly here (the float64
+    product and sum are exact; one rounding to float32)."""
+    st = np.asarray(states, dtype=np.uint64)
+    h = (st * np.uint64(TCQ_LCG_MUL) + np.uint64(TCQ_LCG_ADD)) & np.uint64(0xFFFFFFFF)
+    bsum = sum(((h >> np.uint64(8 * i)) & np.uint64(0xFF)) for i in range(4)).astype(F64)
+    a, b = tcq_code_constants(scale)
+    return (bsum * F64(a) + F64(b)).astype(F32)
+
+
+def tcq_next_state(s, bits_in, L: int, k: int):
+    """The bitshift trellis: the next state shifts the L-bit state left by k
+    and brings in k new bits, so consecutive states share L - k bits ([QTIP]
+    summary: decoding is parallel and stateless, each value depends only on a
+    window of L bits of the stream)."""
+    return ((int(s) << k) | int(bits_in)) & ((1 << L) - 1)
+
+
+def tcq_viterbi(x, L: int, k: int, scale: float = 1.0):
+    """Trellis-coded quantization of the sequence x (length T): the state
+    sequence s_0..s_{T-1} of the bitshift trellis (s_0 free, every later state
+    reachable from the previous one) minimizing sum_t (x_t - c(s_t))^2, with
+    c = ``tcq_code``. Dynamic programming over time (Viterbi) in float64: the
+    best cost of ending in state s' at step t is the best cost over its 2^k
+    predecessors p = (s' >> k) + a 2^(L-k) at step t-1, plus the distortion of
+    s'. Ties go to the lowest a and, at the end, to the lowest state.
+    Returns (states, cost)."""
+    x = np.asarray(x, dtype=F64)
+    T = x.size
+    S = 1 << L
+    G = 1 << (L - k)
+    c = tcq_code(np.arange(S), scale).astype(F64)
+    cost = (x[0] - c) ** 2
+    back = np.zeros((T, G), dtype=np.int64)
+    for t in range(1, T):
+        pred = cost.reshape(1 << k, G)  # pred[a, m] = cost of state m + a G
+        a = np.argmin(pred, axis=0)     # first minimum: the lowest a
+        best = pred[a, np.arange(G)]
+        back[t] = a
+        # state s' = m 2^k + b continues from group m
+        cost = np.repeat(best, 1 << k) + (x[t] - c) ** 2
+    s = int(np.argmin(cost))
+    total = float(cost[s])
+    states = np.zeros(T, dtype=np.int64)
+    for t in range(T - 1, 0, -1):
+        states[t] = s
+        m = s >> k
+        s = m + int(back[t, m]) * G
+    states[0] = s
+    return states, total
+
+
+def tcq_path_cost(x, states, scale: float = 1.0) -> float:
+    """sum_t (x_t - c(s_t))^2 in float64 for a given state sequence."""
+    x = np.asarray(x, dtype=F64)
+    return float(((x - tcq_code(states, scale).astype(F64)) ** 2).sum())
+
+
+def tcq_path_is_valid(states, L: int, k: int) -> bool:
+    """Every state follows from the previous one by the bitshift rule."""
+    mask = (1 << L) - 1
+    st = np.asarray(states, dtype=np.int64)
+    return bool(np.all((st >= 0) & (st <= mask)) and
+                np.all(((st[:-1] << k) & mask) == (st[1:] & ~((1 << k) - 1) & mask)))
+
+
+# --------------------------------------------------------------------------
 # The whole pass (small layers)
 # --------------------------------------------------------------------------
 

@@ -627,3 +627,79 @@ def test_rg_order_on_an_already_sorted_diagonal_changes_nothing():
     assert np.array_equal(c["order"], np.arange(n)[::-1])
     assert np.array_equal(c["codes"], a["codes"])
     assert np.allclose(c["What"], a["What"][:, ::-1], atol=1e-12)
+
+
+# ---------------------------------------------------------------- trellis-coded quantization
+
+def test_tcq_code_hand_worked_values():
+    g = golden("tcq_code_worked.json")
+    for case in g["cases"]:
+        h = int(case["h_hex"], 16)
+        assert [(h >> (8 * i)) & 0xFF for i in range(4)] == case["bytes"]
+        assert sum(case["bytes"]) == case["sum"]
+        want = (case["sum"] - 510) / g["std"]
+        got = float(O.tcq_code([case["state"]])[0])
+        assert abs(got - want) <= 2e-7 * max(1.0, abs(want)), (case, got, want)
+
+
+def test_tcq_code_is_unit_gaussian_like():
+    c = O.tcq_code(np.arange(1 << 16)).astype(np.float64)
+    assert abs(c.mean()) < 0.01 and abs(c.var() - 1.0) < 0.01
+    assert c.min() > -3.5 and c.max() < 3.5  # Irwin-Hall with 4 terms: bounded by 3.46
+    c2 = O.tcq_code(np.arange(1 << 16), 2.0).astype(np.float64)
+    assert np.allclose(c2, 2 * c, rtol=2e-7, atol=1e-7)
+
+
+def _tcq_brute(x, L, k):
+    """Minimum over every valid state sequence, by enumeration."""
+    T = len(x)
+    c = O.tcq_code(np.arange(1 << L)).astype(np.float64)
+    best, arg = np.inf, None
+    for s0 in range(1 << L):
+        for bits in itertools.product(range(1 << k), repeat=T - 1):
+            st = [s0]
+            for b in bits:
+                st.append(O.tcq_next_state(st[-1], b, L, k))
+            v = float(((np.asarray(x) - c[st]) ** 2).sum())
+            if v < best:
+                best, arg = v, st
+    return best, arg
+
+
+@pytest.mark.parametrize("L,k,T", [(4, 2, 4), (3, 1, 7), (5, 2, 3)])
+def test_tcq_viterbi_equals_brute_force(L, k, T):
+    x = rng(61 + L + T).standard_normal(T) * 1.3
+    st, cost = O.tcq_viterbi(x, L, k)
+    best, _ = _tcq_brute(x, L, k)
+    assert np.isclose(cost, best, rtol=1e-12, atol=1e-12)
+    assert O.tcq_path_is_valid(st, L, k)
+    assert np.isclose(O.tcq_path_cost(x, st), cost, rtol=1e-12)
+
+
+def test_tcq_single_step_and_memoryless_special_cases():
+    x = rng(67).standard_normal(9)
+    c = O.tcq_code(np.arange(1 << 6)).astype(np.float64)
+    # T = 1: the nearest of all 2^L codes (lowest state on ties)
+    st, cost = O.tcq_viterbi(x[:1], 6, 2)
+    assert st[0] == int(np.argmin((x[0] - c) ** 2))
+    # k = L: no shared bits, every step picks its own nearest code
+    st, cost = O.tcq_viterbi(x, 6, 6)
+    assert np.isclose(cost, ((x[:, None] - c[None, :]) ** 2).min(axis=1).sum(), rtol=1e-12)
+
+
+def test_tcq_path_validity_check():
+    assert O.tcq_path_is_valid([5, (5 << 2 | 3) & 15, ((5 << 2 | 3) & 15) << 2 & 15], 4, 2)
+    assert O.tcq_path_is_valid([5, 6], 4, 2)  # 6 = (5 << 2 | 2) mod 16
+    assert not O.tcq_path_is_valid([5, 9], 4, 2)  # 9 keeps bits 2-3 = 2, not 1
+    assert not O.tcq_path_is_valid([5, 16], 4, 2)  # outside the 4-bit states
+
+
+def test_tcq_gaussian_mse_between_bound_and_best_scalar():
+    # 2 bits per weight (+ (L - k)/T for the free first state) on i.i.d. N(0,1):
+    # no code beats the distortion-rate bound 2^(-2R); the trellis beats Max's
+    # optimal 4-level scalar quantizer (0.1175)
+    L, k, T = 10, 2, 64
+    X = wl.gaussian_rows(5, 24, T).astype(np.float64)
+    mse = np.mean([O.tcq_viterbi(x, L, k)[1] for x in X]) / T
+    R = k + (L - k) / T
+    assert 2.0 ** (-2 * R) <= mse < 0.1175, mse
