@@ -366,6 +366,38 @@ quip_status quip_diag_order(const float* H, int64_t n, int64_t ldh, int32_t* ord
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * quip_tcq_quantize -- trellis-coded quantization with a bitshift trellis
+ * ([QTIP] summary page, Approach): each row x_0..x_{T-1} of X becomes the
+ * state sequence s_0..s_{T-1} of an L-bit shift register that takes k new
+ * bits per step (s_t = (s_{t-1} << k | b_t) mod 2^L, so the stream is
+ * s_0 followed by k bits per later weight: k + (L - k)/T bits per weight),
+ * minimizing sum_t (x_t - c(s_t))^2 exactly (Viterbi; ties to the lowest
+ * predecessor, then the lowest final state; the first state is free, no
+ * tail-biting). c is a computed pseudorandom Gaussian code (the page names
+ * such codes without a formula; this one is a reading): h = (1664525 s +
+ * 1013904223) mod 2^32, c(s) = fma(sum of the four bytes of h, alpha, beta)
+ * in float32, with alpha = float32(scale / sqrt(21845)) and beta =
+ * float32(-510 scale / sqrt(21845)).
+ *   X: rows x T float32 (device), leading dim ldx >= T.
+ *   L: state bits, 4..15 (the 2^L costs of a row are held in one LDS buffer);
+ *   k: bits per step, 2.
+ *   scale: finite, > 0 (the values are scale times a unit-variance code).
+ *   states: rows x T uint16 (device), leading dim lds >= T.
+ *   Xhat: rows x T float32 (device) with leading dim ldq >= T, or NULL:
+ *     c(states).
+ *   cost: rows float32 (device): the minimum of each row (float32 sums).
+ *   ws: quip_tcq_workspace(rows, T, L) bytes, 256-byte aligned (2-bit
+ *     back-pointers of up to 2048 rows at a time).
+ * Errors: QUIP_ERR_ARG (null pointer, sizes, leading dimensions, scale),
+ * QUIP_ERR_UNSUPPORTED (k != 2, L outside 4..15), QUIP_ERR_WORKSPACE.
+ */
+quip_status quip_tcq_workspace(int64_t rows, int64_t T, int32_t L, size_t* bytes);
+quip_status quip_tcq_quantize(const float* X, int64_t rows, int64_t T, int64_t ldx, int32_t L,
+                              int32_t k, float scale, uint16_t* states, int64_t lds, float* Xhat,
+                              int64_t ldq, float* cost, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
  * quip_e8_codebook -- fills HOST memory with the 65536 smallest-norm points of
  * the E8 lattice (D8 together with D8 + 1/2) ordered by squared norm, then by
  * coordinates ascending with the first coordinate most significant; 65536 x 8

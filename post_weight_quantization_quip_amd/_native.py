@@ -81,6 +81,9 @@ SYMBOLS = {
                              c_vp]),
     "quip_diag_order_workspace": (c_int, [c_i64, ctypes.POINTER(c_sz)]),
     "quip_diag_order": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "quip_tcq_workspace": (c_int, [c_i64, c_i64, ctypes.c_int32, ctypes.POINTER(c_sz)]),
+    "quip_tcq_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, c_f,
+                                  c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "quip_timing_enable": (c_int, [c_int]),
     "quip_timing_reset": (c_int, []),
     "quip_timing_report": (c_int, [ctypes.c_char_p, c_sz, ctypes.POINTER(c_sz)]),
@@ -283,6 +286,19 @@ def quip_diag_order(H, order, stream=None, ws=None):
         ws = _workspace(_ws_query(lib.quip_diag_order_workspace, n), H.device)
     _check(lib.quip_diag_order(_p(H), n, _ld(H), _p(order), _p(ws), 0 if ws is None else ws.numel(),
                                _stream(stream)), "quip_diag_order")
+
+
+def quip_tcq_quantize(X, L: int, states, cost, Xhat=None, k: int = 2, scale: float = 1.0,
+                      stream=None, ws=None):
+    """Bitshift-trellis quantization of the rows of X: states (uint16, rows x T),
+    the row minima (float32), optionally the values c(states)."""
+    rows, T = X.shape
+    if ws is None:
+        ws = _workspace(_ws_query(lib.quip_tcq_workspace, rows, T, L), X.device)
+    _check(lib.quip_tcq_quantize(_p(X), rows, T, _ld(X), L, k, scale, _p(states), _ld(states),
+                                 _p(Xhat), _ld(Xhat) if Xhat is not None else T, _p(cost), _p(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)),
+           "quip_tcq_quantize")
 
 
 def timing_enable(on: bool = True) -> None:

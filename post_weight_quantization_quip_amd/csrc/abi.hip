@@ -404,6 +404,33 @@ quip_status quip_diag_order(const float* H, int64_t n, int64_t ldh, int32_t* ord
   return diag_order(H, n, ldh, order, ws, ws_bytes, stream);
 }
 
+quip_status quip_tcq_workspace(int64_t rows, int64_t T, int32_t L, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(QUIP_ERR_ARG, "quip_tcq_workspace: bytes is null");
+  if (rows <= 0 || T <= 0) return fail(QUIP_ERR_ARG, "quip_tcq_workspace: sizes must be positive");
+  if (L < 4 || L > 15) return fail(QUIP_ERR_UNSUPPORTED, "quip_tcq_workspace: L must be in [4, 15]");
+  *bytes = tcq_workspace_bytes(rows, T, L);
+  return QUIP_OK;
+}
+
+quip_status quip_tcq_quantize(const float* X, int64_t rows, int64_t T, int64_t ldx, int32_t L,
+                              int32_t k, float scale, uint16_t* states, int64_t lds, float* Xhat,
+                              int64_t ldq, float* cost, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  clear_error();
+  const char* who = "quip_tcq_quantize";
+  QUIP_TRY(check_matrix(X, rows, T, ldx, who, "X"));
+  if (!states || !cost) return fail(QUIP_ERR_ARG, std::string(who) + ": states or cost is null");
+  if (lds < T || (Xhat && ldq < T))
+    return fail(QUIP_ERR_ARG, std::string(who) + ": leading dimension smaller than T");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(QUIP_ERR_ARG, std::string(who) + ": scale must be finite and positive");
+  if (k != 2) return fail(QUIP_ERR_UNSUPPORTED, std::string(who) + ": k must be 2");
+  if (L < 4 || L > 15) return fail(QUIP_ERR_UNSUPPORTED, std::string(who) + ": L must be in [4, 15]");
+  QUIP_TRY(check_ws(ws, ws_bytes, tcq_workspace_bytes(rows, T, L), who));
+  return tcq_quantize(X, rows, T, ldx, L, scale, states, lds, Xhat, ldq, cost, ws, ws_bytes, stream);
+}
+
 quip_status quip_proxy_loss_workspace(int64_t m, int64_t n, size_t* bytes) {
   clear_error();
   if (!bytes) return fail(QUIP_ERR_ARG, "quip_proxy_loss_workspace: bytes is null");

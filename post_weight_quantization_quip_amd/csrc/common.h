@@ -129,6 +129,13 @@ size_t diag_order_workspace_bytes(int64_t n);
 quip_status diag_order(const float* H, int64_t n, int64_t ldh, int32_t* order, void* ws,
                        size_t ws_bytes, hipStream_t s);
 
+// ---------------------------------------------------------------- trellis (tcq.hip)
+
+size_t tcq_workspace_bytes(int64_t rows, int64_t T, int L);
+quip_status tcq_quantize(const float* X, int64_t rows, int64_t T, int64_t ldx, int L, float scale,
+                         uint16_t* states, int64_t lds, float* xhat, int64_t ldq, float* cost,
+                         void* ws, size_t ws_bytes, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMM (gemm.hip)
 
 enum GemmEpi {

@@ -174,3 +174,26 @@ def test_permute_and_diag_order_validation():
     assert lib.quip_diag_order(A, 16, 8, fake(), fake(0x100000), 1 << 20, None) == N.QUIP_ERR_ARG
     assert lib.quip_diag_order(A, 16, 16, None, fake(0x100000), 1 << 20, None) == N.QUIP_ERR_ARG
     assert lib.quip_diag_order(A, 16, 16, fake(), fake(0x100000), 4, None) == N.QUIP_ERR_WORKSPACE
+
+
+def test_tcq_validation():
+    lib = N.lib
+    ws = ctypes.c_size_t(0)
+    assert lib.quip_tcq_workspace(4096, 256, 15, ctypes.byref(ws)) == N.QUIP_OK
+    assert ws.value >= 2048 * 256 * 2048  # back-pointers of one 2048-row round
+    assert lib.quip_tcq_workspace(4096, 256, 16, ctypes.byref(ws)) == N.QUIP_ERR_UNSUPPORTED
+    assert lib.quip_tcq_workspace(0, 256, 12, ctypes.byref(ws)) == N.QUIP_ERR_ARG
+    big = fake(0x100000)
+
+    def call(L=12, k=2, scale=1.0, X=fake(), ldx=256, lds=256, xh=fake(), ldq=256, wsb=1 << 40):
+        return lib.quip_tcq_quantize(X, 8, 256, ldx, L, k, scale, fake(), lds, xh, ldq, fake(), big,
+                                     wsb, None)
+    assert call(k=3) == N.QUIP_ERR_UNSUPPORTED
+    assert call(L=3) == N.QUIP_ERR_UNSUPPORTED
+    assert call(scale=0.0) == N.QUIP_ERR_ARG
+    assert call(scale=float("inf")) == N.QUIP_ERR_ARG
+    assert call(X=None) == N.QUIP_ERR_ARG
+    assert call(ldx=100) == N.QUIP_ERR_ARG
+    assert call(lds=100) == N.QUIP_ERR_ARG
+    assert call(ldq=100) == N.QUIP_ERR_ARG
+    assert call(wsb=16) == N.QUIP_ERR_WORKSPACE

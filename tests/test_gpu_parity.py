@@ -713,3 +713,64 @@ def test_layer_pass_with_permutations_and_rg_order():
     # (permutations inside)
     back = O.incoherence_W_inv(O.permute_scatter(host(b["What_t"]), cols=order), L.left, L.right)
     assert P.rel_rows(host(b["What"]), back) <= 1e-5
+
+
+# ------------------------------------------------------------------ trellis-coded quantization
+
+def tcq_gpu(X, L, scale=1.0, ldx=None, with_xhat=True):
+    rows, T = X.shape
+    ldx = T if ldx is None else ldx
+    Xp = np.zeros((rows, ldx), np.float32)
+    Xp[:, :T] = X
+    Xd = dev(Xp)[:, :T] if ldx > T else dev(Xp)
+    st = torch.empty((rows, T), dtype=torch.int16, device=DEV)
+    xh = torch.empty((rows, T), device=DEV) if with_xhat else None
+    cost = torch.empty(rows, device=DEV)
+    Q.quip_tcq_quantize(Xd, L, st, cost, Xhat=xh, scale=scale)
+    s = host(st).astype(np.int64) & 0xFFFF
+    return s, (host(xh) if with_xhat else None), host(cost)
+
+
+def check_tcq_rows(X, L, s, xh, cost, scale=1.0, oracle_rows=None):
+    """Every row: a valid path, values c(states) bit-exact, the reported float32
+    minimum equal to the path's cost up to float32 summation, and the path
+    optimal up to that rounding (the oracle's float64 Viterbi)."""
+    rows, T = X.shape
+    for r in range(rows):
+        assert O.tcq_path_is_valid(s[r], L, 2), r
+        if xh is not None:
+            assert np.array_equal(xh[r], O.tcq_code(s[r], scale)), r
+        pc = O.tcq_path_cost(X[r], s[r], scale)
+        tol = 4e-7 * T * max(pc, 1e-3)  # float32 sums of T terms
+        assert abs(float(cost[r]) - pc) <= tol, (r, float(cost[r]), pc)
+        if oracle_rows is None or r in oracle_rows:
+            _, best = O.tcq_viterbi(X[r], L, 2, scale)
+            assert best - 1e-12 <= pc <= best + tol, (r, pc, best)
+
+
+@pytest.mark.parametrize("L,T,rows,ldx", [(4, 5, 3, 5), (8, 64, 17, 70), (12, 256, 24, 256),
+                                          (15, 256, 6, 260), (10, 1000, 5, 1000), (13, 1, 9, 4)])
+def test_tcq_parity(L, T, rows, ldx):
+    X = wl.gaussian_rows(100 + L, rows, T)
+    s, xh, cost = tcq_gpu(X, L, ldx=ldx)
+    check_tcq_rows(X, L, s, xh, cost)
+
+
+def test_tcq_scale_and_chunks():
+    # more rows than one round of back-pointers (2048), and a scale
+    X = wl.gaussian_rows(111, 4100, 6) * np.float32(0.4)
+    s, xh, cost = tcq_gpu(X, 6, scale=0.37)
+    check_tcq_rows(X, 6, s, xh, cost, scale=0.37, oracle_rows=set(range(0, 4100, 97)))
+
+
+def test_tcq_without_values_and_rejections():
+    X = wl.gaussian_rows(112, 4, 32)
+    s, _, cost = tcq_gpu(X, 9, with_xhat=False)
+    check_tcq_rows(X, 9, s, None, cost)
+    st = torch.empty((4, 32), dtype=torch.int16, device=DEV)
+    c = torch.empty(4, device=DEV)
+    for kw in ({"k": 3}, {"scale": 0.0}, {"scale": float("nan")}):
+        with pytest.raises(Q.QuipError):
+            Q.quip_tcq_quantize(dev(X), 9, st, c, **kw)
+    with pytest.raises(Q.QuipError):
+        Q.quip_tcq_quantize(dev(X), 16, st, c)
