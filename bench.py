@@ -287,6 +287,43 @@ def inference_bench(Q, wl, dev, timed, lp, left, right, cfg) -> dict:
     return out
 
 
+def tcq_bench(Q, wl, dev, timed) -> dict:
+    """Trellis-coded quantization with the bitshift trellis at k = 2 bits per
+    step on an i.i.d. N(0,1) source: 4096 sequences of T = 256 (1M weights),
+    L = 12 and 15 state bits. Reports the mean squared error per weight
+    (against the distortion-rate bound at the rate k + (L - k)/T, and the
+    QTIP page's 256-D TCQ figures 0.068-0.071 as context), the time, and the
+    forward kernel's edge-relaxation rate from the library timing."""
+    import torch
+
+    rows, T = 4096, 256
+    X = torch.from_numpy(wl.gaussian_rows(3, rows, T)).to(dev)
+    st = torch.empty((rows, T), dtype=torch.int16, device=dev)
+    cost = torch.empty(rows, device=dev)
+    out = {"sequences": rows, "T": T, "k": 2, "printed_tcq_256d": [0.068, 0.071]}
+    for L in (12, 15):
+        ws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_tcq_workspace, rows, T, L), dev)
+        ms = timed(lambda: Q.quip_tcq_quantize(X, L, st, cost, ws=ws), 2)
+        Q.timing_reset()
+        Q.timing_enable(True)
+        Q.quip_tcq_quantize(X, L, st, cost, ws=ws)
+        torch.cuda.synchronize()
+        Q.timing_enable(False)
+        rep = Q.timing_report()
+        Q.timing_reset()
+        launches, fms, edges, _ = rep["tcq_forward_kernel"]
+        _, tms, _, _ = rep["tcq_traceback_kernel"]
+        rate = 2 + (L - 2) / T
+        out[f"L{L}"] = {"mse_per_weight": round(float(cost.double().sum().item()) / (rows * T), 5),
+                        "bits_per_weight": round(rate, 4),
+                        "distortion_rate_bound": round(2.0 ** (-2 * rate), 5),
+                        "ms": round(ms, 3), "weights_per_s": round(rows * T / (ms / 1e3), 1),
+                        "forward_ms": round(fms, 3), "traceback_ms": round(tms, 3),
+                        "edge_relaxations_per_s": round(edges / (fms / 1e3), 1)}
+        del ws
+    return out
+
+
 def variants_bench(Q, wl, dev, steps: int) -> dict:
     """The QuIP variants on the 4096 x 11008 MLP layer (3-bit, RHT left,
     Kronecker 64 x 172 right): without them, with the random permutation inside
@@ -520,9 +557,10 @@ def main():
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
     # beside the pass: Gaussian-source VQ, the inference product, the variants
-    gaussian_vq, inference, variants = {}, {}, {}
+    gaussian_vq, inference, variants, tcq = {}, {}, {}, {}
     if not args.no_extras:
         gaussian_vq = gaussian_vq_bench(Q, wl, dev, timed)
+        tcq = tcq_bench(Q, wl, dev, timed)
         inference = inference_bench(Q, wl, dev, timed, lp, left, right, cfg)
         if not args.no_variants:
             variants = variants_bench(Q, wl, dev, max(2, args.steps // 3))
@@ -547,6 +585,7 @@ def main():
         "weights_per_s_from_resident_H_W": round(mn / (from_resident / 1e3), 1),
         "rht": rht,
         "gaussian_vq": gaussian_vq,
+        "tcq": tcq,
         "inference": inference,
         "variants": variants,
         "roofline": roofline,
