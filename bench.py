@@ -260,14 +260,16 @@ def inference_bench(Q, wl, dev, timed, lp, left, right, cfg) -> dict:
             call()
         torch.cuda.synchronize()
         Q.timing_enable(False)
-        launches, kms, _, kbytes = Q.timing_report()["qmatvec_kernel"]
+        rep = Q.timing_report()
+        launches, kms, _, kbytes = rep["qmatvec_kernel"]
         Q.timing_reset()
+        per_kernel_us = {k: round(1e3 * v[1] / v[0], 2) for k, v in rep.items()}
         gbps = kbytes / (kms / 1e3) / 1e9
         return {"m": m, "n": n, "bits": bits, "packed_MB": round(m * rb / 1e6, 2),
                 "copies": len(packs), "product_us": round(1e3 * ms, 2),
                 "qmatvec_kernel_us": round(1e3 * kms / launches, 2),
                 "qmatvec_kernel_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 3),
-                "weights_per_s": round(m * n / (ms / 1e3), 1)}
+                "weights_per_s": round(m * n / (ms / 1e3), 1), "kernels_us": per_kernel_us}
 
     out = {"pass_layer": qmv_case([lp.buffers["codes"]], lp.buffers["scales"], left.signs,
                                   right.signs, cfg.bits, 50)}

@@ -8,16 +8,33 @@
 // [(j w) mod 8, + w) of byte (j w) / 8, w = 2, 4 or 8 the container width
 // (the smallest that holds b bits, so that no code straddles a byte).
 //
-// The product runs in three launches: x' = Q_R x (the row RHT on one row),
-// y' = W^~ x' (qmatvec_kernel), y = Q_L^T y' (the inverse row RHT on one
-// row). qmatvec_kernel is bound by the packed codes it streams and by the
-// VALU work of unpacking them: each thread owns CPT consecutive columns of a
-// row (n / CPT threads per row, CPT <= 64 so x' stays in registers), reads its
-// codes as 32-bit words and unpacks four at a time (a shift, a mask of one
-// code per byte, four byte-to-float conversions), and subtracts the grid
-// offset once through the sum of its x'. Four rows per thread per iteration;
-// the per-row sums are reduced across lanes with shuffles and across waves
-// through LDS.
+// The product runs in five launches: x' = Q_R x in two passes of
+// qmv_vec_fwht_kernel (H_n = H_n1 (x) H_n2: transforms of the contiguous chunks,
+// then of the strided columns, one short transform per wave), per-slice partial
+// sums of W^~ x' (qmv_mfma_kernel), and y = Q_L^T y' in two more passes, the
+// first of which forms y' (the sum of the slices times the row step).
+//
+// qmv_mfma_kernel puts the dot products on the matrix cores
+// (v_mfma_f32_16x16x32_f16), so the vector ALUs only unpack codes. A code c
+// of w bits becomes an exact half-precision value with one shift and one
+// and-or per pair of codes: OR-ing it into the mantissa of 1.0 gives
+// 1 + c 2^-p (p = 2, 4, 8 for w = 2, 4, 8). For w = 4 and 8 a packed half
+// subtraction then centres it, (c - (L-1)/2) 2^-p exactly; for w = 2 the
+// offset is removed once per block through the sum of x' instead (one VALU op
+// per code). x' enters as two half-precision columns, x' = hi + lo (about 22
+// bits), so the products are exact and the matrix cores accumulate in float32.
+//
+// Layout: a work-group is one wave and owns a slice of 256 KS columns (KS = 1
+// for n = 1024, else 2). Lane (r, h) of the wave (r = lane
+// mod 16 the row of the 16-row tile, h = lane / 16) reads one contiguous run of
+// 64 KS codes of its row (KS w / 2 loads of 16 bytes; the four runs of a row
+// are one contiguous 256 KS-code segment), which feeds 8 KS MFMA steps: the
+// k order inside an MFMA is a permutation of the run, and the x' operand (hi in
+// column 0, lo in column 1, zero elsewhere) is built once per work-group in the
+// same order and kept in registers while the work-group walks its row tiles.
+// The two used accumulator columns are added with one lane swap and each
+// slice writes one partial per row; the first pass of the inverse transform
+// sums the slices in a fixed order (deterministic; no atomics, no barriers).
 #include "common.h"
 
 namespace quip {
@@ -42,117 +59,293 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restri
   }
 }
 
-constexpr int QMV_RB = 4;  // rows per row-group and iteration
+typedef _Float16 qmv_half2 __attribute__((ext_vector_type(2)));
+typedef _Float16 qmv_half8 __attribute__((ext_vector_type(8)));
+typedef float qmv_float4 __attribute__((ext_vector_type(4)));
 
-// y'[r] = s_r sum_j (code_j - cen) x'_j for the rows of a persistent
-// work-group. T = n / CPT threads per row (64, 128 or 256).
-template <int W, int CPT>
-__global__ __launch_bounds__(256) void qmatvec_kernel(const uint8_t* __restrict__ packed,
-                                                      int64_t m, int64_t n,
-                                                      const float* __restrict__ scales,
-                                                      const float* __restrict__ xp, float cen,
-                                                      float* __restrict__ yp) {
-  constexpr int NW = CPT * W / 32;  // 32-bit words of codes per thread and row
-  constexpr int CPW = 32 / W;       // codes per word
-  constexpr int CPB = 8 / W;        // codes per byte
-  static_assert(NW >= 1 && CPT % 4 == 0, "thread chunk");
-  __shared__ float red[4][QMV_RB];
+// Position, within a lane's run of codes, of the code in MFMA step s, slot j
+// (j = 2v + t: A register v, half t), matching qmv_unpack.
+template <int W>
+__device__ __forceinline__ int qmv_code_index(int s, int j) {
+  const int v = j >> 1, t = j & 1;
+  if (W == 2) return 16 * (s >> 1) + 4 * (s & 1) + v + 8 * t;  // pairs (c, c + 8) of a word
+  if (W == 4) return 8 * s + v + 4 * t;                          // pairs (c, c + 4) of a word
+  return 4 * (2 * s + (v >> 1)) + (v & 1) + 2 * t;               // pairs (c, c + 2) of a word
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = int(n / CPT);  // threads per row: 64, 128 or 256
-  const int groups = 256 / T;  // row-groups per work-group
-  const int g = tid / T, p = tid % T;
-  const int wpr = T / 64;      // waves per row
-  const int64_t rowbytes = n * W / 8;
+// A operand of step s: four registers of two halves each, 1 + c 2^-p (W = 2)
+// or (c - cen) 2^-p (W = 4, 8), from the lane's code words q.
+// (a & m) | o in one instruction. A vector instruction here may read one
+// scalar register, so m comes from a scalar and o from a vector register
+// (the compiler otherwise splits the pair into an and and an or).
+__device__ __forceinline__ uint32_t qmv_and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
 
-  float x[CPT];
-  float xs = 0.f;
+// kmask selects the two codes' bits after the shift (0x03000300, 0x03C003C0
+// or 0x03FC03FC for W = 2, 4, 8; a kernel argument, so a scalar) and kone is
+// 1.0 in both halves (0x3C003C00, held in a vector register): each pair of
+// codes costs one shift and one v_and_or_b32.
+template <int W>
+__device__ __forceinline__ qmv_half8 qmv_unpack(const uint32_t* q, int s, qmv_half2 sub,
+                                                uint32_t kmask, uint32_t kone) {
+  uint32_t r[4];
+  if (W == 2) {
+    const uint32_t w = q[s >> 1];
+    const int e = s & 1;
 #pragma unroll
-  for (int v = 0; v < CPT / 4; ++v) {
-    const float4 t = *reinterpret_cast<const float4*>(xp + int64_t(p) * CPT + 4 * v);
-    x[4 * v + 0] = t.x;
-    x[4 * v + 1] = t.y;
-    x[4 * v + 2] = t.z;
-    x[4 * v + 3] = t.w;
-    xs += (t.x + t.y) + (t.z + t.w);
+    for (int v = 0; v < 4; ++v) {
+      const int j = 4 * e + v;  // codes j and j + 8 of the word
+      const uint32_t sh = j <= 4 ? (w << (8 - 2 * j)) : (w >> (2 * j - 8));
+      r[v] = qmv_and_or(sh, kmask, kone);
+    }
+  } else if (W == 4) {
+    const uint32_t w = q[s];
+    r[0] = qmv_and_or(w << 6, kmask, kone);
+    r[1] = qmv_and_or(w << 2, kmask, kone);
+    r[2] = qmv_and_or(w >> 2, kmask, kone);
+    r[3] = qmv_and_or(w >> 6, kmask, kone);
+  } else {
+    const uint32_t w0 = q[2 * s], w1 = q[2 * s + 1];
+    r[0] = qmv_and_or(w0 << 2, kmask, kone);
+    r[1] = qmv_and_or(w0 >> 6, kmask, kone);
+    r[2] = qmv_and_or(w1 << 2, kmask, kone);
+    r[3] = qmv_and_or(w1 >> 6, kmask, kone);
   }
-  const float off = cen * xs;  // this thread's share of the grid offset
+  qmv_half8 a;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    qmv_half2 h2 = __builtin_bit_cast(qmv_half2, r[v]);
+    if (W != 2) h2 = h2 - sub;  // exact: (1 + c 2^-p) - (1 + cen 2^-p)
+    a[2 * v] = h2[0];
+    a[2 * v + 1] = h2[1];
+  }
+  return a;
+}
 
-  const int64_t per_iter = int64_t(groups) * QMV_RB;
-  for (int64_t base = int64_t(blockIdx.x) * per_iter; base < m; base += int64_t(gridDim.x) * per_iter) {
-    float part[QMV_RB];
+// part[blockIdx.y][r] = sum over the wave's slice of 256 KS columns of
+// (code - cen) x'_j, for the rows r of the wave's tiles. One wave per
+// work-group: the slice's x' operand stays in registers while the wave walks
+// its row tiles, and every slice writes its own partials (no barriers).
+template <int W, int KS, int PF>
+__global__ __launch_bounds__(64) void qmv_mfma_kernel(const uint8_t* __restrict__ packed,
+                                                      int64_t m, int64_t n,
+                                                      const float* __restrict__ xp, float cen,
+                                                      float* __restrict__ part, uint32_t kmask,
+                                                      uint32_t kone) {
+  constexpr int STEPS = 8 * KS;        // MFMA steps per tile (8 codes per lane and step)
+  constexpr int RUN = 64 * KS;         // codes in a lane's run
+  constexpr int NQ = KS * W / 2;       // 16-byte loads per lane and tile
+  constexpr float P2 = W == 2 ? 4.f : (W == 4 ? 16.f : 256.f);  // 2^p
+
+  const int lane = threadIdx.x;
+  const int c = lane & 15, h = lane >> 4;
+  const int64_t rowbytes = n * W / 8;
+  const int64_t run0 = int64_t(blockIdx.y) * (4 * RUN) + int64_t(h) * RUN;
+
+  // x' operand: hi in the even columns, lo in the odd ones. Only columns 0
+  // and 1 of the product are read; the other columns only feed accumulator
+  // columns that are never used.
+  // (even lanes: hi = x rounded to half; odd lanes: lo = x - hi rounded, the
+  // difference being exact in float32; no select, so nothing stays live)
+  const float odd = float(c & 1);
+  qmv_half8 B[STEPS];
+  float xs = 0.f;  // this lane's halves, summed
 #pragma unroll
-    for (int q = 0; q < QMV_RB; ++q) {
-      const int64_t r = base + int64_t(g) * QMV_RB + q;
-      float acc = 0.f;
-      if (r < m) {
-        const uint32_t* src =
-            reinterpret_cast<const uint32_t*>(packed + r * rowbytes + int64_t(p) * (CPT * W / 8));
-        uint32_t wd[NW];
+  for (int s = 0; s < STEPS; ++s) {
 #pragma unroll
-        for (int i = 0; i < NW; ++i) wd[i] = src[i];
+    for (int j = 0; j < 8; ++j) {
+      const float x = xp[run0 + qmv_code_index<W>(s, j)];
+      const _Float16 b = _Float16(fmaf(-odd, float(_Float16(x)), x));
+      B[s][j] = b;
+      xs += float(b);
+    }
+  }
+  // the slice's sum of x' as the halves represent it (for the W = 2 offset):
+  // hi + lo from a lane pair, then the four runs of the lane groups h
+  xs += __shfl_xor(xs, 1, 64);
+  xs += __shfl_xor(xs, 16, 64);
+  xs += __shfl_xor(xs, 32, 64);
+  const qmv_half2 sub = {_Float16(1.f + cen / P2), _Float16(1.f + cen / P2)};
+  float* const out = part + int64_t(blockIdx.y) * m;
+
+  // code words of the tiles in flight: a ring of PF tiles per lane, refilled
+  // with the tile PF strides ahead as soon as a slot is consumed
+  const uint8_t* const base = packed + run0 * W / 8;
+  auto load = [&](uint32_t* q, int64_t t) {
+    const int64_t row = t * 16 + c;
+    if (row < m) {
+      const uint4* src = reinterpret_cast<const uint4*>(base + row * rowbytes);
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
+      for (int i = 0; i < NQ; ++i) {
+        const uint4 v = src[i];
+        q[4 * i] = v.x;
+        q[4 * i + 1] = v.y;
+        q[4 * i + 2] = v.z;
+        q[4 * i + 3] = v.w;
+      }
+    } else {
 #pragma unroll
-          for (int sh = 0; sh < 8; sh += W) {
-            const uint32_t t = (wd[i] >> sh) & (0x01010101u * ((1u << W) - 1u));
+      for (int i = 0; i < 4 * NQ; ++i) q[i] = 0u;
+    }
+  };
+  const int64_t g = gridDim.x;
+  uint32_t ring[PF][4 * NQ];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float c = float((t >> (8 * k)) & 0xFFu);
-              acc = fmaf(c, x[i * CPW + k * CPB + sh / W], acc);
-            }
+  for (int k = 0; k < PF; ++k) load(ring[k], int64_t(blockIdx.x) + k * g);
+
+  for (int64_t t = blockIdx.x; t * 16 < m;) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      if (t * 16 < m) {
+        qmv_float4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qmv_unpack<W>(ring[k], s, sub, kmask, kone),
+                                                     B[s], D, 0, 0, 0);
+        load(ring[k], t + PF * g);
+        // lane (c, h) holds rows 4h..4h+3 of column c: add columns 0 and 1
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[i] += __shfl_xor(D[i], 1, 64);
+        const int64_t r0 = t * 16 + 4 * h;
+        if (c == 0 && r0 < m) {
+          float4 v;
+          v.x = W == 2 ? P2 * D[0] - (P2 + cen) * xs : P2 * D[0];
+          v.y = W == 2 ? P2 * D[1] - (P2 + cen) * xs : P2 * D[1];
+          v.z = W == 2 ? P2 * D[2] - (P2 + cen) * xs : P2 * D[2];
+          v.w = W == 2 ? P2 * D[3] - (P2 + cen) * xs : P2 * D[3];
+          if (r0 + 4 <= m) {
+            *reinterpret_cast<float4*>(out + r0) = v;
+          } else {  // m < 4 (a power of two: 2)
+            out[r0] = v.x;
+            if (r0 + 1 < m) out[r0 + 1] = v.y;
           }
         }
-        acc -= off;
-      }
-      part[q] = acc;
-    }
-    // sums over the T threads of each row: lanes, then the waves of the row
-#pragma unroll
-    for (int q = 0; q < QMV_RB; ++q) {
-      float v = part[q];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      part[q] = v;
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int q = 0; q < QMV_RB; ++q) red[wave][q] = part[q];
-    }
-    __syncthreads();
-    if (tid < groups * QMV_RB) {
-      const int gg = tid / QMV_RB, q = tid % QMV_RB;
-      const int64_t r = base + int64_t(gg) * QMV_RB + q;
-      if (r < m) {
-        float v = 0.f;
-        for (int w = 0; w < wpr; ++w) v += red[gg * wpr + w][q];
-        yp[r] = scales[r] * v;
+        t += g;
       }
     }
-    __syncthreads();
   }
 }
 
+// One transform of length L <= 128 per wave for a vector of length n = n1 n2
+// seen as an n1 x n2 row-major matrix (index i = a n2 + b): the natural-order
+// Sylvester matrix is H_n = H_n1 (x) H_n2, so H_n v is H_n2 on every row (the
+// contiguous chunks, pass 0) followed by H_n1 on every column (stride n2,
+// pass 1). Lane l holds elements u = l and u = l + 64 of its transform; the
+// butterflies on bits 0..5 of u go through lane shuffles. Options by pass:
+//   pass 0: in[i] times pre[i] (the random signs of the forward transform),
+//           or, with part given, in[i] = scales[i] * sum_b part[b][i] (the
+//           product's partial sums; the finish of the inverse transform);
+//   pass 1: times scale, then times post[i] (the signs of the inverse).
+__global__ __launch_bounds__(64) void qmv_vec_fwht_kernel(
+    const float* __restrict__ in, float* __restrict__ out, int pass, int L, int64_t n2,
+    const float* __restrict__ pre, const float* __restrict__ part, int nblk, int64_t m,
+    const float* __restrict__ scales, const float* __restrict__ post, float scale) {
+  const int lane = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int64_t base = pass == 0 ? t * L : t;      // first element of this transform
+  const int64_t step = pass == 0 ? 1 : n2;         // distance between its elements
+  float v[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = lane + 64 * k;
+    if (u < L) {
+      const int64_t i = base + int64_t(u) * step;
+      float x;
+      if (part) {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;  // nblk is a multiple of 4
+        for (int b = 0; b < nblk; b += 4) {
+          a0 += part[int64_t(b) * m + i];
+          a1 += part[int64_t(b + 1) * m + i];
+          a2 += part[int64_t(b + 2) * m + i];
+          a3 += part[int64_t(b + 3) * m + i];
+        }
+        x = scales[i] * ((a0 + a1) + (a2 + a3));
+      } else {
+        x = in[i];
+      }
+      if (pre) x *= pre[i];
+      v[k] = x;
+    }
+  }
+  if (L == 128) {  // bit 6 of u: within the lane
+    const float a = v[0], b = v[1];
+    v[0] = a + b;
+    v[1] = a - b;
+  }
+  for (int j = 1; j < 64 && j < L; j <<= 1) {  // bits 0..5 of u: across lanes
+    const bool upper = (lane & j) != 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float o = __shfl_xor(v[k], j, 64);
+      v[k] = upper ? o - v[k] : v[k] + o;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = lane + 64 * k;
+    if (u < L) {
+      const int64_t i = base + int64_t(u) * step;
+      float x = v[k] * scale;
+      if (post) x *= post[i];
+      out[i] = x;
+    }
+  }
+}
+
+// n = n1 n2 with n2 = 2^ceil(k/2) <= 128 (n <= 16384)
+inline int64_t vec_n2(int64_t n) { return int64_t(1) << ((ilog2(n) + 1) / 2); }
+
+quip_status vec_fwht_pass(const float* in, float* out, int pass, int64_t n, const float* pre,
+                          const float* part, int nblk, const float* scales, const float* post,
+                          float scale, hipStream_t s) {
+  const int64_t n2 = vec_n2(n), n1 = n / n2;
+  const int L = int(pass == 0 ? n2 : n1);
+  const int64_t count = pass == 0 ? n1 : n2;
+  const double bytes = 8.0 * double(n) + (part ? 4.0 * double(nblk) * double(n) : 0.0);
+  return timed_launch("qmv_vec_fwht_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(qmv_vec_fwht_kernel, dim3(unsigned(count)), dim3(64), 0, s, in, out, pass, L, n2,
+                pre, part, nblk, n, scales, post, scale);
+  }, double(n) * double(ilog2(L)), bytes);
+}
+
+constexpr int QMV_PF = 3;  // tiles in flight per wave
+int qmv_ks(int64_t n) { return n >= 2048 ? 2 : 1; }
+int64_t qmv_blocks(int64_t n) { return n / (256 * qmv_ks(n)); }  // column slices, one per wave
+
 template <int W>
-quip_status qmatvec_t(const uint8_t* packed, int64_t m, int64_t n, const float* scales,
-                      const float* xp, float cen, float* yp, hipStream_t s) {
-  const int cpt = n >= 4096 ? 64 : int(n / 64);
-  const int T = int(n / cpt);
-  const int64_t per_iter = int64_t(256 / T) * QMV_RB;
-  int64_t nwg = cdiv(m, per_iter);
-  if (nwg > 2048) nwg = 2048;
-  const dim3 grid{unsigned(nwg)};
-  const double bytes = double(m) * double(n) * W / 8.0 + 4.0 * double(n + 2 * m);
+quip_status qmv_mfma_t(const uint8_t* packed, int64_t m, int64_t n, const float* xp, float cen,
+                       float* part, hipStream_t s) {
+  const int64_t nblk = qmv_blocks(n);
+  const int64_t tiles = cdiv(m, 16);
+  // as many one-wave work-groups as are resident at once, split over the
+  // column slices; each walks its share of the row tiles
+  const void* kfn = qmv_ks(n) == 2 ? reinterpret_cast<const void*>(&qmv_mfma_kernel<W, 2, QMV_PF>)
+                                   : reinterpret_cast<const void*>(&qmv_mfma_kernel<W, 1, QMV_PF>);
+  int per_cu = 0, dev = 0, cus = 0;
+  int64_t resident = 4096;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, 64, 0) == hipSuccess &&
+      hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      per_cu > 0 && cus > 0)
+    resident = int64_t(per_cu) * cus;
+  int64_t gx = resident / nblk;
+  if (gx < 1) gx = 1;
+  if (gx > tiles) gx = tiles;
+  const dim3 grid{unsigned(gx), unsigned(nblk)};
+  const uint32_t kmask = W == 2 ? 0x03000300u : (W == 4 ? 0x03C003C0u : 0x03FC03FCu);
+  const uint32_t kone = 0x3C003C00u;  // 1.0 in both halves
+  const double bytes = double(m) * double(n) * W / 8.0 + 4.0 * double(n) + 4.0 * double(nblk) * double(m);
   const double flops = 2.0 * double(m) * double(n);
   return timed_launch("qmatvec_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    switch (cpt) {
-#define CASE(C)                                                                           \
-  case C:                                                                                 \
-    QUIP_KERNEL((qmatvec_kernel<W, C>), grid, dim3(256), 0, s, packed, m, n, scales, xp, cen, yp); \
-    break;
-      CASE(16) CASE(32) CASE(64)
-#undef CASE
-    }
+    if (qmv_ks(n) == 2)
+      QUIP_KERNEL((qmv_mfma_kernel<W, 2, QMV_PF>), grid, dim3(64), 0, s, packed, m, n, xp, cen,
+                  part, kmask, kone);
+    else
+      QUIP_KERNEL((qmv_mfma_kernel<W, 1, QMV_PF>), grid, dim3(64), 0, s, packed, m, n, xp, cen,
+                  part, kmask, kone);
   }, flops, bytes);
 }
 
@@ -177,8 +370,9 @@ quip_status pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, 
 
 size_t qmatvec_workspace_bytes(int64_t m, int64_t n) {
   Carver c(nullptr, 0);
-  c.take<float>(size_t(n));  // x'
-  c.take<float>(size_t(m));  // y'
+  c.take<float>(size_t(n));                    // x'
+  c.take<float>(size_t(m > n ? m : n));        // between the two passes of a transform
+  c.take<float>(size_t(qmv_blocks(n) * m));    // per-slice partial sums
   return c.used;
 }
 
@@ -187,15 +381,24 @@ quip_status qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int bits, c
                         float* y, void* ws, size_t ws_bytes, hipStream_t s) {
   Carver c(ws, ws_bytes);
   float* xp = c.take<float>(size_t(n));
-  float* yp = c.take<float>(size_t(m));
+  float* tmp = c.take<float>(size_t(m > n ? m : n));
+  float* part = c.take<float>(size_t(qmv_blocks(n) * m));
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_qmatvec_rht: workspace too small");
   const float cen = 0.5f * float((1 << bits) - 1);
-  QUIP_TRY(rht_rows(x, xp, 1, n, n, signs_right, false, s));  // x' = Q_R x
+  // x' = Q_R x = H_n diag(signs_right) x / sqrt(n): two passes, signs first
+  QUIP_TRY(vec_fwht_pass(x, tmp, 0, n, signs_right, nullptr, 0, nullptr, nullptr, 1.f, s));
+  QUIP_TRY(vec_fwht_pass(tmp, xp, 1, n, nullptr, nullptr, 0, nullptr, nullptr,
+                         1.0f / sqrtf(float(n)), s));
   const int w = code_container_bits(bits);
-  if (w == 2) QUIP_TRY(qmatvec_t<2>(packed, m, n, scales, xp, cen, yp, s));
-  else if (w == 4) QUIP_TRY(qmatvec_t<4>(packed, m, n, scales, xp, cen, yp, s));
-  else QUIP_TRY(qmatvec_t<8>(packed, m, n, scales, xp, cen, yp, s));
-  return rht_rows(yp, y, 1, m, m, signs_left, true, s);  // y = Q_L^T y'
+  if (w == 2) QUIP_TRY(qmv_mfma_t<2>(packed, m, n, xp, cen, part, s));
+  else if (w == 4) QUIP_TRY(qmv_mfma_t<4>(packed, m, n, xp, cen, part, s));
+  else QUIP_TRY(qmv_mfma_t<8>(packed, m, n, xp, cen, part, s));
+  // y = Q_L^T y' = diag(signs_left) H_m y' / sqrt(m), with y' = scales * (sum of
+  // the slices' partials) formed in the first pass
+  const int nblk = int(qmv_blocks(n));
+  QUIP_TRY(vec_fwht_pass(nullptr, tmp, 0, m, nullptr, part, nblk, scales, nullptr, 1.f, s));
+  return vec_fwht_pass(tmp, y, 1, m, nullptr, nullptr, 0, nullptr, signs_left,
+                       1.0f / sqrtf(float(m)), s);
 }
 
 }  // namespace quip
