@@ -326,6 +326,49 @@ def tcq_bench(Q, wl, dev, timed) -> dict:
     return out
 
 
+def e8_config_bench(Q, wl, dev, steps: int) -> dict:
+    """The E8 configuration (4096 x 4096, BlockLDLQ with g = 8 and the 65536-point
+    E8 codebook at 2 bits per weight): time per pass, its phases, and the E8
+    kernels' rates (matrix-core flops of the distance contractions, 2 x 8 per
+    vector and codeword) against the fp32 matrix-core peak."""
+    import torch
+
+    L = wl.make_layer("c5")
+    cfg = L.cfg
+    W = torch.from_numpy(L.W).to(dev)
+    X = torch.from_numpy(L.X).to(dev)
+    lp = Q.LayerPass(cfg.m, cfg.n, Q.SideSpec.from_numpy(L.left, dev), Q.SideSpec.from_numpy(L.right, dev),
+                     quant=cfg.quant, bits=cfg.bits, B=cfg.B, g=cfg.g, alpha=cfg.alpha, device=dev)
+    lp.run(W, X)
+    torch.cuda.synchronize()
+    events = {}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lp.run(W, X, events=events)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    order = ["hessian", "incoherence_H", "incoherence_W", "ldl", "ldlq", "postprocess", "end"]
+    phases = {a: round(float(np.mean([ea.elapsed_time(eb) for ea, eb in zip(events[a], events[b])])), 3)
+              for a, b in zip(order[:-1], order[1:])}
+    Q.timing_reset()
+    Q.timing_enable(True)
+    lp.run(W, X)
+    torch.cuda.synchronize()
+    Q.timing_enable(False)
+    rep = Q.timing_report()
+    Q.timing_reset()
+    kern = {}
+    for k, (launches, kms, flops, _) in sorted(rep.items(), key=lambda kv: -kv[1][1])[:6]:
+        v = {"launches": launches, "ms": round(kms, 3)}
+        if k.startswith("e8_") and flops > 0:
+            tf = flops / (kms / 1e3) / 1e12
+            v.update({"TFLOPs": round(tf, 2), "frac_of_fp32_mfma_peak": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)})
+        kern[k] = v
+    return {"workload": f"c5: {cfg.description}", "ms_per_pass": round(ms, 3),
+            "weights_per_s": round(cfg.m * cfg.n / (ms / 1e3), 1), "phases_ms": phases,
+            "proxy_loss": float(lp.buffers["loss"].item()), "top_kernels": kern}
+
+
 def variants_bench(Q, wl, dev, steps: int) -> dict:
     """The QuIP variants on the 4096 x 11008 MLP layer (3-bit, RHT left,
     Kronecker 64 x 172 right): without them, with the random permutation inside
@@ -559,8 +602,9 @@ def main():
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
     # beside the pass: Gaussian-source VQ, the inference product, the variants
-    gaussian_vq, inference, variants, tcq = {}, {}, {}, {}
+    gaussian_vq, inference, variants, tcq, e8c = {}, {}, {}, {}, {}
     if not args.no_extras:
+        e8c = e8_config_bench(Q, wl, dev, 2)
         gaussian_vq = gaussian_vq_bench(Q, wl, dev, timed)
         tcq = tcq_bench(Q, wl, dev, timed)
         inference = inference_bench(Q, wl, dev, timed, lp, left, right, cfg)
@@ -586,6 +630,7 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in phases.items()},
         "weights_per_s_from_resident_H_W": round(mn / (from_resident / 1e3), 1),
         "rht": rht,
+        "e8_config": e8c,
         "gaussian_vq": gaussian_vq,
         "tcq": tcq,
         "inference": inference,

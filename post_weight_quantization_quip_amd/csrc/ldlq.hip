@@ -425,21 +425,46 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* W, int64_t n,
   for (int64_t j = tid; j < n; j += 256) Wn[row * n + j] = w[j] / r;
 }
 
-__global__ void e8_norms_kernel(const float* C, float* c2) {
+__global__ void e8_norms_kernel(const float* C, float* c2, _Float16* c16) {
   int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= 65536) return;
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s = fmaf(C[i * 8 + k], C[i * 8 + k], s);
+  for (int k = 0; k < 8; ++k) {
+    s = fmaf(C[i * 8 + k], C[i * 8 + k], s);
+    c16[i * 8 + k] = _Float16(C[i * 8 + k]);
+  }
   c2[i] = s;
 }
 
 // Squared error of the nearest codeword, summed over all 8-vectors, for every
 // candidate scale. One wave: 32 vectors x all codewords; lanes 0-31 and 32-63
 // see the same vectors and different codeword rows of each 32x32 block.
+typedef _Float16 e8_half8 __attribute__((ext_vector_type(8)));
+
+// The dot products <y, c> of 32 vectors with a 32-codeword tile in one
+// v_mfma_f32_32x32x16_f16: A holds each codeword twice along k (codewords are
+// exact in half precision), B holds y rounded to half (k < 8) and the half
+// rounding of the remainder (k >= 8), so the product is <c, hi + lo> with
+// hi + lo within about 2^-22 of y, accumulated in float32. Lane (j, g) with
+// j = lane mod 32 gives codeword row j of A (the same 8 halves for g = 0, 1)
+// and column j of B (hi for g = 0, lo for g = 1), and receives the dots of
+// vector j with codewords 8 (r / 4) + 4 g + r mod 4 of the tile (r < 16).
+__device__ __forceinline__ e8_half8 e8_split_operand(const float* y8, int g) {
+  e8_half8 b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const _Float16 hi = _Float16(y8[k]);
+    b[k] = g == 0 ? hi : _Float16(y8[k] - float(hi));
+  }
+  return b;
+}
+
+// Squared error of the nearest codeword, summed over all 8-vectors, for every
+// candidate scale. One wave: 32 vectors x all codewords.
 template <int NC>
 __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__ Y, int64_t nvec,
-                                                       const float* __restrict__ C,
+                                                       const _Float16* __restrict__ C16,
                                                        const float* __restrict__ c2,
                                                        const float* __restrict__ cand, int ncand,
                                                        double* __restrict__ sse) {
@@ -451,39 +476,64 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
   const int j = lane & 31, kh = lane >> 5;
   const int64_t vj = v0 + j;
   const bool live = vj < nvec;
-  float yk[4];
+  float y8[8];
   float y2 = 0.f;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) yk[st] = live ? Y[vj * 8 + 2 * st + kh] : 0.f;
-  if (live) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) y2 = fmaf(Y[vj * 8 + k], Y[vj * 8 + k], y2);
+  for (int k = 0; k < 8; ++k) {
+    y8[k] = live ? Y[vj * 8 + k] : 0.f;
+    y2 = fmaf(y8[k], y8[k], y2);
   }
+  const e8_half8 yb = e8_split_operand(y8, kh);
   float sc[NC], best[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     sc[c] = cand[c < ncand ? c : 0];
     best[c] = 3.4e38f;
   }
+  // For every scale s the distance term is s n_i - 2 <y, c_i> with n_i = |c_i|^2.
+  // Over codewords of one norm it is smallest at the largest dot product, and
+  // fma(s, n, -2 x) does not increase with x, so each lane keeps the largest
+  // dot of the current run of equal norms and folds it into the 32 minima
+  // when the norm changes: the minima equal those over every codeword taken
+  // one by one, for any codebook order (sorted by norm, as quip_e8_codebook
+  // returns it, there are seven runs and almost every tile takes one max per
+  // value).
+  float run_n = c2[0], run_max = -3.4e38f;
+  auto fold = [&]() {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) best[c] = fminf(best[c], fmaf(sc[c], run_n, -2.f * run_max));
+  };
+  // the next tile's codeword (as 8 halves) and norm are loaded one tile ahead
+  uint4 cw_next = reinterpret_cast<const uint4*>(C16)[j];
+  float cn_next = c2[j];
   for (int cw0 = 0; cw0 < 65536; cw0 += 32) {
+    const uint4 cw = cw_next;
+    const float cn = cn_next;  // lane l: the norm of codeword cw0 + (l mod 32)
+    if (cw0 + 32 < 65536) {
+      cw_next = reinterpret_cast<const uint4*>(C16)[cw0 + 32 + j];
+      cn_next = c2[cw0 + 32 + j];
+    }
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, cw), yb, acc, 0, 0, 0);
+    if (__all(cn == run_n)) {  // the whole tile continues the run
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      float av = C[(cw0 + j) * 8 + 2 * st + kh];  // A[i][k] = codeword i, coordinate k
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, yk[st], acc, 0, 0, 0);
-    }
-    // D[i][j]: lane holds vector j and codewords i = 8*(r/4) + 4*kh + r%4
+      for (int r = 0; r < 16; ++r) run_max = fmaxf(run_max, acc[r]);
+    } else {  // a run ends inside this tile
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
-      const float n2 = c2[i];
-      const float d2 = -2.f * acc[r];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) best[c] = fminf(best[c], fmaf(sc[c], n2, d2));
+      for (int r = 0; r < 16; ++r) {
+        const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
+        if (n2 != run_n) {
+          fold();
+          run_n = n2;
+          run_max = -3.4e38f;
+        }
+        run_max = fmaxf(run_max, acc[r]);
+      }
     }
   }
+  fold();
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float other = __shfl_xor(best[c], 32, 64);
@@ -497,60 +547,116 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
   if (tid < ncand && tid < NC) atomicAdd(&sse[tid], red[tid]);
 }
 
-// One group step of BlockLDLQ: pre-rounding vectors of 32 rows (with the
-// in-block feedback of the earlier groups of the block), then the argmin over
-// a chunk of codewords. 4 waves split the chunk; atomicMin per row.
-__global__ __launch_bounds__(256) void e8_argmin_kernel(
+// Pre-rounding vectors of one group step of BlockLDLQ, once per step:
+// y[row][k] = Wn[row][c0 + k] + F[row][c0 + k] + sum_{c < nprev} E[row][c] U[s0 + c][c0 + k]
+// (the in-block feedback of the block's earlier groups). 16 lanes per row
+// split the sum over c and add their partial sums with lane shuffles.
+__global__ __launch_bounds__(256) void e8_prerounding_kernel(
     const float* __restrict__ Wn, int64_t n, const float* __restrict__ F, bool useF,
     const float* __restrict__ Eb, int64_t lde, int nprev, const float* __restrict__ U,
-    int64_t c0, int64_t s0, const float* __restrict__ C, const float* __restrict__ c2,
+    int64_t c0, int64_t s0, int64_t m, float* __restrict__ y8) {
+  const int sub = threadIdx.x & 15;
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (row < m) {
+    for (int c = sub; c < nprev; c += 16) {
+      const float e = Eb[row * lde + c];
+      const float* u = U + (s0 + c) * n + c0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(e, u[k], acc[k]);
+    }
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 64);
+  }
+  if (row < m && sub < 8) {
+    float v = acc[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) v = sub == k ? acc[k] : v;
+    float y = Wn[row * n + c0 + sub] + v;
+    if (useF) y += F[row * n + c0 + sub];
+    y8[row * 8 + sub] = y;
+  }
+}
+
+// One group step of BlockLDLQ: the nearest scaled codeword to each row's
+// pre-rounding vector over a chunk of codewords (4 waves split the chunk;
+// atomicMin of a packed (distance, index) key per row). The dot products come
+// from the split half-precision product of e8_scale_kernel; the distance term
+// s n_i - 2 <y, c_i> is smallest, over a run of equal norms, at the largest
+// dot, so each lane keeps that dot (and its first index) per run and compares
+// runs by distance; ties go to the lower index.
+__global__ __launch_bounds__(256) void e8_argmin_kernel(
+    const float* __restrict__ y8g, const _Float16* __restrict__ C16, const float* __restrict__ c2,
     const float* __restrict__ sp, int64_t m, int chunk, unsigned long long* __restrict__ keys) {
-  __shared__ float ysh[32][8];
   __shared__ unsigned long long ksh[4][32];
   const float s = *sp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t r0 = int64_t(blockIdx.x) * 32;
-  // pre-rounding values: 256 threads = 32 rows x 8 coordinates
-  {
-    const int rr = tid >> 3, kk = tid & 7;
-    const int64_t row = r0 + rr;
-    float y = 0.f;
-    if (row < m) {
-      y = Wn[row * n + c0 + kk];
-      if (useF) y += F[row * n + c0 + kk];
-      // earlier columns of this block: E[row, s0 + c] U[s0 + c, c0 + kk]
-      for (int c = 0; c < nprev; ++c) y = fmaf(Eb[row * lde + c], U[(s0 + c) * n + c0 + kk], y);
-    }
-    ysh[rr][kk] = y;
-  }
-  __syncthreads();
   const int j = lane & 31, kh = lane >> 5;
-  float yk[4];
+  float y8[8];
+  {
+    const int64_t row = r0 + j;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) yk[st] = ysh[j][2 * st + kh];
+    for (int k = 0; k < 8; ++k) y8[k] = row < m ? y8g[row * 8 + k] : 0.f;
+  }
+  const e8_half8 yb = e8_split_operand(y8, kh);
   const int cbeg = blockIdx.y * chunk + wave * (chunk / 4);
   const int cend = cbeg + chunk / 4;
   float bestv = 3.4e38f;
   int besti = cbeg;  // always a valid codeword, even if every distance is NaN
+  float run_n = c2[cbeg], run_max = -3.4e38f;
+  int run_i = cbeg;
+  auto fold = [&]() {
+    const float v = fmaf(s, run_n, -2.f * run_max);
+    if (v < bestv) {  // runs are visited in increasing index within a lane
+      bestv = v;
+      besti = run_i;
+    }
+  };
+  uint4 cw_next = reinterpret_cast<const uint4*>(C16)[cbeg + j];
+  float cn_next = c2[cbeg + j];
   for (int cw0 = cbeg; cw0 < cend; cw0 += 32) {
+    const uint4 cw = cw_next;
+    const float cn = cn_next;
+    if (cw0 + 32 < cend) {
+      cw_next = reinterpret_cast<const uint4*>(C16)[cw0 + 32 + j];
+      cn_next = c2[cw0 + 32 + j];
+    }
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, cw), yb, acc, 0, 0, 0);
+    if (__all(cn == run_n)) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      float av = C[(cw0 + j) * 8 + 2 * st + kh];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, yk[st], acc, 0, 0, 0);
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
+        const bool gt = acc[r] > run_max;
+        run_max = gt ? acc[r] : run_max;
+        run_i = gt ? i : run_i;
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
-      const float v = fmaf(s, c2[i], -2.f * acc[r]);
-      if (v < bestv) {  // codewords visited in increasing index within a lane
-        bestv = v;
-        besti = i;
+      for (int r = 0; r < 16; ++r) {
+        const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
+        const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
+        if (n2 != run_n) {
+          fold();
+          run_n = n2;
+          run_max = -3.4e38f;
+          run_i = i;
+        }
+        const bool gt = acc[r] > run_max;
+        run_max = gt ? acc[r] : run_max;
+        run_i = gt ? i : run_i;
       }
     }
   }
+  fold();
   unsigned long long key = (unsigned long long)ordered_bits(bestv) << 32 | uint32_t(besti);
   unsigned long long other = __shfl_xor(key, 32, 64);
   key = key < other ? key : other;
@@ -565,14 +671,13 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
 
 // Finish a group step: codes, quantized values, errors; reset the keys. With
 // rowloss, also the group's proxy-loss term rms^2 (y - q) D_g (y - q)^T, y the
-// pre-rounding vector (normalized domain) recomputed as in e8_argmin_kernel.
+// pre-rounding vector (normalized domain) of e8_prerounding_kernel.
 __global__ void e8_finish_kernel(const float* __restrict__ Wn, int64_t n, const float* __restrict__ C,
                                  const float* __restrict__ sp, const float* __restrict__ rms,
                                  int64_t c0, int64_t m,
                                  unsigned long long* __restrict__ keys, uint16_t* __restrict__ codes,
                                  int64_t ldcode, float* __restrict__ What, float* __restrict__ Eb,
-                                 int64_t lde, int ecol, const float* __restrict__ F, bool useF,
-                                 const float* __restrict__ U, int64_t s0,
+                                 int64_t lde, int ecol, const float* __restrict__ y8,
                                  const float* __restrict__ Dg, double* __restrict__ rowloss) {
   const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (row >= m) return;
@@ -585,12 +690,7 @@ __global__ void e8_finish_kernel(const float* __restrict__ Wn, int64_t n, const 
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const float qv = s * C[code * 8 + k];
-    if (rowloss) {
-      float y = Wn[row * n + c0 + k];
-      if (useF) y += F[row * n + c0 + k];
-      for (int c = 0; c < ecol; ++c) y = fmaf(Eb[row * lde + c], U[(s0 + c) * n + c0 + k], y);
-      res[k] = double(y) - double(qv);
-    }
+    if (rowloss) res[k] = double(y8[row * 8 + k]) - double(qv);
     Eb[row * lde + ecol + k] = Wn[row * n + c0 + k] - qv;
     if (What) What[row * n + c0 + k] = r * qv;
   }
@@ -658,6 +758,7 @@ struct E8Ws {
   float* Eb;
   unsigned long long* keys;
   float* c2;
+  _Float16* c16;  // the codebook in half precision (exact: multiples of 1/2 up to 3.5)
   float* cand;
   double* sse;
 };
@@ -684,12 +785,12 @@ quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, con
   dim3 grid(unsigned(cdiv(nvec, 128)));
   QUIP_TRY(timed_launch("e8_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (ncand <= 32)
-      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, e.c16, e.c2, e.cand,
                          ncand, e.sse);
     else
-      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, C, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, e.c16, e.c2, e.cand,
                          ncand, e.sse);
-  }));
+  }, 16.0 * 65536.0 * double(nvec), 32.0 * double(nvec)));  // <y, c> for every vector and codeword
   QUIP_TRY(timed_launch("e8_pick_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
   }));
@@ -767,6 +868,7 @@ size_t scales_workspace_bytes(int64_t m, int64_t n, const quip_quantizer& q) {
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
     c.take<float>(65536);          // |c|^2
+    c.take<_Float16>(65536 * 8);   // the codebook in half precision
     c.take<double>(64);            // sse
   }
   return c.used;
@@ -788,6 +890,7 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   E8Ws e{};
   e.Wn = c.take<float>(size_t(m) * n);
   e.c2 = c.take<float>(65536);
+  e.c16 = c.take<_Float16>(65536 * 8);
   e.sse = c.take<double>(64);
   e.cand = fac;
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_scales: workspace too small");
@@ -798,7 +901,7 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
                        true);
   }));
   QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2, e.c16);
   }));
   return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
 }
@@ -823,7 +926,9 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
     c.take<unsigned long long>(size_t(m));
+    c.take<float>(size_t(m) * 8);  // pre-rounding vectors of a group step
     c.take<float>(65536);
+    c.take<_Float16>(65536 * 8);
     c.take<double>(64);
   }
   (void)g;
@@ -874,7 +979,9 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   E8Ws e{};
   e.Wn = c.take<float>(size_t(m) * n);
   e.keys = c.take<unsigned long long>(size_t(m));
+  float* y8 = c.take<float>(size_t(m) * 8);
   e.c2 = c.take<float>(65536);
+  e.c16 = c.take<_Float16>(65536 * 8);
   e.sse = c.take<double>(64);
   e.cand = fac;
   e.F = F;
@@ -886,7 +993,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
                        compute);
   }));
   QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2);
+    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2, e.c16);
   }));
   if (compute) {
     host_e8_candidates(q.n_cand, hostf);
@@ -903,15 +1010,20 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   for (int64_t j0 = 0; j0 < n; j0 += B) {
     const int64_t bo = (n - j0 < B) ? n - j0 : B;
     for (int64_t c0 = j0; c0 < j0 + bo; c0 += 8) {
+      const int nprev = int(c0 - j0);
+      QUIP_TRY(timed_launch("e8_prerounding_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL(e8_prerounding_kernel, dim3(unsigned(cdiv(m, 16))), dim3(256), 0, s, e.Wn, n, F,
+                    j0 > 0, Eb, B, nprev, U, c0, j0, m, y8);
+      }, 16.0 * double(m) * double(nprev), 4.0 * double(m) * (double(nprev) + 24.0)));
       dim3 grid(unsigned(cdiv(m, 32)), unsigned(65536 / chunk));
       QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, e.Wn, n, F, j0 > 0, Eb, B,
-                           int(c0 - j0), U, c0, j0, codebook, e.c2, sglob, m, chunk, e.keys);
-      }));
+        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.c16, e.c2, sglob, m, chunk,
+                    e.keys);
+      }, 16.0 * 65536.0 * double(m), 32.0 * double(m) + 8.0 * double(m) * 8.0));
       QUIP_TRY(timed_launch("e8_finish_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
         QUIP_KERNEL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
                            codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
-                           int(c0 - j0), F, j0 > 0, U, j0, D, rl);
+                           nprev, y8, D, rl);
       }));
     }
     QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
