@@ -503,20 +503,10 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = fminf(best[c], fmaf(sc[c], run_n, -2.f * run_max));
   };
-  // the next tile's codeword (as 8 halves) and norm are loaded one tile ahead
-  uint4 cw_next = reinterpret_cast<const uint4*>(C16)[j];
-  float cn_next = c2[j];
-  for (int cw0 = 0; cw0 < 65536; cw0 += 32) {
-    const uint4 cw = cw_next;
-    const float cn = cn_next;  // lane l: the norm of codeword cw0 + (l mod 32)
-    if (cw0 + 32 < 65536) {
-      cw_next = reinterpret_cast<const uint4*>(C16)[cw0 + 32 + j];
-      cn_next = c2[cw0 + 32 + j];
-    }
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, cw), yb, acc, 0, 0, 0);
+  // tiles go in pairs (two independent products, so one tile's maxima overlap
+  // the other's product); the next pair's codewords (as 8 halves) and norms
+  // are loaded one pair ahead
+  auto tile = [&](const f32x16& acc, float cn) {
     if (__all(cn == run_n)) {  // the whole tile continues the run
 #pragma unroll
       for (int r = 0; r < 16; ++r) run_max = fmaxf(run_max, acc[r]);
@@ -532,6 +522,29 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
         run_max = fmaxf(run_max, acc[r]);
       }
     }
+  };
+  const uint4* C4 = reinterpret_cast<const uint4*>(C16);
+  uint4 na = C4[j], nb = C4[32 + j];
+  float nca = c2[j], ncb = c2[32 + j];
+  for (int cw0 = 0; cw0 < 65536; cw0 += 64) {
+    const uint4 wa = na, wb = nb;
+    const float ca = nca, cb = ncb;
+    if (cw0 + 64 < 65536) {
+      na = C4[cw0 + 64 + j];
+      nb = C4[cw0 + 96 + j];
+      nca = c2[cw0 + 64 + j];
+      ncb = c2[cw0 + 96 + j];
+    }
+    f32x16 aa, ab;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      aa[r] = 0.f;
+      ab[r] = 0.f;
+    }
+    aa = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wa), yb, aa, 0, 0, 0);
+    ab = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wb), yb, ab, 0, 0, 0);
+    tile(aa, ca);
+    tile(ab, cb);
   }
   fold();
 #pragma unroll
@@ -618,19 +631,8 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
       besti = run_i;
     }
   };
-  uint4 cw_next = reinterpret_cast<const uint4*>(C16)[cbeg + j];
-  float cn_next = c2[cbeg + j];
-  for (int cw0 = cbeg; cw0 < cend; cw0 += 32) {
-    const uint4 cw = cw_next;
-    const float cn = cn_next;
-    if (cw0 + 32 < cend) {
-      cw_next = reinterpret_cast<const uint4*>(C16)[cw0 + 32 + j];
-      cn_next = c2[cw0 + 32 + j];
-    }
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, cw), yb, acc, 0, 0, 0);
+  // tiles in pairs, as in e8_scale_kernel
+  auto tile = [&](const f32x16& acc, float cn, int cw0) {
     if (__all(cn == run_n)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -655,6 +657,29 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
         run_i = gt ? i : run_i;
       }
     }
+  };
+  const uint4* C4 = reinterpret_cast<const uint4*>(C16);
+  uint4 na = C4[cbeg + j], nb = C4[cbeg + 32 + j];
+  float nca = c2[cbeg + j], ncb = c2[cbeg + 32 + j];
+  for (int cw0 = cbeg; cw0 < cend; cw0 += 64) {  // chunk / 4 is a multiple of 64
+    const uint4 wa = na, wb = nb;
+    const float ca = nca, cb = ncb;
+    if (cw0 + 64 < cend) {
+      na = C4[cw0 + 64 + j];
+      nb = C4[cw0 + 96 + j];
+      nca = c2[cw0 + 64 + j];
+      ncb = c2[cw0 + 96 + j];
+    }
+    f32x16 aa, ab;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      aa[r] = 0.f;
+      ab[r] = 0.f;
+    }
+    aa = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wa), yb, aa, 0, 0, 0);
+    ab = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wb), yb, ab, 0, 0, 0);
+    tile(aa, ca, cw0);
+    tile(ab, cb, cw0 + 32);
   }
   fold();
   unsigned long long key = (unsigned long long)ordered_bits(bestv) << 32 | uint32_t(besti);
