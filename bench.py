@@ -327,6 +327,37 @@ def tcq_bench(Q, wl, dev, timed) -> dict:
     return out
 
 
+def configs_bench(Q, wl, dev) -> dict:
+    """One warm-up and one timed pass of every configuration (their shapes,
+    bit widths and transforms as the workloads define them): ms per pass and
+    quantized weights per second."""
+    import torch
+
+    out = {}
+    for name in ("c1", "c2", "c3a", "c3b", "c3p", "c4a", "c4b", "c4c", "c5"):
+        L = wl.make_layer(name)
+        cfg = L.cfg
+        W = torch.from_numpy(L.W).to(dev)
+        X = torch.from_numpy(L.X).to(dev)
+        del L
+        lp = Q.LayerPass(cfg.m, cfg.n, Q.SideSpec.from_numpy(wl.side_inputs(cfg, cfg.left, cfg.m, "left"), dev),
+                         Q.SideSpec.from_numpy(wl.side_inputs(cfg, cfg.right, cfg.n, "right"), dev),
+                         quant=cfg.quant, bits=cfg.bits, B=cfg.B, g=cfg.g, alpha=cfg.alpha,
+                         device=dev, rg_order=cfg.rg_order)
+        lp.run(W, X)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lp.run(W, X)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        out[name] = {"m": cfg.m, "n": cfg.n, "N": cfg.N, "bits": cfg.bits, "quant": cfg.quant,
+                     "ms_per_pass": round(ms, 3), "weights_per_s": round(cfg.m * cfg.n / (ms / 1e3), 1),
+                     "info": int(lp.buffers["info"].item())}
+        del lp, W, X
+        torch.cuda.empty_cache()
+    return out
+
+
 def e8_config_bench(Q, wl, dev, steps: int) -> dict:
     """The E8 configuration (4096 x 4096, BlockLDLQ with g = 8 and the 65536-point
     E8 codebook at 2 bits per weight): time per pass, its phases, and the E8
@@ -608,8 +639,9 @@ def main():
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
     # beside the pass: Gaussian-source VQ, the inference product, the variants
-    gaussian_vq, inference, variants, tcq, e8c = {}, {}, {}, {}, {}
+    gaussian_vq, inference, variants, tcq, e8c, allcfg = {}, {}, {}, {}, {}, {}
     if not args.no_extras:
+        allcfg = configs_bench(Q, wl, dev)
         e8c = e8_config_bench(Q, wl, dev, 2)
         gaussian_vq = gaussian_vq_bench(Q, wl, dev, timed)
         tcq = tcq_bench(Q, wl, dev, timed)
@@ -636,6 +668,7 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in phases.items()},
         "weights_per_s_from_resident_H_W": round(mn / (from_resident / 1e3), 1),
         "rht": rht,
+        "configs": allcfg,
         "e8_config": e8c,
         "gaussian_vq": gaussian_vq,
         "tcq": tcq,
