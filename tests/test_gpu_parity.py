@@ -582,7 +582,8 @@ def qmatvec_gpu(codes, scales, bits, sl, sr, x):
 
 
 @pytest.mark.parametrize("m,n,bits", [(256, 1024, 2), (1024, 4096, 2), (64, 2048, 3), (128, 8192, 4),
-                                      (32, 16384, 2), (2, 1024, 8), (4096, 1024, 3)])
+                                      (32, 16384, 2), (2, 1024, 8), (4096, 1024, 3), (16, 2048, 1),
+                                      (64, 4096, 5), (8, 1024, 6), (512, 2048, 7), (16384, 1024, 4)])
 def test_qmatvec_rht_parity(m, n, bits):
     r = rng(m + 3 * n + bits)
     L = 1 << bits
