@@ -43,7 +43,8 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0   # dense fp16 matrix cores
 # source file of each kernel family (the counter summaries are tied to its hash)
 FAMILY_SOURCES = [("gemm:", "gemm.hip"), ("gemm_tail_reduce", "gemm.hip"),
                   ("ldl_block_kernel", "ldl.hip"), ("ldlq_sweep_kernel", "ldlq.hip"),
-                  ("grid_scale_kernel", "ldlq.hip"), ("rht_", "rht.hip")]
+                  ("grid_scale_kernel", "ldlq.hip"), ("e8_", "ldlq.hip"), ("rht_", "rht.hip"),
+                  ("qmatvec_kernel", "qmatvec.hip"), ("tcq_", "tcq.hip"), ("permute_", "permute.hip")]
 
 
 def parse():
@@ -58,6 +59,9 @@ def parse():
                     help="the pass only: skip the Gaussian-source VQ, inference and variant figures "
                          "(profiled runs, whose per-kernel means must cover the pass's launches only)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of W in the oracle LDLQ sample")
+    ap.add_argument("--profile-inference", type=int, metavar="BITS", default=0,
+                    help="run only the inference product on a 16384 x 16384 layer at BITS bits "
+                         "(20 products; for rocprofv3 runs of that kernel alone) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain device copy of COPY_MIB MiB (counter calibration)")
     # summaries of rocprofv3 result databases (host only, no GPU)
@@ -66,6 +70,7 @@ def parse():
     ap.add_argument("--kernel", help="rocprofv3 kernel-name substring of the family's dispatches")
     ap.add_argument("--family", help="library timing family the counters belong to")
     ap.add_argument("--command", default="")
+    ap.add_argument("--title", help="title of a --summarize-trace summary")
     ap.add_argument("--out")
     return ap.parse_args()
 
@@ -87,7 +92,7 @@ def _kernel_rows(db):
     return out
 
 
-def summarize_trace(db, command, out):
+def summarize_trace(db, command, out, title=None):
     rows = _kernel_rows(db)
     agg = {}
     for nm, d in rows:
@@ -95,7 +100,8 @@ def summarize_trace(db, command, out):
         a[0] += d
         a[1] += 1
     tot = sum(v[0] for v in agg.values())
-    lines = ["# rocprofv3 kernel trace: quantization pass, 4096 x 4096 layer (2-bit, RHT, B = 128)", "",
+    title = title or "quantization pass, 4096 x 4096 layer (2-bit, RHT, B = 128)"
+    lines = [f"# rocprofv3 kernel trace: {title}", "",
              f"Command: `{command}`", "",
              "| kernel | calls | total us | avg us | % |", "|---|---:|---:|---:|---:|"]
     for k, (t, c) in sorted(agg.items(), key=lambda kv: -kv[1][0]):
@@ -154,8 +160,10 @@ def summarize_counters(fetch_db, write_db, kernel, family, command, out):
 
     kf, nf = pick(fetch, kernel)
     kw, nw = pick(write, kernel)
-    cf, _ = pick(fetch, COPY_KERNEL)
-    cw, _ = pick(write, COPY_KERNEL)
+    # the calibration copy is the largest dispatch of its kernel (a run may
+    # launch the same elementwise kernel for small tensors too)
+    cf = max(v for k, vals in fetch.items() if COPY_KERNEL in k for v in vals)
+    cw = max(v for k, vals in write.items() if COPY_KERNEL in k for v in vals)
     nbytes = COPY_MIB * 2 ** 20
     f_read = nbytes / (cf * 1024.0)
     f_write = nbytes / (cw * 1024.0)
@@ -325,6 +333,38 @@ def tcq_bench(Q, wl, dev, timed) -> dict:
                         "edge_relaxations_per_s": round(edges / (fms / 1e3), 1)}
         del ws
     return out
+
+
+def profile_inference(Q, dev, bits: int, calibrate_copy: bool) -> None:
+    """20 products y = Q_L^T W^~ Q_R x on one 16384 x 16384 layer of random
+    codes at `bits` bits (four copies cycled, as in the inference figures)."""
+    import torch
+
+    big = 16384
+    gen = torch.Generator(device=dev).manual_seed(11)
+    sl = torch.randint(0, 2, (big,), device=dev, generator=gen).float() * 2 - 1
+    sr = torch.randint(0, 2, (big,), device=dev, generator=gen).float() * 2 - 1
+    sc = torch.rand(big, device=dev, generator=gen) + 0.5
+    rb = Q.quip_packed_row_bytes(big, bits)
+    packs = []
+    for _ in range(4):
+        codes = torch.randint(0, 1 << bits, (big, big), dtype=torch.uint8, device=dev, generator=gen)
+        p = torch.empty((big, rb), dtype=torch.uint8, device=dev)
+        Q.quip_pack_codes(codes, bits, p)
+        packs.append(p)
+        del codes
+    x = torch.randn(big, device=dev, generator=gen)
+    y = torch.empty(big, device=dev)
+    ws = Q.native._workspace(Q.native._ws_query(Q.native.lib.quip_qmatvec_rht_workspace, big, big), dev)
+    for i in range(20):
+        Q.quip_qmatvec_rht(packs[i % 4], big, bits, sc, sl, sr, x, y, ws=ws)
+    torch.cuda.synchronize()
+    if calibrate_copy:
+        src = torch.ones(COPY_MIB * 2 ** 20 // 4, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+    print(json.dumps({"profile_inference": {"bits": bits, "products": 20}}))
 
 
 def configs_bench(Q, wl, dev) -> dict:
@@ -513,7 +553,7 @@ def cpu_baseline(cfg_name: str, rows: int) -> dict:
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.command, args.out)
+        summarize_trace(args.summarize_trace, args.command, args.out, args.title)
         return
     if args.summarize_counters:
         if not args.kernel or not args.family:
@@ -534,6 +574,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = "cuda"
+    if args.profile_inference:
+        profile_inference(Q, dev, args.profile_inference, args.calibrate_copy)
+        return
     L = wl.make_layer(args.config)
     cfg = L.cfg
     W = torch.from_numpy(L.W).to(dev)
