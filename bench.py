@@ -562,7 +562,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the pass is single-GPU here; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the pass runs on one GPU; the per-shard kernels are the same at any GPU count)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

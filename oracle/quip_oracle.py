@@ -22,7 +22,8 @@ were lost in extraction, so the names below are the paper's own section names):
 
 Pins: every public function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, textbook routines, brute force or a value the pages
-print. Readings of points the pages leave open are listed in the design doc.
+print. Where the pages leave a point open, the function that needs it states
+the reading it takes.
 """
 from __future__ import annotations
 

@@ -1,7 +1,7 @@
 """GPU parity of every entry point of the C ABI against the CPU oracle, at sizes
 the oracle finishes in seconds that still span several tiles and ragged tails.
 
-Tolerances ("Parity bar"):
+Tolerances:
   * transforms (RHT, Kronecker): per-row normwise relative error <= 1e-5;
   * Hessian: |dH_ij| <= 2e-5 sqrt(H_ii H_jj)  (float32 sums of N products);
   * LDL: backward error ||(I+U)D(I+U)^T - H|| / ||H|| <= 2e-6 * sqrt(n);
