@@ -775,3 +775,21 @@ def test_tcq_without_values_and_rejections():
             Q.quip_tcq_quantize(dev(X), 9, st, c, **kw)
     with pytest.raises(Q.QuipError):
         Q.quip_tcq_quantize(dev(X), 16, st, c)
+
+
+def test_layer_pass_is_deterministic():
+    # the scalar-grid pass sums in fixed orders (no floating-point atomics):
+    # two passes over the same inputs agree bit for bit, permutations included
+    cfg = wl.custom_config("det", 903, 128, 96, 512, left=wl.RHT, right=wl.KRON(8, 12, perm=True),
+                           bits=3, B=32, rg_order=True)
+    L = wl.make_layer(cfg)
+    W, X = dev(L.W), dev(L.X)
+    outs = []
+    for _ in range(2):
+        lp = Q.LayerPass(cfg.m, cfg.n, Q.SideSpec.from_numpy(L.left, DEV),
+                         Q.SideSpec.from_numpy(L.right, DEV), bits=3, B=32, rg_order=True)
+        b = lp.run(W, X)
+        outs.append({k: host(b[k]).copy() for k in ("H", "Wt", "U", "D", "scales", "codes", "What_t",
+                                                     "What", "row_loss", "loss", "order")})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
