@@ -29,9 +29,10 @@
 // mod 16 the row of the 16-row tile, h = lane / 16) reads one contiguous run of
 // 64 KS codes of its row (KS w / 2 loads of 16 bytes; the four runs of a row
 // are one contiguous 256 KS-code segment), which feeds 8 KS MFMA steps: the
-// k order inside an MFMA is a permutation of the run, and the x' operand (hi in
-// column 0, lo in column 1, zero elsewhere) is built once per work-group in the
-// same order and kept in registers while the work-group walks its row tiles.
+// k order inside an MFMA is a permutation of the run. The x' operand (hi in the
+// even columns, lo in the odd ones) is written in that order by the last pass
+// of the transform of x, loaded once per wave (16 bytes per step and lane) and
+// kept in registers while the wave walks its row tiles.
 // The two used accumulator columns are added with one lane swap and each
 // slice writes one partial per row; the first pass of the inverse transform
 // sums the slices in a fixed order (deterministic; no atomics, no barriers).
@@ -71,6 +72,24 @@ __device__ __forceinline__ int qmv_code_index(int s, int j) {
   if (W == 2) return 16 * (s >> 1) + 4 * (s & 1) + v + 8 * t;  // pairs (c, c + 8) of a word
   if (W == 4) return 8 * s + v + 4 * t;                          // pairs (c, c + 4) of a word
   return 4 * (2 * s + (v >> 1)) + (v & 1) + 2 * t;               // pairs (c, c + 2) of a word
+}
+
+// The inverse of qmv_code_index: step s and slot j of run position r.
+template <int W>
+__device__ __forceinline__ void qmv_slot_of(int r, int& s, int& j) {
+  if (W == 2) {
+    const int rem = r & 15, t = rem >> 3, e = (rem & 7) >> 2, v = rem & 3;
+    s = 2 * (r >> 4) + e;
+    j = 2 * v + t;
+  } else if (W == 4) {
+    const int rem = r & 7, t = rem >> 2, v = rem & 3;
+    s = r >> 3;
+    j = 2 * v + t;
+  } else {
+    const int rem = r & 7, v = 2 * (rem >> 2) + (rem & 1), t = (rem >> 1) & 1;
+    s = r >> 3;
+    j = 2 * v + t;
+  }
 }
 
 // A operand of step s: four registers of two halves each, 1 + c 2^-p (W = 2)
@@ -132,9 +151,9 @@ __device__ __forceinline__ qmv_half8 qmv_unpack(const uint32_t* q, int s, qmv_ha
 template <int W, int KS, int PF>
 __global__ __launch_bounds__(64) void qmv_mfma_kernel(const uint8_t* __restrict__ packed,
                                                       int64_t m, int64_t n,
-                                                      const float* __restrict__ xp, float cen,
-                                                      float* __restrict__ part, uint32_t kmask,
-                                                      uint32_t kone) {
+                                                      const _Float16* __restrict__ xop,
+                                                      float cen, float* __restrict__ part,
+                                                      uint32_t kmask, uint32_t kone) {
   constexpr int STEPS = 8 * KS;        // MFMA steps per tile (8 codes per lane and step)
   constexpr int RUN = 64 * KS;         // codes in a lane's run
   constexpr int NQ = KS * W / 2;       // 16-byte loads per lane and tile
@@ -145,23 +164,19 @@ __global__ __launch_bounds__(64) void qmv_mfma_kernel(const uint8_t* __restrict_
   const int64_t rowbytes = n * W / 8;
   const int64_t run0 = int64_t(blockIdx.y) * (4 * RUN) + int64_t(h) * RUN;
 
-  // x' operand: hi in the even columns, lo in the odd ones. Only columns 0
-  // and 1 of the product are read; the other columns only feed accumulator
-  // columns that are never used.
-  // (even lanes: hi = x rounded to half; odd lanes: lo = x - hi rounded, the
-  // difference being exact in float32; no select, so nothing stays live)
-  const float odd = float(c & 1);
+  // x' operand: hi in the even columns, lo in the odd ones, already in the
+  // slot order of the steps (written by the last pass of the transform of x:
+  // [slice][h][hi, lo][step][8 halves]). Only columns 0 and 1 of the product
+  // are read; the other columns only feed accumulator columns never used.
+  const uint4* xo = reinterpret_cast<const uint4*>(xop) +
+                    ((int64_t(blockIdx.y) * 4 + h) * 2 + (c & 1)) * STEPS;
   qmv_half8 B[STEPS];
   float xs = 0.f;  // this lane's halves, summed
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
+    B[s] = __builtin_bit_cast(qmv_half8, xo[s]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = xp[run0 + qmv_code_index<W>(s, j)];
-      const _Float16 b = _Float16(fmaf(-odd, float(_Float16(x)), x));
-      B[s][j] = b;
-      xs += float(b);
-    }
+    for (int j = 0; j < 8; ++j) xs += float(B[s][j]);
   }
   // the slice's sum of x' as the halves represent it (for the W = 2 offset):
   // hi + lo from a lane pair, then the four runs of the lane groups h
@@ -239,10 +254,23 @@ __global__ __launch_bounds__(64) void qmv_mfma_kernel(const uint8_t* __restrict_
 //           or, with part given, in[i] = scales[i] * sum_b part[b][i] (the
 //           product's partial sums; the finish of the inverse transform);
 //   pass 1: times scale, then times post[i] (the signs of the inverse).
+template <int W>
+__device__ __forceinline__ void qmv_put_operand(_Float16* xop, int64_t i, int ks, float x) {
+  const int64_t run = 64 * ks, slice = i / (4 * run);
+  const int h = int((i % (4 * run)) / run), r = int(i % run);
+  int st, j;
+  qmv_slot_of<W>(r, st, j);
+  const _Float16 hi = _Float16(x), lo = _Float16(x - float(hi));
+  _Float16* base = xop + ((slice * 4 + h) * 2) * (8 * ks * 8) + st * 8 + j;
+  base[0] = hi;           // [slice][h][0][st][j]
+  base[8 * ks * 8] = lo;  // [slice][h][1][st][j]
+}
+
 __global__ __launch_bounds__(64) void qmv_vec_fwht_kernel(
     const float* __restrict__ in, float* __restrict__ out, int pass, int L, int64_t n2,
     const float* __restrict__ pre, const float* __restrict__ part, int nblk, int64_t m,
-    const float* __restrict__ scales, const float* __restrict__ post, float scale) {
+    const float* __restrict__ scales, const float* __restrict__ post, float scale,
+    _Float16* __restrict__ xop, int w, int ks) {
   const int lane = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int64_t base = pass == 0 ? t * L : t;      // first element of this transform
@@ -290,7 +318,12 @@ __global__ __launch_bounds__(64) void qmv_vec_fwht_kernel(
       const int64_t i = base + int64_t(u) * step;
       float x = v[k] * scale;
       if (post) x *= post[i];
-      out[i] = x;
+      if (out) out[i] = x;
+      if (xop) {  // the product's operand layout (hi and lo halves, slot order)
+        if (w == 2) qmv_put_operand<2>(xop, i, ks, x);
+        else if (w == 4) qmv_put_operand<4>(xop, i, ks, x);
+        else qmv_put_operand<8>(xop, i, ks, x);
+      }
     }
   }
 }
@@ -300,14 +333,15 @@ inline int64_t vec_n2(int64_t n) { return int64_t(1) << ((ilog2(n) + 1) / 2); }
 
 quip_status vec_fwht_pass(const float* in, float* out, int pass, int64_t n, const float* pre,
                           const float* part, int nblk, const float* scales, const float* post,
-                          float scale, hipStream_t s) {
+                          float scale, hipStream_t s, _Float16* xop = nullptr, int w = 2,
+                          int ks = 1) {
   const int64_t n2 = vec_n2(n), n1 = n / n2;
   const int L = int(pass == 0 ? n2 : n1);
   const int64_t count = pass == 0 ? n1 : n2;
   const double bytes = 8.0 * double(n) + (part ? 4.0 * double(nblk) * double(n) : 0.0);
   return timed_launch("qmv_vec_fwht_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL(qmv_vec_fwht_kernel, dim3(unsigned(count)), dim3(64), 0, s, in, out, pass, L, n2,
-                pre, part, nblk, n, scales, post, scale);
+                pre, part, nblk, n, scales, post, scale, xop, w, ks);
   }, double(n) * double(ilog2(L)), bytes);
 }
 
@@ -316,8 +350,8 @@ int qmv_ks(int64_t n) { return n >= 2048 ? 2 : 1; }
 int64_t qmv_blocks(int64_t n) { return n / (256 * qmv_ks(n)); }  // column slices, one per wave
 
 template <int W>
-quip_status qmv_mfma_t(const uint8_t* packed, int64_t m, int64_t n, const float* xp, float cen,
-                       float* part, hipStream_t s) {
+quip_status qmv_mfma_t(const uint8_t* packed, int64_t m, int64_t n, const _Float16* xop,
+                       float cen, float* part, hipStream_t s) {
   const int64_t nblk = qmv_blocks(n);
   const int64_t tiles = cdiv(m, 16);
   // as many one-wave work-groups as are resident at once, split over the
@@ -341,10 +375,10 @@ quip_status qmv_mfma_t(const uint8_t* packed, int64_t m, int64_t n, const float*
   const double flops = 2.0 * double(m) * double(n);
   return timed_launch("qmatvec_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (qmv_ks(n) == 2)
-      QUIP_KERNEL((qmv_mfma_kernel<W, 2, QMV_PF>), grid, dim3(64), 0, s, packed, m, n, xp, cen,
+      QUIP_KERNEL((qmv_mfma_kernel<W, 2, QMV_PF>), grid, dim3(64), 0, s, packed, m, n, xop, cen,
                   part, kmask, kone);
     else
-      QUIP_KERNEL((qmv_mfma_kernel<W, 1, QMV_PF>), grid, dim3(64), 0, s, packed, m, n, xp, cen,
+      QUIP_KERNEL((qmv_mfma_kernel<W, 1, QMV_PF>), grid, dim3(64), 0, s, packed, m, n, xop, cen,
                   part, kmask, kone);
   }, flops, bytes);
 }
@@ -370,7 +404,7 @@ quip_status pack_codes(const uint8_t* codes, int64_t m, int64_t n, int64_t ldc, 
 
 size_t qmatvec_workspace_bytes(int64_t m, int64_t n) {
   Carver c(nullptr, 0);
-  c.take<float>(size_t(n));                    // x'
+  c.take<_Float16>(size_t(2 * n));             // x' as the product's operand (hi, lo)
   c.take<float>(size_t(m > n ? m : n));        // between the two passes of a transform
   c.take<float>(size_t(qmv_blocks(n) * m));    // per-slice partial sums
   return c.used;
@@ -380,19 +414,19 @@ quip_status qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int bits, c
                         const float* signs_left, const float* signs_right, const float* x,
                         float* y, void* ws, size_t ws_bytes, hipStream_t s) {
   Carver c(ws, ws_bytes);
-  float* xp = c.take<float>(size_t(n));
+  _Float16* xop = c.take<_Float16>(size_t(2 * n));
   float* tmp = c.take<float>(size_t(m > n ? m : n));
   float* part = c.take<float>(size_t(qmv_blocks(n) * m));
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_qmatvec_rht: workspace too small");
   const float cen = 0.5f * float((1 << bits) - 1);
   // x' = Q_R x = H_n diag(signs_right) x / sqrt(n): two passes, signs first
   QUIP_TRY(vec_fwht_pass(x, tmp, 0, n, signs_right, nullptr, 0, nullptr, nullptr, 1.f, s));
-  QUIP_TRY(vec_fwht_pass(tmp, xp, 1, n, nullptr, nullptr, 0, nullptr, nullptr,
-                         1.0f / sqrtf(float(n)), s));
   const int w = code_container_bits(bits);
-  if (w == 2) QUIP_TRY(qmv_mfma_t<2>(packed, m, n, xp, cen, part, s));
-  else if (w == 4) QUIP_TRY(qmv_mfma_t<4>(packed, m, n, xp, cen, part, s));
-  else QUIP_TRY(qmv_mfma_t<8>(packed, m, n, xp, cen, part, s));
+  QUIP_TRY(vec_fwht_pass(tmp, nullptr, 1, n, nullptr, nullptr, 0, nullptr, nullptr,
+                         1.0f / sqrtf(float(n)), s, xop, w, qmv_ks(n)));
+  if (w == 2) QUIP_TRY(qmv_mfma_t<2>(packed, m, n, xop, cen, part, s));
+  else if (w == 4) QUIP_TRY(qmv_mfma_t<4>(packed, m, n, xop, cen, part, s));
+  else QUIP_TRY(qmv_mfma_t<8>(packed, m, n, xop, cen, part, s));
   // y = Q_L^T y' = diag(signs_left) H_m y' / sqrt(m), with y' = scales * (sum of
   // the slices' partials) formed in the first pass
   const int nblk = int(qmv_blocks(n));
