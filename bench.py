@@ -79,16 +79,35 @@ COPY_MIB = 256
 COPY_KERNEL = "MulFunctor"  # torch.mul(src, 1.0, out=dst): reads and writes COPY_MIB MiB
 
 
-def _kernel_rows(db):
+def _short_name(name: str) -> str:
+    """Kernel name without namespace noise and arguments. rocprofv3 leaves
+    names with a _Float16 parameter (mangled DF16_) mangled; they are
+    demangled here with the older half-precision code (Dh) in its place."""
     import re
+    import subprocess
+
+    if name.startswith("_Z"):
+        try:
+            r = subprocess.run(["c++filt"], input=name.replace("DF16_", "Dh"), capture_output=True,
+                               text=True, timeout=10)
+            if r.returncode == 0 and r.stdout.strip():
+                name = r.stdout.strip()
+        except (OSError, subprocess.SubprocessError):
+            pass
+    nm = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", nm)
+
+
+def _kernel_rows(db):
     import sqlite3
 
     con = sqlite3.connect(db)
     out = []
+    names = {}
     for name, start, end in con.execute("select name, start, end from kernels"):
-        nm = name.replace("(anonymous namespace)::", "").replace("void ", "")
-        nm = re.sub(r"\(.*", "", nm)
-        out.append((nm, (end - start) / 1e3))
+        if name not in names:
+            names[name] = _short_name(name)
+        out.append((names[name], (end - start) / 1e3))
     return out
 
 
@@ -114,16 +133,16 @@ def summarize_trace(db, command, out, title=None):
 
 
 def _counter(db, counter):
-    import re
     import sqlite3
 
     con = sqlite3.connect(db)
     per = {}
+    names = {}
     for name, value in con.execute(
             "select kernel_name, value from counters_collection where counter_name = ?", (counter,)):
-        nm = name.replace("(anonymous namespace)::", "").replace("void ", "")
-        nm = re.sub(r"\(.*", "", nm)
-        per.setdefault(nm, []).append(float(value))
+        if name not in names:
+            names[name] = _short_name(name)
+        per.setdefault(names[name], []).append(float(value))
     return per
 
 
