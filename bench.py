@@ -230,6 +230,34 @@ def kernel_bound(name: str):
     return "hbm", HBM_PEAK_GBS, "GB/s"
 
 
+def attainable_bench(Q, dev, timed) -> dict:
+    """What plain, dependency-free work attains on this card, next to the
+    published peaks the roofline fractions use: a 1 GiB device copy, and
+    loops of independent fp32 and f16 matrix-core instructions and fp32
+    vector FMAs (the library's probe kernels, four waves per SIMD)."""
+    import torch
+
+    count = 2 ** 28  # 1 GiB of float32 each way
+    src = torch.ones(count, device=dev)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: Q.quip_peak_copy(src, dst), 5)
+    copy_gbps = 8.0 * count / (ms / 1e3) / 1e9
+    del src, dst
+    out = torch.zeros(1, device=dev)
+    rates = {}
+    for kind, iters in ((0, 20000), (1, 20000), (2, 100000)):
+        flops = Q.quip_peak_compute(kind, iters, out)
+        ms = timed(lambda: Q.quip_peak_compute(kind, iters, out), 3)
+        rates[kind] = flops / (ms / 1e3) / 1e12
+    return {"hbm_copy_GBps": round(copy_gbps, 1), "hbm_published_GBps": HBM_PEAK_GBS,
+            "mfma_f32_TFLOPs": round(rates[0], 1), "mfma_f32_published_TFLOPs": FP32_MFMA_PEAK_TFLOPS,
+            "mfma_f16_TFLOPs": round(rates[1], 1), "mfma_f16_published_TFLOPs": FP16_MFMA_PEAK_TFLOPS,
+            "valu_f32_fma_TFLOPs": round(rates[2], 1),
+            "valu_f32_published_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
+            "note": "published vector peak counts packed fp32 (2 FMAs per lane); the library "
+                    "issues one FMA per lane and instruction"}
+
+
 def gaussian_vq_bench(Q, wl, dev, timed) -> dict:
     """The E8 codebook at 2 bits per weight on an i.i.d. N(0,1) source (1024 x
     4096 weights, 524288 8-vectors), through the search of the E8
@@ -701,6 +729,8 @@ def main():
                "right_ms": round(r_ms, 4), "left_ms": round(l_ms, 4), "two_sided_ms": round(t_ms, 4),
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
+    attainable = attainable_bench(Q, dev, timed)
+
     # beside the pass: Gaussian-source VQ, the inference product, the variants
     gaussian_vq, inference, variants, tcq, e8c, allcfg = {}, {}, {}, {}, {}, {}
     if not args.no_extras:
@@ -738,6 +768,7 @@ def main():
         "inference": inference,
         "variants": variants,
         "roofline": roofline,
+        "attainable": attainable,
         "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])),
     }
     if args.calibrate_copy:

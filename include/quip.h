@@ -398,6 +398,36 @@ quip_status quip_tcq_quantize(const float* X, int64_t rows, int64_t T, int64_t l
                               hipStream_t stream);
 
 /*
+ * Attainable-rate probes: measurement aids beside the method, not part of it.
+ * The roofline fractions are quoted against the chip's published peaks; these
+ * two calls measure what plain, dependency-free work attains on the device at
+ * hand, with the same launch path (and the same timing registry) as the
+ * library's kernels.
+ *
+ * quip_peak_copy -- dst[i] = src[i] for 0 <= i < count: 8 count bytes of HBM
+ * traffic (16 work-groups per CU looping over the array, four 16-byte
+ * non-temporal loads per thread and round before its four stores).
+ *   src, dst: count float32 (device), 16-byte aligned, not overlapping.
+ * Errors: QUIP_ERR_ARG (negative count, null or misaligned pointer, overlap).
+ *
+ * quip_peak_compute -- `iters` rounds of independent instructions on four
+ * work-groups of 256 threads per CU (four waves per SIMD):
+ *   kind 0: fp32 matrix cores, v_mfma_f32_32x32x2_f32, four accumulators per
+ *     wave (4096 flops per instruction);
+ *   kind 1: f16 matrix cores with fp32 accumulation, v_mfma_f32_16x16x32_f16,
+ *     eight accumulators per wave (16384 flops per instruction);
+ *   kind 2: fp32 vector FMAs, eight chains per lane (2 flops each; one FMA
+ *     per lane and instruction, as everywhere in this library).
+ *   out: 1 float32 (device); written only if the result equals an improbable
+ *     value (the write keeps the work alive), so its content is unspecified.
+ *   flops: host double receiving the launch's flop count, or NULL.
+ * Errors: QUIP_ERR_ARG (kind not 0..2, iters <= 0, null out).
+ */
+quip_status quip_peak_copy(const float* src, float* dst, int64_t count, hipStream_t stream);
+quip_status quip_peak_compute(int32_t kind, int64_t iters, float* out, double* flops,
+                              hipStream_t stream);
+
+/*
  * quip_e8_codebook -- fills HOST memory with the 65536 smallest-norm points of
  * the E8 lattice (D8 together with D8 + 1/2) ordered by squared norm, then by
  * coordinates ascending with the first coordinate most significant; 65536 x 8

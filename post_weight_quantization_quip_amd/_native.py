@@ -84,6 +84,8 @@ SYMBOLS = {
     "quip_tcq_workspace": (c_int, [c_i64, c_i64, ctypes.c_int32, ctypes.POINTER(c_sz)]),
     "quip_tcq_quantize": (c_int, [c_vp, c_i64, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, c_f,
                                   c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "quip_peak_copy": (c_int, [c_vp, c_vp, c_i64, c_vp]),
+    "quip_peak_compute": (c_int, [ctypes.c_int32, c_i64, c_vp, ctypes.POINTER(ctypes.c_double), c_vp]),
     "quip_timing_enable": (c_int, [c_int]),
     "quip_timing_reset": (c_int, []),
     "quip_timing_report": (c_int, [ctypes.c_char_p, c_sz, ctypes.POINTER(c_sz)]),
@@ -299,6 +301,22 @@ def quip_tcq_quantize(X, L: int, states, cost, Xhat=None, k: int = 2, scale: flo
                                  _p(Xhat), _ld(Xhat) if Xhat is not None else T, _p(cost), _p(ws),
                                  0 if ws is None else ws.numel(), _stream(stream)),
            "quip_tcq_quantize")
+
+
+def quip_peak_copy(src, dst, stream=None) -> None:
+    """dst = src (float32, same size, device): the HBM copy probe."""
+    if src.numel() != dst.numel():
+        raise ValueError("quip_peak_copy: src and dst sizes differ")
+    _check(lib.quip_peak_copy(_p(src), _p(dst), src.numel(), _stream(stream)), "quip_peak_copy")
+
+
+def quip_peak_compute(kind: int, iters: int, out, stream=None) -> float:
+    """One launch of the compute probe (0: fp32 MFMA, 1: f16 MFMA, 2: fp32
+    vector FMA); returns its flop count."""
+    flops = ctypes.c_double(0.0)
+    _check(lib.quip_peak_compute(kind, iters, _p(out), ctypes.byref(flops), _stream(stream)),
+           "quip_peak_compute")
+    return flops.value
 
 
 def timing_enable(on: bool = True) -> None:

@@ -387,6 +387,30 @@ quip_status quip_permute(const float* A, int64_t lda, float* out, int64_t ldo, i
   return permute(A, lda, out, ldo, rows, cols, row_index, col_index, scatter != 0, stream);
 }
 
+quip_status quip_peak_copy(const float* src, float* dst, int64_t count, hipStream_t stream) {
+  clear_error();
+  const char* who = "quip_peak_copy";
+  if (count < 0) return fail(QUIP_ERR_ARG, std::string(who) + ": negative count");
+  if (count == 0) return QUIP_OK;
+  if (!src || !dst) return fail(QUIP_ERR_ARG, std::string(who) + ": null pointer");
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(QUIP_ERR_ARG, std::string(who) + ": src and dst must be 16-byte aligned");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t bytes = sizeof(float) * uintptr_t(count);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(QUIP_ERR_ARG, std::string(who) + ": src and dst overlap");
+  return peak_copy(src, dst, count, stream);
+}
+
+quip_status quip_peak_compute(int32_t kind, int64_t iters, float* out, double* flops,
+                              hipStream_t stream) {
+  clear_error();
+  const char* who = "quip_peak_compute";
+  if (kind < 0 || kind > 2) return fail(QUIP_ERR_ARG, std::string(who) + ": kind must be 0, 1 or 2");
+  if (iters <= 0) return fail(QUIP_ERR_ARG, std::string(who) + ": iters must be positive");
+  if (!out) return fail(QUIP_ERR_ARG, std::string(who) + ": out is null");
+  return peak_compute(kind, iters, out, flops, stream);
+}
+
 quip_status quip_diag_order_workspace(int64_t n, size_t* bytes) {
   clear_error();
   if (!bytes) return fail(QUIP_ERR_ARG, "quip_diag_order_workspace: bytes is null");

@@ -131,6 +131,10 @@ quip_status diag_order(const float* H, int64_t n, int64_t ldh, int32_t* order, v
 
 // ---------------------------------------------------------------- trellis (tcq.hip)
 
+// attainable-rate probes (peak.hip)
+quip_status peak_copy(const float* src, float* dst, int64_t count, hipStream_t s);
+quip_status peak_compute(int kind, int64_t iters, float* out, double* flops, hipStream_t s);
+
 size_t tcq_workspace_bytes(int64_t rows, int64_t T, int L);
 quip_status tcq_quantize(const float* X, int64_t rows, int64_t T, int64_t ldx, int L, float scale,
                          uint16_t* states, int64_t lds, float* xhat, int64_t ldq, float* cost,

@@ -197,3 +197,15 @@ def test_tcq_validation():
     assert call(lds=100) == N.QUIP_ERR_ARG
     assert call(ldq=100) == N.QUIP_ERR_ARG
     assert call(wsb=16) == N.QUIP_ERR_WORKSPACE
+
+
+def test_peak_probe_validation():
+    lib = N.lib
+    assert lib.quip_peak_copy(fake(), fake(0x100000), -1, None) == N.QUIP_ERR_ARG
+    assert lib.quip_peak_copy(None, fake(0x100000), 16, None) == N.QUIP_ERR_ARG
+    assert lib.quip_peak_copy(fake(0x1004), fake(0x100000), 16, None) == N.QUIP_ERR_ARG  # misaligned
+    assert lib.quip_peak_copy(fake(0x1000), fake(0x1010), 16, None) == N.QUIP_ERR_ARG  # overlap
+    assert lib.quip_peak_copy(fake(), fake(0x100000), 0, None) == N.QUIP_OK  # nothing to do
+    assert lib.quip_peak_compute(3, 10, fake(), None, None) == N.QUIP_ERR_ARG
+    assert lib.quip_peak_compute(0, 0, fake(), None, None) == N.QUIP_ERR_ARG
+    assert lib.quip_peak_compute(1, 10, None, None, None) == N.QUIP_ERR_ARG

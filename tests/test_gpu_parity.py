@@ -793,3 +793,22 @@ def test_layer_pass_is_deterministic():
                                                      "What", "row_loss", "loss", "order")})
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_peak_probes():
+    # measurement aids: the copy probe copies (float4 body and scalar tail),
+    # the compute probes run and count their flops as documented
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rnd = 16 * cus * 256 * 4  # 16-byte chunks per round of the whole grid
+    for count in (1, 7, 4096 + 3, 4 * (2 * rnd + 700) + 2):
+        src = torch.arange(count, dtype=torch.float32, device=DEV) * 0.5 - 3.0
+        dst = torch.full_like(src, float("nan"))
+        Q.quip_peak_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst), count
+    out = torch.zeros(1, device=DEV)
+    waves = 4 * cus * 4
+    assert Q.quip_peak_compute(0, 3, out) == waves * 3 * 4 * (32 * 32 * 2 * 2)
+    assert Q.quip_peak_compute(1, 3, out) == waves * 3 * 8 * (16 * 16 * 32 * 2)
+    assert Q.quip_peak_compute(2, 3, out) == waves * 64 * 3 * 8 * 2
+    torch.cuda.synchronize()
