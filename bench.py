@@ -67,6 +67,8 @@ def parse():
     # summaries of rocprofv3 result databases (host only, no GPU)
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--summarize-mfma", metavar="DB",
+                    help="matrix-core busy table from a SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE run")
     ap.add_argument("--kernel", help="rocprofv3 kernel-name substring of the family's dispatches")
     ap.add_argument("--family", help="library timing family the counters belong to")
     ap.add_argument("--command", default="")
@@ -161,6 +163,52 @@ def source_sha(src: str) -> str:
 
 def counters_path(family: str) -> str:
     return os.path.join(ROOT, "profiles", "counters_" + family.replace(":", "_") + "_c2.json")
+
+
+def summarize_mfma(db, command, out, title=None):
+    """Matrix-core busy fraction per kernel from one rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE. The ratio
+    MFMA-busy / GPU-active of each kernel is divided by the same ratio for the
+    fp32 matrix-core probe (quip_peak_compute kind 0, measured at ~99% of the
+    fp32 peak), so 1.0 means the matrix cores as busy as in that loop."""
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    disp = {}
+    names = {}
+    for did, name, cname, value in con.execute(
+            "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        if name not in names:
+            names[name] = _short_name(name)
+        d = disp.setdefault(did, {"name": names[name]})
+        d[cname] = d.get(cname, 0.0) + float(value)
+    agg = {}
+    for d in disp.values():
+        a = agg.setdefault(d["name"], [0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a[2] += d.get("SQ_BUSY_CYCLES", 0.0)
+        a[3] += d.get("GRBM_GUI_ACTIVE", 0.0)
+    probe = agg.get("quip::peak_mfma_f32_kernel")
+    if not probe or probe[3] <= 0 or probe[1] <= 0:
+        raise SystemExit("no fp32 matrix-core probe dispatch in the counter database")
+    ref = probe[1] / probe[3]
+    title = title or "quantization pass, 4096 x 4096 layer (2-bit, RHT, B = 128)"
+    lines = [f"# Matrix-core busy fraction: {title}", "",
+             f"Command: `{command}`", "",
+             "Busy = (SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE) of the kernel over the same "
+             f"ratio for the fp32 matrix-core probe ({ref:.2f}). Kernels with no matrix-core "
+             "work are left out.", "",
+             "| kernel | dispatches | MFMA busy | GPU-active cycles per dispatch |",
+             "|---|---:|---:|---:|"]
+    rows = [(k, a) for k, a in agg.items() if a[1] > 0 and a[3] > 0]
+    for k, a in sorted(rows, key=lambda kv: -kv[1][3]):
+        lines.append(f"| `{k}` | {a[0]} | {a[1] / a[3] / ref:.3f} | {a[3] / a[0]:.0f} |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def summarize_counters(fetch_db, write_db, kernel, family, command, out):
@@ -601,6 +649,9 @@ def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.command, args.out, args.title)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.command, args.out, args.title)
         return
     if args.summarize_counters:
         if not args.kernel or not args.family:

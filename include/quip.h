@@ -414,8 +414,8 @@ quip_status quip_tcq_quantize(const float* X, int64_t rows, int64_t T, int64_t l
  * work-groups of 256 threads per CU (four waves per SIMD):
  *   kind 0: fp32 matrix cores, v_mfma_f32_32x32x2_f32, four accumulators per
  *     wave (4096 flops per instruction);
- *   kind 1: f16 matrix cores with fp32 accumulation, v_mfma_f32_16x16x32_f16,
- *     eight accumulators per wave (16384 flops per instruction);
+ *   kind 1: f16 matrix cores with fp32 accumulation, v_mfma_f32_32x32x16_f16,
+ *     four accumulators per wave (32768 flops per instruction);
  *   kind 2: fp32 vector FMAs, eight chains per lane (2 flops each; one FMA
  *     per lane and instruction, as everywhere in this library).
  *   out: 1 float32 (device); written only if the result equals an improbable

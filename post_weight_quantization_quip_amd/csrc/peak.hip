@@ -13,7 +13,7 @@ namespace {
 constexpr int PEAK_THREADS = 256;
 constexpr int PEAK_GROUPS_PER_CU = 4;  // four waves on every SIMD
 constexpr int F32_CHAINS = 4;          // independent 32x32x2 accumulators per wave
-constexpr int F16_CHAINS = 8;          // independent 16x16x32 accumulators per wave
+constexpr int F16_CHAINS = 4;          // independent 32x32x16 accumulators per wave
 constexpr int VALU_CHAINS = 8;         // independent FMA chains per lane
 
 typedef float peak_f32x16 __attribute__((ext_vector_type(16)));
@@ -70,14 +70,16 @@ __global__ __launch_bounds__(PEAK_THREADS) void peak_mfma_f32_kernel(int64_t ite
   if (s == IMPROBABLE) out[0] = s;
 }
 
-// f16 matrix cores: v_mfma_f32_16x16x32_f16, 16384 flops per instruction.
+// f16 matrix cores: v_mfma_f32_32x32x16_f16, 32768 flops per instruction
+// (the 16x16x32 form needs about 16 independent accumulators per wave to come
+// near the same rate).
 __global__ __launch_bounds__(PEAK_THREADS) void peak_mfma_f16_kernel(int64_t iters, float seed,
                                                                      float* out) {
-  peak_f32x4 acc[F16_CHAINS];
+  peak_f32x16 acc[F16_CHAINS];
 #pragma unroll
   for (int c = 0; c < F16_CHAINS; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[c][j] = 0.f;
+    for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
   peak_f16x8 a, b;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -87,13 +89,13 @@ __global__ __launch_bounds__(PEAK_THREADS) void peak_mfma_f16_kernel(int64_t ite
   for (int64_t i = 0; i < iters; ++i) {
 #pragma unroll
     for (int c = 0; c < F16_CHAINS; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < F16_CHAINS; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s += acc[c][j];
+    for (int j = 0; j < 16; ++j) s += acc[c][j];
   if (s == IMPROBABLE) out[0] = s;
 }
 
@@ -149,7 +151,7 @@ quip_status peak_compute(int kind, int64_t iters, float* out, double* flops, hip
       }, f, 0.0);
       break;
     case 1:
-      f = double(waves) * double(iters) * F16_CHAINS * (16.0 * 16.0 * 32.0 * 2.0);
+      f = double(waves) * double(iters) * F16_CHAINS * (32.0 * 32.0 * 16.0 * 2.0);
       st = timed_launch("peak_mfma_f16_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
         QUIP_KERNEL(peak_mfma_f16_kernel, grid, block, 0, s, iters, seed, out);
       }, f, 0.0);

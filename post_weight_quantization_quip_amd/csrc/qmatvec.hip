@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restri
 typedef _Float16 qmv_half2 __attribute__((ext_vector_type(2)));
 typedef _Float16 qmv_half8 __attribute__((ext_vector_type(8)));
 typedef float qmv_float4 __attribute__((ext_vector_type(4)));
+constexpr int QMV_CHAINS = 4;  // independent accumulators per tile
 
 // Position, within a lane's run of codes, of the code in MFMA step s, slot j
 // (j = 2v + t: A register v, half t), matching qmv_unpack.
@@ -215,11 +216,19 @@ __global__ __launch_bounds__(64) void qmv_mfma_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       if (t * 16 < m) {
-        qmv_float4 D = {0.f, 0.f, 0.f, 0.f};
+        // QMV_CHAINS independent accumulators (step s feeds chain s mod
+        // QMV_CHAINS): one dependent chain of 16x16x32 products is bound by
+        // the instruction's latency, not by the matrix cores' rate
+        qmv_float4 Dc[QMV_CHAINS];
+#pragma unroll
+        for (int q = 0; q < QMV_CHAINS; ++q) Dc[q] = qmv_float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < STEPS; ++s)
-          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qmv_unpack<W>(ring[k], s, sub, kmask, kone),
-                                                     B[s], D, 0, 0, 0);
+          Dc[s % QMV_CHAINS] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              qmv_unpack<W>(ring[k], s, sub, kmask, kone), B[s], Dc[s % QMV_CHAINS], 0, 0, 0);
+        qmv_float4 D = Dc[0];
+#pragma unroll
+        for (int q = 1; q < QMV_CHAINS; ++q) D += Dc[q];
         load(ring[k], t + PF * g);
         // lane (c, h) holds rows 4h..4h+3 of column c: add columns 0 and 1
 #pragma unroll

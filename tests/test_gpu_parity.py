@@ -809,6 +809,6 @@ def test_peak_probes():
     out = torch.zeros(1, device=DEV)
     waves = 4 * cus * 4
     assert Q.quip_peak_compute(0, 3, out) == waves * 3 * 4 * (32 * 32 * 2 * 2)
-    assert Q.quip_peak_compute(1, 3, out) == waves * 3 * 8 * (16 * 16 * 32 * 2)
+    assert Q.quip_peak_compute(1, 3, out) == waves * 3 * 4 * (32 * 32 * 16 * 2)
     assert Q.quip_peak_compute(2, 3, out) == waves * 64 * 3 * 8 * 2
     torch.cuda.synchronize()
