@@ -545,8 +545,12 @@ quip_status launch_tiles(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB)
   int64_t t128 = cdiv(a.M, 128) * cdiv(a.N, 128) * a.batch;
   if (a.upper_tiles) t128 = cdiv(a.M, 128) * (cdiv(a.M, 128) + 1) / 2 * a.batch;
   if (t128 < 512) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
-  bool smallM = a.M <= 64;
-  bool smallN = a.N <= 64;
+  // 64 along a dimension that 128-wide tiles would pad by more than half a
+  // 64-tile beyond what 64-wide tiles need (172: 256 against 192). The tile
+  // shape does not change any element's summation order.
+  auto pads = [](int64_t d) { return cdiv(d, 128) * 128 > cdiv(d, 64) * 64 + 32; };
+  bool smallM = a.M <= 64 || pads(a.M);
+  bool smallN = a.N <= 64 || pads(a.N);
   if (a.upper_tiles) smallN = smallM;  // square tiles for the triangular grid
   if (smallM && smallN) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
   if (smallM) return launch_t<64, 128, TA, TB, EPI>(a, s, vecA, vecB);
