@@ -116,15 +116,22 @@ def _kernel_rows(db):
 def summarize_trace(db, command, out, title=None):
     rows = _kernel_rows(db)
     agg = {}
+    probes = 0
     for nm, d in rows:
+        if nm.startswith("quip::peak_"):  # the attainable-rate probes the bench also runs
+            probes += 1
+            continue
         a = agg.setdefault(nm, [0.0, 0])
         a[0] += d
         a[1] += 1
     tot = sum(v[0] for v in agg.values())
     title = title or "quantization pass, 4096 x 4096 layer (2-bit, RHT, B = 128)"
     lines = [f"# rocprofv3 kernel trace: {title}", "",
-             f"Command: `{command}`", "",
-             "| kernel | calls | total us | avg us | % |", "|---|---:|---:|---:|---:|"]
+             f"Command: `{command}`", ""]
+    if probes:
+        lines += [f"The attainable-rate probes (`quip::peak_*`, {probes} dispatches) that the "
+                  "bench runs beside the pass are left out.", ""]
+    lines += ["| kernel | calls | total us | avg us | % |", "|---|---:|---:|---:|---:|"]
     for k, (t, c) in sorted(agg.items(), key=lambda kv: -kv[1][0]):
         lines.append(f"| `{k}` | {c} | {t:.1f} | {t / c:.2f} | {100 * t / tot:.1f} |")
     text = "\n".join(lines) + "\n"
