@@ -25,14 +25,16 @@
 // bits), so the products are exact and the matrix cores accumulate in float32.
 //
 // Layout: a work-group is one wave and owns a slice of 256 KS columns (KS = 1
-// for n = 1024, else 2). Lane (r, h) of the wave (r = lane
+// for n below 2048, else 2). Lane (r, h) of the wave (r = lane
 // mod 16 the row of the 16-row tile, h = lane / 16) reads one contiguous run of
 // 64 KS codes of its row (KS w / 2 loads of 16 bytes; the four runs of a row
 // are one contiguous 256 KS-code segment), which feeds 8 KS MFMA steps: the
 // k order inside an MFMA is a permutation of the run. The x' operand (hi in the
 // even columns, lo in the odd ones) is written in that order by the last pass
 // of the transform of x, loaded once per wave (16 bytes per step and lane) and
-// kept in registers while the wave walks its row tiles.
+// kept in registers while the wave walks its row tiles. The steps of a tile
+// feed QMV_CHAINS independent accumulators, added at the end (one dependent
+// chain of these products would be bound by the instruction's latency).
 // The two used accumulator columns are added with one lane swap and each
 // slice writes one partial per row; the first pass of the inverse transform
 // sums the slices in a fixed order (deterministic; no atomics, no barriers).
