@@ -209,3 +209,18 @@ def test_peak_probe_validation():
     assert lib.quip_peak_compute(3, 10, fake(), None, None) == N.QUIP_ERR_ARG
     assert lib.quip_peak_compute(0, 0, fake(), None, None) == N.QUIP_ERR_ARG
     assert lib.quip_peak_compute(1, 10, None, None, None) == N.QUIP_ERR_ARG
+
+
+def test_empty_sizes_are_rejected_before_any_launch():
+    # a layer, a transform or a trellis of no rows or columns is an argument
+    # error (the permutation and the copy probe treat it as nothing to do)
+    lib = N.lib
+    sz = ctypes.c_size_t(0)
+    assert lib.quip_ldl_workspace(0, 1, ctypes.byref(sz)) == N.QUIP_ERR_SHAPE
+    assert lib.quip_tcq_workspace(0, 8, 8, ctypes.byref(sz)) == N.QUIP_ERR_ARG
+    assert lib.quip_tcq_workspace(4, 0, 8, ctypes.byref(sz)) == N.QUIP_ERR_ARG
+    assert lib.quip_diag_order_workspace(0, ctypes.byref(sz)) == N.QUIP_ERR_ARG
+    assert lib.quip_proxy_loss_workspace(0, 8, ctypes.byref(sz)) == N.QUIP_ERR_ARG
+    assert lib.quip_qmatvec_rht_workspace(0, 1024, ctypes.byref(sz)) == N.QUIP_ERR_ARG
+    assert lib.quip_rht(fake(), fake(), 0, 16, 16, fake(), N.RIGHT, None) == N.QUIP_ERR_ARG
+    assert lib.quip_hessian_workspace(0, 0, ctypes.byref(sz)) == N.QUIP_ERR_ARG

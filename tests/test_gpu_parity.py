@@ -105,6 +105,28 @@ def test_hessian_accumulates_in_chunks():
     assert (np.abs(host(H) - ref) <= 2e-5 * d[:, None] * d[None, :]).all()
 
 
+def test_hessian_of_no_rows():
+    # an empty chunk of calibration rows: H = 0, or H unchanged when accumulating
+    X = torch.empty((0, 70), device=DEV)
+    H = torch.full((70, 70), 3.0, device=DEV)
+    Q.quip_hessian(X, H, accumulate=True)
+    torch.cuda.synchronize()
+    assert bool((H == 3.0).all())
+    Q.quip_hessian(X, H)
+    torch.cuda.synchronize()
+    assert bool((H == 0.0).all())
+
+
+def test_permute_of_empty_matrix_is_a_no_op():
+    out = torch.full((4, 3), 7.0, device=DEV)
+    A = torch.zeros((4, 3), device=DEV)
+    lib = Q.native.lib
+    assert lib.quip_permute(A.data_ptr(), 3, out.data_ptr(), 3, 0, 3, None, None, 0, None) == 0
+    assert lib.quip_permute(A.data_ptr(), 3, out.data_ptr(), 3, 4, 0, None, None, 1, None) == 0
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
 # ------------------------------------------------------------------ RHT
 
 @pytest.mark.parametrize("rows,d", [(37, 2), (5, 4), (9, 8), (33, 16), (17, 32), (17, 64), (300, 256),
