@@ -22,8 +22,10 @@
  *     that must be >= the number of columns.
  *   - The caller owns all memory: inputs, outputs and workspace. Workspace
  *     sizes come from the quip_*_workspace queries; a workspace must be 256-byte
- *     aligned. The library allocates nothing and keeps no global mutable state;
- *     calls on different streams are independent.
+ *     aligned. The library allocates no device memory and keeps no global
+ *     mutable state other than the optional per-kernel timing registry
+ *     (quip_timing_*, off by default); calls on different streams are
+ *     independent.
  *   - Every call only enqueues work on `stream` (asynchronous) and returns at
  *     once. Argument and shape errors are detected on the host before any
  *     launch, and then nothing is enqueued. A failure found on the device (a
