@@ -5,10 +5,11 @@ TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
 never calls it and shares no code with it; the only thing both sides consume in
 common is the seeded input generator in ``workloads``.
 
-Plain numpy in float64 throughout, except the rounding decisions, which are
-taken in float32 exactly as the GPU takes them (a float32 pre-rounding value
-divided by a float32 scale), so that both sides decide an integer code in the
-same precision.
+Plain numpy in float64 throughout, except the scalar grid's rounding
+decision: the pages fix no precision for it, so it is taken in the kernel's
+(a float32 pre-rounding value divided by a float32 scale) and both sides decide
+an integer code in the same precision. Away from a decision boundary that
+decision is the exact nearest level (pinned).
 
 Sources (cited by title and section; the section headings of the QuIP page
 were lost in extraction, so the names below are the paper's own section names):
@@ -320,10 +321,12 @@ def block_diag_D(D) -> np.ndarray:
 
 def uniform_code(x, s, L: int) -> np.ndarray:
     """Nearest point of the L-level midrise grid {(k - (L-1)/2) s}: the code is
-    clamp(floor(x/s + L/2), 0, L-1), ties at a decision boundary going up. The
-    decision is taken in float32 (float32 x, float32 s, IEEE division and add),
-    the precision of the GPU kernel. [QuIP] "Adaptive Rounding Step": rounding
-    to a finite grid."""
+    clamp(floor(x/s + L/2), 0, L-1), ties at a decision boundary going up.
+    [QuIP] "Adaptive Rounding Step": rounding to a finite grid. The pages fix no
+    precision for this decision, so it is taken in the kernel's: float32 x,
+    float32 s, IEEE division and add. Away from a boundary (farther than a few
+    float32 ulps of x/s) this is the exact nearest level of the float64 x; the
+    pins check both that and the tie rule."""
     t = np.asarray(x, dtype=F32) / np.asarray(s, dtype=F32)
     k = np.floor(t + F32(L / 2))
     return np.clip(k, 0, L - 1).astype(np.int64)
@@ -534,13 +537,33 @@ def e8_decode(Y) -> np.ndarray:
 
 
 class E8Index:
-    """Position of a lattice point in the codebook (or -1)."""
+    """Position of a lattice point in the codebook (or -1), and an exact
+    nearest-neighbour structure over the codebook for the points whose nearest
+    lattice point lies outside it."""
 
     def __init__(self, C):
-        V = np.rint(np.asarray(C, dtype=F64) * 2).astype(np.int64)
+        self.C = np.asarray(C, dtype=F64)
+        V = np.rint(self.C * 2).astype(np.int64)
         self.keys = self._key(V)
         self.order = np.argsort(self.keys)
         self.sorted = self.keys[self.order]
+        self._tree = None
+
+    def nearest_exact(self, P):
+        """Exact nearest codeword of every row of P (unscaled units): a k-d tree
+        query (scipy's cKDTree, exact Euclidean search) when scipy is present,
+        else the exhaustive search. Equally near codewords may resolve to either."""
+        P = np.asarray(P, dtype=F64)
+        if len(P) == 0:
+            return np.zeros(0, dtype=np.int64)
+        try:
+            from scipy.spatial import cKDTree
+        except ImportError:  # pragma: no cover
+            return e8_nearest_bruteforce(P, self.C, 1.0)[0]
+        if self._tree is None:
+            self._tree = cKDTree(self.C)
+        _, idx = self._tree.query(P, k=1, workers=-1)
+        return np.asarray(idx, dtype=np.int64)
 
     @staticmethod
     def _key(V):
@@ -566,23 +589,26 @@ class E8Index:
 def e8_nearest(Y, C, s: float, index: E8Index | None = None):
     """Exact nearest codeword, fast: decode y/s on the whole lattice; when that
     lattice point belongs to the codebook it is also the nearest codeword (the
-    codebook is a subset of the lattice). Otherwise fall back to the exhaustive
-    search. Ties between equally near codewords may resolve differently from
-    ``e8_nearest_bruteforce``; the pins compare distances there."""
+    codebook is a subset of the lattice). Otherwise search the codebook exactly
+    (``E8Index.nearest_exact``). Ties between equally near codewords may resolve
+    differently from ``e8_nearest_bruteforce``; the pins compare distances there."""
     Y = np.asarray(Y, dtype=F64)
     index = E8Index(C) if index is None else index
     Z = e8_decode(Y / s)
     codes = index.lookup(Z)
     miss = codes < 0
     if miss.any():
-        codes[miss] = e8_nearest_bruteforce(Y[miss], C, s)[0]
+        codes[miss] = index.nearest_exact(Y[miss] / s)
     Cq = np.asarray(C, dtype=F64)[codes]
     dist = ((Y - s * Cq) ** 2).sum(axis=1)
     return codes, dist
 
 
 def row_rms(W) -> np.ndarray:
-    """Root mean square of every row (1 for an all-zero row)."""
+    """Root mean square of every row, sqrt(sum_j w_j^2 / n) (1 for an all-zero
+    row): the factor by which the E8 configuration normalizes each row of the
+    incoherent weights to unit RMS before the global scale is chosen (a reading;
+    [QuIP#] abstract, E8-lattice codebooks)."""
     W = np.asarray(W, dtype=F64)
     r = np.sqrt((W * W).mean(axis=1))
     return np.where(r > 0, r, 1.0)
@@ -598,9 +624,12 @@ def e8_scale_search(Wn, C, ncand: int = 32, nearest=None):
     the (row-normalized) weights. Returns (s, choice, sse per candidate)."""
     Wn = np.asarray(Wn, dtype=F64)
     Y = Wn.reshape(-1, 8)
-    nearest = e8_nearest if nearest is None else nearest
     cand = e8_scale_candidates(ncand)
-    sse = np.array([nearest(Y, C, s)[1].sum() for s in cand])
+    if nearest is None:
+        index = E8Index(C)
+        sse = np.array([e8_nearest(Y, C, s, index)[1].sum() for s in cand])
+    else:
+        sse = np.array([nearest(Y, C, s)[1].sum() for s in cand])
     choice = int(np.argmin(sse))
     return cand[choice], choice, sse
 

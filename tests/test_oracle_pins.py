@@ -703,3 +703,124 @@ def test_tcq_gaussian_mse_between_bound_and_best_scalar():
     mse = np.mean([O.tcq_viterbi(x, L, k)[1] for x in X]) / T
     R = k + (L - k) / T
     assert 2.0 ** (-2 * R) <= mse < 0.1175, mse
+
+
+# ---------------------------------------------------------------- grid decision vs exact nearest
+
+@pytest.mark.parametrize("L", [2, 4, 8, 16])
+def test_float32_grid_decision_is_the_exact_nearest_level_off_the_boundaries(L):
+    # The decision is taken in float32 (the pages fix no precision); away from
+    # the decision boundaries it must be the exact nearest level of the float64
+    # value, found here by comparing distances to every level in float64.
+    r = rng(200 + L)
+    s32 = np.float32(0.7311)
+    s = np.float64(s32)
+    x = r.uniform(-(L + 1) * s, (L + 1) * s, 20000)
+    bnd = (np.arange(1, L) - L / 2.0) * s  # midpoints between adjacent levels
+    near = (bnd[None, :] + np.outer(np.array([-1.0, 1.0]) * 1e-6, np.maximum(np.abs(bnd), s))).ravel()
+    x = np.concatenate([x, near])
+    levels = (np.arange(L) - (L - 1) / 2.0) * s
+    d = np.abs(x[:, None] - levels[None, :])
+    exact = np.argmin(d, axis=1)
+    got = O.uniform_code(x, s32, L)
+    far = np.min(np.abs(x[:, None] - bnd[None, :]), axis=1) > 1e-7 * np.maximum(np.abs(x), s)
+    assert far.sum() > 19000
+    assert np.array_equal(got[far], exact[far])
+    # on an exact boundary the tie goes up (to the larger level)
+    b = np.float32(bnd[L // 2 - 1]) if L > 2 else np.float32(0.0)
+    assert O.uniform_code(np.array([b]), s32, L)[0] == L // 2
+
+
+# ---------------------------------------------------------------- E8 configuration pass
+
+def test_row_rms_hand_worked_and_loop():
+    gd = golden("row_rms_worked.json")
+    rows = np.array(gd["rows"])
+    assert O.row_rms(rows).tolist() == gd["rms"]
+    W = rng(300).standard_normal((7, 24))
+    W[3] = 0.0
+    loop = []
+    for r in range(7):
+        acc = 0.0
+        for j in range(24):
+            acc += W[r, j] * W[r, j]
+        loop.append(np.sqrt(acc / 24) if acc > 0 else 1.0)
+    assert np.allclose(O.row_rms(W), loop, rtol=1e-14, atol=0)
+
+
+def _identity_kron(d):
+    # Q = I_p (x) I_q = I: a side whose transform leaves the matrix unchanged
+    p = 8 if d % 8 == 0 else 1
+    return {"A": np.eye(p), "B": np.eye(d // p)}
+
+
+def test_quantize_layer_e8_with_block_diagonal_H_is_groupwise_nearest():
+    # With identity transforms and an H that is block diagonal in 8 x 8 blocks,
+    # the block LDL has U = 0, so BlockLDLQ gets no feedback: every group is
+    # rounded to the nearest scaled codeword of the row-normalized weights, the
+    # scale is the argmin of the exhaustive nearest-codeword error, and the
+    # result is rescaled by each row's RMS.
+    m, n = 24, 64
+    r = rng(301)
+    X = np.zeros((8 * 40, n))
+    for g in range(n // 8):  # each calibration row lives in one column group
+        X[40 * g:40 * (g + 1), 8 * g:8 * (g + 1)] = r.standard_normal((40, 8)) * np.exp(r.standard_normal(8))
+    W = r.standard_normal((m, n)) * np.exp(0.5 * r.standard_normal(m))[:, None]
+    C = O.e8_codebook()
+    out = O.quantize_layer(W, X, _identity_kron(m), _identity_kron(n), quant="e8", g=8, codebook=C)
+    assert np.array_equal(out["Ht"], out["H"]) and np.array_equal(out["Wt"], W)
+    assert np.abs(out["U"]).max() == 0.0
+    rms = np.sqrt((W * W).mean(axis=1))
+    assert np.allclose(out["rms"], rms, rtol=1e-14)
+    Wn = W / rms[:, None]
+    s_bf, c_bf, sse_bf = O.e8_scale_search(Wn, C, nearest=O.e8_nearest_bruteforce)
+    assert out["scale_choice"] == c_bf and out["scale"] == s_bf
+    s32 = float(np.float32(s_bf))
+    k_bf, d_bf = O.e8_nearest_bruteforce(Wn.reshape(-1, 8), C, s32)
+    codes = out["codes"].reshape(-1)
+    d_got = ((Wn.reshape(-1, 8) - s32 * C[codes]) ** 2).sum(axis=1)
+    assert np.allclose(d_got, d_bf, rtol=0, atol=1e-12)
+    assert np.mean(codes == k_bf) > 0.99
+    assert np.allclose(out["What_t"], rms[:, None] * s32 * C[out["codes"]].reshape(m, n), rtol=1e-14)
+
+
+def test_quantize_layer_e8_loss_identity_round_trip_and_both_domains():
+    # A general small layer (random-sign Hadamard sides): the loss is the same
+    # in both domains; W^~ / rms is exactly the scaled codewords; and the loss
+    # equals sum_r rms_r^2 sum_K eta_K D_K eta_K^T with eta = P - W^~/rms the
+    # residual of each group's rounding (P the pre-rounding targets).
+    m, n = 16, 64
+    r = rng(302)
+    W = r.standard_normal((m, n))
+    W[r.random((m, n)) < 0.02] *= 10
+    X = r.standard_normal((256, n)) * np.exp(r.standard_normal(n))[None, :]
+    left = {"signs": r.choice([-1.0, 1.0], m)}
+    right = {"signs": r.choice([-1.0, 1.0], n)}
+    C = O.e8_codebook()
+    out = O.quantize_layer(W, X, left, right, quant="e8", g=8, codebook=C)
+    assert np.isclose(out["loss"], out["loss_t"], rtol=1e-9)
+    rms = out["rms"]
+    s32 = float(np.float32(out["scale"]))
+    Whn = out["What_t"] / rms[:, None]
+    assert np.allclose(Whn, s32 * C[out["codes"]].reshape(m, n), rtol=1e-14, atol=1e-15)
+    Wn = out["Wt"] / rms[:, None]
+    P = O.ldlq_prerounding(Wn, out["U"], Whn)
+    eta = (P - Whn).reshape(m, n // 8, 8)
+    blk = np.einsum("rka,kab,rkb->r", eta, out["D"], eta)
+    assert np.isclose((rms * rms * blk).sum(), out["loss_t"], rtol=1e-9)
+    # the scale is the argmin of the exhaustive search on the normalized W~
+    s_bf, c_bf, _ = O.e8_scale_search(Wn, C, nearest=O.e8_nearest_bruteforce)
+    assert out["scale_choice"] == c_bf
+
+
+def test_e8_nearest_exact_fallback_matches_exhaustive_far_outside_the_codebook():
+    # Far from the origin the nearest lattice point is outside the codebook, so
+    # every code comes from the exact codebook search.
+    C = O.e8_codebook()
+    Y = rng(303).standard_normal((400, 8)) * 3.0
+    idx = O.E8Index(C)
+    miss = idx.lookup(O.e8_decode(Y / 0.5)) < 0
+    assert miss.mean() > 0.9
+    k1, d1 = O.e8_nearest_bruteforce(Y, C, 0.5)
+    k2, d2 = O.e8_nearest(Y, C, 0.5, idx)
+    assert np.allclose(d1, d2, rtol=0, atol=1e-10)
