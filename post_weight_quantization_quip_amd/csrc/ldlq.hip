@@ -10,12 +10,12 @@
 //     value being  W_k + F_k + sum_{i in block, i < k} E_i U_ik,  E = W - W^
 //     F[:, j0+B:] += E_block U[j0:j0+B, j0+B:]        (matrix cores)
 //
-// Scalar grid sweep: one wave holds 16 rows; each row is spread over a quad of
-// 4 lanes, lane g owning the 4-column chunks {16t + 4g .. 16t + 4g + 3}. The
-// owner of column k rounds it, the error goes to the quad's other lanes with
-// one DPP quad_perm broadcast, and every lane updates its later columns with
-// the row of U held in LDS (laid out so that each lane's columns are
-// contiguous).
+// Scalar grid sweep: a work-group of 4 waves holds 16 rows; each row is one
+// 16-lane DPP row of its wave, and lane j owns column 16 t + j of the current
+// 16-column chunk t. Every lane evaluates the rounding of its own target; the
+// error of column kk reaches the whole row with one DPP row_newbcast from its
+// owner, and each lane adds its share of the feedback with U's coefficients
+// staged transposed in LDS one chunk ahead.
 //
 // E8 groups: the pre-rounding 8-vectors of all rows are searched against the
 // 65536 codewords as a distance contraction on the matrix cores
@@ -228,21 +228,6 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
   };
   float4 upre[NV];
   load_rows(0, upre);
-  {
-    // Warm this XCD's L2 with U's block: work-groups are dealt round-robin to
-    // the 8 XCDs, and every group reads the whole block, so each takes its
-    // share of the rows of the block once here; the chunk loads then hit L2.
-    const int per_xcd = int((gridDim.x + 7) / 8);
-    const int share = (B + per_xcd - 1) / per_xcd;  // rows per work-group
-    const int r0 = int(blockIdx.x / 8) * share;
-    const int e = tid;  // one float4 per thread
-    const int k = r0 + e / (B / 4), c4 = (e % (B / 4)) * 4;
-    if (e < share * (B / 4) && k < bw && k < r0 + share) {
-      const float* src = U + (s0 + k) * ldu + s0 + c4;
-      const float v = *src;  // one float per 16 bytes touches the line
-      if (v != v && tid > 4096) Ds[0] = v;  // never taken: keeps the load
-    }
-  }
   store_rows(0, upre);
   if (rowloss) {
     for (int i = tid; i < B; i += 256) Ds[i] = i < bw ? Dg[s0 + i] : 0.f;
@@ -462,16 +447,18 @@ __device__ __forceinline__ e8_half8 e8_split_operand(const float* y8, int g) {
 
 // Squared error of the nearest codeword, summed over all 8-vectors, for every
 // candidate scale. One wave: 32 vectors x all codewords.
+// Each work-group writes its NC partial sums to part[blockIdx.x * NC + c]
+// (waves added in a fixed order); e8_sse_reduce_kernel adds the work-groups'
+// partials in a fixed order, so the table, and the scale picked from it, are
+// the same on every run.
 template <int NC>
 __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__ Y, int64_t nvec,
                                                        const _Float16* __restrict__ C16,
                                                        const float* __restrict__ c2,
                                                        const float* __restrict__ cand, int ncand,
-                                                       double* __restrict__ sse) {
-  __shared__ double red[NC];
+                                                       double* __restrict__ part) {
+  __shared__ double red[4][NC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < NC) red[tid] = 0.0;
-  __syncthreads();
   const int64_t v0 = (int64_t(blockIdx.x) * 4 + wave) * 32;
   const int j = lane & 31, kh = lane >> 5;
   const int64_t vj = v0 + j;
@@ -554,10 +541,32 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
     double e = live && kh == 0 ? double(y2) + double(sc[c]) * double(b) : 0.0;
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
-    if (lane == 0 && c < ncand) atomicAdd(&red[c], e);
+    if (lane == 0) red[wave][c] = e;
   }
   __syncthreads();
-  if (tid < ncand && tid < NC) atomicAdd(&sse[tid], red[tid]);
+  if (tid < NC) {
+    part[int64_t(blockIdx.x) * NC + tid] =
+        tid < ncand ? (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]) : 0.0;
+  }
+}
+
+// sse[c] = sum over the nblk work-groups of part[b * NC + c], one work-group per
+// candidate, in a fixed order (strided partial sums, then a tree).
+template <int NC>
+__global__ __launch_bounds__(256) void e8_sse_reduce_kernel(const double* __restrict__ part,
+                                                            int64_t nblk,
+                                                            double* __restrict__ sse) {
+  __shared__ double t[256];
+  const int c = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t b = threadIdx.x; b < nblk; b += 256) acc += part[b * NC + c];
+  t[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (int(threadIdx.x) < h) t[threadIdx.x] += t[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sse[c] = t[0];
 }
 
 // Pre-rounding vectors of one group step of BlockLDLQ, once per step:
@@ -786,7 +795,12 @@ struct E8Ws {
   _Float16* c16;  // the codebook in half precision (exact: multiples of 1/2 up to 3.5)
   float* cand;
   double* sse;
+  double* part;  // per-work-group partial sums of the scale search
 };
+
+// Work-groups of the E8 scale search (128 vectors each) and their partial sums.
+int64_t e8_scale_blocks(int64_t m, int64_t n) { return cdiv(m * (n / 8), 128); }
+size_t e8_partial_count(int64_t m, int64_t n) { return size_t(e8_scale_blocks(m, n)) * 64; }
 
 quip_status grid_scales(const float* W, int64_t m, int64_t n, int64_t ldw, int L, int ncand,
                         float* factors_dev, float* scales, float* mse, hipStream_t s) {
@@ -805,17 +819,25 @@ quip_status grid_scales(const float* W, int64_t m, int64_t n, int64_t ldw, int L
 
 quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, const E8Ws& e,
                       int ncand, float* scales, double* sse_out, hipStream_t s) {
-  QUIP_TRY(fill_f64(e.sse, 64, 0.0, s));
   const int64_t nvec = m * (n / 8);
-  dim3 grid(unsigned(cdiv(nvec, 128)));
+  const int64_t nblk = e8_scale_blocks(m, n);
+  const dim3 grid{unsigned(nblk)};
   QUIP_TRY(timed_launch("e8_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (ncand <= 32)
       QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, e.c16, e.c2, e.cand,
-                         ncand, e.sse);
+                         ncand, e.part);
     else
       QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, e.c16, e.c2, e.cand,
-                         ncand, e.sse);
+                         ncand, e.part);
   }, 16.0 * 65536.0 * double(nvec), 32.0 * double(nvec)));  // <y, c> for every vector and codeword
+  QUIP_TRY(timed_launch("e8_sse_reduce_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    if (ncand <= 32)
+      QUIP_KERNEL((e8_sse_reduce_kernel<32>), dim3(unsigned(ncand)), dim3(256), 0, s, e.part,
+                  nblk, e.sse);
+    else
+      QUIP_KERNEL((e8_sse_reduce_kernel<64>), dim3(unsigned(ncand)), dim3(256), 0, s, e.part,
+                  nblk, e.sse);
+  }));
   QUIP_TRY(timed_launch("e8_pick_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL(e8_pick_scale_kernel, dim3(1), dim3(64), 0, s, e.sse, e.cand, ncand, scales);
   }));
@@ -895,6 +917,7 @@ size_t scales_workspace_bytes(int64_t m, int64_t n, const quip_quantizer& q) {
     c.take<float>(65536);          // |c|^2
     c.take<_Float16>(65536 * 8);   // the codebook in half precision
     c.take<double>(64);            // sse
+    c.take<double>(e8_partial_count(m, n));  // per-work-group partial sums
   }
   return c.used;
 }
@@ -917,6 +940,7 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   e.c2 = c.take<float>(65536);
   e.c16 = c.take<_Float16>(65536 * 8);
   e.sse = c.take<double>(64);
+  e.part = c.take<double>(e8_partial_count(m, n));
   e.cand = fac;
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_scales: workspace too small");
   host_e8_candidates(q.n_cand, hostf);
@@ -955,6 +979,7 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
     c.take<float>(65536);
     c.take<_Float16>(65536 * 8);
     c.take<double>(64);
+    c.take<double>(e8_partial_count(m, n));
   }
   (void)g;
   return c.used;
@@ -1008,6 +1033,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   e.c2 = c.take<float>(65536);
   e.c16 = c.take<_Float16>(65536 * 8);
   e.sse = c.take<double>(64);
+  e.part = c.take<double>(e8_partial_count(m, n));
   e.cand = fac;
   e.F = F;
   e.Eb = Eb;

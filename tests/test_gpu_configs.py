@@ -288,3 +288,103 @@ def test_config_e8():
     assert mism.sum() <= max(1, P.MAX_MISMATCH * cg.size)
     assert np.allclose(What, rms_all[rows][:, None] * s * C[codes].reshape(NSAMP, -1), rtol=1e-6, atol=1e-7)
     check_fused_rows(b, rows, host(b["Wt"])[rows], host(b["What_t"])[rows], host(b["H"]))
+
+
+# ------------------------------------------------------------------ whole-matrix checks
+
+def test_config_c2_whole_matrix():
+    """The 4096 x 4096 headline layer compared in full: H~ and W~ against the
+    oracle's transforms, the LDL factors against the oracle's factorization of
+    the GPU's own H~ (every entry), every row's scale, the conditional replay
+    of all 4096 x 4096 codes, the proxy loss of every row, and the oracle's own
+    run of the whole pass (its own float64 factors)."""
+    L, lp, b, rng = run_config("c2")
+    cfg = L.cfg
+    ref = O.quantize_layer(L.W, L.X, L.left, L.right, quant="uniform", bits=cfg.bits,
+                           use_cholesky=True)
+    H = host(b["H"])
+    assert P.rel_rows(H, ref["Ht"]) <= 2e-5
+    Wt = host(b["Wt"])
+    assert P.rel_rows(Wt, ref["Wt"]) <= 1e-5
+    U, D = host(b["U"]), host(b["D"])
+    assert int(host(b["info"])[0]) == 0
+    assert P.recon_residual(H, U, D) <= 2e-6 * np.sqrt(cfg.n)
+    Uo, Do = O.udu_cholesky(H.astype(np.float64), 1)
+    assert np.linalg.norm(U - Uo) / np.linalg.norm(Uo) <= 1e-3
+    assert np.linalg.norm(D - Do) / np.linalg.norm(Do) <= 1e-3
+    assert np.all(np.tril(U) == 0)
+    Lv = 1 << cfg.bits
+    s = host(b["scales"])
+    s_ref, c_ref, mse_ref = O.uniform_scale_search(Wt, Lv)
+    cand = O.uniform_scale_candidates(np.abs(Wt.astype(np.float64)).max(axis=1), Lv)
+    cg = np.argmin(np.abs(cand - s[:, None].astype(np.float64)), axis=1)
+    assert np.allclose(s, cand[np.arange(cfg.m), cg], rtol=1e-6)
+    rows = np.arange(cfg.m)
+    assert np.all(mse_ref[rows, cg] <= mse_ref[rows, c_ref] * (1 + 1e-5))
+    What = host(b["What_t"])
+    codes = host(b["codes"])
+    mism, bad, tot = P.replay_uniform(Wt, U, What, s, codes, Lv)
+    print(f"c2 replay: {mism} of {tot} codes differ, all in the boundary band" if not bad else "")
+    assert bad == 0 and mism <= P.MAX_MISMATCH * tot
+    E = What.astype(np.float64) - Wt.astype(np.float64)
+    want = np.einsum("ij,ij->i", E @ H.astype(np.float64), E)
+    rl = host(b["row_loss"])
+    assert np.allclose(rl, want, rtol=2e-5)
+    assert abs(float(host(b["loss"])[0]) - want.sum()) <= 1e-5 * want.sum()
+    st = P.compare_independent_run({k: host(b[k]) for k in ("Wt", "H", "U", "D", "scales", "codes",
+                                                             "What_t")}, ref, g=1, L=Lv)
+    print(f"c2 independent run: {st['diverged']} of {st['rows']} rows diverged; loss "
+          f"{st['loss_gpu']:.10g} vs {st['loss_oracle']:.10g} (extra bound {st['extra_bound']:.4g})")
+
+
+@pytest.fixture(scope="module")
+def c5_pass():
+    L, lp, b, rng = run_config("c5")
+    out = {k: host(b[k]) for k in ("H", "Wt", "U", "D", "scales", "codes", "What_t", "row_loss",
+                                   "loss", "info")}
+    return L, out
+
+
+def test_config_e8_whole_matrix(c5_pass):
+    """The E8 layer (4096 x 4096, BlockLDLQ g = 8) in full: every row's RMS,
+    the block LDL factors against the oracle's on the GPU's own H~, the
+    conditional replay of all 2M codes at the GPU's global scale, and every
+    row's proxy loss."""
+    L, b = c5_pass
+    n = L.cfg.n
+    C = O.e8_codebook()
+    H, Wt, U = b["H"], b["Wt"], b["U"]
+    assert int(b["info"][0]) == 0
+    sc = b["scales"]
+    rms = sc[1:].astype(np.float64)
+    assert np.allclose(rms, O.row_rms(Wt), rtol=1e-6)
+    D = b["D"].astype(np.float64)
+    assert P.recon_residual(H, U, D, 8) <= 2e-6 * np.sqrt(n)
+    Uo, Do = O.udu_cholesky(H.astype(np.float64), 8)
+    assert np.linalg.norm(U - Uo) / np.linalg.norm(Uo) <= 1e-3
+    assert np.linalg.norm(D - Do.reshape(-1)) / np.linalg.norm(Do) <= 1e-3
+    Wn = Wt / rms[:, None]
+    Whn = b["What_t"] / rms[:, None]
+    mism, bad, tot = P.replay_e8(Wn, U, Whn, float(sc[0]), b["codes"], C)
+    print(f"c5 replay: {mism} of {tot} codes differ inside the distance band")
+    assert bad == 0 and mism <= max(1, P.MAX_MISMATCH * tot)
+    E = b["What_t"].astype(np.float64) - Wt.astype(np.float64)
+    want = np.einsum("ij,ij->i", E @ H.astype(np.float64), E)
+    assert np.allclose(b["row_loss"], want, rtol=2e-5)
+    assert abs(float(b["loss"][0]) - want.sum()) <= 1e-5 * want.sum()
+
+
+def test_config_e8_global_scale_is_oracle_argmin(c5_pass):
+    """The global scale of the E8 layer is the oracle's argmin of the exact
+    nearest-codeword error over all 2M normalized 8-vectors (candidates ruled
+    out by a lower bound, the rest evaluated exactly)."""
+    L, b = c5_pass
+    C = O.e8_codebook()
+    sc = b["scales"]
+    rms = sc[1:].astype(np.float64)
+    cands = O.e8_scale_candidates()
+    choice = int(np.argmin(np.abs(cands - sc[0])))
+    assert abs(cands[choice] - sc[0]) <= 1e-6 * sc[0]
+    ok, info = P.e8_scale_is_argmin(b["Wt"] / rms[:, None], C, choice)
+    print("c5 scale:", choice, {c: (k, round(v, 2)) for c, (k, v) in sorted(info.items())})
+    assert ok
