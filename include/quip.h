@@ -24,8 +24,9 @@
  *     sizes come from the quip_*_workspace queries; a workspace must be 256-byte
  *     aligned. The library allocates no device memory and keeps no global
  *     mutable state other than the optional per-kernel timing registry
- *     (quip_timing_*, off by default); calls on different streams are
- *     independent.
+ *     (quip_timing_*, off by default) and the static scratch array of
+ *     quip_qmatvec_rht_noalloc; calls on different streams are independent
+ *     (except overlapping calls of quip_qmatvec_rht_noalloc on one GPU).
  *   - Every call only enqueues work on `stream` (asynchronous) and returns at
  *     once. Argument and shape errors are detected on the host before any
  *     launch, and then nothing is enqueued. A failure found on the device (a
@@ -326,6 +327,30 @@ quip_status quip_qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int32_
                              const float* scales, const float* signs_left,
                              const float* signs_right, const float* x, float* y, void* ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * quip_qmatvec_rht_noalloc -- quip_qmatvec_rht without a workspace, for callers
+ * that cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same
+ * arguments, kernels and result as quip_qmatvec_rht (bit for bit); its scratch
+ * (the transformed vector, the transform's intermediate and the per-slice
+ * partial sums) lives in a static device array of 4 MiB inside the library,
+ * one copy per GPU, held until the process ends. Allocates nothing (no
+ * hipMalloc, no library allocation); the first call on a device looks the
+ * array's device address up once (hipGetSymbolAddress).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (different streams, or host threads on the same device) race
+ *   and give undefined results; serialize them. The array keeps the last
+ *   call's contents; every word a call reads it writes first.
+ * Errors: as quip_qmatvec_rht (QUIP_ERR_ARG, QUIP_ERR_SHAPE; the accepted
+ *   shapes, m and n up to 16384, need at most 2.1 MiB of the 4 MiB, and a
+ *   product needing more is refused with QUIP_ERR_SHAPE); QUIP_ERR_HIP if the
+ *   array's address cannot be obtained.
+ */
+quip_status quip_qmatvec_rht_noalloc(const uint8_t* packed, int64_t m, int64_t n, int32_t bits,
+                                     const float* scales, const float* signs_left,
+                                     const float* signs_right, const float* x, float* y,
+                                     hipStream_t stream);
 
 /*
  * quip_permute -- moves the rows and columns of a matrix by index vectors:

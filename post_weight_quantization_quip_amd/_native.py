@@ -77,6 +77,8 @@ SYMBOLS = {
     "quip_qmatvec_rht_workspace": (c_int, [c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "quip_qmatvec_rht": (c_int, [c_vp, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_sz, c_vp]),
+    "quip_qmatvec_rht_noalloc": (c_int, [c_vp, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp, c_vp, c_vp,
+                                         c_vp, c_vp]),
     "quip_permute": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, ctypes.c_int32,
                              c_vp]),
     "quip_diag_order_workspace": (c_int, [c_i64, ctypes.POINTER(c_sz)]),
@@ -271,6 +273,16 @@ def quip_qmatvec_rht(packed, n: int, bits: int, scales, signs_left, signs_right,
                                 _p(signs_right), _p(x), _p(y), _p(ws),
                                 0 if ws is None else ws.numel(), _stream(stream)),
            "quip_qmatvec_rht")
+
+
+def quip_qmatvec_rht_noalloc(packed, n: int, bits: int, scales, signs_left, signs_right, x, y,
+                             stream=None):
+    """quip_qmatvec_rht with its scratch in the library's static device array:
+    no workspace, no allocation (calls that overlap on one GPU race)."""
+    m = scales.numel()
+    _check(lib.quip_qmatvec_rht_noalloc(_p(packed), m, n, bits, _p(scales), _p(signs_left),
+                                        _p(signs_right), _p(x), _p(y), _stream(stream)),
+           "quip_qmatvec_rht_noalloc")
 
 
 def quip_permute(A, out, row_index=None, col_index=None, scatter: bool = False, stream=None):

@@ -367,6 +367,25 @@ quip_status quip_qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int32_
                      stream);
 }
 
+quip_status quip_qmatvec_rht_noalloc(const uint8_t* packed, int64_t m, int64_t n, int32_t bits,
+                                     const float* scales, const float* signs_left,
+                                     const float* signs_right, const float* x, float* y,
+                                     hipStream_t stream) {
+  clear_error();
+  const char* who = "quip_qmatvec_rht_noalloc";
+  if (!packed || !scales || !signs_left || !signs_right || !x || !y)
+    return fail(QUIP_ERR_ARG, std::string(who) + ": null pointer");
+  if (bits < 1 || bits > 8) return fail(QUIP_ERR_ARG, std::string(who) + ": bits must be in [1, 8]");
+  if (!is_pow2(m) || m < 2 || m > 16384)
+    return fail(QUIP_ERR_SHAPE, std::string(who) + ": m must be a power of two in [2, 16384]");
+  if (!is_pow2(n) || n < 1024 || n > 16384)
+    return fail(QUIP_ERR_SHAPE, std::string(who) + ": n must be a power of two in [1024, 16384]");
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(y) || !aligned16(signs_left) ||
+      !aligned16(signs_right))
+    return fail(QUIP_ERR_ARG, std::string(who) + ": packed, x, y and the signs must be 16-byte aligned");
+  return qmatvec_rht_noalloc(packed, m, n, bits, scales, signs_left, signs_right, x, y, stream);
+}
+
 quip_status quip_permute(const float* A, int64_t lda, float* out, int64_t ldo, int64_t rows,
                          int64_t cols, const int32_t* row_index, const int32_t* col_index,
                          int32_t scatter, hipStream_t stream) {

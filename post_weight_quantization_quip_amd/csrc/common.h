@@ -118,6 +118,12 @@ size_t qmatvec_workspace_bytes(int64_t m, int64_t n);
 quip_status qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int bits, const float* scales,
                         const float* signs_left, const float* signs_right, const float* x,
                         float* y, void* ws, size_t ws_bytes, hipStream_t s);
+// The same product with its scratch in a static device array (no workspace).
+size_t qmatvec_scratch_bytes();
+quip_status qmatvec_rht_noalloc(const uint8_t* packed, int64_t m, int64_t n, int bits,
+                                const float* scales, const float* signs_left,
+                                const float* signs_right, const float* x, float* y,
+                                hipStream_t s);
 
 // ---------------------------------------------------------------- permutations (permute.hip)
 

@@ -38,7 +38,15 @@
 // The two used accumulator columns are added with one lane swap and each
 // slice writes one partial per row; the first pass of the inverse transform
 // sums the slices in a fixed order (deterministic; no atomics, no barriers).
+#include <mutex>
+#include <string>
+
 #include "common.h"
+
+// Size of the allocation-free product's scratch: the workspace of the largest
+// product the entry points accept (m = n = 16384: 2.1 MiB) with room to spare.
+#define QMV_SCRATCH_BYTES (4u << 20)
+#define QMV_MAX_DEVICES 64
 
 namespace quip {
 namespace {
@@ -394,6 +402,14 @@ quip_status qmv_mfma_t(const uint8_t* packed, int64_t m, int64_t n, const _Float
   }, flops, bytes);
 }
 
+// Scratch of the allocation-free variant of the product: partial sums, the
+// transformed vector and the transform's intermediate live in this array
+// instead of a caller workspace. One copy per GPU, held until the process
+// ends. Host code never passes the array's name to a kernel (on the host it is
+// a stand-in, not a device address): it uses the address hipGetSymbolAddress
+// gives for the current device.
+static __device__ __align__(256) unsigned char scratch[QMV_SCRATCH_BYTES];
+
 }  // namespace
 
 int code_container_bits(int bits) { return bits <= 2 ? 2 : (bits <= 4 ? 4 : 8); }
@@ -444,6 +460,44 @@ quip_status qmatvec_rht(const uint8_t* packed, int64_t m, int64_t n, int bits, c
   QUIP_TRY(vec_fwht_pass(nullptr, tmp, 0, m, nullptr, part, nblk, scales, nullptr, 1.f, s));
   return vec_fwht_pass(tmp, y, 1, m, nullptr, nullptr, 0, nullptr, signs_left,
                        1.0f / sqrtf(float(m)), s);
+}
+
+size_t qmatvec_scratch_bytes() { return QMV_SCRATCH_BYTES; }
+
+// Device address of `scratch` on the current device, looked up once per device.
+static quip_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[QMV_MAX_DEVICES] = {};
+  int dev = 0;
+  QUIP_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= QMV_MAX_DEVICES)
+    return fail(QUIP_ERR_UNSUPPORTED, "quip_qmatvec_rht_noalloc: device index out of range");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    QUIP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(QUIP_ERR_HIP, "quip_qmatvec_rht_noalloc: no address for the scratch array");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return QUIP_OK;
+}
+
+quip_status qmatvec_rht_noalloc(const uint8_t* packed, int64_t m, int64_t n, int bits,
+                                const float* scales, const float* signs_left,
+                                const float* signs_right, const float* x, float* y,
+                                hipStream_t s) {
+  const size_t need = qmatvec_workspace_bytes(m, n);
+  if (need > QMV_SCRATCH_BYTES)
+    return fail(QUIP_ERR_SHAPE, "quip_qmatvec_rht_noalloc: the product of this size needs " +
+                                    std::to_string(need) + " bytes of scratch, more than the " +
+                                    std::to_string(size_t(QMV_SCRATCH_BYTES)) + " it has");
+  void* ws = nullptr;
+  QUIP_TRY(scratch_address(&ws));
+  // every scratch word the product reads is written earlier in the same call,
+  // so nothing needs clearing between calls
+  return qmatvec_rht(packed, m, n, bits, scales, signs_left, signs_right, x, y, ws,
+                     QMV_SCRATCH_BYTES, s);
 }
 
 }  // namespace quip
