@@ -652,6 +652,47 @@ def cpu_baseline(cfg_name: str, rows: int) -> dict:
     }
 
 
+def north_star_targets(kernels: dict, phases: dict, rht: dict, cfg) -> dict:
+    """The phase-level figures the pass is held to, each next to its target:
+    the two-sided random-sign Hadamard transform against the HBM peak (>= 60 %),
+    the proxy-Hessian product and the LDLQ trailing update (inner and outer
+    products together) against the fp32 matrix-core peak (>= 50 %), and the
+    LDL phase (n^3 / 3 flops over its wall time; reported, no target)."""
+
+    def family_frac(names):
+        fl = sum(kernels[n]["algorithmic_flops_per_launch"] * kernels[n]["launches_per_step"]
+                 for n in names if n in kernels)
+        ms = sum(kernels[n]["ms_per_step"] for n in names if n in kernels)
+        return (fl / (ms / 1e3) / 1e12 / FP32_MFMA_PEAK_TFLOPS if ms > 0 else None), ms
+
+    out = {}
+    if rht:
+        out["rht_two_sided_frac_of_hbm"] = {
+            "measured": round(rht["two_sided_effective_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+        out["rht_right_pass_frac_of_hbm"] = {
+            "measured": round(rht["right_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+        out["rht_left_pass_frac_of_hbm"] = {
+            "measured": round(rht["left_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+    f, ms = family_frac(["gemm:hessian"])
+    if f is not None:
+        out["hessian_frac_of_mfma"] = {"measured": round(f, 3), "target": 0.50, "ms": round(ms, 4)}
+    f, ms = family_frac(["gemm:ldlq_inner", "gemm:ldlq_outer"])
+    if f is not None:
+        out["ldlq_trailing_update_frac_of_mfma"] = {"measured": round(f, 3), "target": 0.50,
+                                                    "ms": round(ms, 4)}
+    n = float(cfg.n)
+    if phases.get("ldl"):
+        out["ldl_phase_frac_of_mfma"] = {
+            "measured": round(n ** 3 / 3 / (phases["ldl"] / 1e3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            "target": None, "ms": round(phases["ldl"], 4)}
+    if phases.get("ldlq"):
+        out["ldlq_phase_ms"] = {"measured": round(phases["ldlq"], 4), "target": None}
+    for v in out.values():
+        if v.get("target") is not None:
+            v["meets"] = bool(v["measured"] >= v["target"])
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -788,6 +829,7 @@ def main():
                "frac_of_hbm_peak_right": round(nbytes / r_ms / 1e6 / HBM_PEAK_GBS, 3)}
 
     attainable = attainable_bench(Q, dev, timed)
+    targets = north_star_targets(kernels, phases, rht, cfg)
 
     # beside the pass: Gaussian-source VQ, the inference product, the variants
     gaussian_vq, inference, variants, tcq, e8c, allcfg = {}, {}, {}, {}, {}, {}
@@ -826,6 +868,7 @@ def main():
         "inference": inference,
         "variants": variants,
         "roofline": roofline,
+        "targets": targets,
         "attainable": attainable,
         "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])),
     }
