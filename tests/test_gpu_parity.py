@@ -257,7 +257,8 @@ def ldl_gpu(H32, g):
 
 
 @pytest.mark.parametrize("n,g", [(256, 1), (256, 8), (200, 1), (200, 8), (8, 8), (1, 1), (130, 1),
-                                 (600, 1), (600, 8), (520, 1), (1000, 1)])
+                                 (600, 1), (600, 8), (520, 1), (1000, 1), (2000, 1), (1536, 8),
+                                 (3000, 1)])
 def test_ldl_parity(n, g):
     H = spd32(n * 11 + g, n)
     U, D, info = ldl_gpu(H, g)
