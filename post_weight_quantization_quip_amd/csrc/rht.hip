@@ -16,7 +16,7 @@
 // LEFT side (along a column, strided by the row pitch). For d = 4096 and
 // float4-aligned rows, one pass over memory, a work-group per column block:
 // rht_cols_panel16 (16 columns, 64-byte row segments, the panel in registers,
-// two LDS exchanges in halves) when the column count is a multiple of 16, else
+// one LDS exchange in halves) when the column count is a multiple of 16, else
 // rht_cols_panel (8 columns in LDS, 128 KB + padding: the top four index bits
 // in registers right after the load, the middle four through one LDS round
 // trip, the low four in registers right before the store). Row segments
@@ -396,87 +396,80 @@ __device__ __forceinline__ void fwht32_f4(float4 (&v)[32]) {
     }
 }
 
+// In-register butterflies over the index bits of v[0..63] (float2 of two
+// columns per index).
+__device__ __forceinline__ void fwht64_f2(float2 (&v)[64]) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (i & h) continue;
+      const float2 u = v[i], w = v[i | h];
+      v[i] = make_float2(u.x + w.x, u.y + w.y);
+      v[i | h] = make_float2(u.x - w.x, u.y - w.y);
+    }
+}
+
 // Column transform of length 4096 for 16 consecutive columns per work-group
-// (64-byte row segments: four lanes per row), in one pass over memory. 512
-// threads; thread t holds column group g = t % 4 (4 columns) of 32 rows in
-// registers (the 256 KB panel lives in registers). Index bits 7..11 are done
-// right after the load (rows k + 128 i), bits 2..6 after one exchange (rows
-// l + 4 i + 128 h), bits 0..1 after a second one (rows 32 k + i), then the
-// store. Each exchange goes through LDS in two halves of 8 columns (128 KB +
-// padding: slot 2 r + g' + r / 16 of a half). Needs cols % 16 == 0, ld % 4 ==
-// 0 and 16-byte aligned A and out; A == out is allowed.
+// (64-byte row segments: eight lanes per row), in one pass over memory. 512
+// threads; thread t holds the column pair g = t % 8 of 64 rows in registers
+// (the 256 KB panel lives in registers). Index bits 6..11 are done right after
+// the load (rows k + 64 i), bits 0..5 after one exchange (rows 64 k + i), then
+// the store. The exchange goes through LDS in two halves of 8 columns (128 KB
+// + padding: float2 slot 4 r + g' + r / 16 of a half, so that both the
+// row-contiguous writes and the 64-row-strided reads of a wave's active lanes
+// fall on distinct banks). Needs cols % 16 == 0, ld % 2 == 0 and 8-byte
+// aligned A and out; A == out is allowed.
+template <bool INV>
 __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* out, int64_t ld,
                                                         int nblk,
                                                         const float* __restrict__ signs,
-                                                        float scale, bool inverse) {
-  extern __shared__ __align__(16) float4 P[];
-  auto slot = [](int r, int g2) { return 2 * r + g2 + (r >> 4); };
+                                                        float scale) {
+  constexpr bool inverse = INV;
+  extern __shared__ __align__(16) float2 P2[];
+  auto slot = [](int r, int g4) { return 4 * r + g4 + (r >> 4); };
   const int t = threadIdx.x;
-  const int g = t & 3, k = t >> 2;  // column group, row index of the thread (0..127)
-  const int64_t c = int64_t(xcd_remap(int(blockIdx.x), nblk)) * 16 + 4 * g;
-  float4 v[32];
+  const int g = t & 7, k = t >> 3;  // column pair, row index of the thread (0..63)
+  // the block's first column (uniform) and the lane's offset from it, so that
+  // every access is a uniform base plus one 32-bit lane offset
+  const int64_t cb = int64_t(xcd_remap(int(blockIdx.x), nblk)) * 16;
+  const uint32_t lin = uint32_t(k * ld + 2 * g);        // rows k + 64 i
+  const uint32_t lout = uint32_t(64 * k * ld + 2 * g);  // rows 64 k + i
+  float2 v[64];
 
-  // ---- rows k + 128 i: bits 7..11
+  // ---- rows k + 64 i: bits 6..11
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    v[i] = *reinterpret_cast<const float4*>(A + int64_t(k + 128 * i) * ld + c);
+  for (int i = 0; i < 64; ++i)
+    v[i] = *reinterpret_cast<const float2*>(A + cb + int64_t(64 * i) * ld + lin);
   if (!inverse) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float sg = signs[k + 128 * i];
-      v[i] = make_float4(v[i].x * sg, v[i].y * sg, v[i].z * sg, v[i].w * sg);
+    for (int i = 0; i < 64; ++i) {
+      const float sg = signs[k + 64 * i];
+      v[i] = make_float2(v[i].x * sg, v[i].y * sg);
     }
   }
-  fwht32_f4(v);
-  // ---- exchange to rows l + 4 i + 128 h (l = k % 4, h = k / 4): bits 2..6
-  const int l = k & 3, h = k >> 2;
+  fwht64_f2(v);
+  // ---- exchange to rows 64 k + i: bits 0..5 (and the store layout)
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const bool mine = (g >> 1) == half;
+    const bool mine = (g >> 2) == half;
     if (half) __syncthreads();  // the first half's reads are done
     if (mine) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) P[slot(k + 128 * i, g & 1)] = v[i];
+      for (int i = 0; i < 64; ++i) P2[slot(k + 64 * i, g & 3)] = v[i];
     }
     __syncthreads();
     if (mine) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = P[slot(l + 4 * i + 128 * h, g & 1)];
+      for (int i = 0; i < 64; ++i) v[i] = P2[slot(64 * k + i, g & 3)];
     }
   }
-  fwht32_f4(v);
-  // ---- exchange to rows 32 k + i: bits 0..1 (and the store layout)
+  fwht64_f2(v);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const bool mine = (g >> 1) == half;
-    __syncthreads();  // the previous reads of the buffer are done
-    if (mine) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) P[slot(l + 4 * i + 128 * h, g & 1)] = v[i];
-    }
-    __syncthreads();
-    if (mine) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = P[slot(32 * k + i, g & 1)];
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 32; q += 4) {  // bits 0..1: groups of four consecutive rows
-#pragma unroll
-    for (int hb = 1; hb < 4; hb <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i & hb) continue;
-        const float4 u = v[q + i], w = v[q + (i | hb)];
-        v[q + i] = make_float4(u.x + w.x, u.y + w.y, u.z + w.z, u.w + w.w);
-        v[q + (i | hb)] = make_float4(u.x - w.x, u.y - w.y, u.z - w.z, u.w - w.w);
-      }
-  }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float sg = scale * (inverse ? signs[32 * k + i] : 1.f);
-    *reinterpret_cast<float4*>(out + int64_t(32 * k + i) * ld + c) =
-        make_float4(v[i].x * sg, v[i].y * sg, v[i].z * sg, v[i].w * sg);
+  for (int i = 0; i < 64; ++i) {
+    const float sg = scale * (inverse ? signs[64 * k + i] : 1.f);
+    *reinterpret_cast<float2*>(out + cb + int64_t(i) * ld + lout) =
+        make_float2(v[i].x * sg, v[i].y * sg);
   }
 }
 
@@ -603,12 +596,20 @@ quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
     const float scale = 1.0f / 64.0f;  // 1 / sqrt(4096)
     if (cols % 16 == 0) {  // 64-byte row segments
-      QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel16),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+      // half a panel (8 columns x 4096 rows) plus one float2 of padding per 16 rows
+      const size_t shmem16 = size_t(4 * 4096 + 4096 / 16) * sizeof(float2);
+      QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel16<false>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem16)));
+      QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel16<true>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem16)));
       const int nblk = int(cols / 16);
       return timed_launch("rht_cols_panel16", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(rht_cols_panel16, dim3(unsigned(nblk)), dim3(512), shmem, st, A, out, ld,
-                    nblk, signs, scale, inverse);
+        if (inverse)
+          QUIP_KERNEL(rht_cols_panel16<true>, dim3(unsigned(nblk)), dim3(512), shmem16, st, A,
+                      out, ld, nblk, signs, scale);
+        else
+          QUIP_KERNEL(rht_cols_panel16<false>, dim3(unsigned(nblk)), dim3(512), shmem16, st, A,
+                      out, ld, nblk, signs, scale);
       }, double(rows) * double(cols) * 14.0, 8.0 * double(rows) * double(cols));
     }
     const dim3 grid{unsigned(cdiv(cols, 8))};
