@@ -388,3 +388,23 @@ def test_config_e8_global_scale_is_oracle_argmin(c5_pass):
     ok, info = P.e8_scale_is_argmin(b["Wt"] / rms[:, None], C, choice)
     print("c5 scale:", choice, {c: (k, round(v, 2)) for c, (k, v) in sorted(info.items())})
     assert ok
+
+
+@pytest.mark.parametrize("name", ["c3a", "c3b", "c3p", "c4a", "c4b", "c4c"])
+def test_config_replay_all_rows(name):
+    """Conditional replay of every code of the full-size layer (every row, every
+    column): each pre-rounding value recomputed in float64 from the GPU's own
+    factors and earlier decisions; a code may differ from the float32 decision
+    only inside the boundary band, by one level, and at most 1e-4 of the codes.
+    W^~ is the grid value of its code exactly."""
+    L, lp, b, rng = run_config(name)
+    cfg = L.cfg
+    Lv = 1 << cfg.bits
+    assert int(host(b["info"])[0]) == 0
+    Wt, U, What = host(b["Wt"]), host(b["U"]), host(b["What_t"])
+    s, codes = host(b["scales"]), host(b["codes"])
+    mism, bad, tot = P.replay_uniform(Wt, U, What, s, codes, Lv)
+    print(f"{name} replay: {mism} of {tot} codes differ, {bad} outside the band")
+    assert bad == 0 and mism <= P.MAX_MISMATCH * tot
+    lv = (codes.astype(np.float32) - np.float32((Lv - 1) / 2)) * s.astype(np.float32)[:, None]
+    assert np.array_equal(What, lv)
