@@ -408,3 +408,31 @@ def test_config_replay_all_rows(name):
     assert bad == 0 and mism <= P.MAX_MISMATCH * tot
     lv = (codes.astype(np.float32) - np.float32((Lv - 1) / 2)) * s.astype(np.float32)[:, None]
     assert np.array_equal(What, lv)
+
+
+@pytest.mark.parametrize("name", ["c3a", "c3b", "c4a", "c4b"])
+def test_config_independent_run_sampled_rows(name):
+    """The oracle's own pass on 48 sampled rows of the full-size layer (its own
+    float64 Hessian, transforms, LDL factors, scale search and LDLQ; rows are
+    independent given the factors and the scales), against the GPU's rows with
+    the rule of the independent-run comparison: 1e-4 on agreeing rows, a
+    diverged row explained by a near-tie and bounded by its larger tail."""
+    L, lp, b, rng = run_config(name)
+    cfg = L.cfg
+    Lv = 1 << cfg.bits
+    rows = np.sort(rng.choice(cfg.m, 48, replace=False))
+    H = O.damp(O.proxy_hessian(L.X), cfg.alpha)
+    Ht = O.incoherence_H(H, L.right)
+    Uo, Do = O.udu_cholesky(Ht, 1)
+    Wt_rows = right_apply_rows(side_rows(L.left, cfg.m, rows) @ L.W.astype(np.float64), L.right)
+    s_o, _, _ = O.uniform_scale_search(Wt_rows, Lv)
+    s32 = s_o.astype(np.float32)
+    codes_o, What_o = O.ldlq(Wt_rows, Uo, O.uniform_quantizer(s32, Lv), g=1)
+    ref = {"Wt": Wt_rows, "Ht": Ht, "U": Uo, "D": Do, "scales": s32, "codes": codes_o,
+           "What_t": What_o}
+    gpu = {"Wt": host(b["Wt"])[rows], "H": host(b["H"]), "U": host(b["U"]), "D": host(b["D"]),
+           "scales": host(b["scales"])[rows], "codes": host(b["codes"])[rows],
+           "What_t": host(b["What_t"])[rows]}
+    st = P.compare_independent_run(gpu, ref, g=1, L=Lv)
+    print(f"{name} independent run: {st['diverged']} of {st['rows']} rows diverged; loss "
+          f"{st['loss_gpu']:.10g} vs {st['loss_oracle']:.10g} (extra bound {st['extra_bound']:.4g})")
