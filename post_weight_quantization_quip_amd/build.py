@@ -7,7 +7,8 @@ builds).
 
 Every source under csrc/ is compiled with hipcc for gfx950 only and linked
 into one shared library next to this file. Packed-FP32 instruction selection
-is switched off for all device code.
+is switched off for all device code, and matrix-core results are kept in
+ordinary vector registers.
 """
 from __future__ import annotations
 
@@ -35,6 +36,9 @@ FLAGS = [
     "-Wno-unused-function",
     "-Wno-unused-variable",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: without it the compiler may put
+    # them in AGPRs and copy every element out before the vector ALUs use it
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

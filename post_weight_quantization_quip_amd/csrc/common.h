@@ -192,6 +192,7 @@ struct GemmArgs {
 
 // Partial-tile workspace (floats) that gemm() uses for the leftover tiles of
 // the Hessian's upper-tile product X^T X (X: K x n); 0 when there are none.
+int device_cus();
 size_t gemm_upper_tail_floats(int64_t n, int64_t K);
 
 quip_status gemm(const GemmArgs& a, hipStream_t stream);

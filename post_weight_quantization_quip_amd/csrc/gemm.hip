@@ -431,18 +431,6 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a, int tiles_
   }
 }
 
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cached[dev] = cus;
-  }
-  return cached[dev];
-}
 
 struct TailPlan {
   int T = 0, R = 0, kp = 1;
@@ -569,6 +557,20 @@ quip_status launch_epi(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB) {
 }
 
 }  // namespace
+
+// Compute units of the current device (256 if the query fails), cached per device.
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
 
 size_t gemm_upper_tail_floats(int64_t n, int64_t K) {
   // the Hessian product: upper tiles, op(A) = X^T, op(B) = X, tile size as launch_tiles picks it

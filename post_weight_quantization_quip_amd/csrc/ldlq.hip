@@ -410,14 +410,23 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* W, int64_t n,
   for (int64_t j = tid; j < n; j += 256) Wn[row * n + j] = w[j] / r;
 }
 
+// The search kernels load the codewords of the next two pairs of 32-codeword
+// tiles ahead of their use, also past their last pair (up to three pairs past
+// it); the half-precision copy and the norms carry E8_PAD more rows (copies of
+// the first codewords) so those loads stay inside the buffers. Their products
+// are never used.
+constexpr int E8_PAD = 256;
+constexpr int E8_ROWS = 65536 + E8_PAD;
+
 __global__ void e8_norms_kernel(const float* C, float* c2, _Float16* c16) {
-  int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= 65536) return;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= E8_ROWS) return;
+  const int src = i & 65535;
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    s = fmaf(C[i * 8 + k], C[i * 8 + k], s);
-    c16[i * 8 + k] = _Float16(C[i * 8 + k]);
+    s = fmaf(C[src * 8 + k], C[src * 8 + k], s);
+    c16[i * 8 + k] = _Float16(C[src * 8 + k]);
   }
   c2[i] = s;
 }
@@ -445,6 +454,29 @@ __device__ __forceinline__ e8_half8 e8_split_operand(const float* y8, int g) {
   return b;
 }
 
+// The largest of the 16 values of an accumulator tile and x (max3 tree).
+__device__ __forceinline__ float e8_max16(const f32x16& a, float x) {
+  const float t0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  const float t1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float t2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  const float t3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  const float t4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  const float u0 = fmaxf(fmaxf(t0, t1), t2);
+  const float u1 = fmaxf(fmaxf(t3, t4), a[15]);
+  return fmaxf(fmaxf(u0, u1), x);
+}
+
+// One pair of 32-codeword tiles against the 32 vectors of a wave (split-half
+// products, see e8_split_operand).
+__device__ __forceinline__ void e8_pair_products(const uint4& wa, const uint4& wb,
+                                                 const e8_half8& yb, f32x16& aa, f32x16& ab) {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  aa = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wa), yb, z, 0, 0, 0);
+  ab = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wb), yb, z, 0, 0, 0);
+}
+
 // Squared error of the nearest codeword, summed over all 8-vectors, for every
 // candidate scale. One wave: 32 vectors x all codewords.
 // Each work-group writes its NC partial sums to part[blockIdx.x * NC + c]
@@ -458,6 +490,10 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
                                                        const float* __restrict__ cand, int ncand,
                                                        double* __restrict__ part) {
   __shared__ double red[4][NC];
+  __shared__ float sc[NC];
+  // best[c * 256 + tid]: the lane's minimum for candidate c, in LDS (written
+  // only when a run ends), so the loop carries no per-candidate state
+  extern __shared__ float best[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t v0 = (int64_t(blockIdx.x) * 4 + wave) * 32;
   const int j = lane & 31, kh = lane >> 5;
@@ -471,12 +507,10 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
     y2 = fmaf(y8[k], y8[k], y2);
   }
   const e8_half8 yb = e8_split_operand(y8, kh);
-  float sc[NC], best[NC];
+  if (tid < NC) sc[tid] = cand[tid < ncand ? tid : 0];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    sc[c] = cand[c < ncand ? c : 0];
-    best[c] = 3.4e38f;
-  }
+  for (int c = 0; c < NC; ++c) best[c * 256 + tid] = 3.4e38f;
+  __syncthreads();
   // For every scale s the distance term is s n_i - 2 <y, c_i> with n_i = |c_i|^2.
   // Over codewords of one norm it is smallest at the largest dot product, and
   // fma(s, n, -2 x) does not increase with x, so each lane keeps the largest
@@ -488,15 +522,16 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
   float run_n = c2[0], run_max = -3.4e38f;
   auto fold = [&]() {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) best[c] = fminf(best[c], fmaf(sc[c], run_n, -2.f * run_max));
+    for (int c = 0; c < NC; ++c)
+      best[c * 256 + tid] = fminf(best[c * 256 + tid], fmaf(sc[c], run_n, -2.f * run_max));
   };
-  // tiles go in pairs (two independent products, so one tile's maxima overlap
-  // the other's product); the next pair's codewords (as 8 halves) and norms
-  // are loaded one pair ahead
+  // tiles go in pairs (two independent products); the products of the next
+  // pair are issued before the current pair's maxima are taken, so the matrix
+  // cores run while the vector ALUs fold, and the codewords (as 8 halves) and
+  // norms are loaded two pairs ahead
   auto tile = [&](const f32x16& acc, float cn) {
     if (__all(cn == run_n)) {  // the whole tile continues the run
-#pragma unroll
-      for (int r = 0; r < 16; ++r) run_max = fmaxf(run_max, acc[r]);
+      run_max = e8_max16(acc, run_max);
     } else {  // a run ends inside this tile
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -510,34 +545,46 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
       }
     }
   };
-  const uint4* C4 = reinterpret_cast<const uint4*>(C16);
-  uint4 na = C4[j], nb = C4[32 + j];
-  float nca = c2[j], ncb = c2[32 + j];
-  for (int cw0 = 0; cw0 < 65536; cw0 += 64) {
-    const uint4 wa = na, wb = nb;
-    const float ca = nca, cb = ncb;
-    if (cw0 + 64 < 65536) {
-      na = C4[cw0 + 64 + j];
-      nb = C4[cw0 + 96 + j];
-      nca = c2[cw0 + 64 + j];
-      ncb = c2[cw0 + 96 + j];
-    }
-    f32x16 aa, ab;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      aa[r] = 0.f;
-      ab[r] = 0.f;
-    }
-    aa = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wa), yb, aa, 0, 0, 0);
-    ab = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wb), yb, ab, 0, 0, 0);
+  // cp and np point at the current pair (the same address in every lane)
+  const uint4* cp = reinterpret_cast<const uint4*>(C16);
+  const float* np = c2;
+  // two pairs per iteration, so that the products of the two pairs in flight
+  // keep their registers (aa, ab and xa, xb swap roles) instead of being copied
+  f32x16 aa, ab, xa, xb;
+  e8_pair_products(cp[j], cp[32 + j], yb, aa, ab);
+  float ca = np[j], cb = np[32 + j], xca, xcb;
+  uint4 na = cp[64 + j], nb = cp[96 + j];
+  float nca = np[64 + j], ncb = np[96 + j];
+  for (int p = 0; p < 1024; p += 2) {
+    e8_pair_products(na, nb, yb, xa, xb);  // pair p + 1
+    xca = nca;
+    xcb = ncb;
+    cp += 64;
+    np += 64;
+    na = cp[64 + j];  // pair p + 2
+    nb = cp[96 + j];
+    nca = np[64 + j];
+    ncb = np[96 + j];
     tile(aa, ca);
     tile(ab, cb);
+    e8_pair_products(na, nb, yb, aa, ab);  // pair p + 2 (the padding at the end: unused)
+    ca = nca;
+    cb = ncb;
+    cp += 64;
+    np += 64;
+    na = cp[64 + j];  // pair p + 3
+    nb = cp[96 + j];
+    nca = np[64 + j];
+    ncb = np[96 + j];
+    tile(xa, xca);
+    tile(xb, xcb);
   }
   fold();
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    float other = __shfl_xor(best[c], 32, 64);
-    float b = fminf(best[c], other);
+    const float mine = best[c * 256 + tid];
+    const float other = __shfl_xor(mine, 32, 64);
+    const float b = fminf(mine, other);
     double e = live && kh == 0 ? double(y2) + double(sc[c]) * double(b) : 0.0;
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
@@ -605,19 +652,114 @@ __global__ __launch_bounds__(256) void e8_prerounding_kernel(
   }
 }
 
+// Finish a group step for one row: code, quantized values, errors. With
+// rowloss, also the group's proxy-loss term rms^2 (y - q) D_g (y - q)^T, y the
+// pre-rounding vector (normalized domain) of e8_prerounding_kernel.
+struct E8Finish {
+  const float* Wn;
+  int64_t n;
+  const float* C;
+  const float* rms;
+  int64_t c0;
+  uint16_t* codes;
+  int64_t ldcode;
+  float* What;
+  float* Eb;
+  int64_t lde;
+  int ecol;
+  const float* y8;
+  const float* Dg;
+  double* rowloss;
+};
+
+// Low word of a search key: a codeword index, or (E8_TILE set) one half of a
+// 32-codeword tile (tile base | half) whose 16 codewords, all of one norm,
+// hold the best dot product that the search saw.
+constexpr uint32_t E8_TILE = 0x80000000u;
+
+// The codeword a key names for the pre-rounding vector y: an index as it
+// stands; for a tile half, the largest float32 dot <y, c> of its 16 codewords
+// (one norm: the largest dot is the nearest), the lower index on ties. Eight
+// lanes per row (sub = 0..7) take two codewords each and agree by shuffles.
+__device__ __forceinline__ uint32_t e8_resolve(const E8Finish& f, const float* y, uint32_t ref,
+                                               int sub) {
+  if (!(ref & E8_TILE)) return ref;
+  const uint32_t base = ref & 0x7FFFFFE0u, kh = ref & 1u;
+  float bv = 0.f;
+  uint32_t bi = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 2 * sub + q;
+    const uint32_t i = base + 8 * (r / 4) + 4 * kh + (r % 4);
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d = fmaf(f.C[i * 8 + k], y[k], d);
+    if (d != d) d = -INFINITY;  // a NaN dot ranks last, the same in every lane
+    if (q == 0 || d > bv) {
+      bv = d;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    const float ov = __shfl_xor(bv, o, 8);
+    const uint32_t oi = __shfl_xor(bi, o, 8);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  return bi;
+}
+
+// Lane sub of the row's eight writes dimension sub of W^ and of the errors.
+__device__ __forceinline__ void e8_finish_row(const E8Finish& f, float s, int64_t row,
+                                              uint32_t code, const float* y, int sub) {
+  if (sub == 0) f.codes[row * f.ldcode + f.c0 / 8] = uint16_t(code);
+  const float r = f.rms[row];
+  const float qs = s * f.C[code * 8 + sub];
+  f.Eb[row * f.lde + f.ecol + sub] = f.Wn[row * f.n + f.c0 + sub] - qs;
+  if (f.What) f.What[row * f.n + f.c0 + sub] = r * qs;
+  if (f.rowloss) {
+    double res[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) res[k] = double(y[k]) - double(s * f.C[code * 8 + k]);
+    double acc = 0.0;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      double t = 0.0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) t += double(f.Dg[(f.c0 + a) * 8 + b]) * res[b];
+      acc += res[a] * t;
+    }
+    if (sub == 0) f.rowloss[row] += double(r) * double(r) * acc;
+  }
+}
+
 // One group step of BlockLDLQ: the nearest scaled codeword to each row's
-// pre-rounding vector over a chunk of codewords (4 waves split the chunk;
-// atomicMin of a packed (distance, index) key per row). The dot products come
-// from the split half-precision product of e8_scale_kernel; the distance term
-// s n_i - 2 <y, c_i> is smallest, over a run of equal norms, at the largest
-// dot, so each lane keeps that dot (and its first index) per run and compares
-// runs by distance; ties go to the lower index.
+// pre-rounding vector. A work-group takes 32 rows; its 4 waves and the
+// gridDim.y work-groups of those rows split the 1024 pairs of 32-codeword tiles
+// evenly (gridDim.y <= 256), and the per-row results meet in an atomicMin of a
+// packed (distance, reference) key. The dot products come from the split
+// half-precision product of e8_scale_kernel; the distance term s n_i - 2 <y, c_i>
+// is smallest, over a run of equal norms, at the largest dot, so each lane
+// keeps that dot per run, and where it was, and compares runs by distance.
+// Inside a tile of one norm a lane takes only the tile's largest dot (one max3
+// tree) and remembers the tile; the codeword in it is found once per row, by
+// the finisher (e8_resolve). Where a run ends inside a tile, the lane goes
+// through the tile's dots one by one and keeps exact indices. Ties go to the
+// lower index within a lane and to the lower reference between lanes.
 __global__ __launch_bounds__(256) void e8_argmin_kernel(
     const float* __restrict__ y8g, const _Float16* __restrict__ C16, const float* __restrict__ c2,
-    const float* __restrict__ sp, int64_t m, int chunk, unsigned long long* __restrict__ keys) {
+    const float* __restrict__ sp, int64_t m, unsigned long long* __restrict__ keys,
+    unsigned* __restrict__ done, E8Finish fin) {
   __shared__ unsigned long long ksh[4][32];
+  __shared__ float bestv_sh[256];
+  __shared__ uint32_t bestref_sh[256];
+  __shared__ unsigned last_sh;
   const float s = *sp;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t r0 = int64_t(blockIdx.x) * 32;
   const int j = lane & 31, kh = lane >> 5;
   float y8[8];
@@ -627,71 +769,84 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
     for (int k = 0; k < 8; ++k) y8[k] = row < m ? y8g[row * 8 + k] : 0.f;
   }
   const e8_half8 yb = e8_split_operand(y8, kh);
-  const int cbeg = blockIdx.y * chunk + wave * (chunk / 4);
-  const int cend = cbeg + chunk / 4;
-  float bestv = 3.4e38f;
-  int besti = cbeg;  // always a valid codeword, even if every distance is NaN
-  float run_n = c2[cbeg], run_max = -3.4e38f;
-  int run_i = cbeg;
+  const int nw = int(gridDim.y) * 4, gw = int(blockIdx.y) * 4 + wave;
+  const int p0 = gw * 1024 / nw, p1 = (gw + 1) * 1024 / nw;  // this wave's pairs
+  // the lane's best run so far lives in LDS (written only when a run ends),
+  // so the loop carries only the current run
+  // Inside the loop a reference is a tile base (this lane's half implied) or
+  // an exact index tagged with E8_EXACT; it becomes a key's low word at the end.
+  constexpr uint32_t E8_EXACT = 0x40000000u;
+  bestv_sh[tid] = 3.4e38f;
+  bestref_sh[tid] = uint32_t(p0 * 64) | E8_EXACT;  // valid even if every distance is NaN
+  float run_n = c2[p0 * 64], run_max = -3.4e38f;
+  uint32_t run_ref = uint32_t(p0 * 64) | E8_EXACT;
   auto fold = [&]() {
     const float v = fmaf(s, run_n, -2.f * run_max);
-    if (v < bestv) {  // runs are visited in increasing index within a lane
-      bestv = v;
-      besti = run_i;
+    if (v < bestv_sh[tid]) {  // runs are visited in increasing index within a lane
+      bestv_sh[tid] = v;
+      bestref_sh[tid] = run_ref;
     }
   };
-  // tiles in pairs, as in e8_scale_kernel
-  auto tile = [&](const f32x16& acc, float cn, int cw0) {
-    if (__all(cn == run_n)) {
+  auto tile = [&](const f32x16& acc, float cn, int t) {
+    if (__all(cn == run_n)) {  // the whole tile continues the run
+      const float mx = e8_max16(acc, run_max);
+      run_ref = mx > run_max ? uint32_t(t) : run_ref;
+      run_max = mx;
+    } else {  // a run ends inside this tile
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
-        const bool gt = acc[r] > run_max;
-        run_max = gt ? acc[r] : run_max;
-        run_i = gt ? i : run_i;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = cw0 + 8 * (r / 4) + 4 * kh + (r % 4);
+        const int i = t + 8 * (r / 4) + 4 * kh + (r % 4);
         const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
         if (n2 != run_n) {
           fold();
           run_n = n2;
           run_max = -3.4e38f;
-          run_i = i;
         }
         const bool gt = acc[r] > run_max;
         run_max = gt ? acc[r] : run_max;
-        run_i = gt ? i : run_i;
+        run_ref = gt ? uint32_t(i) | E8_EXACT : run_ref;
       }
     }
   };
-  const uint4* C4 = reinterpret_cast<const uint4*>(C16);
-  uint4 na = C4[cbeg + j], nb = C4[cbeg + 32 + j];
-  float nca = c2[cbeg + j], ncb = c2[cbeg + 32 + j];
-  for (int cw0 = cbeg; cw0 < cend; cw0 += 64) {  // chunk / 4 is a multiple of 64
-    const uint4 wa = na, wb = nb;
-    const float ca = nca, cb = ncb;
-    if (cw0 + 64 < cend) {
-      na = C4[cw0 + 64 + j];
-      nb = C4[cw0 + 96 + j];
-      nca = c2[cw0 + 64 + j];
-      ncb = c2[cw0 + 96 + j];
+  // tiles in pairs, pipelined as in e8_scale_kernel; cp and np point at the
+  // current pair (the same address in every lane)
+  const uint4* cp = reinterpret_cast<const uint4*>(C16) + p0 * 64;
+  const float* np = c2 + p0 * 64;
+  f32x16 aa, ab, xa, xb;
+  e8_pair_products(cp[j], cp[32 + j], yb, aa, ab);
+  float ca = np[j], cb = np[32 + j], xca, xcb;
+  uint4 na = cp[64 + j], nb = cp[96 + j];
+  float nca = np[64 + j], ncb = np[96 + j];
+  for (int p = p0; p < p1; p += 2) {  // two pairs per iteration, as in e8_scale_kernel
+    e8_pair_products(na, nb, yb, xa, xb);  // pair p + 1
+    xca = nca;
+    xcb = ncb;
+    cp += 64;
+    np += 64;
+    na = cp[64 + j];  // pair p + 2
+    nb = cp[96 + j];
+    nca = np[64 + j];
+    ncb = np[96 + j];
+    tile(aa, ca, p * 64);
+    tile(ab, cb, p * 64 + 32);
+    e8_pair_products(na, nb, yb, aa, ab);  // pair p + 2
+    ca = nca;
+    cb = ncb;
+    cp += 64;
+    np += 64;
+    na = cp[64 + j];  // pair p + 3 (at most the padding past the codebook)
+    nb = cp[96 + j];
+    nca = np[64 + j];
+    ncb = np[96 + j];
+    if (p + 1 < p1) {
+      tile(xa, xca, (p + 1) * 64);
+      tile(xb, xcb, (p + 1) * 64 + 32);
     }
-    f32x16 aa, ab;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      aa[r] = 0.f;
-      ab[r] = 0.f;
-    }
-    aa = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wa), yb, aa, 0, 0, 0);
-    ab = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wb), yb, ab, 0, 0, 0);
-    tile(aa, ca, cw0);
-    tile(ab, cb, cw0 + 32);
   }
   fold();
-  unsigned long long key = (unsigned long long)ordered_bits(bestv) << 32 | uint32_t(besti);
+  const uint32_t ref = bestref_sh[tid];
+  const uint32_t low = (ref & E8_EXACT) ? (ref ^ E8_EXACT) : (E8_TILE | ref | uint32_t(kh));
+  unsigned long long key = (unsigned long long)ordered_bits(bestv_sh[tid]) << 32 | low;
   unsigned long long other = __shfl_xor(key, 32, 64);
   key = key < other ? key : other;
   if (kh == 0) ksh[wave][j] = key;
@@ -701,44 +856,33 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
     for (int wv = 1; wv < 4; ++wv) k2 = ksh[wv][tid] < k2 ? ksh[wv][tid] : k2;
     if (r0 + tid < m) atomicMin(&keys[r0 + tid], k2);
   }
-}
-
-// Finish a group step: codes, quantized values, errors; reset the keys. With
-// rowloss, also the group's proxy-loss term rms^2 (y - q) D_g (y - q)^T, y the
-// pre-rounding vector (normalized domain) of e8_prerounding_kernel.
-__global__ void e8_finish_kernel(const float* __restrict__ Wn, int64_t n, const float* __restrict__ C,
-                                 const float* __restrict__ sp, const float* __restrict__ rms,
-                                 int64_t c0, int64_t m,
-                                 unsigned long long* __restrict__ keys, uint16_t* __restrict__ codes,
-                                 int64_t ldcode, float* __restrict__ What, float* __restrict__ Eb,
-                                 int64_t lde, int ecol, const float* __restrict__ y8,
-                                 const float* __restrict__ Dg, double* __restrict__ rowloss) {
-  const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (row >= m) return;
-  const float s = *sp;
-  const uint32_t code = uint32_t(keys[row] & 0xFFFFull);
-  keys[row] = ~0ull;
-  codes[row * ldcode + c0 / 8] = uint16_t(code);
-  const float r = rms[row];
-  double res[8];
+  // The last of the gridDim.y work-groups of these 32 rows to get here
+  // finishes the step for them (a counter per row block; no group waits).
+  // The keys are only touched by atomics: each group waits until its own
+  // atomicMin operations are complete before it counts, and the finisher takes
+  // each key with an atomic exchange (a read-modify-write sees the latest
+  // value), which also resets it for the next step. No cache-wide fence is
+  // needed (and none is taken: they would flush the L2 holding the codebook).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) last_sh = atomicAdd(&done[blockIdx.x], 1u) == gridDim.y - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!last_sh) return;
+  {
+    const int sub = tid & 7;
+    const int64_t row = r0 + (tid >> 3);
+    if (row < m) {  // the same for the eight lanes of a row
+      unsigned long long rk = 0ull;
+      if (sub == 0) rk = atomicExch(&keys[row], ~0ull);
+      rk = __shfl(rk, lane & ~7, 64);
+      float y[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float qv = s * C[code * 8 + k];
-    if (rowloss) res[k] = double(y8[row * 8 + k]) - double(qv);
-    Eb[row * lde + ecol + k] = Wn[row * n + c0 + k] - qv;
-    if (What) What[row * n + c0 + k] = r * qv;
-  }
-  if (rowloss) {
-    double acc = 0.0;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      double t = 0.0;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) t += double(Dg[(c0 + a) * 8 + b]) * res[b];
-      acc += res[a] * t;
+      for (int k = 0; k < 8; ++k) y[k] = fin.y8[row * 8 + k];
+      const uint32_t code = e8_resolve(fin, y, uint32_t(rk & 0xFFFFFFFFull), sub);
+      e8_finish_row(fin, s, row, code, y, sub);
     }
-    rowloss[row] += double(r) * double(r) * acc;
   }
+  if (tid == 0) done[blockIdx.x] = 0u;
 }
 
 // loss = sum of the row losses, in a fixed order (one work-group).
@@ -798,6 +942,29 @@ struct E8Ws {
   double* part;  // per-work-group partial sums of the scale search
 };
 
+// Work-groups per 32-row block of a group step's search (gridDim.y of
+// e8_argmin_kernel): the split of the 1024 tile pairs that ends soonest when
+// the row blocks x split work-groups run in rounds of the resident slots,
+// counting about four pairs of set-up and reduction per work-group.
+int e8_argmin_split(int64_t m) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&e8_argmin_kernel), 256, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  const int64_t slots = int64_t(per_cu) * device_cus(), rb = cdiv(m, 32);
+  int best = 1;
+  double best_t = 1e300;
+  for (int y = 1; y <= 256; ++y) {
+    const double t = double(cdiv(rb * y, slots)) * (1024.0 / y + 4.0);
+    if (t < best_t) {
+      best_t = t;
+      best = y;
+    }
+  }
+  return best;
+}
+
 // Work-groups of the E8 scale search (128 vectors each) and their partial sums.
 int64_t e8_scale_blocks(int64_t m, int64_t n) { return cdiv(m * (n / 8), 128); }
 size_t e8_partial_count(int64_t m, int64_t n) { return size_t(e8_scale_blocks(m, n)) * 64; }
@@ -822,12 +989,16 @@ quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, con
   const int64_t nvec = m * (n / 8);
   const int64_t nblk = e8_scale_blocks(m, n);
   const dim3 grid{unsigned(nblk)};
+  const size_t sh32 = sizeof(float) * 32 * 256, sh64 = sizeof(float) * 64 * 256;
+  if (ncand > 32)
+    QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&e8_scale_kernel<64>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(sh64)));
   QUIP_TRY(timed_launch("e8_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (ncand <= 32)
-      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), 0, s, Wn, nvec, e.c16, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), sh32, s, Wn, nvec, e.c16, e.c2, e.cand,
                          ncand, e.part);
     else
-      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), 0, s, Wn, nvec, e.c16, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), sh64, s, Wn, nvec, e.c16, e.c2, e.cand,
                          ncand, e.part);
   }, 16.0 * 65536.0 * double(nvec), 32.0 * double(nvec)));  // <y, c> for every vector and codeword
   QUIP_TRY(timed_launch("e8_sse_reduce_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
@@ -914,8 +1085,8 @@ size_t scales_workspace_bytes(int64_t m, int64_t n, const quip_quantizer& q) {
   c.take<float>(64);  // candidate factors
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
-    c.take<float>(65536);          // |c|^2
-    c.take<_Float16>(65536 * 8);   // the codebook in half precision
+    c.take<float>(E8_ROWS);          // |c|^2
+    c.take<_Float16>(size_t(E8_ROWS) * 8);   // the codebook in half precision
     c.take<double>(64);            // sse
     c.take<double>(e8_partial_count(m, n));  // per-work-group partial sums
   }
@@ -937,8 +1108,8 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   }
   E8Ws e{};
   e.Wn = c.take<float>(size_t(m) * n);
-  e.c2 = c.take<float>(65536);
-  e.c16 = c.take<_Float16>(65536 * 8);
+  e.c2 = c.take<float>(E8_ROWS);
+  e.c16 = c.take<_Float16>(size_t(E8_ROWS) * 8);
   e.sse = c.take<double>(64);
   e.part = c.take<double>(e8_partial_count(m, n));
   e.cand = fac;
@@ -950,7 +1121,7 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
                        true);
   }));
   QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2, e.c16);
+    QUIP_KERNEL(e8_norms_kernel, dim3(unsigned(cdiv(E8_ROWS, 256))), dim3(256), 0, s, codebook, e.c2, e.c16);
   }));
   return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
 }
@@ -976,8 +1147,9 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
     c.take<float>(size_t(m) * n);  // Wn
     c.take<unsigned long long>(size_t(m));
     c.take<float>(size_t(m) * 8);  // pre-rounding vectors of a group step
-    c.take<float>(65536);
-    c.take<_Float16>(65536 * 8);
+    c.take<unsigned>(size_t(cdiv(m, 32)));  // per row block: chunk groups done
+    c.take<float>(E8_ROWS);
+    c.take<_Float16>(size_t(E8_ROWS) * 8);
     c.take<double>(64);
     c.take<double>(e8_partial_count(m, n));
   }
@@ -1030,8 +1202,9 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   e.Wn = c.take<float>(size_t(m) * n);
   e.keys = c.take<unsigned long long>(size_t(m));
   float* y8 = c.take<float>(size_t(m) * 8);
-  e.c2 = c.take<float>(65536);
-  e.c16 = c.take<_Float16>(65536 * 8);
+  unsigned* done = c.take<unsigned>(size_t(cdiv(m, 32)));
+  e.c2 = c.take<float>(E8_ROWS);
+  e.c16 = c.take<_Float16>(size_t(E8_ROWS) * 8);
   e.sse = c.take<double>(64);
   e.part = c.take<double>(e8_partial_count(m, n));
   e.cand = fac;
@@ -1044,7 +1217,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
                        compute);
   }));
   QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(e8_norms_kernel, dim3(256), dim3(256), 0, s, codebook, e.c2, e.c16);
+    QUIP_KERNEL(e8_norms_kernel, dim3(unsigned(cdiv(E8_ROWS, 256))), dim3(256), 0, s, codebook, e.c2, e.c16);
   }));
   if (compute) {
     host_e8_candidates(q.n_cand, hostf);
@@ -1056,8 +1229,9 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   QUIP_TRY(timed_launch("fill_u64_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
   }));
+  QUIP_TRY(fill_f32(reinterpret_cast<float*>(done), cdiv(m, 32), 0.f, s));  // counters <- 0
   uint16_t* cd = static_cast<uint16_t*>(codes);
-  const int chunk = 4096;
+  const int ysplit = e8_argmin_split(m);
   for (int64_t j0 = 0; j0 < n; j0 += B) {
     const int64_t bo = (n - j0 < B) ? n - j0 : B;
     for (int64_t c0 = j0; c0 < j0 + bo; c0 += 8) {
@@ -1066,16 +1240,13 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
         QUIP_KERNEL(e8_prerounding_kernel, dim3(unsigned(cdiv(m, 16))), dim3(256), 0, s, e.Wn, n, F,
                     j0 > 0, Eb, B, nprev, U, c0, j0, m, y8);
       }, 16.0 * double(m) * double(nprev), 4.0 * double(m) * (double(nprev) + 24.0)));
-      dim3 grid(unsigned(cdiv(m, 32)), unsigned(65536 / chunk));
+      const dim3 grid(unsigned(cdiv(m, 32)), unsigned(ysplit));
+      E8Finish fin{e.Wn, n, codebook, scales + 1, c0, cd, n / 8, What, Eb, B, nprev, y8, D, rl};
+      // the search, and the step's codes, W^, errors and loss term
       QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.c16, e.c2, sglob, m, chunk,
-                    e.keys);
+        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.c16, e.c2, sglob, m,
+                    e.keys, done, fin);
       }, 16.0 * 65536.0 * double(m), 32.0 * double(m) + 8.0 * double(m) * 8.0));
-      QUIP_TRY(timed_launch("e8_finish_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(e8_finish_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.Wn, n,
-                           codebook, sglob, scales + 1, c0, m, e.keys, cd, n / 8, What, Eb, B,
-                           nprev, y8, D, rl);
-      }));
     }
     QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
   }
