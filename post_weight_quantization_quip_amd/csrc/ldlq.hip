@@ -18,9 +18,11 @@
 // staged transposed in LDS one chunk ahead.
 //
 // E8 groups: the pre-rounding 8-vectors of all rows are searched against the
-// 65536 codewords as a distance contraction on the matrix cores
-// (codewords x rows, K = 8), with the per-row argmin kept as a packed
-// (order-preserving distance bits, index) 64-bit key and atomicMin.
+// 65536 codewords as a dot-product contraction on the matrix cores
+// (codewords x rows; each vector as two half-precision parts, K = 16), with
+// the per-row result kept as a packed (order-preserving distance bits,
+// reference) 64-bit key and atomicMin; the last work-group of each row block
+// resolves the codes and finishes the step.
 #include <type_traits>
 
 #include <utility>
@@ -431,9 +433,102 @@ __global__ void e8_norms_kernel(const float* C, float* c2, _Float16* c16) {
   c2[i] = s;
 }
 
-// Squared error of the nearest codeword, summed over all 8-vectors, for every
-// candidate scale. One wave: 32 vectors x all codewords; lanes 0-31 and 32-63
-// see the same vectors and different codeword rows of each 32x32 block.
+// The lattice is symmetric: -c is a lattice point of the same norm as c. In
+// the codebook of quip_e8_codebook (squared norm, then coordinates in
+// increasing order) each full shell of squared norm 2, 4, 6, 8 and 10,
+// [E8_SH_A[r], E8_SH_A[r] + E8_SH_S[r]), holds the negation of its i-th point
+// at position a + S - 1 - i (negation reverses the coordinate order). A search
+// over one member of each such pair, with |<y, c>| in place of <y, c>, finds the
+// same minima: over {c, -c}, s |c|^2 - 2 <y, +-c> is smallest at the sign of
+// <y, c>. The search layout holds the first halves of the five shells (the
+// symmetric region, E8_SYM_CW entries with padding) and then the zero vector and
+// the partial shell of squared norm 12 as they are (the plain region). For any
+// other codebook the pairing check fails and the kernels search the codebook
+// as given.
+__constant__ int E8_SH_A[5] = {1, 241, 2401, 9121, 26641};
+__constant__ int E8_SH_S[5] = {240, 2160, 6720, 17520, 30240};
+__constant__ int E8_SH_OFF[6] = {0, 120, 1200, 4560, 13320, 28440};
+constexpr int E8_SYM_HALF = 28440;                          // first halves of the five shells
+constexpr int E8_SYM_CW = 28480;                            // padded to whole pairs (445)
+constexpr int E8_PLAIN_CW = 1 + (65536 - 56881);            // zero vector + the partial shell
+constexpr int E8_LAYOUT_CW = E8_SYM_CW + 8704;              // plain region padded (136 pairs)
+static_assert(E8_PLAIN_CW <= 8704, "plain region");
+
+// One thread per entry of the symmetric search layout: its codeword (half
+// precision) and norm, the codebook index it stands for and that of its
+// negation. Padding repeats the region's last entry. bad is set if a pair of
+// the symmetric region is not c, -c.
+__global__ void e8_layout_kernel(const float* __restrict__ C, _Float16* __restrict__ c16,
+                                 float* __restrict__ c2, uint32_t* __restrict__ orig,
+                                 uint32_t* __restrict__ neg, int* __restrict__ bad) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E8_LAYOUT_CW) return;
+  int i, partner;
+  if (e < E8_SYM_CW) {
+    const int h = e < E8_SYM_HALF ? e : E8_SYM_HALF - 1;
+    int r = 0;
+#pragma unroll
+    for (int q = 1; q < 5; ++q) r = h >= E8_SH_OFF[q] ? q : r;
+    i = E8_SH_A[r] + (h - E8_SH_OFF[r]);
+    partner = 2 * E8_SH_A[r] + E8_SH_S[r] - 1 - i;
+  } else {
+    const int q0 = e - E8_SYM_CW;
+    const int q = q0 < E8_PLAIN_CW ? q0 : E8_PLAIN_CW - 1;
+    i = q == 0 ? 0 : 56880 + q;
+    partner = i;
+  }
+  float v[8];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    v[k] = C[i * 8 + k];
+    s = fmaf(v[k], v[k], s);
+    c16[e * 8 + k] = _Float16(v[k]);
+  }
+  c2[e] = s;
+  orig[e] = uint32_t(i);
+  neg[e] = uint32_t(partner);
+  if (e < E8_SYM_HALF) {
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ok = ok && (C[partner * 8 + k] == -v[k]);
+    if (!ok) atomicOr(bad, 1);
+  }
+}
+
+// The codebook as the search kernels see it: the symmetric layout when its
+// pairing check passed, else the codebook as given (identity map).
+struct E8Book {
+  const _Float16* c16p;  // as given: 65536 codewords (+ E8_PAD) in half precision
+  const float* c2p;
+  const _Float16* c16s;  // the symmetric layout
+  const float* c2s;
+  const uint32_t* orig;
+  const uint32_t* neg;
+  const int* bad;
+};
+
+struct E8View {
+  const uint4* cw;        // codewords as 8 halves, one uint4 each
+  const float* nm;        // norms
+  const uint32_t* orig;   // null: identity
+  const uint32_t* neg;
+  int sym_pairs;          // pairs [0, sym_pairs) search one member per {c, -c}
+  int pairs;              // pairs in all
+};
+
+__device__ __forceinline__ E8View e8_view(const E8Book& b) {
+  const bool sym = __builtin_amdgcn_readfirstlane(*b.bad) == 0;
+  E8View v;
+  v.cw = reinterpret_cast<const uint4*>(sym ? b.c16s : b.c16p);
+  v.nm = sym ? b.c2s : b.c2p;
+  v.orig = sym ? b.orig : nullptr;
+  v.neg = sym ? b.neg : nullptr;
+  v.sym_pairs = sym ? E8_SYM_CW / 64 : 0;
+  v.pairs = sym ? E8_LAYOUT_CW / 64 : 1024;
+  return v;
+}
+
 typedef _Float16 e8_half8 __attribute__((ext_vector_type(8)));
 
 // The dot products <y, c> of 32 vectors with a 32-codeword tile in one
@@ -454,15 +549,18 @@ __device__ __forceinline__ e8_half8 e8_split_operand(const float* y8, int g) {
   return b;
 }
 
-// The largest of the 16 values of an accumulator tile and x (max3 tree).
+// The largest of the 16 values of an accumulator tile (of their magnitudes
+// with ABS) and x (max3 tree; the magnitudes are operand modifiers).
+template <bool ABS>
 __device__ __forceinline__ float e8_max16(const f32x16& a, float x) {
-  const float t0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  const float t1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  const float t2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
-  const float t3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
-  const float t4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  auto v = [&](int r) { return ABS ? fabsf(a[r]) : a[r]; };
+  const float t0 = fmaxf(fmaxf(v(0), v(1)), v(2));
+  const float t1 = fmaxf(fmaxf(v(3), v(4)), v(5));
+  const float t2 = fmaxf(fmaxf(v(6), v(7)), v(8));
+  const float t3 = fmaxf(fmaxf(v(9), v(10)), v(11));
+  const float t4 = fmaxf(fmaxf(v(12), v(13)), v(14));
   const float u0 = fmaxf(fmaxf(t0, t1), t2);
-  const float u1 = fmaxf(fmaxf(t3, t4), a[15]);
+  const float u1 = fmaxf(fmaxf(t3, t4), v(15));
   return fmaxf(fmaxf(u0, u1), x);
 }
 
@@ -477,6 +575,54 @@ __device__ __forceinline__ void e8_pair_products(const uint4& wa, const uint4& w
   ab = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8_half8, wb), yb, z, 0, 0, 0);
 }
 
+// The pairs [pb, pe) of 32-codeword tiles of a search view against a wave's 32
+// vectors: tile(acc, cn, t) for every tile, in order (acc: the lane's 16 dot
+// products, cn: the norm of the lane's codeword row j, t: the tile's first
+// entry). The products of the next pair are issued before the current pair's
+// tiles are taken, so the matrix cores run while the vector ALUs reduce; the
+// codewords (as 8 halves) and norms are loaded two pairs ahead, up to three
+// pairs past pe (inside the buffers' padding). Two pairs per iteration, so the
+// products of the two pairs in flight keep their registers (aa, ab and xa, xb
+// swap roles) instead of being copied.
+template <typename Tile>
+__device__ __forceinline__ void e8_pairs(const uint4* cw, const float* nm, int pb, int pe, int j,
+                                         const e8_half8& yb, Tile&& tile) {
+  if (pb >= pe) return;
+  const uint4* cp = cw + pb * 64;  // the current pair (the same address in every lane)
+  const float* np = nm + pb * 64;
+  f32x16 aa, ab, xa, xb;
+  e8_pair_products(cp[j], cp[32 + j], yb, aa, ab);
+  float ca = np[j], cb = np[32 + j], xca, xcb;
+  uint4 na = cp[64 + j], nb = cp[96 + j];
+  float nca = np[64 + j], ncb = np[96 + j];
+  for (int p = pb; p < pe; p += 2) {
+    e8_pair_products(na, nb, yb, xa, xb);  // pair p + 1
+    xca = nca;
+    xcb = ncb;
+    cp += 64;
+    np += 64;
+    na = cp[64 + j];  // pair p + 2
+    nb = cp[96 + j];
+    nca = np[64 + j];
+    ncb = np[96 + j];
+    tile(aa, ca, p * 64);
+    tile(ab, cb, p * 64 + 32);
+    e8_pair_products(na, nb, yb, aa, ab);  // pair p + 2
+    ca = nca;
+    cb = ncb;
+    cp += 64;
+    np += 64;
+    na = cp[64 + j];  // pair p + 3
+    nb = cp[96 + j];
+    nca = np[64 + j];
+    ncb = np[96 + j];
+    if (p + 1 < pe) {
+      tile(xa, xca, (p + 1) * 64);
+      tile(xb, xcb, (p + 1) * 64 + 32);
+    }
+  }
+}
+
 // Squared error of the nearest codeword, summed over all 8-vectors, for every
 // candidate scale. One wave: 32 vectors x all codewords.
 // Each work-group writes its NC partial sums to part[blockIdx.x * NC + c]
@@ -485,8 +631,7 @@ __device__ __forceinline__ void e8_pair_products(const uint4& wa, const uint4& w
 // the same on every run.
 template <int NC>
 __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__ Y, int64_t nvec,
-                                                       const _Float16* __restrict__ C16,
-                                                       const float* __restrict__ c2,
+                                                       E8Book book,
                                                        const float* __restrict__ cand, int ncand,
                                                        double* __restrict__ part) {
   __shared__ double red[4][NC];
@@ -516,69 +661,37 @@ __global__ __launch_bounds__(256) void e8_scale_kernel(const float* __restrict__
   // fma(s, n, -2 x) does not increase with x, so each lane keeps the largest
   // dot of the current run of equal norms and folds it into the 32 minima
   // when the norm changes: the minima equal those over every codeword taken
-  // one by one, for any codebook order (sorted by norm, as quip_e8_codebook
-  // returns it, there are seven runs and almost every tile takes one max per
-  // value).
-  float run_n = c2[0], run_max = -3.4e38f;
+  // one by one, for any codebook order (in the symmetric layout there are
+  // seven runs and almost every tile takes one max per value). In the
+  // symmetric region the dot's magnitude stands for the pair {c, -c}.
+  const E8View v = e8_view(book);
+  float run_n = v.nm[0], run_max = -3.4e38f;
   auto fold = [&]() {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       best[c * 256 + tid] = fminf(best[c * 256 + tid], fmaf(sc[c], run_n, -2.f * run_max));
   };
-  // tiles go in pairs (two independent products); the products of the next
-  // pair are issued before the current pair's maxima are taken, so the matrix
-  // cores run while the vector ALUs fold, and the codewords (as 8 halves) and
-  // norms are loaded two pairs ahead
-  auto tile = [&](const f32x16& acc, float cn) {
-    if (__all(cn == run_n)) {  // the whole tile continues the run
-      run_max = e8_max16(acc, run_max);
-    } else {  // a run ends inside this tile
+  auto tile_of = [&](auto abs_tag) {
+    constexpr bool ABS = decltype(abs_tag)::value;
+    return [&](const f32x16& acc, float cn, int) {
+      if (__all(cn == run_n)) {  // the whole tile continues the run
+        run_max = e8_max16<ABS>(acc, run_max);
+      } else {  // a run ends inside this tile
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
-        if (n2 != run_n) {
-          fold();
-          run_n = n2;
-          run_max = -3.4e38f;
+        for (int r = 0; r < 16; ++r) {
+          const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
+          if (n2 != run_n) {
+            fold();
+            run_n = n2;
+            run_max = -3.4e38f;
+          }
+          run_max = fmaxf(run_max, ABS ? fabsf(acc[r]) : acc[r]);
         }
-        run_max = fmaxf(run_max, acc[r]);
       }
-    }
+    };
   };
-  // cp and np point at the current pair (the same address in every lane)
-  const uint4* cp = reinterpret_cast<const uint4*>(C16);
-  const float* np = c2;
-  // two pairs per iteration, so that the products of the two pairs in flight
-  // keep their registers (aa, ab and xa, xb swap roles) instead of being copied
-  f32x16 aa, ab, xa, xb;
-  e8_pair_products(cp[j], cp[32 + j], yb, aa, ab);
-  float ca = np[j], cb = np[32 + j], xca, xcb;
-  uint4 na = cp[64 + j], nb = cp[96 + j];
-  float nca = np[64 + j], ncb = np[96 + j];
-  for (int p = 0; p < 1024; p += 2) {
-    e8_pair_products(na, nb, yb, xa, xb);  // pair p + 1
-    xca = nca;
-    xcb = ncb;
-    cp += 64;
-    np += 64;
-    na = cp[64 + j];  // pair p + 2
-    nb = cp[96 + j];
-    nca = np[64 + j];
-    ncb = np[96 + j];
-    tile(aa, ca);
-    tile(ab, cb);
-    e8_pair_products(na, nb, yb, aa, ab);  // pair p + 2 (the padding at the end: unused)
-    ca = nca;
-    cb = ncb;
-    cp += 64;
-    np += 64;
-    na = cp[64 + j];  // pair p + 3
-    nb = cp[96 + j];
-    nca = np[64 + j];
-    ncb = np[96 + j];
-    tile(xa, xca);
-    tile(xb, xcb);
-  }
+  e8_pairs(v.cw, v.nm, 0, v.sym_pairs, j, yb, tile_of(std::true_type{}));
+  e8_pairs(v.cw, v.nm, v.sym_pairs, v.pairs, j, yb, tile_of(std::false_type{}));
   fold();
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -672,44 +785,66 @@ struct E8Finish {
   double* rowloss;
 };
 
-// Low word of a search key: a codeword index, or (E8_TILE set) one half of a
-// 32-codeword tile (tile base | half) whose 16 codewords, all of one norm,
-// hold the best dot product that the search saw.
+// Low word of a search key: an entry of the search view, with E8_NEG when
+// the entry's negation is meant, or (E8_TILE set) one half of a 32-entry tile
+// (tile base | half) whose 16 entries, all of one norm, hold the best dot
+// product (its magnitude, in the symmetric region) that the search saw.
 constexpr uint32_t E8_TILE = 0x80000000u;
+constexpr uint32_t E8_NEG = 0x20000000u;
 
-// The codeword a key names for the pre-rounding vector y: an index as it
-// stands; for a tile half, the largest float32 dot <y, c> of its 16 codewords
-// (one norm: the largest dot is the nearest), the lower index on ties. Eight
-// lanes per row (sub = 0..7) take two codewords each and agree by shuffles.
-__device__ __forceinline__ uint32_t e8_resolve(const E8Finish& f, const float* y, uint32_t ref,
-                                               int sub) {
-  if (!(ref & E8_TILE)) return ref;
-  const uint32_t base = ref & 0x7FFFFFE0u, kh = ref & 1u;
-  float bv = 0.f;
-  uint32_t bi = 0;
+// The codebook index a key names for the pre-rounding vector y. For a tile
+// half: the largest float32 dot <y, c> over its 16 entries (one norm: the
+// largest dot is the nearest), or in the symmetric region the largest |<y, c>|
+// and the member of {c, -c} its sign gives (c for a zero dot); the lower entry
+// on ties. Eight lanes per row (sub = 0..7) take two entries each and agree by
+// shuffles.
+__device__ __forceinline__ uint32_t e8_resolve(const E8Finish& f, const E8View& v, const float* y,
+                                               uint32_t ref, int sub) {
+  uint32_t e;
+  bool negate;
+  if (!(ref & E8_TILE)) {
+    e = ref & ~E8_NEG;
+    negate = (ref & E8_NEG) != 0;
+  } else {
+    const uint32_t base = ref & 0x7FFFFFE0u, kh = ref & 1u;
+    const bool sym = base < uint32_t(v.sym_pairs) * 64u;
+    float bv = 0.f;
+    uint32_t bi = 0;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 2 * sub + q;
-    const uint32_t i = base + 8 * (r / 4) + 4 * kh + (r % 4);
-    float d = 0.f;
+    for (int q = 0; q < 2; ++q) {
+      const int r = 2 * sub + q;
+      const uint32_t i = base + 8 * (r / 4) + 4 * kh + (r % 4);
+      const uint32_t ci = v.orig ? v.orig[i] : i;
+      float d = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) d = fmaf(f.C[i * 8 + k], y[k], d);
-    if (d != d) d = -INFINITY;  // a NaN dot ranks last, the same in every lane
-    if (q == 0 || d > bv) {
-      bv = d;
-      bi = i;
+      for (int k = 0; k < 8; ++k) d = fmaf(f.C[ci * 8 + k], y[k], d);
+      // the sign rides in the low bit of the entry: entries are compared with
+      // it cleared
+      uint32_t tag = i << 1;
+      if (sym) {
+        tag |= d < 0.f ? 1u : 0u;
+        d = fabsf(d);
+      }
+      if (d != d) d = -INFINITY;  // a NaN dot ranks last, the same in every lane
+      if (q == 0 || d > bv) {
+        bv = d;
+        bi = tag;
+      }
     }
-  }
 #pragma unroll
-  for (int o = 1; o < 8; o <<= 1) {
-    const float ov = __shfl_xor(bv, o, 8);
-    const uint32_t oi = __shfl_xor(bi, o, 8);
-    if (ov > bv || (ov == bv && oi < bi)) {
-      bv = ov;
-      bi = oi;
+    for (int o = 1; o < 8; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 8);
+      const uint32_t oi = __shfl_xor(bi, o, 8);
+      if (ov > bv || (ov == bv && (oi >> 1) < (bi >> 1))) {
+        bv = ov;
+        bi = oi;
+      }
     }
+    e = bi >> 1;
+    negate = (bi & 1u) != 0;
   }
-  return bi;
+  if (!v.orig) return e;
+  return negate ? v.neg[e] : v.orig[e];
 }
 
 // Lane sub of the row's eight writes dimension sub of W^ and of the errors.
@@ -738,26 +873,27 @@ __device__ __forceinline__ void e8_finish_row(const E8Finish& f, float s, int64_
 
 // One group step of BlockLDLQ: the nearest scaled codeword to each row's
 // pre-rounding vector. A work-group takes 32 rows; its 4 waves and the
-// gridDim.y work-groups of those rows split the 1024 pairs of 32-codeword tiles
+// gridDim.y work-groups of those rows split the tile pairs of the search view
 // evenly (gridDim.y <= 256), and the per-row results meet in an atomicMin of a
 // packed (distance, reference) key. The dot products come from the split
 // half-precision product of e8_scale_kernel; the distance term s n_i - 2 <y, c_i>
-// is smallest, over a run of equal norms, at the largest dot, so each lane
-// keeps that dot per run, and where it was, and compares runs by distance.
-// Inside a tile of one norm a lane takes only the tile's largest dot (one max3
-// tree) and remembers the tile; the codeword in it is found once per row, by
-// the finisher (e8_resolve). Where a run ends inside a tile, the lane goes
-// through the tile's dots one by one and keeps exact indices. Ties go to the
-// lower index within a lane and to the lower reference between lanes.
+// is smallest, over a run of equal norms, at the largest dot (in the symmetric
+// region: the largest magnitude, for the pair {c, -c}), so each lane keeps that
+// dot per run, and where it was, and compares runs by distance. Inside a tile
+// of one norm a lane takes only the tile's largest dot (one max3 tree) and
+// remembers the tile; the codeword in it is found once per row, by the
+// finisher (e8_resolve). Where a run ends inside a tile, the lane goes through
+// the tile's dots one by one and keeps exact entries. Ties go to the lower
+// entry within a lane and to the lower reference between lanes.
 __global__ __launch_bounds__(256) void e8_argmin_kernel(
-    const float* __restrict__ y8g, const _Float16* __restrict__ C16, const float* __restrict__ c2,
-    const float* __restrict__ sp, int64_t m, unsigned long long* __restrict__ keys,
-    unsigned* __restrict__ done, E8Finish fin) {
+    const float* __restrict__ y8g, E8Book book, const float* __restrict__ sp, int64_t m,
+    unsigned long long* __restrict__ keys, unsigned* __restrict__ done, E8Finish fin) {
   __shared__ unsigned long long ksh[4][32];
   __shared__ float bestv_sh[256];
   __shared__ uint32_t bestref_sh[256];
   __shared__ unsigned last_sh;
   const float s = *sp;
+  const E8View v = e8_view(book);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t r0 = int64_t(blockIdx.x) * 32;
@@ -770,79 +906,51 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
   }
   const e8_half8 yb = e8_split_operand(y8, kh);
   const int nw = int(gridDim.y) * 4, gw = int(blockIdx.y) * 4 + wave;
-  const int p0 = gw * 1024 / nw, p1 = (gw + 1) * 1024 / nw;  // this wave's pairs
-  // the lane's best run so far lives in LDS (written only when a run ends),
-  // so the loop carries only the current run
-  // Inside the loop a reference is a tile base (this lane's half implied) or
-  // an exact index tagged with E8_EXACT; it becomes a key's low word at the end.
+  const int p0 = gw * v.pairs / nw, p1 = (gw + 1) * v.pairs / nw;  // this wave's pairs
+  // The lane's best run so far lives in LDS (written only when a run ends),
+  // so the loop carries only the current run. Inside the loop a reference is a
+  // tile base (this lane's half implied) or an exact entry tagged with
+  // E8_EXACT (and E8_NEG); it becomes a key's low word at the end.
   constexpr uint32_t E8_EXACT = 0x40000000u;
   bestv_sh[tid] = 3.4e38f;
   bestref_sh[tid] = uint32_t(p0 * 64) | E8_EXACT;  // valid even if every distance is NaN
-  float run_n = c2[p0 * 64], run_max = -3.4e38f;
+  float run_n = v.nm[p0 * 64], run_max = -3.4e38f;
   uint32_t run_ref = uint32_t(p0 * 64) | E8_EXACT;
   auto fold = [&]() {
-    const float v = fmaf(s, run_n, -2.f * run_max);
-    if (v < bestv_sh[tid]) {  // runs are visited in increasing index within a lane
-      bestv_sh[tid] = v;
+    const float d = fmaf(s, run_n, -2.f * run_max);
+    if (d < bestv_sh[tid]) {  // runs are visited in increasing entry order within a lane
+      bestv_sh[tid] = d;
       bestref_sh[tid] = run_ref;
     }
   };
-  auto tile = [&](const f32x16& acc, float cn, int t) {
-    if (__all(cn == run_n)) {  // the whole tile continues the run
-      const float mx = e8_max16(acc, run_max);
-      run_ref = mx > run_max ? uint32_t(t) : run_ref;
-      run_max = mx;
-    } else {  // a run ends inside this tile
+  auto tile_of = [&](auto abs_tag) {
+    constexpr bool ABS = decltype(abs_tag)::value;
+    return [&](const f32x16& acc, float cn, int t) {
+      if (__all(cn == run_n)) {  // the whole tile continues the run
+        const float mx = e8_max16<ABS>(acc, run_max);
+        run_ref = mx > run_max ? uint32_t(t) : run_ref;
+        run_max = mx;
+      } else {  // a run ends inside this tile
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = t + 8 * (r / 4) + 4 * kh + (r % 4);
-        const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
-        if (n2 != run_n) {
-          fold();
-          run_n = n2;
-          run_max = -3.4e38f;
+        for (int r = 0; r < 16; ++r) {
+          const int i = t + 8 * (r / 4) + 4 * kh + (r % 4);
+          const float n2 = __shfl(cn, 8 * (r / 4) + 4 * kh + (r % 4), 64);
+          if (n2 != run_n) {
+            fold();
+            run_n = n2;
+            run_max = -3.4e38f;
+          }
+          const float x = ABS ? fabsf(acc[r]) : acc[r];
+          const bool gt = x > run_max;
+          run_max = gt ? x : run_max;
+          const uint32_t sg = (ABS && acc[r] < 0.f) ? E8_NEG : 0u;
+          run_ref = gt ? (uint32_t(i) | E8_EXACT | sg) : run_ref;
         }
-        const bool gt = acc[r] > run_max;
-        run_max = gt ? acc[r] : run_max;
-        run_ref = gt ? uint32_t(i) | E8_EXACT : run_ref;
       }
-    }
+    };
   };
-  // tiles in pairs, pipelined as in e8_scale_kernel; cp and np point at the
-  // current pair (the same address in every lane)
-  const uint4* cp = reinterpret_cast<const uint4*>(C16) + p0 * 64;
-  const float* np = c2 + p0 * 64;
-  f32x16 aa, ab, xa, xb;
-  e8_pair_products(cp[j], cp[32 + j], yb, aa, ab);
-  float ca = np[j], cb = np[32 + j], xca, xcb;
-  uint4 na = cp[64 + j], nb = cp[96 + j];
-  float nca = np[64 + j], ncb = np[96 + j];
-  for (int p = p0; p < p1; p += 2) {  // two pairs per iteration, as in e8_scale_kernel
-    e8_pair_products(na, nb, yb, xa, xb);  // pair p + 1
-    xca = nca;
-    xcb = ncb;
-    cp += 64;
-    np += 64;
-    na = cp[64 + j];  // pair p + 2
-    nb = cp[96 + j];
-    nca = np[64 + j];
-    ncb = np[96 + j];
-    tile(aa, ca, p * 64);
-    tile(ab, cb, p * 64 + 32);
-    e8_pair_products(na, nb, yb, aa, ab);  // pair p + 2
-    ca = nca;
-    cb = ncb;
-    cp += 64;
-    np += 64;
-    na = cp[64 + j];  // pair p + 3 (at most the padding past the codebook)
-    nb = cp[96 + j];
-    nca = np[64 + j];
-    ncb = np[96 + j];
-    if (p + 1 < p1) {
-      tile(xa, xca, (p + 1) * 64);
-      tile(xb, xcb, (p + 1) * 64 + 32);
-    }
-  }
+  e8_pairs(v.cw, v.nm, p0, p1 < v.sym_pairs ? p1 : v.sym_pairs, j, yb, tile_of(std::true_type{}));
+  e8_pairs(v.cw, v.nm, p0 > v.sym_pairs ? p0 : v.sym_pairs, p1, j, yb, tile_of(std::false_type{}));
   fold();
   const uint32_t ref = bestref_sh[tid];
   const uint32_t low = (ref & E8_EXACT) ? (ref ^ E8_EXACT) : (E8_TILE | ref | uint32_t(kh));
@@ -878,7 +986,7 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
       float y[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[k] = fin.y8[row * 8 + k];
-      const uint32_t code = e8_resolve(fin, y, uint32_t(rk & 0xFFFFFFFFull), sub);
+      const uint32_t code = e8_resolve(fin, v, y, uint32_t(rk & 0xFFFFFFFFull), sub);
       e8_finish_row(fin, s, row, code, y, sub);
     }
   }
@@ -937,10 +1045,41 @@ struct E8Ws {
   unsigned long long* keys;
   float* c2;
   _Float16* c16;  // the codebook in half precision (exact: multiples of 1/2 up to 3.5)
+  float* c2s;     // the symmetric search layout (e8_layout_kernel)
+  _Float16* c16s;
+  uint32_t* orig;
+  uint32_t* neg;
+  int* bad;
   float* cand;
   double* sse;
   double* part;  // per-work-group partial sums of the scale search
+  E8Book book() const { return E8Book{c16, c2, c16s, c2s, orig, neg, bad}; }
 };
+
+// Codebook-side buffers of the E8 search, carved in this order.
+void e8_take_book(Carver& c, E8Ws& e) {
+  e.c2 = c.take<float>(E8_ROWS);
+  e.c16 = c.take<_Float16>(size_t(E8_ROWS) * 8);
+  e.c2s = c.take<float>(E8_ROWS);
+  e.c16s = c.take<_Float16>(size_t(E8_ROWS) * 8);
+  e.orig = c.take<uint32_t>(E8_ROWS);
+  e.neg = c.take<uint32_t>(E8_ROWS);
+  e.bad = c.take<int>(16);
+}
+
+// Both views of the codebook: as given, and the symmetric layout with its
+// pairing check.
+quip_status e8_prepare_book(const float* codebook, const E8Ws& e, hipStream_t s) {
+  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(e8_norms_kernel, dim3(unsigned(cdiv(E8_ROWS, 256))), dim3(256), 0, s, codebook,
+                e.c2, e.c16);
+  }));
+  QUIP_TRY(fill_f32(reinterpret_cast<float*>(e.bad), 1, 0.f, s));  // bad <- 0 (bit pattern)
+  return timed_launch("e8_layout_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(e8_layout_kernel, dim3(unsigned(cdiv(E8_LAYOUT_CW, 256))), dim3(256), 0, s,
+                codebook, e.c16s, e.c2s, e.orig, e.neg, e.bad);
+  });
+}
 
 // Work-groups per 32-row block of a group step's search (gridDim.y of
 // e8_argmin_kernel): the split of the 1024 tile pairs that ends soonest when
@@ -995,10 +1134,10 @@ quip_status e8_scales(const float* Wn, int64_t m, int64_t n, const float* C, con
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(sh64)));
   QUIP_TRY(timed_launch("e8_scale_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     if (ncand <= 32)
-      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), sh32, s, Wn, nvec, e.c16, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<32>), grid, dim3(256), sh32, s, Wn, nvec, e.book(), e.cand,
                          ncand, e.part);
     else
-      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), sh64, s, Wn, nvec, e.c16, e.c2, e.cand,
+      QUIP_KERNEL((e8_scale_kernel<64>), grid, dim3(256), sh64, s, Wn, nvec, e.book(), e.cand,
                          ncand, e.part);
   }, 16.0 * 65536.0 * double(nvec), 32.0 * double(nvec)));  // <y, c> for every vector and codeword
   QUIP_TRY(timed_launch("e8_sse_reduce_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
@@ -1085,8 +1224,8 @@ size_t scales_workspace_bytes(int64_t m, int64_t n, const quip_quantizer& q) {
   c.take<float>(64);  // candidate factors
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
-    c.take<float>(E8_ROWS);          // |c|^2
-    c.take<_Float16>(size_t(E8_ROWS) * 8);   // the codebook in half precision
+    E8Ws e{};
+    e8_take_book(c, e);            // the codebook's half-precision views
     c.take<double>(64);            // sse
     c.take<double>(e8_partial_count(m, n));  // per-work-group partial sums
   }
@@ -1108,8 +1247,7 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
   }
   E8Ws e{};
   e.Wn = c.take<float>(size_t(m) * n);
-  e.c2 = c.take<float>(E8_ROWS);
-  e.c16 = c.take<_Float16>(size_t(E8_ROWS) * 8);
+  e8_take_book(c, e);
   e.sse = c.take<double>(64);
   e.part = c.take<double>(e8_partial_count(m, n));
   e.cand = fac;
@@ -1120,9 +1258,7 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
     QUIP_KERNEL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
                        true);
   }));
-  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(e8_norms_kernel, dim3(unsigned(cdiv(E8_ROWS, 256))), dim3(256), 0, s, codebook, e.c2, e.c16);
-  }));
+  QUIP_TRY(e8_prepare_book(codebook, e, s));
   return e8_scales(e.Wn, m, n, codebook, e, q.n_cand, scales, static_cast<double*>(mse_out), s);
 }
 
@@ -1148,8 +1284,8 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
     c.take<unsigned long long>(size_t(m));
     c.take<float>(size_t(m) * 8);  // pre-rounding vectors of a group step
     c.take<unsigned>(size_t(cdiv(m, 32)));  // per row block: chunk groups done
-    c.take<float>(E8_ROWS);
-    c.take<_Float16>(size_t(E8_ROWS) * 8);
+    E8Ws e{};
+    e8_take_book(c, e);
     c.take<double>(64);
     c.take<double>(e8_partial_count(m, n));
   }
@@ -1203,8 +1339,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   e.keys = c.take<unsigned long long>(size_t(m));
   float* y8 = c.take<float>(size_t(m) * 8);
   unsigned* done = c.take<unsigned>(size_t(cdiv(m, 32)));
-  e.c2 = c.take<float>(E8_ROWS);
-  e.c16 = c.take<_Float16>(size_t(E8_ROWS) * 8);
+  e8_take_book(c, e);
   e.sse = c.take<double>(64);
   e.part = c.take<double>(e8_partial_count(m, n));
   e.cand = fac;
@@ -1216,9 +1351,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
     QUIP_KERNEL(rownorm_kernel, dim3(unsigned(m)), dim3(256), 0, s, W, n, ldw, e.Wn, scales + 1,
                        compute);
   }));
-  QUIP_TRY(timed_launch("e8_norms_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(e8_norms_kernel, dim3(unsigned(cdiv(E8_ROWS, 256))), dim3(256), 0, s, codebook, e.c2, e.c16);
-  }));
+  QUIP_TRY(e8_prepare_book(codebook, e, s));
   if (compute) {
     host_e8_candidates(q.n_cand, hostf);
     QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
@@ -1244,7 +1377,7 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       E8Finish fin{e.Wn, n, codebook, scales + 1, c0, cd, n / 8, What, Eb, B, nprev, y8, D, rl};
       // the search, and the step's codes, W^, errors and loss term
       QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.c16, e.c2, sglob, m,
+        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.book(), sglob, m,
                     e.keys, done, fin);
       }, 16.0 * 65536.0 * double(m), 32.0 * double(m) + 8.0 * double(m) * 8.0));
     }

@@ -128,6 +128,26 @@ def test_e8_codebook_matches_oracle_enumeration():
     assert N.lib.quip_e8_codebook(None) == N.QUIP_ERR_ARG
 
 
+def test_e8_codebook_shells_hold_negations_in_reverse_order():
+    """The structure the E8 search's symmetric layout assumes of this codebook
+    (the GPU checks the pairing again on every call and falls back to the
+    plain search when it fails): the zero vector first, then the full shells of
+    squared norm 2, 4, 6, 8, 10 (the theta series' 240, 2160, 6720, 17520,
+    30240), each holding the negation of its i-th point at its (S - 1 - i)-th
+    place, then the first 8655 points of the norm-12 shell."""
+    cb = Q.quip_e8_codebook().numpy().astype(np.float64)
+    norms = (cb * cb).sum(1)
+    assert np.all(cb[0] == 0)
+    a = 1
+    for norm, size in zip((2, 4, 6, 8, 10), (240, 2160, 6720, 17520, 30240)):
+        shell = cb[a:a + size]
+        assert np.all(norms[a:a + size] == norm)
+        assert np.array_equal(shell[::-1], -shell)
+        a += size
+    assert a == 56881
+    assert np.all(norms[a:] == 12) and len(norms) - a == 8655
+
+
 def test_packed_codes_and_inference_product_validation():
     lib = N.lib
     # row sizes: 2-, 4- or 8-bit containers

@@ -492,6 +492,31 @@ def test_block_ldlq_e8_replay(m, n, B, codebook):
     assert np.allclose(What, rms[:, None] * float(s[0]) * cw, rtol=1e-6, atol=1e-7)
 
 
+def test_e8_search_any_codebook_order(codebook):
+    """A codebook without the shells' negation pairing (a random row order)
+    takes the plain search over all 65536 codewords: the scale table and the
+    replayed codes against the oracle on that same codebook."""
+    perm = rng(77).permutation(65536)
+    cb = np.ascontiguousarray(codebook[perm])
+    m, n = 64, 128
+    W = rng(31).standard_normal((m, n)).astype(np.float32)
+    scales = torch.empty(m + 1, device=DEV)
+    sse = torch.empty(32, dtype=torch.float64, device=DEV)
+    Q.quip_scales(dev(W), Q.quantizer(Q.Q_E8, 2), scales, mse_out=sse, codebook=dev(cb))
+    sg, eg = host(scales), host(sse)
+    Wn = (W / sg[1:, None].astype(np.float64))
+    _, _, sse_ref = O.e8_scale_search(Wn, cb)
+    assert np.allclose(eg, sse_ref, rtol=1e-4)
+    H = spd32(m + n + 1, n)
+    U, D, info = ldl_gpu(H, 8)
+    assert info == 0
+    s, codes, What = ldlq_gpu(W, U, D, 8, 64, 2, codebook=cb)
+    rms = s[1:].astype(np.float64)
+    mism, bad, tot = P.replay_e8(W / rms[:, None], U, What / rms[:, None], float(s[0]), codes, cb)
+    assert bad == 0
+    assert mism <= max(1, P.MAX_MISMATCH * tot)
+
+
 @pytest.mark.parametrize("m,n,B", [(64, 128, 64), (33, 256, 128)])
 def test_block_ldlq_e8_fused_loss(m, n, B, codebook):
     H = spd32(m + n + 5, n)
