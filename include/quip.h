@@ -199,7 +199,9 @@ quip_status quip_ldl(const float* H, int64_t n, int64_t ldh, int64_t g, float* U
  *     nearest-codeword squared error of all 8-vectors of the row-normalized
  *     W; scales[1 + r] = root-mean-square of row r (1 for an all-zero row).
  *   W: m x n, leading dim ldw. codebook: 65536 x 8 device floats for E8,
- *   else NULL. mse_out: optional (may be NULL) device output of the squared
+ *   else NULL; any order works, and quip_e8_codebook's order (whose full
+ *   shells hold each point's negation in reverse order, checked on the device
+ *   every call) lets the search take one member of each pair {c, -c}. mse_out: optional (may be NULL) device output of the squared
  *   error per candidate: m x n_cand (UNIFORM) or n_cand (E8), float64 for E8,
  *   float32 for UNIFORM.
  * Errors: QUIP_ERR_ARG, QUIP_ERR_SHAPE (n % 8 != 0 for E8), QUIP_ERR_WORKSPACE.
@@ -228,8 +230,9 @@ quip_status quip_scales(const float* W, int64_t m, int64_t n, int64_t ldw, const
  *   What: optional (may be NULL) m x n output (leading dim n) of the
  *     quantized weights in the same (incoherent) domain as W; for E8 rows are
  *     scaled back by their RMS.
- *   codebook: 65536 x 8 device floats for E8 (quip_e8_codebook order), else
- *     NULL.
+ *   codebook: 65536 x 8 device floats for E8, else NULL. Codes index this
+ *     array; any order works, and quip_e8_codebook's order searches faster
+ *     (one member of each pair {c, -c} of its full shells; see quip_scales).
  *   row_loss, loss: optional (may be NULL) device float64 outputs, m values
  *     and one value: the proxy loss tr((W^ - W) H (W^ - W)^T) ([QuIP]
  *     "Introduction") per row and summed, in W's domain, for the H whose
