@@ -783,6 +783,12 @@ struct E8Finish {
   const float* y8;
   const float* Dg;
   double* rowloss;
+  // the next group step of the same block, when there is one: its
+  // pre-rounding vectors (as e8_prerounding_kernel forms them) go to ynext
+  float* ynext;
+  const float* F;  // null: no outer-block feedback yet
+  const float* U;
+  int64_t s0;      // first column of the block
 };
 
 // Low word of a search key: an entry of the search view, with E8_NEG when
@@ -847,28 +853,62 @@ __device__ __forceinline__ uint32_t e8_resolve(const E8Finish& f, const E8View& 
   return negate ? v.neg[e] : v.orig[e];
 }
 
-// Lane sub of the row's eight writes dimension sub of W^ and of the errors.
-__device__ __forceinline__ void e8_finish_row(const E8Finish& f, float s, int64_t row,
-                                              uint32_t code, const float* y, int sub) {
+// Lane sub of the row's eight writes dimension sub of W^ and of the errors
+// (and returns its error).
+__device__ __forceinline__ float e8_finish_row(const E8Finish& f, float s, int64_t row,
+                                               uint32_t code, const float* y, int sub) {
   if (sub == 0) f.codes[row * f.ldcode + f.c0 / 8] = uint16_t(code);
   const float r = f.rms[row];
   const float qs = s * f.C[code * 8 + sub];
-  f.Eb[row * f.lde + f.ecol + sub] = f.Wn[row * f.n + f.c0 + sub] - qs;
+  const float err = f.Wn[row * f.n + f.c0 + sub] - qs;
+  f.Eb[row * f.lde + f.ecol + sub] = err;
   if (f.What) f.What[row * f.n + f.c0 + sub] = r * qs;
   if (f.rowloss) {
-    double res[8];
+    // lane sub forms res_sub (D_g res)_sub; the eight lanes' terms are added
+    // by shuffles in a fixed order
+    double t = 0.0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) res[k] = double(y[k]) - double(s * f.C[code * 8 + k]);
-    double acc = 0.0;
+    for (int b = 0; b < 8; ++b)
+      t += double(f.Dg[(f.c0 + sub) * 8 + b]) * (double(y[b]) - double(s * f.C[code * 8 + b]));
+    double acc = (double(y[sub]) - double(qs)) * t;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      double t = 0.0;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) t += double(f.Dg[(f.c0 + a) * 8 + b]) * res[b];
-      acc += res[a] * t;
-    }
+    for (int o = 1; o < 8; o <<= 1) acc += __shfl_xor(acc, o, 8);
     if (sub == 0) f.rowloss[row] += double(r) * double(r) * acc;
   }
+  return err;
+}
+
+// Dimension sub of the row's pre-rounding vector for the block's next group
+// (columns c0 + 8 ..): Wn + sum over the block's groups so far of E U, + F.
+// Lane sub of the row's eight takes the block's columns c = sub mod 8 for all
+// eight dimensions, and the eight partial vectors are added by shuffles; this
+// group's errors come from the lanes.
+__device__ __forceinline__ void e8_next_prerounding(const E8Finish& f, int64_t row, int sub,
+                                                    float err, int lane) {
+  const int64_t cn = f.c0 + 8;  // the next group's first column
+  const int nprev = f.ecol;     // the block's columns before this group
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  auto add = [&](float e, int64_t urow) {
+    const float* u = f.U + urow * f.n + cn;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(e, u[k], acc[k]);
+  };
+  for (int c = sub; c < nprev; c += 8) add(f.Eb[row * f.lde + c], f.s0 + c);
+  add(err, f.s0 + nprev + sub);  // this group: lane sub holds column nprev + sub
+#pragma unroll
+  for (int o = 4; o > 0; o >>= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 8);
+  }
+  float v = acc[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) v = sub == k ? acc[k] : v;
+  float yv = f.Wn[row * f.n + cn + sub] + v;
+  if (f.F) yv += f.F[row * f.n + cn + sub];
+  f.ynext[row * 8 + sub] = yv;
+  (void)lane;
 }
 
 // One group step of BlockLDLQ: the nearest scaled codeword to each row's
@@ -987,7 +1027,8 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[k] = fin.y8[row * 8 + k];
       const uint32_t code = e8_resolve(fin, v, y, uint32_t(rk & 0xFFFFFFFFull), sub);
-      e8_finish_row(fin, s, row, code, y, sub);
+      const float err = e8_finish_row(fin, s, row, code, y, sub);
+      if (fin.ynext) e8_next_prerounding(fin, row, sub, err, lane);
     }
   }
   if (tid == 0) done[blockIdx.x] = 0u;
@@ -1082,26 +1123,18 @@ quip_status e8_prepare_book(const float* codebook, const E8Ws& e, hipStream_t s)
 }
 
 // Work-groups per 32-row block of a group step's search (gridDim.y of
-// e8_argmin_kernel): the split of the 1024 tile pairs that ends soonest when
-// the row blocks x split work-groups run in rounds of the resident slots,
-// counting about four pairs of set-up and reduction per work-group.
+// e8_argmin_kernel). The total search work does not depend on the split; the
+// launch's fixed part (first loads after the kernel boundary, the key exchange,
+// the finish) does, per work-group. Measured on 256 CUs with n = 256 (µs per
+// step, argmin plus the pre-rounding launch where it is separate): m = 1024:
+// 8 splits 13.7 (16: 14.0, 4: 16.2); m = 4096: 4 splits 19.4 (8: 20.5, 3:
+// 24.0); m = 8192: 4 splits 27.3 (2: 29.4); m = 16384: 2 splits 46.2 (4: 48.9,
+// 1: 51.1). Two work-groups per CU, at least two and at most eight splits,
+// comes within 8% of the best at every size.
 int e8_argmin_split(int64_t m) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&e8_argmin_kernel), 256, 0) != hipSuccess ||
-      per_cu <= 0)
-    per_cu = 1;
-  const int64_t slots = int64_t(per_cu) * device_cus(), rb = cdiv(m, 32);
-  int best = 1;
-  double best_t = 1e300;
-  for (int y = 1; y <= 256; ++y) {
-    const double t = double(cdiv(rb * y, slots)) * (1024.0 / y + 4.0);
-    if (t < best_t) {
-      best_t = t;
-      best = y;
-    }
-  }
-  return best;
+  const int64_t rb = cdiv(m, 32);
+  const int64_t y = cdiv(2 * int64_t(device_cus()), rb);
+  return int(y < 2 ? 2 : (y > 8 ? 8 : y));
 }
 
 // Work-groups of the E8 scale search (128 vectors each) and their partial sums.
@@ -1282,7 +1315,8 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
   if (q.kind == QUIP_Q_E8) {
     c.take<float>(size_t(m) * n);  // Wn
     c.take<unsigned long long>(size_t(m));
-    c.take<float>(size_t(m) * 8);  // pre-rounding vectors of a group step
+    c.take<float>(size_t(m) * 8);  // pre-rounding vectors of two group steps
+    c.take<float>(size_t(m) * 8);
     c.take<unsigned>(size_t(cdiv(m, 32)));  // per row block: chunk groups done
     E8Ws e{};
     e8_take_book(c, e);
@@ -1337,7 +1371,9 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   E8Ws e{};
   e.Wn = c.take<float>(size_t(m) * n);
   e.keys = c.take<unsigned long long>(size_t(m));
-  float* y8 = c.take<float>(size_t(m) * 8);
+  float* ybuf[2];  // pre-rounding vectors, alternating between group steps
+  ybuf[0] = c.take<float>(size_t(m) * 8);
+  ybuf[1] = c.take<float>(size_t(m) * 8);
   unsigned* done = c.take<unsigned>(size_t(cdiv(m, 32)));
   e8_take_book(c, e);
   e.sse = c.take<double>(64);
@@ -1365,21 +1401,34 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   QUIP_TRY(fill_f32(reinterpret_cast<float*>(done), cdiv(m, 32), 0.f, s));  // counters <- 0
   uint16_t* cd = static_cast<uint16_t*>(codes);
   const int ysplit = e8_argmin_split(m);
+  int par = 0;
+  const bool fused_pre = ysplit >= 4;
   for (int64_t j0 = 0; j0 < n; j0 += B) {
     const int64_t bo = (n - j0 < B) ? n - j0 : B;
     for (int64_t c0 = j0; c0 < j0 + bo; c0 += 8) {
       const int nprev = int(c0 - j0);
-      QUIP_TRY(timed_launch("e8_prerounding_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(e8_prerounding_kernel, dim3(unsigned(cdiv(m, 16))), dim3(256), 0, s, e.Wn, n, F,
-                    j0 > 0, Eb, B, nprev, U, c0, j0, m, y8);
-      }, 16.0 * double(m) * double(nprev), 4.0 * double(m) * (double(nprev) + 24.0)));
+      float* y8 = ybuf[par];
+      // A block's first group needs the outer feedback F just updated. The
+      // later groups' vectors come from the previous step's finish when the
+      // search splits each row block over several work-groups (only one of
+      // them finishes); with few, every group finishes and the separate
+      // launch costs less than the finishers' extra latency.
+      if (nprev == 0 || !fused_pre)
+        QUIP_TRY(timed_launch("e8_prerounding_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+          QUIP_KERNEL(e8_prerounding_kernel, dim3(unsigned(cdiv(m, 16))), dim3(256), 0, s, e.Wn, n,
+                      F, j0 > 0, Eb, B, nprev, U, c0, j0, m, y8);
+        }, 16.0 * double(m) * double(nprev), 4.0 * double(m) * (double(nprev) + 24.0)));
+      const bool more = fused_pre && c0 + 8 < j0 + bo;
       const dim3 grid(unsigned(cdiv(m, 32)), unsigned(ysplit));
-      E8Finish fin{e.Wn, n, codebook, scales + 1, c0, cd, n / 8, What, Eb, B, nprev, y8, D, rl};
-      // the search, and the step's codes, W^, errors and loss term
+      E8Finish fin{e.Wn, n, codebook, scales + 1, c0, cd, n / 8, What, Eb, B, nprev, y8, D, rl,
+                   more ? ybuf[par ^ 1] : nullptr, j0 > 0 ? F : nullptr, U, j0};
+      // the search, the step's codes, W^, errors and loss term, and the next
+      // step's pre-rounding vectors
       QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
         QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.book(), sglob, m,
                     e.keys, done, fin);
       }, 16.0 * 65536.0 * double(m), 32.0 * double(m) + 8.0 * double(m) * 8.0));
+      par ^= 1;
     }
     QUIP_TRY(feedback_gemm(Eb, B, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
   }
