@@ -457,7 +457,8 @@ static_assert(E8_PLAIN_CW <= 8704, "plain region");
 // One thread per entry of the symmetric search layout: its codeword (half
 // precision) and norm, the codebook index it stands for and that of its
 // negation. Padding repeats the region's last entry. bad is set if a pair of
-// the symmetric region is not c, -c.
+// the symmetric region is not c, -c, or a codeword is not exact in half
+// precision.
 __global__ void e8_layout_kernel(const float* __restrict__ C, _Float16* __restrict__ c16,
                                  float* __restrict__ c2, uint32_t* __restrict__ orig,
                                  uint32_t* __restrict__ neg, int* __restrict__ bad) {
@@ -488,12 +489,16 @@ __global__ void e8_layout_kernel(const float* __restrict__ C, _Float16* __restri
   c2[e] = s;
   orig[e] = uint32_t(i);
   neg[e] = uint32_t(partner);
+  // the pairing, and codewords exact in half precision (the finish takes
+  // the winner's coordinates from the half copy)
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ok = ok && (float(_Float16(v[k])) == v[k]);
   if (e < E8_SYM_HALF) {
-    bool ok = true;
 #pragma unroll
     for (int k = 0; k < 8; ++k) ok = ok && (C[partner * 8 + k] == -v[k]);
-    if (!ok) atomicOr(bad, 1);
   }
+  if (!ok) atomicOr(bad, 1);
 }
 
 // The codebook as the search kernels see it: the symmetric layout when its
@@ -798,44 +803,139 @@ struct E8Finish {
 constexpr uint32_t E8_TILE = 0x80000000u;
 constexpr uint32_t E8_NEG = 0x20000000u;
 
-// The codebook index a key names for the pre-rounding vector y. For a tile
-// half: the largest float32 dot <y, c> over its 16 entries (one norm: the
-// largest dot is the nearest), or in the symmetric region the largest |<y, c>|
-// and the member of {c, -c} its sign gives (c for a zero dot); the lower entry
-// on ties. Eight lanes per row (sub = 0..7) take two entries each and agree by
-// shuffles.
-__device__ __forceinline__ uint32_t e8_resolve(const E8Finish& f, const E8View& v, const float* y,
-                                               uint32_t ref, int sub) {
+// The coordinates of search entry e (negated with neg): from the half copy
+// when the view is the symmetric layout (whose codewords the layout kernel
+// checked to be exact in half precision), else from the codebook as given.
+__device__ __forceinline__ void e8_coords(const E8Finish& f, const E8View& v, uint32_t e, bool neg,
+                                          float* c) {
+  if (v.orig) {
+    const e8_half8 h = __builtin_bit_cast(e8_half8, v.cw[e]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = neg ? -float(h[k]) : float(h[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = f.C[e * 8 + k];
+  }
+}
+
+// Finishes a group step for the row of this lane's group of eight (sub = 0..7):
+// the codeword its key names, the code, W^, the errors, the loss term and,
+// when there is a next group in the block, its pre-rounding vector. Loads that
+// do not depend on the key are issued first, so their latency overlaps the
+// key's exchange.
+//
+// The key: an entry as it stands (E8_NEG: its negation); for a tile half, the
+// largest float32 dot <y, c> over its 16 entries (one norm: the largest dot is
+// the nearest), or in the symmetric region the largest |<y, c>| and the member
+// of {c, -c} its sign gives (c for a zero dot); the lower entry on ties. Lane
+// sub takes two entries of the tile half and the eight agree by shuffles.
+//
+// Loss term: lane sub forms res_sub (D_g res)_sub; the eight lanes' terms are
+// added by shuffles in a fixed order. Next pre-rounding vector (as
+// e8_prerounding_kernel forms it): Wn + sum over the block's groups so far of
+// E U, + F; lane sub takes the block's columns c = sub mod 8 for all eight
+// dimensions, and the eight partial vectors are added by shuffles.
+__device__ __forceinline__ void e8_finish(const E8Finish& f, const E8View& v, float s,
+                                          unsigned long long* __restrict__ keys, int64_t row,
+                                          int sub, int lane) {
+  // ---- independent of the key
+  unsigned long long rk = 0ull;
+  if (sub == 0) rk = atomicExch(&keys[row], ~0ull);
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = f.y8[row * 8 + k];
+  const float r = f.rms[row];
+  const float wn = f.Wn[row * f.n + f.c0 + sub];
+  float dg[8];
+  if (f.rowloss) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) dg[b] = f.Dg[(f.c0 + sub) * 8 + b];
+  }
+  const int64_t cn = f.c0 + 8;  // the next group's first column
+  const int nprev = f.ecol;     // the block's columns before this group
+  float acc[8], ucur[8];
+  float wnx = 0.f, fx = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (f.ynext) {
+    wnx = f.Wn[row * f.n + cn + sub];
+    if (f.F) fx = f.F[row * f.n + cn + sub];
+    const float* uc = f.U + (f.s0 + nprev + sub) * f.n + cn;  // this group's column nprev + sub
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ucur[k] = uc[k];
+    // the earlier groups' columns, four at a time, loads before products
+    for (int c0 = sub; c0 < nprev; c0 += 32) {
+      float e[4], u[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + 8 * q;
+        const bool ok = c < nprev;
+        const int cc = ok ? c : sub;
+        e[q] = ok ? f.Eb[row * f.lde + cc] : 0.f;
+        const float* ur = f.U + (f.s0 + cc) * f.n + cn;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) u[q][k] = ur[k];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = fmaf(e[q], u[q][k], acc[k]);
+    }
+  }
+  // ---- the key: the entry, its sign, its coordinates
+  rk = __shfl(rk, lane & ~7, 64);
+  const uint32_t ref = uint32_t(rk & 0xFFFFFFFFull);
   uint32_t e;
   bool negate;
+  float cw[8];
   if (!(ref & E8_TILE)) {
     e = ref & ~E8_NEG;
     negate = (ref & E8_NEG) != 0;
+    e8_coords(f, v, e, negate, cw);
   } else {
     const uint32_t base = ref & 0x7FFFFFE0u, kh = ref & 1u;
     const bool sym = base < uint32_t(v.sym_pairs) * 64u;
-    float bv = 0.f;
-    uint32_t bi = 0;
+    // this lane's two entries of the tile half: places r = 2 sub and 2 sub + 1
+    // (adjacent entries); both loads are issued before either is used
+    const uint32_t i0 = base + 8 * ((2 * sub) / 4) + 4 * kh + (2 * sub) % 4, i1 = i0 + 1;
+    float a0[8], a1[8];
+    if (v.orig) {
+      const e8_half8 h0 = __builtin_bit_cast(e8_half8, v.cw[i0]);
+      const e8_half8 h1 = __builtin_bit_cast(e8_half8, v.cw[i1]);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = 2 * sub + q;
-      const uint32_t i = base + 8 * (r / 4) + 4 * kh + (r % 4);
-      const uint32_t ci = v.orig ? v.orig[i] : i;
-      float d = 0.f;
+      for (int k = 0; k < 8; ++k) {
+        a0[k] = float(h0[k]);
+        a1[k] = float(h1[k]);
+      }
+    } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) d = fmaf(f.C[ci * 8 + k], y[k], d);
-      // the sign rides in the low bit of the entry: entries are compared with
-      // it cleared
-      uint32_t tag = i << 1;
-      if (sym) {
-        tag |= d < 0.f ? 1u : 0u;
-        d = fabsf(d);
+      for (int k = 0; k < 8; ++k) {
+        a0[k] = f.C[i0 * 8 + k];
+        a1[k] = f.C[i1 * 8 + k];
       }
-      if (d != d) d = -INFINITY;  // a NaN dot ranks last, the same in every lane
-      if (q == 0 || d > bv) {
-        bv = d;
-        bi = tag;
-      }
+    }
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      d0 = fmaf(a0[k], y[k], d0);
+      d1 = fmaf(a1[k], y[k], d1);
+    }
+    // the sign rides in the low bit of the entry: entries are compared with it
+    // cleared
+    uint32_t t0 = i0 << 1, t1 = i1 << 1;
+    if (sym) {
+      t0 |= d0 < 0.f ? 1u : 0u;
+      t1 |= d1 < 0.f ? 1u : 0u;
+      d0 = fabsf(d0);
+      d1 = fabsf(d1);
+    }
+    if (d0 != d0) d0 = -INFINITY;  // a NaN dot ranks last, the same in every lane
+    if (d1 != d1) d1 = -INFINITY;
+    float bv = d0;
+    uint32_t bi = t0;
+    if (d1 > bv) {
+      bv = d1;
+      bi = t1;
     }
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) {
@@ -848,67 +948,51 @@ __device__ __forceinline__ uint32_t e8_resolve(const E8Finish& f, const E8View& 
     }
     e = bi >> 1;
     negate = (bi & 1u) != 0;
+    // the winner's coordinates from the lane that loaded them
+    const uint32_t off = e - base - 4 * kh;         // 8 (r / 4) + r mod 4
+    const int rw = int(4 * (off / 8) + (off % 8));  // the winner's place r in 0..15
+    const int src = (lane & ~7) + rw / 2;
+    const bool second = (rw & 1) != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float c = __shfl(second ? a1[k] : a0[k], src, 64);
+      cw[k] = negate ? -c : c;
+    }
   }
-  if (!v.orig) return e;
-  return negate ? v.neg[e] : v.orig[e];
-}
-
-// Lane sub of the row's eight writes dimension sub of W^ and of the errors
-// (and returns its error).
-__device__ __forceinline__ float e8_finish_row(const E8Finish& f, float s, int64_t row,
-                                               uint32_t code, const float* y, int sub) {
+  const uint32_t code = !v.orig ? e : (negate ? v.neg[e] : v.orig[e]);
+  // ---- outputs
   if (sub == 0) f.codes[row * f.ldcode + f.c0 / 8] = uint16_t(code);
-  const float r = f.rms[row];
-  const float qs = s * f.C[code * 8 + sub];
-  const float err = f.Wn[row * f.n + f.c0 + sub] - qs;
+  float mycw = cw[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) mycw = sub == k ? cw[k] : mycw;
+  const float qs = s * mycw;
+  const float err = wn - qs;
   f.Eb[row * f.lde + f.ecol + sub] = err;
   if (f.What) f.What[row * f.n + f.c0 + sub] = r * qs;
   if (f.rowloss) {
-    // lane sub forms res_sub (D_g res)_sub; the eight lanes' terms are added
-    // by shuffles in a fixed order
     double t = 0.0;
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
-      t += double(f.Dg[(f.c0 + sub) * 8 + b]) * (double(y[b]) - double(s * f.C[code * 8 + b]));
-    double acc = (double(y[sub]) - double(qs)) * t;
+    for (int b = 0; b < 8; ++b) t += double(dg[b]) * (double(y[b]) - double(s * cw[b]));
+    double al = (double(y[sub]) - double(qs)) * t;
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) acc += __shfl_xor(acc, o, 8);
-    if (sub == 0) f.rowloss[row] += double(r) * double(r) * acc;
+    for (int o = 1; o < 8; o <<= 1) al += __shfl_xor(al, o, 8);
+    if (sub == 0) f.rowloss[row] += double(r) * double(r) * al;
   }
-  return err;
-}
-
-// Dimension sub of the row's pre-rounding vector for the block's next group
-// (columns c0 + 8 ..): Wn + sum over the block's groups so far of E U, + F.
-// Lane sub of the row's eight takes the block's columns c = sub mod 8 for all
-// eight dimensions, and the eight partial vectors are added by shuffles; this
-// group's errors come from the lanes.
-__device__ __forceinline__ void e8_next_prerounding(const E8Finish& f, int64_t row, int sub,
-                                                    float err, int lane) {
-  const int64_t cn = f.c0 + 8;  // the next group's first column
-  const int nprev = f.ecol;     // the block's columns before this group
-  float acc[8];
+  if (f.ynext) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  auto add = [&](float e, int64_t urow) {
-    const float* u = f.U + urow * f.n + cn;
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(err, ucur[k], acc[k]);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = fmaf(e, u[k], acc[k]);
-  };
-  for (int c = sub; c < nprev; c += 8) add(f.Eb[row * f.lde + c], f.s0 + c);
-  add(err, f.s0 + nprev + sub);  // this group: lane sub holds column nprev + sub
+    for (int o = 4; o > 0; o >>= 1) {
 #pragma unroll
-  for (int o = 4; o > 0; o >>= 1) {
+      for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 8);
+    }
+    float vv = acc[0];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 8);
+    for (int k = 1; k < 8; ++k) vv = sub == k ? acc[k] : vv;
+    float yv = wnx + vv;
+    if (f.F) yv += fx;
+    f.ynext[row * 8 + sub] = yv;
   }
-  float v = acc[0];
-#pragma unroll
-  for (int k = 1; k < 8; ++k) v = sub == k ? acc[k] : v;
-  float yv = f.Wn[row * f.n + cn + sub] + v;
-  if (f.F) yv += f.F[row * f.n + cn + sub];
-  f.ynext[row * 8 + sub] = yv;
-  (void)lane;
 }
 
 // One group step of BlockLDLQ: the nearest scaled codeword to each row's
@@ -922,18 +1006,25 @@ __device__ __forceinline__ void e8_next_prerounding(const E8Finish& f, int64_t r
 // dot per run, and where it was, and compares runs by distance. Inside a tile
 // of one norm a lane takes only the tile's largest dot (one max3 tree) and
 // remembers the tile; the codeword in it is found once per row, by the
-// finisher (e8_resolve). Where a run ends inside a tile, the lane goes through
+// finisher (e8_finish). Where a run ends inside a tile, the lane goes through
 // the tile's dots one by one and keeps exact entries. Ties go to the lower
 // entry within a lane and to the lower reference between lanes.
-__global__ __launch_bounds__(256) void e8_argmin_kernel(
-    const float* __restrict__ y8g, E8Book book, const float* __restrict__ sp, int64_t m,
-    unsigned long long* __restrict__ keys, unsigned* __restrict__ done, E8Finish fin) {
-  __shared__ unsigned long long ksh[4][32];
-  __shared__ float bestv_sh[256];
-  __shared__ uint32_t bestref_sh[256];
-  __shared__ unsigned last_sh;
-  const float s = *sp;
-  const E8View v = e8_view(book);
+struct E8Shared {
+  unsigned long long ksh[4][32];
+  float bestv[256];
+  uint32_t bestref[256];
+  unsigned last;
+};
+
+// Returns (the same in every thread) whether this work-group finished the
+// step: the one whose count, added to `cnt`, reaches `target`.
+__device__ __forceinline__ bool e8_step(E8Shared& sh, const E8View& v, float s, int64_t m,
+                                        unsigned long long* __restrict__ keys,
+                                        unsigned* __restrict__ cnt, unsigned target,
+                                        const E8Finish& fin) {
+  float* bestv_sh = sh.bestv;
+  uint32_t* bestref_sh = sh.bestref;
+  const float* y8g = fin.y8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t r0 = int64_t(blockIdx.x) * 32;
@@ -997,11 +1088,11 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
   unsigned long long key = (unsigned long long)ordered_bits(bestv_sh[tid]) << 32 | low;
   unsigned long long other = __shfl_xor(key, 32, 64);
   key = key < other ? key : other;
-  if (kh == 0) ksh[wave][j] = key;
+  if (kh == 0) sh.ksh[wave][j] = key;
   __syncthreads();
   if (tid < 32) {
-    unsigned long long k2 = ksh[0][tid];
-    for (int wv = 1; wv < 4; ++wv) k2 = ksh[wv][tid] < k2 ? ksh[wv][tid] : k2;
+    unsigned long long k2 = sh.ksh[0][tid];
+    for (int wv = 1; wv < 4; ++wv) k2 = sh.ksh[wv][tid] < k2 ? sh.ksh[wv][tid] : k2;
     if (r0 + tid < m) atomicMin(&keys[r0 + tid], k2);
   }
   // The last of the gridDim.y work-groups of these 32 rows to get here
@@ -1009,29 +1100,33 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(
   // The keys are only touched by atomics: each group waits until its own
   // atomicMin operations are complete before it counts, and the finisher takes
   // each key with an atomic exchange (a read-modify-write sees the latest
-  // value), which also resets it for the next step. No cache-wide fence is
+  // value), which also resets it for the next use. No cache-wide fence is
   // needed (and none is taken: they would flush the L2 holding the codebook).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) last_sh = atomicAdd(&done[blockIdx.x], 1u) == gridDim.y - 1 ? 1u : 0u;
+  if (tid == 0) sh.last = atomicAdd(cnt, 1u) == target - 1u ? 1u : 0u;
   __syncthreads();
-  if (!last_sh) return;
+  if (!sh.last) return false;
   {
     const int sub = tid & 7;
     const int64_t row = r0 + (tid >> 3);
     if (row < m) {  // the same for the eight lanes of a row
-      unsigned long long rk = 0ull;
-      if (sub == 0) rk = atomicExch(&keys[row], ~0ull);
-      rk = __shfl(rk, lane & ~7, 64);
-      float y[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = fin.y8[row * 8 + k];
-      const uint32_t code = e8_resolve(fin, v, y, uint32_t(rk & 0xFFFFFFFFull), sub);
-      const float err = e8_finish_row(fin, s, row, code, y, sub);
-      if (fin.ynext) e8_next_prerounding(fin, row, sub, err, lane);
+      e8_finish(fin, v, s, keys, row, sub, lane);
     }
   }
-  if (tid == 0) done[blockIdx.x] = 0u;
+  return true;
+}
+
+// One group step per launch.
+__global__ __launch_bounds__(256) void e8_argmin_kernel(E8Book book, const float* __restrict__ sp,
+                                                        int64_t m,
+                                                        unsigned long long* __restrict__ keys,
+                                                        unsigned* __restrict__ done, E8Finish fin) {
+  __shared__ E8Shared sh;
+  const E8View v = e8_view(book);
+  if (e8_step(sh, v, *sp, m, keys, &done[blockIdx.x], gridDim.y, fin) &&
+      threadIdx.x == 0)
+    done[blockIdx.x] = 0u;
 }
 
 // loss = sum of the row losses, in a fixed order (one work-group).
@@ -1317,7 +1412,7 @@ size_t ldlq_workspace_bytes(int64_t m, int64_t n, int g, int64_t B, const quip_q
     c.take<unsigned long long>(size_t(m));
     c.take<float>(size_t(m) * 8);  // pre-rounding vectors of two group steps
     c.take<float>(size_t(m) * 8);
-    c.take<unsigned>(size_t(cdiv(m, 32)));  // per row block: chunk groups done
+    c.take<unsigned>(size_t(cdiv(m, 32)));  // per row block: groups done
     E8Ws e{};
     e8_take_book(c, e);
     c.take<double>(64);
@@ -1374,7 +1469,8 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   float* ybuf[2];  // pre-rounding vectors, alternating between group steps
   ybuf[0] = c.take<float>(size_t(m) * 8);
   ybuf[1] = c.take<float>(size_t(m) * 8);
-  unsigned* done = c.take<unsigned>(size_t(cdiv(m, 32)));
+  const int64_t rbk = cdiv(m, 32);
+  unsigned* done = c.take<unsigned>(size_t(rbk));  // per row block: groups done
   e8_take_book(c, e);
   e.sse = c.take<double>(64);
   e.part = c.take<double>(e8_partial_count(m, n));
@@ -1398,9 +1494,10 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   QUIP_TRY(timed_launch("fill_u64_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL(fill_u64_kernel, dim3(unsigned(cdiv(m, 256))), dim3(256), 0, s, e.keys, m, ~0ull);
   }));
-  QUIP_TRY(fill_f32(reinterpret_cast<float*>(done), cdiv(m, 32), 0.f, s));  // counters <- 0
+  QUIP_TRY(fill_f32(reinterpret_cast<float*>(done), rbk, 0.f, s));  // counters <- 0
   uint16_t* cd = static_cast<uint16_t*>(codes);
   const int ysplit = e8_argmin_split(m);
+  const dim3 grid{unsigned(rbk), unsigned(ysplit)};
   int par = 0;
   const bool fused_pre = ysplit >= 4;
   for (int64_t j0 = 0; j0 < n; j0 += B) {
@@ -1419,14 +1516,12 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
                       F, j0 > 0, Eb, B, nprev, U, c0, j0, m, y8);
         }, 16.0 * double(m) * double(nprev), 4.0 * double(m) * (double(nprev) + 24.0)));
       const bool more = fused_pre && c0 + 8 < j0 + bo;
-      const dim3 grid(unsigned(cdiv(m, 32)), unsigned(ysplit));
       E8Finish fin{e.Wn, n, codebook, scales + 1, c0, cd, n / 8, What, Eb, B, nprev, y8, D, rl,
                    more ? ybuf[par ^ 1] : nullptr, j0 > 0 ? F : nullptr, U, j0};
       // the search, the step's codes, W^, errors and loss term, and the next
       // step's pre-rounding vectors
       QUIP_TRY(timed_launch("e8_argmin_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, y8, e.book(), sglob, m,
-                    e.keys, done, fin);
+        QUIP_KERNEL(e8_argmin_kernel, grid, dim3(256), 0, s, e.book(), sglob, m, e.keys, done, fin);
       }, 16.0 * 65536.0 * double(m), 32.0 * double(m) + 8.0 * double(m) * 8.0));
       par ^= 1;
     }

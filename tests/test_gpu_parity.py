@@ -473,7 +473,10 @@ def test_e8_scale_search_parity(codebook):
     assert sse_ref[cg] <= sse_ref[c_ref] * (1 + 1e-5)
 
 
-@pytest.mark.parametrize("m,n,B", [(64, 128, 64), (40, 64, 32), (33, 256, 128)])
+# 16448 rows: two work-groups per 32-row block, so every step launches its own
+# pre-rounding kernel (the smaller sizes form the next step's vectors in the
+# finishing work-group)
+@pytest.mark.parametrize("m,n,B", [(64, 128, 64), (40, 64, 32), (33, 256, 128), (16448, 64, 32)])
 def test_block_ldlq_e8_replay(m, n, B, codebook):
     H = spd32(m + n + 1, n)
     Wt = (rng(n).standard_normal((m, n)) * np.exp(0.3 * rng(m).standard_normal(m))[:, None]).astype(np.float32)
