@@ -59,7 +59,8 @@ __device__ __forceinline__ float row_bcast(float v) {
 // Cholesky of the 8x8 block P (upper triangle read) followed by its inverse;
 // every lane computes the same values. Returns false on a non-positive pivot.
 __device__ bool chol_inv8(const float (*P)[17], int r0, float (&Pinv)[8][8]) {
-  float L[8][8];
+  float L[8][8];  // lower triangle used
+  float rl[8];    // 1 / L[a][a]
   bool ok = true;
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
@@ -67,39 +68,42 @@ __device__ bool chol_inv8(const float (*P)[17], int r0, float (&Pinv)[8][8]) {
 #pragma unroll
     for (int x = 0; x < a; ++x) sd = fmaf(-L[a][x], L[a][x], sd);
     ok = ok && (sd > 0.f);
-    const float la = sqrtf(sd);
-    const float rla = 1.f / la;
-    L[a][a] = la;
+    // 1/sqrt to 1 ulp (the hardware's), and the root from it
+    const float r = __builtin_amdgcn_rsqf(sd);
+    rl[a] = r;
+    L[a][a] = sd * r;
 #pragma unroll
     for (int b = a + 1; b < 8; ++b) {
       float v = P[r0 + a][r0 + b];
 #pragma unroll
       for (int x = 0; x < a; ++x) v = fmaf(-L[b][x], L[a][x], v);
-      L[b][a] = v * rla;
+      L[b][a] = v * rl[a];
     }
   }
-  float Li[8][8];  // L^{-1}, lower triangular
+  // L^{-1}, lower triangular, column by column (only its nonzero entries:
+  // the loops run over the triangle, so no products with known zeros)
+  float Li[8][8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int c = 0; c < 8; ++c) {
+    Li[c][c] = rl[c];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < c) {
-        Li[i][c] = 0.f;
-      } else {
-        float v = (i == c) ? 1.f : 0.f;
+    for (int i = c + 1; i < 8; ++i) {
+      float v = 0.f;
 #pragma unroll
-        for (int x = c; x < i; ++x) v = fmaf(-L[i][x], Li[x][c], v);
-        Li[i][c] = v / L[i][i];
-      }
+      for (int x = c; x < i; ++x) v = fmaf(L[i][x], Li[x][c], v);
+      Li[i][c] = -v * rl[i];
     }
+  }
+  // P^{-1} = L^{-T} L^{-1}, symmetric: entry (a, b), a <= b, sums x >= b
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = a; b < 8; ++b) {
       float v = 0.f;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) v = fmaf(Li[x][a], Li[x][b], v);
+      for (int x = b; x < 8; ++x) v = fmaf(Li[x][a], Li[x][b], v);
       Pinv[a][b] = v;
+      Pinv[b][a] = v;
     }
   return ok;
 }
