@@ -285,26 +285,28 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     // One pass over the 16 columns of the chunk; returns this lane's
     // accumulator as it stood at its own column (it does not change after: the
     // remaining coefficients lie below the diagonal and are zero), so the
-    // owner's rounding is redone once afterwards with the same arithmetic.
-    // EXACT = false rounds with p * (1/s); when an owner lane lands within 1e-4
-    // of a decision boundary, where p * (1/s) and the IEEE quotient p / s might
-    // differ, the chunk is redone with EXACT = true. The error sent to the row
-    // is w - q with q = (k - c) * s, each rounded once (no contraction), the
-    // same values the outputs store.
+    // owner's rounding is redone once afterwards. EXACT = false rounds with
+    // a * (1/s) + (w * (1/s) + L/2), the part that does not depend on the
+    // feedback formed before the chain; when an owner lane lands within 1e-4
+    // of a decision boundary, where that and the IEEE quotient (w + a) / s
+    // might differ, the chunk is redone with EXACT = true, so every code sent
+    // is the one the outputs store. The error sent to the row is
+    // (w + c s) - k s (one fma on the precomputed w + c s), the value the
+    // outputs store.
+    const float wh = fmaf(w, inv, half), wcs = fmaf(cen, s, w);
     auto pass = [&](auto exact_tag) -> float {
       constexpr bool EXACT = decltype(exact_tag)::value;
       float a = acc;
       static_for<16>([&](auto KI) {
         constexpr int kk = decltype(KI)::value;
-        const float p = w + a;
         float y;
         if constexpr (EXACT) {
-          y = p / s + half;
+          y = (w + a) / s + half;
         } else {
-          y = fmaf(p, inv, half);
+          y = fmaf(a, inv, wh);
         }
         const float kf = __builtin_amdgcn_fmed3f(floorf(y), 0.f, hi);
-        const float ev = __fsub_rn(w, __fmul_rn(kf - cen, s));
+        const float ev = fmaf(-s, kf, wcs);
         const float eb = row_bcast<kk>(ev);
         e16[kk] = eb;
         a = fmaf(eb, u16[kk], a);  // zero coefficient on and below the diagonal
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     }
     const float kf = __builtin_amdgcn_fmed3f(floorf(y), 0.f, hi);
     const float q = __fmul_rn(kf - cen, s);
-    const float err = __fsub_rn(w, q);
+    const float err = fmaf(-s, kf, wcs);
     const float res = p - q;
     const uint32_t code = uint32_t(kf);
     // outputs of this chunk: one column per lane
