@@ -169,18 +169,34 @@ __device__ __forceinline__ float row_bcast(float v) {
 // a two-chunk ring, one 16-row chunk ahead of their use, so that a lane's 16
 // coefficients of a chunk are four float4 reads and the LDS footprint does not
 // grow with B.
+//
+// Feedback of the earlier sub-blocks of the same batch (left-looking): the
+// columns [kb0, s0) with kb0 = s0 - kfold were rounded by earlier launches,
+// their errors are in Ef (same rows, leading dimension lde), and their share
+// of this block's targets, G = Ef[:, 0:kfold] U[kb0:s0, s0:s0+bw], is formed
+// here on the matrix cores before the sweep starts and added to the
+// accumulators (the rest of the matrix receives it through the batch's outer
+// product). F holds the earlier batches' feedback when useF.
+template <int B, bool VEC>
+__device__ __forceinline__ void sweep_fold(const float* __restrict__ Ef, int64_t lde,
+                                           const float* __restrict__ U, int64_t ldu, int64_t s0,
+                                           int kfold, int bw, int64_t row0, int64_t m,
+                                           float* __restrict__ Gs);
+
 template <int B>
 __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
     const float* __restrict__ U, int64_t ldu, const float* __restrict__ scales, int L, int64_t m,
     int64_t s0, int bw, uint8_t* __restrict__ codes, int64_t ldcode, float* __restrict__ What,
     int64_t ldwh, float* __restrict__ Eb, int64_t lde, const float* __restrict__ Dg,
-    double* __restrict__ rowloss, bool vec) {
+    double* __restrict__ rowloss, bool vec, const float* __restrict__ Ef, int kfold) {
   constexpr int NT = B / 16;  // 16-column chunks
   constexpr int UP = 36;      // two 16-row chunks of U (a ring) and a pad, per column
+  constexpr int GLD = B + 4;  // row length of the fold's result tile
   extern __shared__ __align__(16) float sm[];
   float* Ut = sm;            // [B][UP]: column c of U's rows of the current and next chunk
   float* Ds = sm + B * UP;   // [B]: D of the block (proxy loss)
+  float* Gs = Ds + B;        // [16][GLD]: the fold's feedback for the 16 rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,6 +260,20 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     for (int i = 0; i < NT - 1; ++i) {
       const int c = 16 * (i + 1) + j;
       if (c < bw) ar[i] = F[row * ldf + s0 + c];
+    }
+  }
+  if (kfold > 0) {
+    if (vec)
+      sweep_fold<B, true>(Ef, lde, U, ldu, s0, kfold, bw, int64_t(blockIdx.x) * 16, m, Gs);
+    else
+      sweep_fold<B, false>(Ef, lde, U, ldu, s0, kfold, bw, int64_t(blockIdx.x) * 16, m, Gs);
+    __syncthreads();
+    const float* g = Gs + (tid >> 4) * GLD;
+    if (j < bw) acc += g[j];
+#pragma unroll
+    for (int i = 0; i < NT - 1; ++i) {
+      const int c = 16 * (i + 1) + j;
+      if (c < bw) ar[i] += g[c];
     }
   }
   __syncthreads();
@@ -373,6 +403,111 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
     if (live && j == 0) rowloss[row] += lsum;  // one work-group per row per launch
+  }
+}
+
+typedef float sw_f32x4 __attribute__((ext_vector_type(4)));
+
+// G[r][c] = sum_k Ef[row0 + r][k] U[s0 - kfold + k][s0 + c] for the 16 rows
+// of the work-group, written to Gs[r][c] (row length B + 4); columns c >= bw
+// and rows past m hold values of clamped addresses that the caller ignores.
+// v_mfma_f32_16x16x4f32 on 16 x 16 tiles, tile t of the block on wave t % 4:
+// lane (i, h) = (lane % 16, lane / 16) supplies A[i][k] and B[k][i] for the k
+// of its quarter h, and holds D[4 h + r][i] in element r. A 16-wide k step is
+// one float4 of Ef per lane (quarter h takes k = 4 h .. 4 h + 3, one per
+// instruction) and four U values per tile; four steps are in flight. kfold is
+// a multiple of 32.
+template <int B, bool VEC>
+__device__ __forceinline__ void sweep_fold(const float* __restrict__ Ef, int64_t lde,
+                                           const float* __restrict__ U, int64_t ldu, int64_t s0,
+                                           int kfold, int bw, int64_t row0, int64_t m,
+                                           float* __restrict__ Gs) {
+  constexpr int CT = B / 16;         // 16-column tiles of the block
+  constexpr int TW = (CT + 3) / 4;   // tiles per wave
+  constexpr int GLD = B + 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, h = lane >> 4;
+  // tile tt of this wave exists (known at compile time unless B = 32)
+  auto has = [&](int tt) { return CT >= 4 * (tt + 1) || wave + 4 * tt < CT; };
+  const float* ea = Ef + (row0 + li < m ? row0 + li : 0) * lde + 4 * h;
+  const float* ub[TW];
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) {
+    const int col = 16 * (wave + 4 * tt) + li;
+    ub[tt] = U + (s0 - kfold + 4 * h) * ldu + s0 + (col < bw ? col : 0);
+  }
+  sw_f32x4 acc[TW];
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) acc[tt] = sw_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Ops {
+    float a[4];
+    float b[TW][4];
+  };
+  auto load = [&](int kb, Ops& o) {
+    if constexpr (VEC) {
+      const float4 v = *reinterpret_cast<const float4*>(ea + kb);
+      o.a[0] = v.x;
+      o.a[1] = v.y;
+      o.a[2] = v.z;
+      o.a[3] = v.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o.a[t] = ea[kb + t];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) {
+      if (has(tt)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o.b[tt][t] = ub[tt][int64_t(kb + t) * ldu];
+      }
+    }
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) {
+      if (has(tt)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[t], o.b[tt][t], acc[tt], 0, 0, 0);
+      }
+    }
+  };
+  // loads are never skipped (a step past the end reloads the last one), so
+  // the loop body has no branch around a load and four steps stay in flight
+  auto kc = [&](int k) { return k < kfold ? k : kfold - 16; };
+  Ops o0, o1, o2, o3;
+  load(0, o0);
+  load(16, o1);
+  load(kc(32), o2);
+  load(kc(48), o3);
+  // (the scheduling barriers keep this order: otherwise the compiler sinks
+  // the loads next to their use and only one step is in flight)
+  for (int kb = 0; kb < kfold; kb += 64) {
+    mma(o0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(kc(kb + 64), o0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(o1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(kc(kb + 80), o1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 32 < kfold) {
+      mma(o2);
+      mma(o3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load(kc(kb + 96), o2);
+    load(kc(kb + 112), o3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) {
+    if (has(tt)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Gs[(4 * h + r) * GLD + 16 * (wave + 4 * tt) + li] = acc[tt][r];
+    }
   }
 }
 
@@ -1289,39 +1424,43 @@ template <int B>
 quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
                     const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                     int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
-                    int64_t lde, const float* D, double* rowloss, hipStream_t s) {
-  const size_t shmem = (size_t(B) * 36 + B) * sizeof(float);
+                    int64_t lde, const float* D, double* rowloss, const float* Ef, int kfold,
+                    hipStream_t s) {
+  const size_t shmem = (size_t(B) * 36 + B + 16 * (B + 4)) * sizeof(float);
   if (shmem > 65536)
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
   // float4 paths need 16-byte alignment of every row start and of the block start
-  const bool vec = aligned16(W) && aligned16(F) && aligned16(U) && aligned16(Eb) &&
+  const bool vec = aligned16(W) && aligned16(F) && aligned16(U) && aligned16(Eb) && aligned16(Ef) &&
                    (What == nullptr || aligned16(What)) &&
                    ((reinterpret_cast<uintptr_t>(codes) & 3) == 0) && ldw % 4 == 0 &&
                    ldf % 4 == 0 && ldu % 4 == 0 && ldc % 4 == 0 && ldwh % 4 == 0 &&
                    lde % 4 == 0 && s0 % 4 == 0;
-  // work: per row the in-block feedback (bw (bw - 1) flops) and the rounding;
-  // reads W, F and the U block, writes codes, W^ and the errors
-  const double md = double(m), bd = double(bw);
-  const double flops = md * (bd * (bd - 1.0) + 6.0 * bd);
+  // work: per row the batch's earlier feedback (2 kfold bw flops), the
+  // in-block feedback (bw (bw - 1) flops) and the rounding; reads W, F, the
+  // earlier errors and the U block and the rows above it, writes codes, W^
+  // and the errors
+  const double md = double(m), bd = double(bw), kd = double(kfold);
+  const double flops = md * (2.0 * kd * bd + bd * (bd - 1.0) + 6.0 * bd);
   const double bytes = md * bd * (4.0 + (useF ? 4.0 : 0.0) + 1.0 + (What ? 4.0 : 0.0) + 4.0) +
-                       4.0 * bd * bd + (rowloss ? 16.0 * md : 0.0);
+                       4.0 * bd * bd + 4.0 * kd * (md + bd) + (rowloss ? 16.0 * md : 0.0);
   return timed_launch("ldlq_sweep_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s, W, ldw,
                        F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
-                       D, rowloss, vec);
+                       D, rowloss, vec, Ef, kfold);
   }, flops, bytes);
 }
 
 quip_status sweep(int b, const float* W, int64_t ldw, const float* F, int64_t ldf, bool useF,
                   const float* U, int64_t ldu, const float* scales, int L, int64_t m, int64_t s0,
                   int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
-                  int64_t lde, const float* D, double* rowloss, hipStream_t s) {
+                  int64_t lde, const float* D, double* rowloss, const float* Ef, int kfold,
+                  hipStream_t s) {
   switch (b) {
-    case 32: return sweep_t<32>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
-    case 64: return sweep_t<64>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
-    case 128: return sweep_t<128>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
-    case 256: return sweep_t<256>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, s);
+    case 32: return sweep_t<32>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, Ef, kfold, s);
+    case 64: return sweep_t<64>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, Ef, kfold, s);
+    case 128: return sweep_t<128>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, Ef, kfold, s);
+    case 256: return sweep_t<256>(W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde, D, rowloss, Ef, kfold, s);
   }
   return fail(QUIP_ERR_UNSUPPORTED, "ldlq: inner block size");
 }
@@ -1393,10 +1532,12 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
 }
 
 // Trailing-update batch of the scalar sweep: the lazily updated block of B
-// columns is swept in sub-blocks of at most 128 columns (the sweep kernel), the
-// rest of each 512-column batch is updated after every sub-block, and the rest
-// of the matrix once per batch (one K = 512 product instead of four K = 128
-// ones: a quarter of the read-modify-write traffic of F).
+// columns is swept in sub-blocks of at most 256 columns (the sweep kernel);
+// each sub-block takes the feedback of the batch's earlier sub-blocks itself
+// (left-looking, on the matrix cores, inside the sweep launch), and the rest
+// of the matrix is updated once per 512-column batch (one K = 512 product
+// instead of four K = 128 ones: a quarter of the read-modify-write traffic of
+// F).
 static int64_t outer_block(int64_t n, int g, int64_t B) {
   if (g != 1) return B;
   int64_t bo = B >= 512 ? B : B * (512 / B);
@@ -1453,11 +1594,9 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       const int64_t bo = (n - j0 < Bo) ? n - j0 : Bo;
       for (int64_t s0 = j0; s0 < j0 + bo; s0 += bi) {
         const int bw = int((j0 + bo - s0) < bi ? (j0 + bo - s0) : bi);
-        QUIP_TRY(sweep(bi, W, ldw, F, n, s0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
-                       Eb + (s0 - j0), Bo, D, rl, s));
-        // rest of this batch
-        QUIP_TRY(feedback_gemm(Eb, Bo, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
-                               !(j0 == 0 && s0 == 0), "gemm:ldlq_inner", s));
+        // the earlier sub-blocks of this batch feed back inside the sweep
+        QUIP_TRY(sweep(bi, W, ldw, F, n, j0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
+                       Eb + (s0 - j0), Bo, D, rl, Eb, int(s0 - j0), s));
       }
       QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
     }
