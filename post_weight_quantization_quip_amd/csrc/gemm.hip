@@ -533,6 +533,15 @@ quip_status launch_tiles(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB)
   int64_t t128 = cdiv(a.M, 128) * cdiv(a.N, 128) * a.batch;
   if (a.upper_tiles) t128 = cdiv(a.M, 128) * (cdiv(a.M, 128) + 1) / 2 * a.batch;
   if (t128 < 512) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
+  // a plain product whose 64x64 grid fills whole rounds of resident
+  // work-groups (two per CU) where the 128x128 grid would leave the last round
+  // part empty (the LDLQ feedback with N = 3072 or 2560 at M = 4096: 1.5 and
+  // 1.25 rounds): all products 0.669 -> 0.635 ms per 4096 x 4096 pass
+  if (!a.upper_tiles && EPI == EPI_STORE) {
+    const int64_t slots = 2 * int64_t(device_cus());
+    const int64_t t64 = cdiv(a.M, 64) * cdiv(a.N, 64) * a.batch;
+    if (t128 % slots != 0 && t64 % slots == 0) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
+  }
   // 64 along a dimension that 128-wide tiles would pad by more than half a
   // 64-tile beyond what 64-wide tiles need (172: 256 against 192). The tile
   // shape does not change any element's summation order.
