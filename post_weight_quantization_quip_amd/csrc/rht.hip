@@ -418,8 +418,10 @@ __device__ __forceinline__ void fwht64_f2(float2 (&v)[64]) {
 // the store. The exchange goes through LDS in two halves of 8 columns (128 KB
 // + padding: float2 slot 4 r + g' + r / 16 of a half, so that both the
 // row-contiguous writes and the 64-row-strided reads of a wave's active lanes
-// fall on distinct banks). Needs cols % 16 == 0, ld % 2 == 0 and 8-byte
-// aligned A and out; A == out is allowed.
+// fall on distinct banks). The forward direction stages the signs, times the
+// scale, in LDS (each thread's 64 signs are 16 float4 reads). Needs
+// cols % 16 == 0, ld % 2 == 0, 8-byte aligned A and out and 16-byte aligned
+// signs; A == out is allowed.
 template <bool INV>
 __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* out, int64_t ld,
                                                         int nblk,
@@ -427,6 +429,10 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
                                                         float scale) {
   constexpr bool inverse = INV;
   extern __shared__ __align__(16) float2 P2[];
+  // forward: the signs times the scale, Sg[k][i] = s[k + 64 i] / 64, rows of
+  // 68 floats after the exchange buffer (a power-of-two scale commutes exactly
+  // with the butterflies, so it is applied once, with the signs)
+  float* Sg = reinterpret_cast<float*>(P2 + (4 * 4096 + 4096 / 16));
   auto slot = [](int r, int g4) { return 4 * r + g4 + (r >> 4); };
   const int t = threadIdx.x;
   const int g = t & 7, k = t >> 3;  // column pair, row index of the thread (0..63)
@@ -442,10 +448,26 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
   for (int i = 0; i < 64; ++i)
     v[i] = *reinterpret_cast<const float2*>(A + cb + int64_t(64 * i) * ld + lin);
   if (!inverse) {
+    // thread t stages s[8 t .. 8 t + 7]: element e sits at Sg[e % 64][e / 64]
+    const float4 s0 = *reinterpret_cast<const float4*>(signs + 8 * t);
+    const float4 s1 = *reinterpret_cast<const float4*>(signs + 8 * t + 4);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const float sg = signs[k + 64 * i];
-      v[i] = make_float2(v[i].x * sg, v[i].y * sg);
+    for (int q = 0; q < 8; ++q) {
+      const int e = 8 * t + q;
+      Sg[(e & 63) * 68 + (e >> 6)] = sv[q] * scale;
+    }
+    __syncthreads();
+    const float4* sk = reinterpret_cast<const float4*>(Sg + k * 68);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const float4 sq = sk[c];
+      const float sw[4] = {sq.x, sq.y, sq.z, sq.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * c + q;
+        v[i] = make_float2(v[i].x * sw[q], v[i].y * sw[q]);
+      }
     }
   }
   fwht64_f2(v);
@@ -467,9 +489,11 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
   fwht64_f2(v);
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    const float sg = scale * (inverse ? signs[64 * k + i] : 1.f);
-    *reinterpret_cast<float2*>(out + cb + int64_t(i) * ld + lout) =
-        make_float2(v[i].x * sg, v[i].y * sg);
+    if (inverse) {
+      const float sg = scale * signs[64 * k + i];
+      v[i] = make_float2(v[i].x * sg, v[i].y * sg);
+    }
+    *reinterpret_cast<float2*>(out + cb + int64_t(i) * ld + lout) = v[i];
   }
 }
 
@@ -595,9 +619,10 @@ quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int
     QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
     const float scale = 1.0f / 64.0f;  // 1 / sqrt(4096)
-    if (cols % 16 == 0) {  // 64-byte row segments
-      // half a panel (8 columns x 4096 rows) plus one float2 of padding per 16 rows
-      const size_t shmem16 = size_t(4 * 4096 + 4096 / 16) * sizeof(float2);
+    if (cols % 16 == 0 && aligned16(signs)) {  // 64-byte row segments
+      // half a panel (8 columns x 4096 rows) plus one float2 of padding per 16
+      // rows, then the scaled signs (64 rows of 68 floats)
+      const size_t shmem16 = size_t(4 * 4096 + 4096 / 16) * sizeof(float2) + 64 * 68 * sizeof(float);
       QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel16<false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem16)));
       QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rht_cols_panel16<true>),
