@@ -49,6 +49,47 @@ __device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t 
   return v;
 }
 
+// Tile (tm, tn), tm <= tn, of an upper-triangular tile grid with tiles_m
+// tile rows, numbered super-block by super-block: blocks of 8 x 8 tiles, the
+// off-diagonal blocks first (row-major), then the diagonal blocks (their upper
+// tiles, row-major inside). With the XCD remap giving each XCD a contiguous
+// range of numbers, the 64 work-groups an XCD holds at once cover one block:
+// 16 operand panels (8 on the diagonal) instead of up to 35 for a run of
+// row-major tiles, so each L2 re-reads fewer panels.
+__device__ __forceinline__ void upper_tile(int bid, int tiles_m, int& tm, int& tn) {
+  constexpr int S = 8;
+  const int sg = (tiles_m + S - 1) / S;
+  auto ext = [&](int I) { return tiles_m - S * I < S ? tiles_m - S * I : S; };
+  int rem = bid;
+  for (int I = 0; I < sg; ++I)
+    for (int J = I + 1; J < sg; ++J) {
+      const int cnt = ext(I) * ext(J);
+      if (rem < cnt) {
+        const int cj = ext(J);
+        tm = S * I + rem / cj;
+        tn = S * J + rem % cj;
+        return;
+      }
+      rem -= cnt;
+    }
+  for (int I = 0; I < sg; ++I) {
+    const int e = ext(I);
+    const int cnt = e * (e + 1) / 2;
+    if (rem < cnt) {
+      int r = 0;
+      while (rem >= e - r) {
+        rem -= e - r;
+        ++r;
+      }
+      tm = S * I + r;
+      tn = S * I + r + rem;
+      return;
+    }
+    rem -= cnt;
+  }
+  tm = tn = 0;  // not reached: bid < tiles_m (tiles_m + 1) / 2
+}
+
 template <int BM, int BN, bool TA, bool TB, int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n,
                                                       int total, bool vecA, bool vecB) {
@@ -77,13 +118,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   bid += a.tile0;
   int tm, tn;
   if (a.upper_tiles) {
-    int rem = bid, r = 0;
-    while (rem >= tiles_m - r) {
-      rem -= tiles_m - r;
-      ++r;
-    }
-    tm = r;
-    tn = r + rem;
+    upper_tile(bid, tiles_m, tm, tn);
   } else if (EPI == EPI_DOT_SYM) {
     // column tile tn has K range [0, (tn+1) BN): longest tiles first, dealt
     // round-robin over the XCDs, so the short ones fill the tail
@@ -394,12 +429,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a, int tiles_m) {
   const int r = blockIdx.x;  // leftover tile
-  int rem = a.tile0 + r, tr = 0;
-  while (rem >= tiles_m - tr) {
-    rem -= tiles_m - tr;
-    ++tr;
-  }
-  const int tm = tr, tn = tr + rem;
+  int tm, tn;
+  upper_tile(a.tile0 + r, tiles_m, tm, tn);
   const int e4 = (int(blockIdx.y) * 256 + int(threadIdx.x)) * 4;  // 4 consecutive elements
   if (e4 >= BM * BN) return;
   const int i = e4 / BN, j0 = e4 % BN;
