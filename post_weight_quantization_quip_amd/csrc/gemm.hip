@@ -50,13 +50,26 @@ __device__ __forceinline__ float4 load4(const float* base, int64_t row, int64_t 
 }
 
 // Tile (tm, tn), tm <= tn, of an upper-triangular tile grid with tiles_m
-// tile rows, numbered super-block by super-block: blocks of 8 x 8 tiles, the
-// off-diagonal blocks first (row-major), then the diagonal blocks (their upper
-// tiles, row-major inside). With the XCD remap giving each XCD a contiguous
-// range of numbers, the 64 work-groups an XCD holds at once cover one block:
-// 16 operand panels (8 on the diagonal) instead of up to 35 for a run of
-// row-major tiles, so each L2 re-reads fewer panels.
-__device__ __forceinline__ void upper_tile(int bid, int tiles_m, int& tm, int& tn) {
+// tile rows. `blocked` (products with a long K, where the operand panels are
+// the traffic): numbered super-block by super-block, blocks of 8 x 8 tiles,
+// the off-diagonal blocks first (row-major), then the diagonal blocks (their
+// upper tiles, row-major inside). With the XCD remap giving each XCD a
+// contiguous range of numbers, the 64 work-groups an XCD holds at once cover
+// one block: 16 operand panels (8 on the diagonal) instead of up to 35 for a
+// run of row-major tiles, so each L2 re-reads fewer panels. Otherwise
+// (short K: the C tiles are the traffic) row-major, so that consecutive tiles
+// read and write neighbouring stretches of C's rows.
+__device__ __forceinline__ void upper_tile(int bid, int tiles_m, bool blocked, int& tm, int& tn) {
+  if (!blocked) {  // row-major: consecutive tiles along a tile row
+    int rem = bid, r = 0;
+    while (rem >= tiles_m - r) {
+      rem -= tiles_m - r;
+      ++r;
+    }
+    tm = r;
+    tn = r + rem;
+    return;
+  }
   constexpr int S = 8;
   const int sg = (tiles_m + S - 1) / S;
   auto ext = [&](int I) { return tiles_m - S * I < S ? tiles_m - S * I : S; };
@@ -118,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a, int tiles_m, i
   bid += a.tile0;
   int tm, tn;
   if (a.upper_tiles) {
-    upper_tile(bid, tiles_m, tm, tn);
+    upper_tile(bid, tiles_m, a.K >= 1024, tm, tn);
   } else if (EPI == EPI_DOT_SYM) {
     // column tile tn has K range [0, (tn+1) BN): longest tiles first, dealt
     // round-robin over the XCDs, so the short ones fill the tail
@@ -430,7 +443,7 @@ template <int BM, int BN>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a, int tiles_m) {
   const int r = blockIdx.x;  // leftover tile
   int tm, tn;
-  upper_tile(a.tile0 + r, tiles_m, tm, tn);
+  upper_tile(a.tile0 + r, tiles_m, a.K >= 1024, tm, tn);
   const int e4 = (int(blockIdx.y) * 256 + int(threadIdx.x)) * 4;  // 4 consecutive elements
   if (e4 >= BM * BN) return;
   const int i = e4 / BN, j0 = e4 % BN;
@@ -564,14 +577,17 @@ quip_status launch_tiles(const GemmArgs& a, hipStream_t s, bool vecA, bool vecB)
   int64_t t128 = cdiv(a.M, 128) * cdiv(a.N, 128) * a.batch;
   if (a.upper_tiles) t128 = cdiv(a.M, 128) * (cdiv(a.M, 128) + 1) / 2 * a.batch;
   if (t128 < 512) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
-  // a plain product whose 64x64 grid fills whole rounds of resident
-  // work-groups (two per CU) where the 128x128 grid would leave the last round
-  // part empty (the LDLQ feedback with N = 3072 or 2560 at M = 4096: 1.5 and
-  // 1.25 rounds): all products 0.669 -> 0.635 ms per 4096 x 4096 pass
+  // a plain product of a few rounds whose 64x64 grid fills whole rounds of
+  // resident work-groups (two per CU) where the 128x128 grid would leave the
+  // last round part empty (the LDLQ feedback with N = 3072 or 2560 at
+  // M = 4096: 1.5 and 1.25 rounds): all products 0.669 -> 0.635 ms per
+  // 4096 x 4096 pass. With many rounds the part-empty last one costs less
+  // than the smaller tiles (8192 x 28672 layer: 59.3 against 61.4 ms).
   if (!a.upper_tiles && EPI == EPI_STORE) {
     const int64_t slots = 2 * int64_t(device_cus());
     const int64_t t64 = cdiv(a.M, 64) * cdiv(a.N, 64) * a.batch;
-    if (t128 % slots != 0 && t64 % slots == 0) return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
+    if (t128 < 4 * slots && t128 % slots != 0 && t64 % slots == 0)
+      return launch_t<64, 64, TA, TB, EPI>(a, s, vecA, vecB);
   }
   // 64 along a dimension that 128-wide tiles would pad by more than half a
   // 64-tile beyond what 64-wide tiles need (172: 256 against 192). The tile

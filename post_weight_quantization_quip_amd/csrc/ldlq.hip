@@ -183,7 +183,7 @@ __device__ __forceinline__ void sweep_fold(const float* __restrict__ Ef, int64_t
                                            int kfold, int bw, int64_t row0, int64_t m,
                                            float* __restrict__ Gs);
 
-template <int B>
+template <int B, bool FOLD>
 __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
     const float* __restrict__ W, int64_t ldw, const float* __restrict__ F, int64_t ldf, bool useF,
     const float* __restrict__ U, int64_t ldu, const float* __restrict__ scales, int L, int64_t m,
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
       if (c < bw) ar[i] = F[row * ldf + s0 + c];
     }
   }
-  if (kfold > 0) {
+  if (FOLD && kfold > 0) {
     if (vec)
       sweep_fold<B, true>(Ef, lde, U, ldu, s0, kfold, bw, int64_t(blockIdx.x) * 16, m, Gs);
     else
@@ -1426,10 +1426,14 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
                     int bw, uint8_t* codes, int64_t ldc, float* What, int64_t ldwh, float* Eb,
                     int64_t lde, const float* D, double* rowloss, const float* Ef, int kfold,
                     hipStream_t s) {
-  const size_t shmem = (size_t(B) * 36 + B + 16 * (B + 4)) * sizeof(float);
+  // the fold in its own instantiation, with its result tile: the kernel
+  // without it keeps its registers and LDS (occupancy of the many-row layers)
+  const bool fold = kfold > 0;
+  const void* fn = fold ? reinterpret_cast<const void*>(&ldlq_sweep_kernel<B, true>)
+                        : reinterpret_cast<const void*>(&ldlq_sweep_kernel<B, false>);
+  const size_t shmem = (size_t(B) * 36 + B + (fold ? 16 * (B + 4) : 0)) * sizeof(float);
   if (shmem > 65536)
-    QUIP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&ldlq_sweep_kernel<B>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
+    QUIP_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem)));
   // float4 paths need 16-byte alignment of every row start and of the block start
   const bool vec = aligned16(W) && aligned16(F) && aligned16(U) && aligned16(Eb) && aligned16(Ef) &&
                    (What == nullptr || aligned16(What)) &&
@@ -1445,9 +1449,14 @@ quip_status sweep_t(const float* W, int64_t ldw, const float* F, int64_t ldf, bo
   const double bytes = md * bd * (4.0 + (useF ? 4.0 : 0.0) + 1.0 + (What ? 4.0 : 0.0) + 4.0) +
                        4.0 * bd * bd + 4.0 * kd * (md + bd) + (rowloss ? 16.0 * md : 0.0);
   return timed_launch("ldlq_sweep_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL((ldlq_sweep_kernel<B>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s, W, ldw,
-                       F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb, lde,
-                       D, rowloss, vec, Ef, kfold);
+    if (fold)
+      QUIP_KERNEL((ldlq_sweep_kernel<B, true>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s,
+                  W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb,
+                  lde, D, rowloss, vec, Ef, kfold);
+    else
+      QUIP_KERNEL((ldlq_sweep_kernel<B, false>), dim3(unsigned(cdiv(m, 16))), dim3(256), shmem, s,
+                  W, ldw, F, ldf, useF, U, ldu, scales, L, m, s0, bw, codes, ldc, What, ldwh, Eb,
+                  lde, D, rowloss, vec, Ef, kfold);
   }, flops, bytes);
 }
 
@@ -1533,11 +1542,12 @@ quip_status scales_run(const float* W, int64_t m, int64_t n, int64_t ldw, const 
 
 // Trailing-update batch of the scalar sweep: the lazily updated block of B
 // columns is swept in sub-blocks of at most 256 columns (the sweep kernel);
-// each sub-block takes the feedback of the batch's earlier sub-blocks itself
-// (left-looking, on the matrix cores, inside the sweep launch), and the rest
-// of the matrix is updated once per 512-column batch (one K = 512 product
-// instead of four K = 128 ones: a quarter of the read-modify-write traffic of
-// F).
+// each sub-block receives the feedback of the batch's earlier sub-blocks
+// (inside the sweep launch, left-looking on the matrix cores, when the rows
+// fit one work-group per CU; else from a product after each sub-block), and
+// the rest of the matrix is updated once per 512-column batch (one K = 512
+// product instead of four K = 128 ones: a quarter of the read-modify-write
+// traffic of F).
 static int64_t outer_block(int64_t n, int g, int64_t B) {
   if (g != 1) return B;
   int64_t bo = B >= 512 ? B : B * (512 / B);
@@ -1589,14 +1599,21 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       QUIP_TRY(grid_scales(W, m, n, ldw, L, q.n_cand, fac, scales, nullptr, s));
     }
     const int bi = B >= 256 ? 256 : (B >= 128 ? 128 : (B >= 64 ? 64 : 32));
+    // With at most one sweep work-group per CU, each sub-block takes the
+    // batch's earlier feedback itself (one launch per sub-block instead of
+    // two); with more rows a separate product after each sub-block is faster
+    // (28672 x 8192 layer: sweeps 3.6 -> 5.9 ms with the in-sweep feedback).
+    const bool fold = cdiv(m, 16) <= int64_t(device_cus());
     uint8_t* cd = static_cast<uint8_t*>(codes);
     for (int64_t j0 = 0; j0 < n; j0 += Bo) {
       const int64_t bo = (n - j0 < Bo) ? n - j0 : Bo;
       for (int64_t s0 = j0; s0 < j0 + bo; s0 += bi) {
         const int bw = int((j0 + bo - s0) < bi ? (j0 + bo - s0) : bi);
-        // the earlier sub-blocks of this batch feed back inside the sweep
-        QUIP_TRY(sweep(bi, W, ldw, F, n, j0 > 0, U, n, scales, L, m, s0, bw, cd, n, What, n,
-                       Eb + (s0 - j0), Bo, D, rl, Eb, int(s0 - j0), s));
+        QUIP_TRY(sweep(bi, W, ldw, F, n, fold ? j0 > 0 : s0 > 0, U, n, scales, L, m, s0, bw, cd,
+                       n, What, n, Eb + (s0 - j0), Bo, D, rl, Eb, fold ? int(s0 - j0) : 0, s));
+        if (!fold)  // rest of this batch
+          QUIP_TRY(feedback_gemm(Eb, Bo, s0 - j0, bw, U, n, s0, s0 + bw, j0 + bo, F, m,
+                                 !(j0 == 0 && s0 == 0), "gemm:ldlq_inner", s));
       }
       QUIP_TRY(feedback_gemm(Eb, Bo, 0, bo, U, n, j0, j0 + bo, n, F, m, j0 > 0, "gemm:ldlq_outer", s));
     }
