@@ -1598,12 +1598,16 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
       QUIP_HIP(hipMemcpyAsync(fac, hostf, sizeof(float) * q.n_cand, hipMemcpyHostToDevice, s));
       QUIP_TRY(grid_scales(W, m, n, ldw, L, q.n_cand, fac, scales, nullptr, s));
     }
-    const int bi = B >= 256 ? 256 : (B >= 128 ? 128 : (B >= 64 ? 64 : 32));
     // With at most one sweep work-group per CU, each sub-block takes the
     // batch's earlier feedback itself (one launch per sub-block instead of
     // two); with more rows a separate product after each sub-block is faster
     // (28672 x 8192 layer: sweeps 3.6 -> 5.9 ms with the in-sweep feedback).
     const bool fold = cdiv(m, 16) <= int64_t(device_cus());
+    // Sub-block width: B's, up to 256. Without the fold, B = 128 is swept 256
+    // columns at a time (half the sweeps and products: 11008 x 4096 layer
+    // LDLQ 3.37 -> 3.05 ms); with it, 256-wide sweeps cost more than the
+    // launches they save (4096 x 4096: 1.38 -> 1.45 ms).
+    const int bi = (B >= 256 || (!fold && B >= 128)) ? 256 : (B >= 128 ? 128 : (B >= 64 ? 64 : 32));
     uint8_t* cd = static_cast<uint8_t*>(codes);
     for (int64_t j0 = 0; j0 < n; j0 += Bo) {
       const int64_t bo = (n - j0 < Bo) ? n - j0 : Bo;
