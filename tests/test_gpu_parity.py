@@ -369,7 +369,7 @@ def check_fused_loss(Wt, What, H, row_loss, loss):
 
 
 @pytest.mark.parametrize("m,n,B,bits", [(256, 256, 32, 2), (37, 200, 64, 3), (300, 384, 128, 4),
-                                        (1, 8, 8, 2), (70, 1100, 256, 2)])
+                                        (1, 8, 8, 2), (70, 1100, 256, 2), (4112, 520, 128, 2)])
 def test_ldlq_fused_loss(m, n, B, bits):
     H = spd32(m + 3 * n, n)
     Wt = (rng(m + n).standard_normal((m, n)) * 0.7).astype(np.float32)
@@ -401,8 +401,13 @@ def check_uniform_replay(Wt, U, What, s, codes, L):
     assert np.array_equal(What, lv)
 
 
+# more rows than one sweep work-group per CU (16 x 256) take the path with a
+# product after each sub-block, and B = 128 is then swept 256 columns at a
+# time; fewer take the batch's earlier feedback inside the sweep
 @pytest.mark.parametrize("m,n,B,bits", [(256, 256, 32, 2), (37, 200, 64, 3), (100, 512, 256, 4),
-                                        (16, 48, 32, 2), (1, 8, 8, 2), (300, 384, 128, 2)])
+                                        (16, 48, 32, 2), (1, 8, 8, 2), (300, 384, 128, 2),
+                                        (4112, 520, 128, 3), (4200, 300, 32, 2),
+                                        (4097, 1100, 256, 4)])
 def test_ldlq_replay(m, n, B, bits):
     L = 1 << bits
     H = spd32(m + n, n)
