@@ -49,7 +49,10 @@ def spd32(seed, n, N=None, sigma=1.0):
 
 # ------------------------------------------------------------------ Hessian
 
-@pytest.mark.parametrize("N,n", [(2048, 256), (1000, 200), (64, 1000), (5, 3), (1, 1), (300, 129)])
+# N >= 1024 numbers the output tiles by 8 x 8 super-blocks: 1500 x 1100 has 18
+# tile rows of 64, so the last super-blocks are partial
+@pytest.mark.parametrize("N,n", [(2048, 256), (1000, 200), (64, 1000), (5, 3), (1, 1), (300, 129),
+                                 (1500, 1100)])
 def test_hessian_parity(N, n):
     X = (rng(N * 7 + n).standard_normal((N, n)) * np.exp(rng(n).standard_normal(n))).astype(np.float32)
     H = torch.empty((n, n), device=DEV)
@@ -256,9 +259,11 @@ def ldl_gpu(H32, g):
     return host(U), host(D), int(host(info)[0])
 
 
+# above n = 4096 the outer blocks are 512 columns wide (4500 and 4616 end in a
+# partial one)
 @pytest.mark.parametrize("n,g", [(256, 1), (256, 8), (200, 1), (200, 8), (8, 8), (1, 1), (130, 1),
                                  (600, 1), (600, 8), (520, 1), (1000, 1), (2000, 1), (1536, 8),
-                                 (3000, 1)])
+                                 (3000, 1), (4500, 1), (4616, 8)])
 def test_ldl_parity(n, g):
     H = spd32(n * 11 + g, n)
     U, D, info = ldl_gpu(H, g)
