@@ -408,11 +408,13 @@ def check_uniform_replay(Wt, U, What, s, codes, L):
 
 # more rows than one sweep work-group per CU (16 x 256) take the path with a
 # product after each sub-block, and B = 128 is then swept 256 columns at a
-# time; fewer take the batch's earlier feedback inside the sweep
+# time; fewer take the batch's earlier feedback inside the sweep. Above
+# n = 4096 the batches are 1024 columns wide.
 @pytest.mark.parametrize("m,n,B,bits", [(256, 256, 32, 2), (37, 200, 64, 3), (100, 512, 256, 4),
                                         (16, 48, 32, 2), (1, 8, 8, 2), (300, 384, 128, 2),
                                         (4112, 520, 128, 3), (4200, 300, 32, 2),
-                                        (4097, 1100, 256, 4)])
+                                        (4097, 1100, 256, 4), (64, 4500, 128, 2),
+                                        (4112, 4200, 64, 3)])
 def test_ldlq_replay(m, n, B, bits):
     L = 1 << bits
     H = spd32(m + n, n)
