@@ -418,8 +418,8 @@ __device__ __forceinline__ void fwht64_f2(float2 (&v)[64]) {
 // the store. The exchange goes through LDS in two halves of 8 columns (128 KB
 // + padding: float2 slot 4 r + g' + r / 16 of a half, so that both the
 // row-contiguous writes and the 64-row-strided reads of a wave's active lanes
-// fall on distinct banks). The forward direction stages the signs, times the
-// scale, in LDS (each thread's 64 signs are 16 float4 reads). Needs
+// fall on distinct banks). Both directions stage the signs, times the scale,
+// in LDS (each thread's 64 signs are 16 float4 reads). Needs
 // cols % 16 == 0, ld % 2 == 0, 8-byte aligned A and out and 16-byte aligned
 // signs; A == out is allowed.
 template <bool INV>
@@ -429,9 +429,10 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
                                                         float scale) {
   constexpr bool inverse = INV;
   extern __shared__ __align__(16) float2 P2[];
-  // forward: the signs times the scale, Sg[k][i] = s[k + 64 i] / 64, rows of
-  // 68 floats after the exchange buffer (a power-of-two scale commutes exactly
-  // with the butterflies, so it is applied once, with the signs)
+  // the signs times the scale, rows of 68 floats after the exchange buffer:
+  // forward Sg[k][i] = s[k + 64 i] / 64, inverse Sg[k][i] = s[64 k + i] / 64
+  // (a power-of-two scale commutes exactly with the butterflies, so it is
+  // applied once, with the signs)
   float* Sg = reinterpret_cast<float*>(P2 + (4 * 4096 + 4096 / 16));
   auto slot = [](int r, int g4) { return 4 * r + g4 + (r >> 4); };
   const int t = threadIdx.x;
@@ -447,16 +448,23 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
 #pragma unroll
   for (int i = 0; i < 64; ++i)
     v[i] = *reinterpret_cast<const float2*>(A + cb + int64_t(64 * i) * ld + lin);
-  if (!inverse) {
+  {
     // thread t stages s[8 t .. 8 t + 7]: element e sits at Sg[e % 64][e / 64]
+    // (forward: thread k applies s[k + 64 i] after the load) or at
+    // Sg[e / 64][e % 64] (inverse: s[64 k + i] before the store)
     const float4 s0 = *reinterpret_cast<const float4*>(signs + 8 * t);
     const float4 s1 = *reinterpret_cast<const float4*>(signs + 8 * t + 4);
     const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = 8 * t + q;
-      Sg[(e & 63) * 68 + (e >> 6)] = sv[q] * scale;
+      if (inverse)
+        Sg[(e >> 6) * 68 + (e & 63)] = sv[q] * scale;
+      else
+        Sg[(e & 63) * 68 + (e >> 6)] = sv[q] * scale;
     }
+  }
+  if (!inverse) {
     __syncthreads();
     const float4* sk = reinterpret_cast<const float4*>(Sg + k * 68);
 #pragma unroll
@@ -487,14 +495,22 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
     }
   }
   fwht64_f2(v);
+  if (inverse) {  // staged before the exchange's barriers
+    const float4* sk = reinterpret_cast<const float4*>(Sg + k * 68);
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    if (inverse) {
-      const float sg = scale * signs[64 * k + i];
-      v[i] = make_float2(v[i].x * sg, v[i].y * sg);
+    for (int c = 0; c < 16; ++c) {
+      const float4 sq = sk[c];
+      const float sw[4] = {sq.x, sq.y, sq.z, sq.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * c + q;
+        v[i] = make_float2(v[i].x * sw[q], v[i].y * sw[q]);
+      }
     }
-    *reinterpret_cast<float2*>(out + cb + int64_t(i) * ld + lout) = v[i];
   }
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    *reinterpret_cast<float2*>(out + cb + int64_t(i) * ld + lout) = v[i];
 }
 
 // Column transform of length 2, 4 or 8: one thread per column.
