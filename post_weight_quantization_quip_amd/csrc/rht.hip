@@ -415,10 +415,10 @@ __device__ __forceinline__ void fwht64_f2(float2 (&v)[64]) {
 // threads; thread t holds the column pair g = t % 8 of 64 rows in registers
 // (the 256 KB panel lives in registers). Index bits 6..11 are done right after
 // the load (rows k + 64 i), bits 0..5 after one exchange (rows 64 k + i), then
-// the store. The exchange goes through LDS in two rounds of 2048 rows (128 KB
-// + padding each); the waves whose rows come out of the first round run their
-// last butterflies and their store while the others finish the second. Both
-// directions stage the signs, times the scale,
+// the store. The exchange goes through LDS in two halves of 8 columns (128 KB
+// + padding: float2 slot 4 r + g' + r / 16 of a half, so that both the
+// row-contiguous writes and the 64-row-strided reads of a wave's active lanes
+// fall on distinct banks). Both directions stage the signs, times the scale,
 // in LDS (each thread's 64 signs are 16 float4 reads). Needs
 // cols % 16 == 0, ld % 2 == 0, 8-byte aligned A and out and 16-byte aligned
 // signs; A == out is allowed.
@@ -434,10 +434,7 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
   // (a power-of-two scale commutes exactly with the butterflies, so it is
   // applied once, with the signs)
   float* Sg = reinterpret_cast<float*>(P2 + (4 * 4096 + 4096 / 16));
-  // exchange slot of row r (0..2047 within a round) and column pair g: one
-  // float2 of padding per 8 rows, so that both the row-contiguous writes and
-  // the 64-row-strided reads of a wave take the minimum two LDS passes
-  auto xslot = [](int r, int g2) { return 8 * r + g2 + (r >> 3); };
+  auto slot = [](int r, int g4) { return 4 * r + g4 + (r >> 4); };
   const int t = threadIdx.x;
   const int g = t & 7, k = t >> 3;  // column pair, row index of the thread (0..63)
   // the block's first column (uniform) and the lane's offset from it, so that
@@ -482,31 +479,20 @@ __global__ __launch_bounds__(512) void rht_cols_panel16(const float* A, float* o
     }
   }
   fwht64_f2(v);
-  // ---- exchange to rows 64 k + i: bits 0..5 (and the store layout), in two
-  // rounds of 2048 rows (all 16 columns). Round 1: every thread writes its rows
-  // k + 64 i, i < 32; the threads k < 32 (waves 0..3) read their rows 64 k + i.
-  // Round 2: the rows from 2048 on, read by the threads k >= 32 (waves 4..7).
-  // Waves 0..3 keep their rows of round 2 aside while they read round 1, and
-  // after writing them run their last butterflies and store while waves 4..7
-  // are still in round 2.
-  const bool first = k < 32;  // uniform per wave
-  float2 keep[32];
+  // ---- exchange to rows 64 k + i: bits 0..5 (and the store layout)
 #pragma unroll
-  for (int i = 0; i < 32; ++i) P2[xslot(k + 64 * i, g)] = v[i];
-  __syncthreads();
-  if (first) {
+  for (int half = 0; half < 2; ++half) {
+    const bool mine = (g >> 2) == half;
+    if (half) __syncthreads();  // the first half's reads are done
+    if (mine) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) keep[i] = v[32 + i];
+      for (int i = 0; i < 64; ++i) P2[slot(k + 64 * i, g & 3)] = v[i];
+    }
+    __syncthreads();
+    if (mine) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = P2[xslot(64 * k + i, g)];
-  }
-  __syncthreads();  // round 1's reads are done
-#pragma unroll
-  for (int i = 0; i < 32; ++i) P2[xslot(k + 64 * i, g)] = first ? keep[i] : v[32 + i];
-  __syncthreads();
-  if (!first) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = P2[xslot(64 * (k - 32) + i, g)];
+      for (int i = 0; i < 64; ++i) v[i] = P2[slot(64 * k + i, g & 3)];
+    }
   }
   fwht64_f2(v);
   if (inverse) {  // staged before the exchange's barriers
