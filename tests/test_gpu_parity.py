@@ -171,6 +171,26 @@ def test_rht_left(d, cols):
     assert np.array_equal(host(Ad), host(out))
 
 
+@pytest.mark.parametrize("cols,ld", [(48, 64), (4112, 4112)])
+def test_rht_left_panel16_strided_and_many_panels(cols, ld):
+    """The 16-column panel kernel (d = 4096) with rows wider than the block
+    (ld > cols) and with more panels than one work-group per CU (4112 columns:
+    257 panels), both directions against the oracle."""
+    d = 4096
+    base = rng(cols + 7).standard_normal((d, ld)).astype(np.float32)
+    s = signs(cols + 11, d)
+    A = dev(base)[:, :cols]
+    out_full = torch.zeros((d, ld), device=DEV)
+    out = out_full[:, :cols]
+    Q.quip_rht(A, out, dev(s), Q.LEFT)
+    ref = O.rht(base[:, :cols], s, "left")
+    assert P.rel_rows(host(out).T, ref.T) <= 1e-5
+    back = torch.zeros((d, ld), device=DEV)[:, :cols]
+    Q.quip_rht_inv(out, back, dev(s), Q.LEFT)
+    assert P.rel_rows(host(back).T, base[:, :cols].T) <= 1e-5
+    assert np.all(host(out_full[:, cols:]) == 0)  # the columns past the block are untouched
+
+
 def test_rht_left_unaligned_rows():
     # row pitch 131 floats: not float4-aligned, so d = 4096 goes through the
     # multi-pass column kernels; it must agree with the oracle all the same
@@ -187,10 +207,11 @@ def test_rht_leading_dimension():
     base = rng(5).standard_normal((64, 300)).astype(np.float32)
     A = dev(base)[:, :256]  # ld = 300 > cols
     s = signs(9, 256)
-    out = torch.zeros((64, 300), device=DEV)[:, :256]
+    out_full = torch.zeros((64, 300), device=DEV)
+    out = out_full[:, :256]
     Q.quip_rht(A, out, dev(s), Q.RIGHT)
     assert P.rel_rows(host(out), O.rht(base[:, :256], s, "right")) <= 1e-5
-    assert np.all(host(torch.zeros((1,), device=DEV)) == 0)
+    assert np.all(host(out_full[:, 256:]) == 0)  # the columns past the rows are untouched
 
 
 @pytest.mark.parametrize("m,n", [(256, 256), (64, 4096), (4096, 64), (2, 2)])
