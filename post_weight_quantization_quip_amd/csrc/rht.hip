@@ -11,7 +11,9 @@
 // fit on a CU; XOR swizzle on bits 2..4 so the strided round patterns hit
 // distinct banks). A last transpose brings the data back to the float4 layout
 // for the store. As many work-groups as fit at once, each looping over rows
-// with the next row's loads issued before the current row's transform.
+// with the next row's loads issued before the current row's transform. Rows
+// are read and written with non-temporal accesses: whole 16-byte chunks of
+// contiguous rows, which no other work-group touches.
 //
 // LEFT side (along a column, strided by the row pitch). For d = 4096 and
 // float4-aligned rows, one pass over memory, a work-group per column block:
@@ -36,6 +38,8 @@ __device__ __forceinline__ int swz(int i) {
   int f = ((i >> 5) ^ (i >> 8) ^ (i >> 11)) & 7;
   return i ^ (f << 2);
 }
+
+typedef float rht_f4 __attribute__((ext_vector_type(4)));
 
 template <int LOGN, int LE>
 __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* out, int64_t rows,
@@ -78,7 +82,8 @@ __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* ou
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (r < rows) {
         if (vec) {
-          v = *reinterpret_cast<const float4*>(src + i);
+          const rht_f4 t = __builtin_nontemporal_load(reinterpret_cast<const rht_f4*>(src + i));
+          v = make_float4(t.x, t.y, t.z, t.w);
         } else {
           v.x = src[i];
           v.y = src[i + 1];
@@ -183,8 +188,8 @@ __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* ou
       for (int c = 0; c < E / 4; ++c) {
         int i = idx0(4 * c);
         if (vec) {
-          *reinterpret_cast<float4*>(dst + i) =
-              make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+          __builtin_nontemporal_store(rht_f4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]},
+                                      reinterpret_cast<rht_f4*>(dst + i));
         } else {
           dst[i] = x[4 * c];
           dst[i + 1] = x[4 * c + 1];
