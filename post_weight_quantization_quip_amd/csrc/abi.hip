@@ -197,7 +197,7 @@ quip_status quip_rht2(const float* A, float* out, int64_t rows, int64_t cols, in
   clear_error();
   QUIP_TRY(rht_validate(A, out, rows, cols, ld, signs_left, QUIP_LEFT, "quip_rht2"));
   QUIP_TRY(rht_validate(A, out, rows, cols, ld, signs_right, QUIP_RIGHT, "quip_rht2"));
-  QUIP_TRY(rht_rows(A, out, rows, cols, ld, signs_right, false, stream));
+  QUIP_TRY(rht_rows(A, out, rows, cols, ld, signs_right, false, stream, /*last_pass=*/false));
   return rht_cols(out, out, rows, cols, ld, signs_left, false, stream);
 }
 

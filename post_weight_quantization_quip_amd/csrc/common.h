@@ -210,8 +210,10 @@ quip_status copy_matrix(const float* src, int64_t lds, float* dst, int64_t ldd, 
 
 // ---------------------------------------------------------------- RHT (rht.hip)
 
+// last_pass: no other pass of the same transform reads `out` next (its rows
+// are then written with non-temporal stores)
 quip_status rht_rows(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
-                     const float* signs, bool inverse, hipStream_t stream);
+                     const float* signs, bool inverse, hipStream_t stream, bool last_pass = true);
 quip_status rht_cols(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
                      const float* signs, bool inverse, hipStream_t stream);
 

@@ -12,8 +12,10 @@
 // distinct banks). A last transpose brings the data back to the float4 layout
 // for the store. As many work-groups as fit at once, each looping over rows
 // with the next row's loads issued before the current row's transform. Rows
-// are read and written with non-temporal accesses: whole 16-byte chunks of
-// contiguous rows, which no other work-group touches.
+// are read with non-temporal loads (whole 16-byte chunks of contiguous rows,
+// which no other work-group touches), and written with non-temporal stores
+// when no other pass of the same transform follows (a following column pass
+// reads the result back while it is still in the last-level cache).
 //
 // LEFT side (along a column, strided by the row pitch). For d = 4096 and
 // float4-aligned rows, one pass over memory, a work-group per column block:
@@ -44,7 +46,8 @@ typedef float rht_f4 __attribute__((ext_vector_type(4)));
 template <int LOGN, int LE>
 __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* out, int64_t rows,
                                                        int64_t ld, const float* __restrict__ signs,
-                                                       float scale, bool inverse, bool vec) {
+                                                       float scale, bool inverse, bool vec,
+                                                       bool nt_out) {
   constexpr int N = 1 << LOGN;
   constexpr int E = 1 << LE;
   constexpr int T = N / E;                    // threads per row
@@ -187,9 +190,12 @@ __global__ __launch_bounds__(512) void rht_rows_kernel(const float* A, float* ou
 #pragma unroll
       for (int c = 0; c < E / 4; ++c) {
         int i = idx0(4 * c);
-        if (vec) {
+        if (vec && nt_out) {
           __builtin_nontemporal_store(rht_f4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]},
                                       reinterpret_cast<rht_f4*>(dst + i));
+        } else if (vec) {
+          *reinterpret_cast<float4*>(dst + i) =
+              make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
         } else {
           dst[i] = x[4 * c];
           dst[i + 1] = x[4 * c + 1];
@@ -542,7 +548,7 @@ __global__ void rht_cols_small_kernel(const float* A, float* out, int64_t cols, 
 
 template <int LOGN>
 quip_status rows_t(const float* A, float* out, int64_t rows, int64_t ld, const float* s,
-                   bool inverse, hipStream_t st) {
+                   bool inverse, bool nt_out, hipStream_t st) {
   constexpr int LE = LOGN >= 14 ? 5 : 4;
   constexpr int N = 1 << LOGN;
   constexpr int T = N >> LE;
@@ -566,7 +572,7 @@ quip_status rows_t(const float* A, float* out, int64_t rows, int64_t ld, const f
   const dim3 grid{unsigned(nwg)};
   return timed_launch("rht_rows_kernel", st, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
     QUIP_KERNEL((rht_rows_kernel<LOGN, LE>), grid, dim3(T * RW), shmem, st, A, out, rows, ld,
-                       s, scale, inverse, vec);
+                       s, scale, inverse, vec, nt_out);
   }, double(rows) * N * (LOGN + 2), 8.0 * double(rows) * N);
 }
 
@@ -611,14 +617,14 @@ quip_status cols_pass(int kr, const float* A, float* out, int64_t d, int64_t col
 }  // namespace
 
 quip_status rht_rows(const float* A, float* out, int64_t rows, int64_t cols, int64_t ld,
-                     const float* signs, bool inverse, hipStream_t st) {
+                     const float* signs, bool inverse, hipStream_t st, bool last_pass) {
   if (rows == 0) return QUIP_OK;
   switch (ilog2(cols)) {
     case 1: return rows_small_t<2>(A, out, rows, ld, signs, inverse, st);
     case 2: return rows_small_t<4>(A, out, rows, ld, signs, inverse, st);
     case 3: return rows_small_t<8>(A, out, rows, ld, signs, inverse, st);
 #define CASE(L) \
-  case L: return rows_t<L>(A, out, rows, ld, signs, inverse, st);
+  case L: return rows_t<L>(A, out, rows, ld, signs, inverse, last_pass, st);
     CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14)
 #undef CASE
   }
