@@ -654,8 +654,9 @@ def cpu_baseline(cfg_name: str, rows: int) -> dict:
 
 def north_star_targets(kernels: dict, phases: dict, rht: dict, cfg) -> dict:
     """The phase-level figures the pass is held to, each next to its target:
-    the two-sided random-sign Hadamard transform against the HBM peak (>= 60 %;
-    on a cache-resident matrix, and on matrices read from and written to HBM),
+    the two-sided random-sign Hadamard transform against the HBM peak (>= 60 %,
+    on matrices read from and written to HBM; the cache-resident figures are
+    reported beside them),
     the proxy-Hessian product and the LDLQ trailing update (the per-batch
     outer product; the feedback inside a batch is taken by the sweep kernel
     itself) against the fp32 matrix-core peak (>= 50 %), and the LDL and LDLQ
@@ -670,20 +671,23 @@ def north_star_targets(kernels: dict, phases: dict, rht: dict, cfg) -> dict:
 
     out = {}
     if rht:
+        # against the HBM peak with the bytes coming from and going to HBM
+        # (six matrices in turn); the same passes on one matrix that stays in
+        # the last-level cache are reported beside them
+        hr = rht.get("hbm_resident") or rht
         out["rht_two_sided_frac_of_hbm"] = {
-            "measured": round(rht["two_sided_effective_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+            "measured": round(hr["two_sided_effective_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
         out["rht_right_pass_frac_of_hbm"] = {
-            "measured": round(rht["right_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+            "measured": round(hr["right_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
         out["rht_left_pass_frac_of_hbm"] = {
-            "measured": round(rht["left_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
-        hr = rht.get("hbm_resident")
-        if hr:  # the same with the bytes coming from and going to HBM
-            out["rht_two_sided_frac_of_hbm_hbm_resident"] = {
-                "measured": round(hr["two_sided_effective_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
-            out["rht_right_pass_frac_of_hbm_hbm_resident"] = {
-                "measured": round(hr["right_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
-            out["rht_left_pass_frac_of_hbm_hbm_resident"] = {
-                "measured": round(hr["left_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+            "measured": round(hr["left_pass_GBps"] / HBM_PEAK_GBS, 3), "target": 0.60}
+        if "hbm_resident" in rht:
+            out["rht_two_sided_frac_of_hbm_cache_resident"] = {
+                "measured": round(rht["two_sided_effective_GBps"] / HBM_PEAK_GBS, 3), "target": None}
+            out["rht_right_pass_frac_of_hbm_cache_resident"] = {
+                "measured": round(rht["right_pass_GBps"] / HBM_PEAK_GBS, 3), "target": None}
+            out["rht_left_pass_frac_of_hbm_cache_resident"] = {
+                "measured": round(rht["left_pass_GBps"] / HBM_PEAK_GBS, 3), "target": None}
     f, ms = family_frac(["gemm:hessian"])
     if f is not None:
         out["hessian_frac_of_mfma"] = {"measured": round(f, 3), "target": 0.50, "ms": round(ms, 4)}
