@@ -178,7 +178,9 @@ __device__ __forceinline__ void tile_io(float (*T)[65], const float* gsrc, float
 // [0, PR): the rows prow0 + r of the matrix above the block; rows PR + i:
 // row i of the diagonal block, stored in full) restricted to the 16 columns
 // [16 qt, 16 qt + 16) of the block, in registers s[0..15]. Global reads and
-// writes go through LDS tiles so that they are coalesced.
+// the diagonal block's U go through LDS tiles so that they are coalesced; the
+// rows above write their X and U straight from the registers (64 contiguous
+// bytes per thread).
 // Column groups of 16 are processed from the last (gq = 3) to the first:
 //   leaf  - the wave holding the group's 16 diagonal rows (one 16-lane DPP
 //           row) factors the 16 x 16 sub-block S_gg = (I + U_gg) D_g
@@ -199,7 +201,6 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
   constexpr int NB = 64, ROWS = PR + NB, NT = 4 * ROWS;
   __shared__ float tile[NB][65];   // diagonal block (upper triangle), later U's diagonal block
   __shared__ float ptile[PR][65];  // rows above, later their U
-  __shared__ float xtile[PR][65];  // X of the rows above
   __shared__ __align__(16) float Xs[ROWS][20];
   __shared__ __align__(16) float Us[NB][16];
   // column l of U_gg (rows j < l), packed: float4 slots ut_off(l) .. + ceil(l/4)
@@ -220,6 +221,8 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
   const int di = r - PR;  // row of the diagonal block (diagonal rows only)
 
   const bool vin = (w == NB) && (lds_ % 4 == 0) && ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+  const bool vout = (w == NB) && (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
+  const bool vx = (w == NB) && (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(Xp) & 15) == 0);
   tile_io<NT, NB, true>(tile, src + k0 * lds_ + k0, nullptr, lds_, w, w, vin);
   tile_io<NT, PR, true>(ptile, src + prow0 * lds_ + k0, nullptr, lds_, npan, w, vin);
   if (t == 0) bad_sh = -1;
@@ -373,9 +376,18 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           x4[v] = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
-        if (is_panel) {
+        if (is_panel) {  // X of this row straight from the registers (64 bytes)
+          float* xr = Xp + (prow0 + r) * ldx + c0;
+          if (vx) {
+            float4* x4g = reinterpret_cast<float4*>(xr);
 #pragma unroll
-          for (int l = 0; l < 16; ++l) xtile[r][c0 + l] = s[l];
+            for (int v = 0; v < 4; ++v)
+              x4g[v] = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+          } else {
+#pragma unroll
+            for (int l = 0; l < 16; ++l)
+              if (c0 + l < w) xr[l] = s[l];
+          }
         }
         if constexpr (G == 1) {
 #pragma unroll
@@ -448,10 +460,22 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
     }
   }
 
-  // ---- outputs through the LDS tiles
+  // ---- outputs: the rows above straight from the registers (16 columns,
+  // 64 bytes, per thread); the diagonal block through its LDS tile
   if (is_panel) {
+    if (live) {
+      float* ur = U + (prow0 + r) * n + k0 + 16 * qt;
+      if (vout) {
+        float4* u4 = reinterpret_cast<float4*>(ur);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) ptile[r][16 * qt + m] = s[m];
+        for (int v = 0; v < 4; ++v)
+          u4[v] = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (16 * qt + m < w) ur[m] = s[m];
+      }
+    }
   } else if (blockIdx.x == 0) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
@@ -460,12 +484,8 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
       tile[di][c] = up ? s[m] : 0.f;
     }
   }
-  __syncthreads();
-  const bool vout = (w == NB) && (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
-  const bool vx = (w == NB) && (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(Xp) & 15) == 0);
-  tile_io<NT, PR, false>(ptile, nullptr, U + prow0 * n + k0, n, npan, w, vout);
-  tile_io<NT, PR, false>(xtile, nullptr, Xp + prow0 * ldx, ldx, npan, w, vx);
   if (blockIdx.x == 0) {
+    __syncthreads();
     tile_io<NT, NB, false>(tile, nullptr, U + k0 * n + k0, n, w, w, vout);
     if (t < w) {
 #pragma unroll
