@@ -177,10 +177,10 @@ __device__ __forceinline__ void tile_io(float (*T)[65], const float* gsrc, float
 // Layout: thread t = ROWS * qt + r holds row r of the tall panel (rows
 // [0, PR): the rows prow0 + r of the matrix above the block; rows PR + i:
 // row i of the diagonal block, stored in full) restricted to the 16 columns
-// [16 qt, 16 qt + 16) of the block, in registers s[0..15]. Global reads and
-// the diagonal block's U go through LDS tiles so that they are coalesced; the
-// rows above write their X and U straight from the registers (64 contiguous
-// bytes per thread).
+// [16 qt, 16 qt + 16) of the block, in registers s[0..15]. The diagonal block
+// is read and its U written through an LDS tile (coalesced, and its lower
+// triangle taken from the upper one); the rows above are read and their X
+// and U written straight from the registers (64 contiguous bytes per thread).
 // Column groups of 16 are processed from the last (gq = 3) to the first:
 //   leaf  - the wave holding the group's 16 diagonal rows (one 16-lane DPP
 //           row) factors the 16 x 16 sub-block S_gg = (I + U_gg) D_g
@@ -200,7 +200,6 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
                                                                   int64_t ldx, int32_t* info) {
   constexpr int NB = 64, ROWS = PR + NB, NT = 4 * ROWS;
   __shared__ float tile[NB][65];   // diagonal block (upper triangle), later U's diagonal block
-  __shared__ float ptile[PR][65];  // rows above, later their U
   __shared__ __align__(16) float Xs[ROWS][20];
   __shared__ __align__(16) float Us[NB][16];
   // column l of U_gg (rows j < l), packed: float4 slots ut_off(l) .. + ceil(l/4)
@@ -224,23 +223,36 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
   const bool vout = (w == NB) && (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(U) & 15) == 0);
   const bool vx = (w == NB) && (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(Xp) & 15) == 0);
   tile_io<NT, NB, true>(tile, src + k0 * lds_ + k0, nullptr, lds_, w, w, vin);
-  tile_io<NT, PR, true>(ptile, src + prow0 * lds_ + k0, nullptr, lds_, npan, w, vin);
+  float s[16];
+  if (is_panel) {  // (uniform per wave) the row's 16 columns straight into registers
+    const float* ar = src + (prow0 + r) * lds_ + k0 + 16 * qt;
+    if (live && vin) {
+      const float4* a4 = reinterpret_cast<const float4*>(ar);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 x = a4[v];
+        s[4 * v + 0] = x.x;
+        s[4 * v + 1] = x.y;
+        s[4 * v + 2] = x.z;
+        s[4 * v + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) s[m] = (live && 16 * qt + m < w) ? ar[m] : 0.f;
+    }
+  }
   if (t == 0) bad_sh = -1;
   __syncthreads();
-  float s[16];
-  {
-    // branch-free: every candidate is read (indices clamped), then selected
-    const int rp = is_panel ? r : 0;
-    const int dr = is_panel ? 0 : di;
+  if (!is_panel) {
+    // the diagonal block from its tile (upper triangle stored; identity past w)
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       const int c = 16 * qt + m;
-      const float vp = ptile[rp][c];
-      const float va = tile[dr][c];
-      const float vb = tile[c][dr];
-      float vd = (dr <= c) ? va : vb;
-      vd = (dr >= w || c >= w) ? (dr == c ? 1.f : 0.f) : vd;
-      s[m] = is_panel ? vp : vd;
+      const float va = tile[di][c];
+      const float vb = tile[c][di];
+      float vd = (di <= c) ? va : vb;
+      vd = (di >= w || c >= w) ? (di == c ? 1.f : 0.f) : vd;
+      s[m] = vd;
     }
   }
 
