@@ -87,3 +87,24 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
     assert d["read_bytes_per_launch"] == pytest.approx(200.0 * 2 * 1024)
     assert d["write_bytes_per_launch"] == pytest.approx(50.0 * 1024)
     assert d["source"] == "ldl.hip" and len(d["source_sha"]) == 16
+
+
+def test_rht_targets_use_the_hbm_resident_rates():
+    """The RHT targets divide the HBM-resident rates by the HBM peak; the
+    back-to-back (cache-resident) rates are reported beside them without a
+    target, and without HBM-resident figures the cache-resident ones stand in."""
+    class Cfg:
+        m = n = 4096
+
+    peak = bench.HBM_PEAK_GBS
+    hot = {"right_pass_GBps": 0.62 * peak, "left_pass_GBps": 0.56 * peak,
+           "two_sided_effective_GBps": 0.60 * peak}
+    cold = {"right_pass_GBps": 0.63 * peak, "left_pass_GBps": 0.50 * peak,
+            "two_sided_effective_GBps": 0.64 * peak}
+    t = bench.north_star_targets({}, {}, dict(hot, hbm_resident=cold), Cfg)
+    assert t["rht_two_sided_frac_of_hbm"] == {"measured": 0.64, "target": 0.60, "meets": True}
+    assert t["rht_left_pass_frac_of_hbm"] == {"measured": 0.5, "target": 0.60, "meets": False}
+    assert t["rht_left_pass_frac_of_hbm_cache_resident"] == {"measured": 0.56, "target": None}
+    t = bench.north_star_targets({}, {}, hot, Cfg)
+    assert t["rht_right_pass_frac_of_hbm"]["measured"] == 0.62
+    assert "rht_right_pass_frac_of_hbm_cache_resident" not in t
