@@ -42,6 +42,23 @@ __global__ void copy_matrix_kernel(const float* s, int64_t lds, float* d, int64_
     d[r * ldd + c] = s[r * lds + c];
 }
 
+// Row i of an n x n matrix: zeros in the columns [0, bs floor(i / bs)), the
+// part left of its diagonal block. One work-group per row; float4 stores when
+// the rows are 16-byte aligned.
+__global__ __launch_bounds__(256) void fill_lower_blocks_kernel(float* p, int64_t n, int64_t ld,
+                                                                int64_t bs, bool vec) {
+  const int64_t i = blockIdx.x;
+  const int64_t cnt = bs * (i / bs);
+  float* row = p + i * ld;
+  if (vec) {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t c = 4 * int64_t(threadIdx.x); c < cnt; c += 1024)
+      *reinterpret_cast<float4*>(row + c) = z;
+  } else {
+    for (int64_t c = threadIdx.x; c < cnt; c += 256) row[c] = 0.f;
+  }
+}
+
 dim3 grid2d(int64_t rows, int64_t cols) {
   int64_t gx = cdiv(cols, 1024);
   if (gx > 64) gx = 64;
@@ -49,6 +66,14 @@ dim3 grid2d(int64_t rows, int64_t cols) {
 }
 
 }  // namespace
+
+quip_status fill_lower_blocks(float* p, int64_t n, int64_t ld, int64_t bs, hipStream_t s) {
+  if (n <= bs) return QUIP_OK;
+  const bool vec = ld % 4 == 0 && bs % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+  return timed_launch("fill_lower_blocks", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+    QUIP_KERNEL(fill_lower_blocks_kernel, dim3(unsigned(n)), dim3(256), 0, s, p, n, ld, bs, vec);
+  });
+}
 
 quip_status fill_f32(float* p, int64_t count, float v, hipStream_t s) {
   if (count <= 0) return QUIP_OK;
