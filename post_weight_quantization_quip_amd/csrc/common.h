@@ -200,8 +200,10 @@ quip_status gemm(const GemmArgs& a, hipStream_t stream);
 // ---------------------------------------------------------------- misc kernels (misc.hip)
 
 quip_status fill_f32(float* p, int64_t count, float v, hipStream_t stream);
-// zeros in row i, columns [0, bs floor(i / bs)) of an n x n matrix
-quip_status fill_lower_blocks(float* p, int64_t n, int64_t ld, int64_t bs, hipStream_t stream);
+// zeros in row i, columns [0, bs floor(i / bs)) of an n x n matrix, and in
+// *word when word is not null
+quip_status fill_lower_blocks(float* p, int64_t n, int64_t ld, int64_t bs, int32_t* word,
+                              hipStream_t stream);
 quip_status fill_matrix(float* p, int64_t rows, int64_t cols, int64_t ld, float v,
                         hipStream_t stream);
 quip_status sub_matrix(const float* a, const float* b, float* out, int64_t rows, int64_t cols,

@@ -528,9 +528,9 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
   if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldl: workspace too small");
 
   // the kernels write every entry of U from each diagonal block's rows up
-  // (zeros below the diagonal inside the block); the rest is zero
-  QUIP_TRY(fill_lower_blocks(U, n, n, NB, s));
-  QUIP_TRY(fill_f32(reinterpret_cast<float*>(info), 1, 0.f, s));  // info <- 0 (bit pattern)
+  // (zeros below the diagonal inside the block); the rest is zero, and so is
+  // info, in the same launch
+  QUIP_TRY(fill_lower_blocks(U, n, n, NB, info, s));
 
   // Outer blocks of NO columns from the last to the first; inside each, blocks
   // of NB columns (factor + rows above in one kernel, then the update of the

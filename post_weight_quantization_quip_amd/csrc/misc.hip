@@ -46,8 +46,10 @@ __global__ void copy_matrix_kernel(const float* s, int64_t lds, float* d, int64_
 // part left of its diagonal block. One work-group per row; float4 stores when
 // the rows are 16-byte aligned.
 __global__ __launch_bounds__(256) void fill_lower_blocks_kernel(float* p, int64_t n, int64_t ld,
-                                                                int64_t bs, bool vec) {
+                                                                int64_t bs, bool vec,
+                                                                int32_t* word) {
   const int64_t i = blockIdx.x;
+  if (word && i == 0 && threadIdx.x == 0) *word = 0;
   const int64_t cnt = bs * (i / bs);
   float* row = p + i * ld;
   if (vec) {
@@ -67,11 +69,13 @@ dim3 grid2d(int64_t rows, int64_t cols) {
 
 }  // namespace
 
-quip_status fill_lower_blocks(float* p, int64_t n, int64_t ld, int64_t bs, hipStream_t s) {
-  if (n <= bs) return QUIP_OK;
+quip_status fill_lower_blocks(float* p, int64_t n, int64_t ld, int64_t bs, int32_t* word,
+                              hipStream_t s) {
+  if (n <= 0) return QUIP_OK;
   const bool vec = ld % 4 == 0 && bs % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
   return timed_launch("fill_lower_blocks", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(fill_lower_blocks_kernel, dim3(unsigned(n)), dim3(256), 0, s, p, n, ld, bs, vec);
+    QUIP_KERNEL(fill_lower_blocks_kernel, dim3(unsigned(n)), dim3(256), 0, s, p, n, ld, bs, vec,
+                word);
   });
 }
 
