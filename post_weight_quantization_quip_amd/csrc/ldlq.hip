@@ -402,7 +402,8 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
   if (rowloss) {
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-    if (live && j == 0) rowloss[row] += lsum;  // one work-group per row per launch
+    // one work-group per row per launch; the sweep at column 0 starts the sum
+    if (live && j == 0) rowloss[row] = (s0 == 0 ? 0.0 : rowloss[row]) + lsum;
   }
 }
 
@@ -1591,7 +1592,8 @@ quip_status ldlq_run(const float* W, int64_t m, int64_t n, int64_t ldw, const fl
   float hostf[64];
   // per-row proxy loss: the caller's buffer, or the workspace when only the total is wanted
   double* rl = row_loss ? row_loss : (loss ? rl_ws : nullptr);
-  if (rl && c.fits()) QUIP_TRY(fill_f64(rl, m, 0.0, s));
+  // the grid path's first sweep starts every row's sum itself
+  if (rl && c.fits() && (q.kind != QUIP_Q_UNIFORM || n == 0)) QUIP_TRY(fill_f64(rl, m, 0.0, s));
 
   if (q.kind == QUIP_Q_UNIFORM) {
     if (!c.fits()) return fail(QUIP_ERR_WORKSPACE, "quip_ldlq: workspace too small");
