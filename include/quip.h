@@ -112,7 +112,7 @@ quip_status quip_hessian(const float* X, int64_t N, int64_t n, int64_t ldx, floa
  * quip_hessian_finalize -- H <- H / N_total + alpha * mean(diag(H / N_total)) * I
  *   ([QuIP] "Experiments / Methods": damping for numerical stability).
  *   In place on the n x n matrix H (leading dim ldh). alpha >= 0.
- *   ws: device workspace of at least 256 bytes (holds the trace).
+ *   ws: device workspace of at least 256 bytes (holds partial traces).
  * Errors: QUIP_ERR_ARG (null H, N_total <= 0, alpha < 0 or not finite),
  *   QUIP_ERR_WORKSPACE.
  */

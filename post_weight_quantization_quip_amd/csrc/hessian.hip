@@ -10,27 +10,33 @@
 namespace quip {
 namespace {
 
-__global__ void trace_kernel(const float* H, int64_t n, int64_t ldh, double* out) {
-  __shared__ double part[16];
+// Partial traces: work-group p of TRACE_PARTS sums the diagonal entries of
+// its contiguous slice of rows and writes out[p] (the finalize sums the parts
+// in a fixed order).
+constexpr int TRACE_PARTS = 32;
+static_assert(TRACE_PARTS * sizeof(double) <= 256, "the parts fit the finalize's 256-byte workspace");
+__global__ __launch_bounds__(256) void trace_kernel(const float* H, int64_t n, int64_t ldh,
+                                                    double* out) {
+  __shared__ double part[4];
+  const int64_t per = (n + TRACE_PARTS - 1) / TRACE_PARTS;
+  const int64_t i0 = int64_t(blockIdx.x) * per;
+  const int64_t i1 = (i0 + per < n) ? i0 + per : n;
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += double(H[i * ldh + i]);
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) s += double(H[i * ldh + i]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int w = 0; w < int(blockDim.x >> 6); ++w) t += part[w];
-    *out = t;
-  }
+  if (threadIdx.x == 0) out[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// One row per work-group; float4 accesses when every row start is 16-byte
-// aligned.
 __global__ __launch_bounds__(256) void finalize_kernel(float* H, int64_t n, int64_t ldh,
-                                                       const double* trace, double inv_n_total,
-                                                       double alpha, bool vec) {
-  const float shift = float(alpha * (*trace) * inv_n_total / double(n));
+                                                       const double* trace_parts,
+                                                       double inv_n_total, double alpha, bool vec) {
+  double trace = 0.0;
+#pragma unroll
+  for (int p = 0; p < TRACE_PARTS; ++p) trace += trace_parts[p];
+  const float shift = float(alpha * trace * inv_n_total / double(n));
   const float scale = float(inv_n_total);
   const int64_t r = blockIdx.x;
   float* row = H + r * ldh;
@@ -87,7 +93,7 @@ quip_status hessian_accumulate(const float* X, int64_t N, int64_t n, int64_t ldx
 quip_status hessian_finalize(float* H, int64_t n, int64_t ldh, int64_t N_total, float alpha,
                              double* scratch, hipStream_t s) {
   QUIP_TRY(timed_launch("trace_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(trace_kernel, dim3(1), dim3(1024), 0, s, H, n, ldh, scratch);
+    QUIP_KERNEL(trace_kernel, dim3(TRACE_PARTS), dim3(256), 0, s, H, n, ldh, scratch);
   }));
   const bool vec = aligned16(H) && ldh % 4 == 0 && n % 4 == 0;
   return timed_launch("finalize_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
