@@ -1268,18 +1268,23 @@ __global__ __launch_bounds__(256) void e8_argmin_kernel(E8Book book, const float
 }
 
 // loss = sum of the row losses, in a fixed order (one work-group).
-__global__ __launch_bounds__(256) void sum_rows_kernel(const double* __restrict__ rowloss,
-                                                       int64_t m, double* __restrict__ out) {
-  __shared__ double part[256];
+// Sum of the per-row losses: 1024 threads, each a strided slice, then wave
+// sums by shuffles and the 16 wave sums added in a fixed order.
+__global__ __launch_bounds__(1024) void sum_rows_kernel(const double* __restrict__ rowloss,
+                                                        int64_t m, double* __restrict__ out) {
+  __shared__ double part[16];
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < m; i += 256) acc += rowloss[i];
-  part[threadIdx.x] = acc;
+  for (int64_t i = threadIdx.x; i < m; i += 1024) acc += rowloss[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if (int(threadIdx.x) < h) part[threadIdx.x] += part[threadIdx.x + h];
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += part[w];
+    *out = t;
   }
-  if (threadIdx.x == 0) *out = part[0];
 }
 
 __global__ void fill_u64_kernel(unsigned long long* p, int64_t count, unsigned long long v) {
@@ -1308,7 +1313,7 @@ void host_e8_candidates(int ncand, float* out) {
 quip_status finish_loss(const double* rl, int64_t m, double* loss, hipStream_t s) {
   if (!loss) return QUIP_OK;
   return timed_launch("sum_rows_kernel", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-    QUIP_KERNEL(sum_rows_kernel, dim3(1), dim3(256), 0, s, rl, m, loss);
+    QUIP_KERNEL(sum_rows_kernel, dim3(1), dim3(1024), 0, s, rl, m, loss);
   });
 }
 
