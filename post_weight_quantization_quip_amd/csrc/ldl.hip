@@ -507,6 +507,54 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
   }
 }
 
+typedef float ldl_f32x4 __attribute__((ext_vector_type(4)));
+
+// Inner update of an outer block with K = 64: C[m][c] = Cin[m][c] -
+// sum_k X[m][k] U[c][k] for m < M, c < N (M, N multiples of 32). One
+// work-group of four waves per 32 x 32 tile, each wave a 16 x 16 block on
+// v_mfma_f32_16x16x4f32 with its operands straight from memory: lane
+// (i, h) = (lane % 16, lane / 16) loads the 16 consecutive k of quarter h of
+// row i of X and of U (step t takes k = 16 h + t), and holds C's rows 4 h + r
+// of column i. Two accumulators (even and odd steps) halve the dependent
+// chain. No LDS and no barrier: the product is too small for operand reuse
+// to pay, and the latency of its few steps is what it costs.
+__global__ __launch_bounds__(256) void ldl_inner_kernel(const float* __restrict__ X, int64_t ldx,
+                                                        const float* __restrict__ Ub, int64_t ldu,
+                                                        const float* Cin, int64_t ldcin, float* C,
+                                                        int64_t ldc, int tiles_n) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = lane & 15, h = lane >> 4;
+  const int tm = int(blockIdx.x) / tiles_n, tn = int(blockIdx.x) % tiles_n;
+  const int64_t m0 = int64_t(tm) * 32 + (wave >> 1) * 16;
+  const int64_t n0 = int64_t(tn) * 32 + (wave & 1) * 16;
+  const float4* xa = reinterpret_cast<const float4*>(X + (m0 + i) * ldx + 16 * h);
+  const float4* ub = reinterpret_cast<const float4*>(Ub + (n0 + i) * ldu + 16 * h);
+  float a[16], b[16];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float4 p = xa[v], q = ub[v];
+    a[4 * v] = p.x;
+    a[4 * v + 1] = p.y;
+    a[4 * v + 2] = p.z;
+    a[4 * v + 3] = p.w;
+    b[4 * v] = q.x;
+    b[4 * v + 1] = q.y;
+    b[4 * v + 2] = q.z;
+    b[4 * v + 3] = q.w;
+  }
+  float cin[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cin[r] = Cin[(m0 + 4 * h + r) * ldcin + n0 + i];
+  ldl_f32x4 e = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 16; t += 2) {
+    e = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], e, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t + 1], b[t + 1], o, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) C[(m0 + 4 * h + r) * ldc + n0 + i] = cin[r] - (e[r] + o[r]);
+}
+
 }  // namespace
 
 size_t ldl_workspace_bytes(int64_t n) {
@@ -565,7 +613,18 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
       }, 2.0 / 3.0 * wd * wd * wd + kd * (wd * wd + wd),
          4.0 * ((kd + wd) * wd + 2.0 * kd * wd + wd * wd + wd * g)));
       if (k0 == 0) break;
-      if (b > 0) {
+      if (b > 0 && w == NB && k0 % 32 == 0 && (k0 - o0) % 32 == 0 && NO % 4 == 0 &&
+          n % 4 == 0 && aligned16(Xp) && aligned16(U)) {
+        // the outer block's columns left of this one: A[:k0, o0:k0] -= X U[o0:k0, blk]^T
+        const int tiles_n = int((k0 - o0) / 32);
+        const double md = double(k0), nd = double(k0 - o0);
+        QUIP_TRY(timed_launch("gemm:ldl_inner", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+          QUIP_KERNEL(ldl_inner_kernel, dim3(unsigned((k0 / 32) * tiles_n)), dim3(256), 0, s,
+                      Xp + (k0 - o0), int64_t(NO), U + o0 * n + k0, n, src + o0, lsrc, Aw + o0,
+                      n, tiles_n);
+        }, 2.0 * md * nd * NB, 4.0 * (md * NB + nd * NB + 2.0 * md * nd)));
+        aw_outer = true;
+      } else if (b > 0) {
         // the outer block's columns left of this one: A[:k0, o0:k0] -= X U[o0:k0, blk]^T
         GemmArgs t;
         t.M = k0;
