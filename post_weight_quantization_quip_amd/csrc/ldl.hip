@@ -509,29 +509,45 @@ __global__ __launch_bounds__(4 * (PR + 64)) void ldl_block_kernel(const float* s
 
 typedef float ldl_f32x4 __attribute__((ext_vector_type(4)));
 
-// Inner update of an outer block with K = 64: C[m][c] = Cin[m][c] -
-// sum_k X[m][k] U[c][k] for m < M, c < N (M, N multiples of 32). One
-// work-group of four waves per 32 x 32 tile, each wave a 16 x 16 block on
-// v_mfma_f32_16x16x4f32 with its operands straight from memory: lane
-// (i, h) = (lane % 16, lane / 16) loads the 16 consecutive k of quarter h of
-// row i of X and of U (step t takes k = 16 h + t), and holds C's rows 4 h + r
-// of column i. Two accumulators (even and odd steps) halve the dependent
-// chain. No LDS and no barrier: the product is too small for operand reuse
-// to pay, and the latency of its few steps is what it costs.
-__global__ __launch_bounds__(256) void ldl_inner_kernel(const float* __restrict__ X, int64_t ldx,
-                                                        const float* __restrict__ Ub, int64_t ldu,
-                                                        const float* Cin, int64_t ldcin, float* C,
-                                                        int64_t ldc, int tiles_n) {
+// Small trailing updates straight on the matrix cores: C[m][c] = Cin[m][c] -
+// sum_k X[m][k] U[c][k], with K = 64 (an outer block's inner update) or
+// K = 256 (the update of a small leading block, upper tiles only: tile row <=
+// tile column, row-major). One work-group of four waves per 32 x 32 tile,
+// each wave a 16 x 16 block on v_mfma_f32_16x16x4f32 with its operands
+// straight from memory: lane (i, h) = (lane % 16, lane / 16) loads the K / 4
+// consecutive k of quarter h of row i of X and of U (step t takes
+// k = h K / 4 + t), and holds C's rows 4 h + r of column i. Two accumulators
+// (even and odd steps) halve the dependent chain. No LDS and no barrier:
+// these products are too small for operand reuse to pay, and the latency of
+// their few steps is what they cost.
+template <int K, bool UPPER>
+__global__ __launch_bounds__(256) void ldl_update_kernel(const float* __restrict__ X, int64_t ldx,
+                                                         const float* __restrict__ Ub, int64_t ldu,
+                                                         const float* Cin, int64_t ldcin, float* C,
+                                                         int64_t ldc, int tiles_n) {
+  constexpr int KQ = K / 4;  // steps, and k per lane and quarter
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = lane & 15, h = lane >> 4;
-  const int tm = int(blockIdx.x) / tiles_n, tn = int(blockIdx.x) % tiles_n;
+  int tm, tn;
+  if (UPPER) {  // row-major over the upper tiles of a tiles_n x tiles_n grid
+    int rem = int(blockIdx.x), r = 0;
+    while (rem >= tiles_n - r) {
+      rem -= tiles_n - r;
+      ++r;
+    }
+    tm = r;
+    tn = r + rem;
+  } else {
+    tm = int(blockIdx.x) / tiles_n;
+    tn = int(blockIdx.x) % tiles_n;
+  }
   const int64_t m0 = int64_t(tm) * 32 + (wave >> 1) * 16;
   const int64_t n0 = int64_t(tn) * 32 + (wave & 1) * 16;
-  const float4* xa = reinterpret_cast<const float4*>(X + (m0 + i) * ldx + 16 * h);
-  const float4* ub = reinterpret_cast<const float4*>(Ub + (n0 + i) * ldu + 16 * h);
-  float a[16], b[16];
+  const float4* xa = reinterpret_cast<const float4*>(X + (m0 + i) * ldx + KQ * h);
+  const float4* ub = reinterpret_cast<const float4*>(Ub + (n0 + i) * ldu + KQ * h);
+  float a[KQ], b[KQ];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < KQ / 4; ++v) {
     const float4 p = xa[v], q = ub[v];
     a[4 * v] = p.x;
     a[4 * v + 1] = p.y;
@@ -547,7 +563,7 @@ __global__ __launch_bounds__(256) void ldl_inner_kernel(const float* __restrict_
   for (int r = 0; r < 4; ++r) cin[r] = Cin[(m0 + 4 * h + r) * ldcin + n0 + i];
   ldl_f32x4 e = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < 16; t += 2) {
+  for (int t = 0; t < KQ; t += 2) {
     e = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], e, 0, 0, 0);
     o = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t + 1], b[t + 1], o, 0, 0, 0);
   }
@@ -623,7 +639,7 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
         const int tiles_n = int((k0 - o0) / 32);
         const double md = double(k0), nd = double(k0 - o0);
         QUIP_TRY(timed_launch("gemm:ldl_inner", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
-          QUIP_KERNEL(ldl_inner_kernel, dim3(unsigned((k0 / 32) * tiles_n)), dim3(256), 0, s,
+          QUIP_KERNEL((ldl_update_kernel<64, false>), dim3(unsigned((k0 / 32) * tiles_n)), dim3(256), 0, s,
                       Xp + (k0 - o0), int64_t(NO), U + o0 * n + k0, n, src + o0, lsrc, Aw + o0,
                       n, tiles_n);
         }, 2.0 * md * nd * NB, 4.0 * (md * NB + nd * NB + 2.0 * md * nd)));
@@ -654,6 +670,20 @@ quip_status ldl_factor(const float* H, int64_t n, int64_t ldh, int g, float* U, 
     // trailing update of the leading o0 x o0 block (upper tiles), K = outer width
     const float* src = aw_lead ? Aw : H;
     const int64_t lsrc = aw_lead ? n : ldh;
+    const int64_t tu = o0 / 32;  // 32 x 32 tiles per side
+    if (o1 - o0 == 256 && o0 % 32 == 0 && NO % 4 == 0 && n % 4 == 0 && aligned16(Xp) &&
+        aligned16(U) && tu * (tu + 1) / 2 <= 2 * int64_t(device_cus())) {
+      // a small leading block (o0 <= 992 here): the direct kernel, 6-7 us
+      // against 13 us for the LDS-tiled product, whose eight K steps each wait
+      // on their loads; larger grids read too much from L2 without LDS reuse
+      const double od = double(o0);
+      QUIP_TRY(timed_launch("gemm:ldl_outer", s, [&](hipEvent_t ev_start_, hipEvent_t ev_stop_) {
+        QUIP_KERNEL((ldl_update_kernel<256, true>), dim3(unsigned(tu * (tu + 1) / 2)), dim3(256),
+                    0, s, Xp, int64_t(NO), U + o0, n, src, lsrc, Aw, n, int(tu));
+      }, od * (od + 32.0) * 256.0, 4.0 * (2.0 * od * 256.0 + od * (od + 32.0))));
+      aw_lead = true;
+      continue;
+    }
     GemmArgs t;
     t.M = o0;
     t.N = o0;
