@@ -652,7 +652,7 @@ def cpu_baseline(cfg_name: str, rows: int) -> dict:
     }
 
 
-def north_star_targets(kernels: dict, phases: dict, rht: dict, cfg) -> dict:
+def pass_targets(kernels: dict, phases: dict, rht: dict, cfg) -> dict:
     """The phase-level figures the pass is held to, each next to its target:
     the two-sided random-sign Hadamard transform against the HBM peak (>= 60 %,
     on matrices read from and written to HBM; the cache-resident figures are
@@ -875,7 +875,7 @@ def main():
         del mats
 
     attainable = attainable_bench(Q, dev, timed)
-    targets = north_star_targets(kernels, phases, rht, cfg)
+    targets = pass_targets(kernels, phases, rht, cfg)
 
     # beside the pass: Gaussian-source VQ, the inference product, the variants
     gaussian_vq, inference, variants, tcq, e8c, allcfg = {}, {}, {}, {}, {}, {}

@@ -101,10 +101,10 @@ def test_rht_targets_use_the_hbm_resident_rates():
            "two_sided_effective_GBps": 0.60 * peak}
     cold = {"right_pass_GBps": 0.63 * peak, "left_pass_GBps": 0.50 * peak,
             "two_sided_effective_GBps": 0.64 * peak}
-    t = bench.north_star_targets({}, {}, dict(hot, hbm_resident=cold), Cfg)
+    t = bench.pass_targets({}, {}, dict(hot, hbm_resident=cold), Cfg)
     assert t["rht_two_sided_frac_of_hbm"] == {"measured": 0.64, "target": 0.60, "meets": True}
     assert t["rht_left_pass_frac_of_hbm"] == {"measured": 0.5, "target": 0.60, "meets": False}
     assert t["rht_left_pass_frac_of_hbm_cache_resident"] == {"measured": 0.56, "target": None}
-    t = bench.north_star_targets({}, {}, hot, Cfg)
+    t = bench.pass_targets({}, {}, hot, Cfg)
     assert t["rht_right_pass_frac_of_hbm"]["measured"] == 0.62
     assert "rht_right_pass_frac_of_hbm_cache_resident" not in t
