@@ -370,25 +370,38 @@ __global__ __launch_bounds__(256) void ldlq_sweep_kernel(
         lsum += double(Ds[c]) * (r * r);
       }
     }
-    // rank-16 update of the later chunks, then shift them down by one
+    // rank-16 update of the NR = NT - 1 - tk later chunks, then shift them
+    // down by one. NR is made a compile-time count so that the NR chains go
+    // interleaved (one LDS read of every chain, then four fmas of every chain,
+    // per float4 of coefficients); each chain keeps its own order of fmas.
+    auto rank_update = [&](auto nr_tag) {
+      constexpr int NR = decltype(nr_tag)::value;
 #pragma unroll
-    for (int i = 0; i < NT - 1; ++i) {
-      if (i < NT - 1 - tk) {
-        const int cc = c + 16 * (i + 1);
-        const float4* up = reinterpret_cast<const float4*>(Ut + cc * UP);
-        const int sw = (cc >> 2) & 7;
-        float t = ar[i];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4 x = up[((4 * tk + v) & 7) ^ sw];
-          t = fmaf(e16[4 * v + 0], x.x, t);
-          t = fmaf(e16[4 * v + 1], x.y, t);
-          t = fmaf(e16[4 * v + 2], x.z, t);
-          t = fmaf(e16[4 * v + 3], x.w, t);
-        }
-        ar[i] = t;
+      for (int v = 0; v < 4; ++v) {
+        float4 x[NR];
+        static_for<NR>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          const int cc = c + 16 * (i + 1);
+          const float4* up = reinterpret_cast<const float4*>(Ut + cc * UP);
+          x[i] = up[((4 * tk + v) & 7) ^ ((cc >> 2) & 7)];
+        });
+        static_for<NR>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          float t = ar[i];
+          t = fmaf(e16[4 * v + 0], x[i].x, t);
+          t = fmaf(e16[4 * v + 1], x[i].y, t);
+          t = fmaf(e16[4 * v + 2], x[i].z, t);
+          t = fmaf(e16[4 * v + 3], x[i].w, t);
+          ar[i] = t;
+        });
       }
-    }
+    };
+    static_for<NT>([&](auto K) {
+      constexpr int NR = decltype(K)::value;
+      if constexpr (NR > 0) {
+        if (NR == NT - 1 - tk) rank_update(std::integral_constant<int, NR>{});
+      }
+    });
     if (NT > 1) {
       acc = ar[0];
 #pragma unroll
